@@ -1,0 +1,307 @@
+/*
+ * CPU oracle for the delayed-scaling FP8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this code.  It shares no source, header,
+ * table or helper with the GPU library, and the GPU library never calls it.
+ *
+ * Everything here is a plain, slow, single-threaded restatement of what the
+ * pages define, written so that it can be checked against them by eye:
+ *
+ *   - the OCP FP8 formats float8_e4m3fn and float8_e5m2 (the finfo table and
+ *     the worked cast table in "Accelerating PyTorch Training Workloads with
+ *     FP8 -- Part 2", section on PyTorch-native FP8 data types);
+ *   - the per-tensor amax and the amax-history "max" recipe with history
+ *     length 16 ("CPU Overhead of te.Linear FP8 Layers", the DelayedScaling
+ *     recipe in the reproduction script; "support delayed scaling of weight in
+ *     float8 all-gather", the amax / amax-history / scale buffers);
+ *   - the scale-inverse snapshot held by each FP8 tensor ("[PyTorch] Refactor
+ *     FP8 workspaces in linear modules", first motivation);
+ *   - the per-tensor-scaled FP8 matrix product with bias (the torch._scaled_mm
+ *     example of the Part 2 blog).
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   - the cast computes v = fp32(x) * scale as one IEEE fp32 multiply and
+ *     rounds v to FP8 with round-to-nearest-even and SATURATION: every finite
+ *     overflow and +-inf goes to +-max, NaN goes to sign|0x7F;
+ *   - amax is the maximum of |x| over the UNSCALED source, ordered by the
+ *     sign-cleared fp32 bit pattern (so a NaN dominates everything);
+ *   - the scale formula is the conventional one, not printed on the pages:
+ *     scale = fp8_max / (max(history) * 2^margin) in fp32, kept unchanged when
+ *     the history maximum is zero or not finite or the quotient is not a
+ *     finite positive number;
+ *   - the product is the exact sum of decoded FP8 products (accumulated here
+ *     in fp64), times both scale-inverses, plus bias, rounded once to the
+ *     output type.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+#define ORC_E4M3 0
+#define ORC_E5M2 1
+
+/* Field widths of the two OCP 8-bit formats (Part 2 blog: float8_e4m3fn has
+ * 3 mantissa bits, float8_e5m2 has 2). */
+typedef struct {
+    int ebits;
+    int mbits;
+    int bias;
+} orc_fmt;
+
+static int orc_get_fmt(int fmt, orc_fmt *f) {
+    if (fmt == ORC_E4M3) { f->ebits = 4; f->mbits = 3; f->bias = 7;  return 0; }
+    if (fmt == ORC_E5M2) { f->ebits = 5; f->mbits = 2; f->bias = 15; return 0; }
+    return -1;
+}
+
+/* Largest finite magnitude: E4M3 has no infinities and only S.1111.111 is NaN,
+ * so its largest finite code is 0x7E = 1.75 * 2^8 = 448; E5M2 keeps IEEE-style
+ * infinities, so its largest finite code is 0x7B = 1.75 * 2^15 = 57344. */
+double orc_fp8_max(int fmt) {
+    orc_fmt f;
+    if (orc_get_fmt(fmt, &f)) return NAN;
+    if (fmt == ORC_E4M3) return ldexp(1.75, 15 - f.bias);   /* exponent field 15 */
+    return ldexp(1.75, 30 - f.bias);                        /* exponent field 30 */
+}
+
+static uint8_t orc_max_code(int fmt) { return fmt == ORC_E4M3 ? 0x7E : 0x7B; }
+
+/* Value of an FP8 code, straight from the field definition. */
+double orc_fp8_decode(uint8_t code, int fmt) {
+    orc_fmt f;
+    if (orc_get_fmt(fmt, &f)) return NAN;
+    int s = code >> 7;
+    int e = (code >> f.mbits) & ((1 << f.ebits) - 1);
+    int m = code & ((1 << f.mbits) - 1);
+    int emax_field = (1 << f.ebits) - 1;
+    double v;
+    if (fmt == ORC_E4M3 && e == emax_field && m == (1 << f.mbits) - 1) return NAN;
+    if (fmt == ORC_E5M2 && e == emax_field) {
+        if (m != 0) return NAN;
+        return s ? -INFINITY : INFINITY;
+    }
+    if (e == 0)
+        v = ldexp((double)m, 1 - f.bias - f.mbits);              /* subnormal */
+    else
+        v = ldexp(1.0 + ldexp((double)m, -f.mbits), e - f.bias); /* normal */
+    return s ? -v : v;
+}
+
+/* Saturating round-to-nearest-even of an fp32 value to an FP8 code. */
+uint8_t orc_fp8_encode(float v, int fmt) {
+    orc_fmt f;
+    if (orc_get_fmt(fmt, &f)) return 0;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;
+    double a = fabs((double)v);
+    double maxval = orc_fp8_max(fmt);
+    if (a >= maxval) return sign | orc_max_code(fmt);            /* saturate */
+    if (a == 0.0) return sign;                                   /* signed zero */
+
+    int emin = 1 - f.bias;                  /* exponent of the smallest normal */
+    int ex;
+    frexp(a, &ex);                          /* a = g * 2^ex, g in [0.5, 1) */
+    int e = ex - 1;                         /* floor(log2(a)) */
+    if (e < emin) e = emin;                 /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, e - f.mbits);
+    double n = nearbyint(a / quantum);      /* exact division; ties to even */
+    double r = n * quantum;                 /* rounded magnitude */
+    if (r == 0.0) return sign;
+    if (r > maxval) return sign | orc_max_code(fmt);   /* cannot happen, kept for safety */
+
+    /* Re-encode the rounded magnitude. */
+    int rex;
+    frexp(r, &rex);
+    int re = rex - 1;
+    int efield, mfield;
+    if (re < emin) {                        /* subnormal: r = m * 2^(emin - mbits) */
+        efield = 0;
+        mfield = (int)ldexp(r, f.mbits - emin);
+    } else {
+        efield = re + f.bias;
+        mfield = (int)(ldexp(r, f.mbits - re) - ldexp(1.0, f.mbits));
+    }
+    return sign | (uint8_t)((efield << f.mbits) | mfield);
+}
+
+/* ---- bfloat16 <-> fp32 ------------------------------------------------ */
+
+static uint32_t orc_f32_bits(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float orc_bits_f32(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+/* bf16 is the top half of an fp32 pattern, so widening is exact. */
+float orc_bf16_to_f32(uint16_t b) { return orc_bits_f32((uint32_t)b << 16); }
+
+/* Round a double to the nearest bf16 (8 significant bits, fp32 exponent
+ * range with subnormals), ties to even; overflow to infinity. */
+uint16_t orc_f64_to_bf16(double x) {
+    if (isnan(x)) return signbit(x) ? 0xFFC0 : 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;
+    if (e < -126) e = -126;
+    double quantum = ldexp(1.0, e - 7);
+    double r = nearbyint(a / quantum) * quantum;
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;
+    /* r is representable in bf16, hence exactly in fp32. */
+    return sign | (uint16_t)(orc_f32_bits((float)r) >> 16);
+}
+
+/* ---- amax, cast, transpose ------------------------------------------- */
+
+/* Order of magnitudes used for amax: the fp32 pattern with the sign cleared,
+ * compared as an unsigned integer.  For non-NaN values this is the order of
+ * |x|; every NaN compares above +inf. */
+static uint32_t orc_abs_key(float x) { return orc_f32_bits(x) & 0x7FFFFFFFu; }
+
+static float orc_load_src(const void *x, int src, int64_t idx) {
+    if (src == 0) return orc_bf16_to_f32(((const uint16_t *)x)[idx]);
+    return ((const float *)x)[idx];
+}
+
+/*
+ * One cast of a row-major [rows, cols] source with leading dimension ld
+ * (elements) to FP8 with the given scale.  Writes q [rows, cols] and / or its
+ * transpose qt [cols, rows] (either may be NULL), folds |x| into *amax_inout
+ * and writes 1/scale to *scale_inv_out (either may be NULL).
+ * src: 0 = bf16, 1 = fp32.  Returns 0, or -1 for a bad argument.
+ */
+int orc_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
+                            int64_t ld, float scale, int fmt, uint8_t *q,
+                            uint8_t *qt, float *amax_inout, float *scale_inv_out) {
+    orc_fmt f;
+    if (orc_get_fmt(fmt, &f) || (src != 0 && src != 1) || rows < 0 || cols < 0 || ld < cols)
+        return -1;
+    uint32_t amax_key = amax_inout ? orc_abs_key(*amax_inout) : 0u;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            float xv = orc_load_src(x, src, r * ld + c);
+            uint32_t k = orc_abs_key(xv);
+            if (k > amax_key) amax_key = k;
+            float v = xv * scale;                  /* one fp32 multiply */
+            uint8_t code = orc_fp8_encode(v, fmt);
+            if (q) q[r * cols + c] = code;
+            if (qt) qt[c * rows + r] = code;
+        }
+    }
+    if (amax_inout) *amax_inout = orc_bits_f32(amax_key);
+    if (scale_inv_out) *scale_inv_out = 1.0f / scale;
+    return 0;
+}
+
+/* ---- amax history and scale update ----------------------------------- */
+
+/*
+ * Delayed-scaling update of T per-tensor records at once.
+ *   hist      [T, H]  amax history, newest first (hist[t*H + 0])
+ *   amax_cur  [T]     amax recorded since the last update; reset to 0 here
+ *   scale     [T]     quantisation scale used by the next casts
+ *   scale_inv [T]     1 / scale
+ *   fmt       [T]     0 = E4M3, 1 = E5M2 (selects fp8_max)
+ * algo 0 = "max" over the history window (the only algorithm the pages use).
+ * Returns 0, or -1 for a bad argument.
+ */
+int orc_scale_update(float *hist, float *amax_cur, float *scale, float *scale_inv,
+                     const uint8_t *fmt, int T, int H, int margin, int algo) {
+    if (T < 0 || H < 1 || algo != 0) return -1;
+    for (int t = 0; t < T; ++t) {
+        if (fmt[t] != ORC_E4M3 && fmt[t] != ORC_E5M2) return -1;
+    }
+    for (int t = 0; t < T; ++t) {
+        float *h = hist + (int64_t)t * H;
+        /* Roll the window by one and record the newest amax in front. */
+        for (int i = H - 1; i > 0; --i) h[i] = h[i - 1];
+        h[0] = amax_cur[t];
+        /* "max" over the window, in the same order as amax itself. */
+        uint32_t best = orc_abs_key(h[0]);
+        float m = h[0];
+        for (int i = 1; i < H; ++i) {
+            uint32_t k = orc_abs_key(h[i]);
+            if (k > best) { best = k; m = h[i]; }
+        }
+        m = fabsf(m);
+        if (isfinite(m) && m > 0.0f) {
+            float fp8_max = (float)orc_fp8_max(fmt[t]);
+            float denom = ldexpf(m, margin);
+            float s = fp8_max / denom;             /* fp32, correctly rounded */
+            if (isfinite(s) && s > 0.0f) scale[t] = s;
+        }
+        scale_inv[t] = 1.0f / scale[t];
+        amax_cur[t] = 0.0f;
+    }
+    return 0;
+}
+
+/* ---- scaled FP8 matrix product --------------------------------------- */
+
+static double orc_bias_at(const uint16_t *bias, int64_t j) {
+    return bias ? (double)orc_bf16_to_f32(bias[j]) : 0.0;
+}
+
+static void orc_store_out(void *out, int out_kind, int64_t idx, double y) {
+    if (out_kind == 0)
+        ((uint16_t *)out)[idx] = orc_f64_to_bf16(y);
+    else
+        ((float *)out)[idx] = (float)y;
+}
+
+/* One output of C = A . B^T with A [*, K] (lda), B [*, K] (ldb), both FP8. */
+static double orc_dot(const uint8_t *A, int fa, int64_t lda, const uint8_t *B,
+                      int fb, int64_t ldb, int64_t i, int64_t j, int64_t K) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += orc_fp8_decode(A[i * lda + k], fa) * orc_fp8_decode(B[j * ldb + k], fb);
+    return acc;
+}
+
+/*
+ * out[i, j] = round_out( (sum_k dec(A[i,k]) * dec(B[j,k])) * sinv_a * sinv_b
+ *                        + bias[j] )
+ * A is [M, K] row-major (lda), B is [N, K] row-major (ldb): the "NT" product
+ * torch._scaled_mm computes for a row-major first operand and a transposed
+ * second one.  out is [M, N] row-major (ldo); out_kind 0 = bf16 (RNE),
+ * 1 = fp32 (RNE).  bias is bf16 [N] or NULL.  Returns 0 or -1.
+ */
+int orc_gemm_nt(const uint8_t *A, int fa, int64_t lda, const uint8_t *B, int fb,
+                int64_t ldb, int64_t M, int64_t N, int64_t K, float sinv_a,
+                float sinv_b, const uint16_t *bias, int out_kind, void *out,
+                int64_t ldo) {
+    orc_fmt f;
+    if (orc_get_fmt(fa, &f) || orc_get_fmt(fb, &f) || M < 0 || N < 0 || K < 0 ||
+        (out_kind != 0 && out_kind != 1))
+        return -1;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = orc_dot(A, fa, lda, B, fb, ldb, i, j, K);
+            double y = acc * (double)sinv_a * (double)sinv_b + orc_bias_at(bias, j);
+            orc_store_out(out, out_kind, i * ldo + j, y);
+        }
+    return 0;
+}
+
+/* The same definition evaluated only at the listed (rows[s], cols[s]) pairs;
+ * out receives `count` values of the output type, in list order. */
+int orc_gemm_nt_sampled(const uint8_t *A, int fa, int64_t lda, const uint8_t *B,
+                        int fb, int64_t ldb, int64_t K, float sinv_a, float sinv_b,
+                        const uint16_t *bias, int out_kind, const int64_t *rows,
+                        const int64_t *cols, int64_t count, void *out) {
+    orc_fmt f;
+    if (orc_get_fmt(fa, &f) || orc_get_fmt(fb, &f) || K < 0 || count < 0 ||
+        (out_kind != 0 && out_kind != 1))
+        return -1;
+    for (int64_t s = 0; s < count; ++s) {
+        double acc = orc_dot(A, fa, lda, B, fb, ldb, rows[s], cols[s], K);
+        double y = acc * (double)sinv_a * (double)sinv_b + orc_bias_at(bias, cols[s]);
+        orc_store_out(out, out_kind, s, y);
+    }
+    return 0;
+}
