@@ -1,0 +1,224 @@
+/*
+ * fp8dsl.h -- C ABI of the delayed-scaling FP8 linear library for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The library implements the data-parallel hot path of an FP8 linear layer
+ * trained with delayed scaling:
+ *
+ *   fp8_cast_transpose_amax  scaled, saturating cast of a bf16/fp32 tensor to
+ *                            OCP E4M3 or E5M2, writing the row-major codes, the
+ *                            cached transpose, the per-tensor amax and the
+ *                            scale-inverse snapshot in one pass;
+ *   fp8_scale_update         the amax-history "max" recipe for every scaled
+ *                            tensor of a model in one launch;
+ *   fp8_linear_fwd           Y  = X W^T (+ bias)  E4M3 x E4M3 -> bf16
+ *   fp8_linear_dgrad         dX = dY W            E5M2 x E4M3 -> bf16
+ *   fp8_linear_wgrad         dW = dY^T X          E5M2 x E4M3 -> fp32 / bf16
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer to tensor data is a DEVICE pointer (memory the caller got
+ *    from hipMalloc or from a framework allocator on the current device).
+ *    The fp8_tensor_t descriptors themselves live in HOST memory and are read
+ *    during the call only.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream).  No entry point synchronises, allocates, frees, or
+ *    reads device memory from the host, so every call can be captured in a
+ *    HIP graph.
+ *  - The caller owns every buffer.  The library keeps no state between calls.
+ *  - Return value: FP8_OK (0) or a negative fp8_status_t.  On an error
+ *    nothing has been enqueued.  Faults inside a kernel surface later, as HIP
+ *    reports them, on the stream.
+ *  - Layouts are row-major with unit stride in the last dimension.
+ *  - FP8 codes are OCP float8_e4m3fn / float8_e5m2 bytes.
+ */
+#ifndef FP8DSL_H
+#define FP8DSL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8DSL_ABI_VERSION 1
+
+/* A hipStream_t, passed as an opaque pointer so that this header needs no
+ * HIP include. */
+typedef void *fp8_stream_t;
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_NULL = -1,      /* a required pointer is NULL                       */
+    FP8_ERR_SHAPE = -2,     /* negative size, or a size rule below is broken    */
+    FP8_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned          */
+    FP8_ERR_FORMAT = -4,    /* an FP8 format this entry point does not accept   */
+    FP8_ERR_ARG = -5,       /* another argument out of range (dtype, algo, ...) */
+    FP8_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch         */
+    FP8_ERR_DEVICE = -7     /* the current device is not a gfx950 GPU           */
+} fp8_status_t;
+
+/* OCP 8-bit float formats ("Accelerating PyTorch Training Workloads with FP8
+ * -- Part 2", PyTorch-native FP8 data types: float8_e4m3fn with 3 mantissa
+ * bits, max 448; float8_e5m2 with 2 mantissa bits, max 57344).  Under the
+ * HYBRID recipe of "CPU Overhead of te.Linear FP8 Layers" forward tensors use
+ * E4M3 and gradients E5M2. */
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format_t;
+
+/* Element type of a cast source or of a GEMM output. */
+typedef enum { FP8_DTYPE_BF16 = 0, FP8_DTYPE_FP32 = 1 } fp8_dtype_t;
+
+/* Amax-history reduction; "max" is the only one the recipe on the pages uses. */
+typedef enum { FP8_AMAX_ALGO_MAX = 0 } fp8_amax_algo_t;
+
+/*
+ * An FP8 tensor: codes, optional cached transpose and the scale-inverse that
+ * was in force when the codes were written.  This is the plain-memory form of
+ * the Float8Tensor of "[PyTorch] Refactor FP8 workspaces in linear modules":
+ * it holds a private copy of the FP8 scale-inverse that later scale updates
+ * do not touch (first motivation of that change) and a transpose cache filled
+ * by the cast rather than lazily by a separate transpose kernel.
+ */
+typedef struct fp8_tensor {
+    uint8_t *data;       /* [rows, cols] codes, or NULL                        */
+    uint8_t *data_t;     /* [cols, rows] codes (transpose of data), or NULL    */
+    float *scale_inv;    /* 1 float: 1/scale at cast time                      */
+    int32_t fmt;         /* fp8_format_t                                       */
+    int32_t reserved;    /* must be 0                                          */
+    int64_t rows;
+    int64_t cols;
+} fp8_tensor_t;
+
+/*
+ * fp8_scale_update -- delayed-scaling update of T scaled tensors in one launch.
+ *
+ * Defined by the DelayedScaling recipe (amax_history_len = 16,
+ * amax_compute_algo = "max") in "CPU Overhead of te.Linear FP8 Layers", by the
+ * scale update that "[PyTorch] Refactor FP8 workspaces in linear modules" runs
+ * for every FP8 tensor each forward pass, and by the single packed amax
+ * tensor that "support delayed scaling of weight in float8 all-gather" syncs
+ * once per step.  The pages do not print the scale formula; this library uses
+ * the conventional one.  For every t in [0, T):
+ *
+ *   amax_history[t, 1:H] = amax_history[t, 0:H-1]    (roll by one)
+ *   amax_history[t, 0]   = amax_cur[t]
+ *   m = max_i |amax_history[t, i]|   (ordered by the sign-cleared fp32 pattern)
+ *   if m is finite and m > 0:
+ *       s = fp8_max(fmt[t]) / ldexp(m, margin)         (fp32, correctly rounded)
+ *       if s is finite and s > 0: scale[t] = s          (else scale is kept)
+ *   scale_inv[t] = 1 / scale[t]                        (fp32, correctly rounded)
+ *   amax_cur[t]  = 0
+ *
+ * amax_history [T, H] fp32 (in/out), amax_cur [T] fp32 (in/out), scale [T]
+ * fp32 (in/out), scale_inv [T] fp32 (out), fmt [T] uint8 (fp8_format_t).
+ * Constraints: T >= 0 (T == 0 is a no-op), 1 <= H <= 1024, -126 <= margin <= 126,
+ * algo == FP8_AMAX_ALGO_MAX.  An fmt entry that is not a valid format leaves
+ * that record unchanged (the host cannot read device memory to reject it).
+ * Errors: FP8_ERR_NULL, FP8_ERR_ARG, FP8_ERR_LAUNCH.
+ */
+int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *scale_inv,
+                     const uint8_t *fmt, int32_t T, int32_t H, int32_t margin, int32_t algo,
+                     fp8_stream_t stream);
+
+/*
+ * fp8_cast_transpose_amax -- one HBM pass over a bf16/fp32 tensor.
+ *
+ * Defined by the FP8 casts of "Accelerating PyTorch Training Workloads with
+ * FP8 -- Part 2" (round to nearest even onto the float8_e4m3fn / float8_e5m2
+ * grids of its finfo table), by the transpose cache and scale-inverse copy of
+ * "[PyTorch] Refactor FP8 workspaces in linear modules", by the noop flag that
+ * change passes to its transpose for CUDA-graph weight caching, and by the
+ * per-tensor amax buffers of "support delayed scaling of weight in float8
+ * all-gather".  For every element:
+ *
+ *   v = fp32(x[r, c]) * (*scale)                 one fp32 multiply, RNE
+ *   code = NaN(v)            ? 0x7F | (sign(x) ^ sign(*scale))
+ *        : |v| >= fp8_max    ? sign(v) | max code (0x7E E4M3, 0x7B E5M2)
+ *        :                   round v to the FP8 grid, ties to even
+ *   out->data[r, c] = code;  out->data_t[c, r] = code     (each if non-NULL)
+ *   *amax_cur = max(*amax_cur, |x[r, c]|)    (sign-cleared fp32 bit order; the
+ *                                             UNSCALED source)
+ * and *out->scale_inv = 1 / *scale (if out->scale_inv is non-NULL).
+ *
+ * x       device, [rows, cols] with row stride ld elements; src selects bf16 or
+ *         fp32.  ld >= cols.
+ * scale   device, 1 float (the delayed scale recorded by fp8_scale_update).
+ * out     host descriptor; out->rows == rows, out->cols == cols, out->fmt the
+ *         target format; data and/or data_t non-NULL.
+ * amax_cur device, 1 float, max-accumulated (atomically, so several casts of
+ *         one tensor in a step combine); must hold a non-negative value, e.g.
+ *         0 after fp8_scale_update.  May be NULL to skip the amax.
+ * noop_flag NULL, or a device int32: when it is non-zero at kernel time the
+ *         call does nothing (weight caching under graph replay).
+ * Constraints: rows, cols >= 0 and multiples of 16; x, data, data_t 16-byte
+ * aligned; ld a multiple of 8 (bf16) or 4 (fp32).
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_FORMAT,
+ * FP8_ERR_ARG, FP8_ERR_LAUNCH.
+ */
+int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
+                            const float *scale, const fp8_tensor_t *out, float *amax_cur,
+                            const int32_t *noop_flag, fp8_stream_t stream);
+
+/*
+ * fp8_linear_fwd -- Y = X W^T + bias on FP8 operands.
+ *
+ * Defined by torch._scaled_mm in "Accelerating PyTorch Training Workloads with
+ * FP8 -- Part 2" (first operand row-major, second transposed, per-tensor
+ * scales held on the device, optional bf16 bias, chosen output type) and by
+ * the te.Linear forward of "CPU Overhead of te.Linear FP8 Layers":
+ *
+ *   y[m, n] = bf16_rne( (sum_k dec(x[m,k]) dec(w[n,k])) * x_sinv * w_sinv + bias[n] )
+ *
+ * with fp32 accumulation.  x->data [M, K] and w->data [N, K] (E4M3 or E5M2
+ * each), their scale_inv snapshots, bias device bf16 [N] or NULL, y device
+ * bf16 [M, N].
+ * Constraints: M, N >= 0 (0 is a no-op), K >= 0 and a multiple of 16, 16-byte
+ * aligned pointers, N a multiple of 8.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_FORMAT,
+ * FP8_ERR_LAUNCH.
+ */
+int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                   uint16_t *y, fp8_stream_t stream);
+
+/*
+ * fp8_linear_dgrad -- dX = dY W on FP8 operands, using W's cached transpose.
+ *
+ * The backward data product of te.Linear ("CPU Overhead of te.Linear FP8
+ * Layers", loss.backward under fp8_autocast with the HYBRID format: gradients
+ * in E5M2) reading the transpose cache of "[PyTorch] Refactor FP8 workspaces
+ * in linear modules":
+ *
+ *   dx[m, k] = bf16_rne( (sum_n dec(dy[m,n]) dec(w_t[k,n])) * dy_sinv * w_sinv )
+ *
+ * dy->data [M, N], w->data_t [K, N] (w->rows = N, w->cols = K), dx device
+ * bf16 [M, K].  Constraints as fp8_linear_fwd with the contraction N a
+ * multiple of 16 and K a multiple of 8.
+ */
+int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
+                     fp8_stream_t stream);
+
+/*
+ * fp8_linear_wgrad -- dW = dY^T X on FP8 operands, using both transposes.
+ *
+ *   dw[n, k] = out( (sum_m dec(dy_t[n,m]) dec(x_t[k,m])) * dy_sinv * x_sinv )
+ *
+ * dy->data_t [N, M] (dy->rows = M, dy->cols = N), x->data_t [K, M]
+ * (x->rows = M, x->cols = K), dw device [N, K] in out_dtype (FP8_DTYPE_FP32
+ * for fp32 master weights, as in the FP8 run of the reproduction script of
+ * "CPU Overhead of te.Linear FP8 Layers", or FP8_DTYPE_BF16).  Constraints as
+ * fp8_linear_fwd with the contraction M a multiple of 16 and K a multiple of 8.
+ */
+int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, int32_t out_dtype,
+                     fp8_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *fp8_status_string(int status);
+
+/* FP8DSL_ABI_VERSION of the built library. */
+int fp8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8DSL_H */

@@ -24,7 +24,8 @@
  * the design notes of the repository):
  *   - the cast computes v = fp32(x) * scale as one IEEE fp32 multiply and
  *     rounds v to FP8 with round-to-nearest-even and SATURATION: every finite
- *     overflow and +-inf goes to +-max, NaN goes to sign|0x7F;
+ *     overflow and +-inf goes to +-max, NaN goes to sign|0x7F, where the sign
+ *     of a NaN product is sign(x) XOR sign(scale) (IEEE leaves it open);
  *   - amax is the maximum of |x| over the UNSCALED source, ordered by the
  *     sign-cleared fp32 bit pattern (so a NaN dominates everything);
  *   - the scale formula is the conventional one, not printed on the pages:
@@ -188,7 +189,11 @@ int orc_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
             uint32_t k = orc_abs_key(xv);
             if (k > amax_key) amax_key = k;
             float v = xv * scale;                  /* one fp32 multiply */
-            uint8_t code = orc_fp8_encode(v, fmt);
+            uint8_t code;
+            if (isnan(v))   /* sign of a NaN product: the multiply's sign rule */
+                code = 0x7F | ((signbit(xv) ? 0x80 : 0) ^ (signbit(scale) ? 0x80 : 0));
+            else
+                code = orc_fp8_encode(v, fmt);
             if (q) q[r * cols + c] = code;
             if (qt) qt[c * rows + r] = code;
         }

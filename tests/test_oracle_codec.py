@@ -219,3 +219,17 @@ def test_random_fp32_patterns_against_torch(fmt):
     v = np.concatenate([v, v2])
     q = oracle.fp8_encode(v, fmt)
     np.testing.assert_array_equal(q, _torch_ref(v, fmt))
+
+
+def test_nan_product_sign_rule():
+    """A NaN product takes sign(x) XOR sign(scale); inf * 0 is such a NaN."""
+    def code(x, scale, fmt=oracle.E4M3):
+        q, _, _, _ = oracle.cast_transpose_amax(np.array([[x]], dtype=np.float32), scale, fmt)
+        return int(q[0, 0])
+    nan = np.float32(np.nan)
+    assert code(nan, 2.0) == 0x7F and code(-nan, 2.0) == 0xFF
+    assert code(nan, -2.0) == 0xFF and code(-nan, -2.0) == 0x7F
+    assert code(np.inf, 0.0) == 0x7F and code(-np.inf, 0.0) == 0xFF
+    assert code(0.0, np.inf, oracle.E5M2) == 0x7F and code(-0.0, np.inf, oracle.E5M2) == 0xFF
+    assert code(1.0, nan) == 0x7F
+    assert code(-1.0, -np.inf) == 0x7E and code(1.0, -np.inf, oracle.E5M2) == 0xFB
