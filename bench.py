@@ -1,0 +1,257 @@
+"""Benchmark of the delayed-scaling FP8 linear hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of the toy transformer's
+MLP layer (X [8192, 2048], W [8192, 2048], dY [8192, 8192], HYBRID format,
+history 16):
+
+    cast X (E4M3, codes + transpose + amax)   cast W (E4M3, codes + transpose + amax)
+    Y  = X W^T + b   (fp8_linear_fwd,   E4M3 x E4M3 -> bf16)
+    cast dY (E5M2, codes + transpose + amax)
+    dX = dY W        (fp8_linear_dgrad, E5M2 x E4M3 -> bf16)
+    dW = dY^T X      (fp8_linear_wgrad, E5M2 x E4M3 -> fp32)
+    one scale update over the three amax histories
+
+`value` is the step's GEMM throughput (3 x 2*8192*8192*2048 FLOP per step over
+the measured step time, casts and update included).  Per-kernel durations are
+taken with HIP events around each launch on the launch stream inside the
+timed region.  The cast-transpose-amax bandwidth is also measured on its own
+workload (bf16 [4096, 4096], 0.1% outliers) rotating over 640 MiB of buffers
+so that the 256 MiB last-level cache cannot serve it.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+M, N, K = 8192, 8192, 2048
+GEMM_FLOP = 2 * M * N * K
+CAST_R = CAST_C = 4096
+CAST_BYTES = 2 * CAST_R * CAST_C + 2 * CAST_R * CAST_C     # bf16 read + 2 FP8 writes
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cast-iters", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Timer:
+    """Event pairs around launches on the current stream; average in ms."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def start(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return (name, e)
+
+    def stop(self, tok):
+        name, s = tok
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+
+    def avg_ms(self, name):
+        v = [s.elapsed_time(e) for s, e in self.pairs[name]]
+        return sum(v) / len(v)
+
+
+def gpu_step(dsl, st, t: Timer | None):
+    def run(name, fn, *a):
+        tok = t.start(name) if t else None
+        fn(*a)
+        if t:
+            t.stop(tok)
+
+    g = st["state"]
+    run("cast_x", dsl.fp8_cast_transpose_amax, st["x"], g.scale[0:1], st["qx"], g.amax_cur[0:1])
+    run("cast_w", dsl.fp8_cast_transpose_amax, st["w"], g.scale[1:2], st["qw"], g.amax_cur[1:2])
+    run("gemm_fwd", dsl.fp8_linear_fwd, st["qx"], st["qw"], st["b"], st["y"])
+    run("cast_dy", dsl.fp8_cast_transpose_amax, st["dy"], g.scale[2:3], st["qdy"], g.amax_cur[2:3])
+    run("gemm_dgrad", dsl.fp8_linear_dgrad, st["qdy"], st["qw"], st["dx"])
+    run("gemm_wgrad", dsl.fp8_linear_wgrad, st["qdy"], st["qx"], st["dw"])
+    run("scale_update", g.update)
+
+
+def cast_bandwidth(dsl, workloads, iters: int):
+    """configs: bf16 [4096, 4096] -> E4M3 codes + transpose + amax, rotating
+    over 10 buffer sets (640 MiB)."""
+    dev = "cuda"
+    src = workloads.cast_only().to(dev)
+    nsets = 10
+    xs = [src.clone() for _ in range(nsets)]
+    outs = [dsl.Float8Tensor.empty(CAST_R, CAST_C, 0, device=dev) for _ in range(nsets)]
+    scale = torch.tensor([448.0 / 3920.0], device=dev)
+    amax = torch.zeros(1, device=dev)
+    for i in range(nsets):                                   # warm-up
+        dsl.fp8_cast_transpose_amax(xs[i], scale, outs[i], amax)
+    torch.cuda.synchronize()
+    t = Timer()
+    for i in range(iters):
+        j = i % nsets
+        tok = t.start("cast")
+        dsl.fp8_cast_transpose_amax(xs[j], scale, outs[j], amax)
+        t.stop(tok)
+    torch.cuda.synchronize()
+    ms = t.avg_ms("cast")
+    gbs = CAST_BYTES / (ms * 1e-3) / 1e9
+    del xs, outs
+    torch.cuda.empty_cache()
+    return ms, gbs
+
+
+def cpu_baseline(workloads):
+    """The oracle (plain single-threaded C) on a bounded sample of the step:
+    the full X and W casts, 512 of the 8192 rows of the dY cast, and 32 of the
+    8192 output rows of each of the three GEMMs; extrapolated linearly to one
+    full step."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+
+    def b16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    x, w, _ = workloads.mlp_forward(0)
+    dy = workloads.mlp_grad()
+    xb, wb, dyb = b16(x), b16(w), b16(dy[:512])
+    t0 = time.perf_counter()
+    qx, qxt, _, _ = oracle.cast_transpose_amax(xb, 100.0, 0)
+    qw, qwt, _, _ = oracle.cast_transpose_amax(wb, 4000.0, 0)
+    t_cast_xw = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.cast_transpose_amax(dyb, 5e6, 1)
+    t_cast_dy = (time.perf_counter() - t0) * (M / 512)
+    rows = 32
+    qdy = np.ascontiguousarray(qx[:, :2048].repeat(4, axis=1)[:rows])   # stand-in E5M2 codes
+    t0 = time.perf_counter()
+    oracle.gemm_nt(qx[:rows], 0, qw, 0, 1.0, 1.0)                      # fwd rows
+    oracle.gemm_nt(qdy, 1, qwt, 0, 1.0, 1.0)                           # dgrad rows
+    oracle.gemm_nt(np.ascontiguousarray(qwt[:rows].repeat(4, axis=1)), 1, qxt, 0, 1.0, 1.0,
+                   out_kind=oracle.OUT_FP32)                           # wgrad rows
+    t_gemm = (time.perf_counter() - t0) * (M / rows)
+    t_step = t_cast_xw + t_cast_dy + t_gemm
+    sample_s = t_cast_xw + t_cast_dy * 512 / M + t_gemm * rows / M
+    return {"value": round(3 * GEMM_FLOP / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"oracle C, 1 thread: full X and W casts, 512/8192 rows of the dY cast, "
+                       f"{rows}/8192 output rows of each GEMM ({sample_s:.1f} s of CPU work), "
+                       f"extrapolated to one step = {t_step:.0f} s")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs "
+              "are not part of this library's measured path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import delayed_scaling_linear_amd as dsl
+    import workloads
+
+    dev = "cuda"
+    x, w, b = workloads.mlp_forward(0)
+    dy = workloads.mlp_grad()
+    st = {
+        "x": x.to(dev), "w": w.to(dev), "b": b.to(dev), "dy": dy.to(dev),
+        "qx": dsl.Float8Tensor.empty(M, K, 0, device=dev),
+        "qw": dsl.Float8Tensor.empty(N, K, 0, device=dev),
+        "qdy": dsl.Float8Tensor.empty(M, N, 1, device=dev),
+        "y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+        "dx": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+        "dw": torch.empty(N, K, dtype=torch.float32, device=dev),
+        "state": dsl.DelayedScalingState([0, 0, 1], device=dev),
+    }
+    for _ in range(args.warmup):
+        gpu_step(dsl, st, None)
+    torch.cuda.synchronize()
+
+    # Whole-step timing (no per-kernel events inside).
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        gpu_step(dsl, st, None)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # Same steps again with an event pair around every launch.
+    timer = Timer()
+    for _ in range(args.steps):
+        gpu_step(dsl, st, timer)
+    torch.cuda.synchronize()
+    kernels = {}
+    for name in ("cast_x", "cast_w", "gemm_fwd", "cast_dy", "gemm_dgrad", "gemm_wgrad",
+                 "scale_update"):
+        ms = timer.avg_ms(name)
+        k = {"us": round(ms * 1e3, 2)}
+        if name.startswith("gemm"):
+            k["TFLOP/s"] = round(GEMM_FLOP / (ms * 1e-3) / 1e12, 1)
+        elif name == "cast_dy":
+            k["GB/s"] = round(4 * M * N / (ms * 1e-3) / 1e9, 1)
+        elif name.startswith("cast"):
+            k["GB/s"] = round(4 * M * K / (ms * 1e-3) / 1e9, 1)
+        kernels[name] = k
+
+    cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
+    fwd_ms = timer.avg_ms("gemm_fwd")
+    fwd_tflops = GEMM_FLOP / (fwd_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": "FP8 GEMM TFLOP/s (M8192 K2048 N8192) + cast-transpose-amax HBM GB/s",
+        "value": round(3 * GEMM_FLOP / (ms_step * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded: X ~U(0,1), W ~N(0,0.02), dY ~N(0,1e-3), bf16)",
+        "config": {"workload": "FP8 linear fwd+bwd, HYBRID, X/W [8192,2048], dY [8192,8192], "
+                               "history 16 (toy-block MLP shape: hidden 2048, batch 8, seq 1024)",
+                   "M": M, "N": N, "K": K, "global_batch": 8, "seq_len": 1024,
+                   "parallelism": "none (1 GPU)"},
+        "gemm_fwd_tflops": round(fwd_tflops, 1),
+        "cast_transpose_amax_gbs": round(cast_gbs, 1),
+        "cast_transpose_amax_us": round(cast_ms * 1e3, 2),
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": "gemm_fwd (fp8_linear_fwd)",
+                     "achieved": round(fwd_tflops, 1), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "roofline_cast": {"bound": "hbm", "kernel": "fp8_cast_transpose_amax bf16 [4096,4096]",
+                          "achieved": round(cast_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(cast_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(workloads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

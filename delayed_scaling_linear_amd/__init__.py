@@ -1,0 +1,244 @@
+"""Delayed-scaling FP8 linear layer for AMD MI355X (gfx950): Python binding.
+
+Thin ctypes binding over ``libfp8dsl.so``, whose C ABI is declared in
+``include/fp8dsl.h``.  The functions here have the same names as the C entry
+points and only marshal arguments: they take torch tensors for device memory,
+pass ``data_ptr()`` and the current HIP stream, and turn status codes into
+exceptions.  Every step of the computation runs in the HIP kernels.  There is
+no CPU fallback: importing this package fails loudly when the library has not
+been built.
+
+The pieces, with the pages that define them:
+
+* :class:`Float8Tensor` -- FP8 codes + cached transpose + scale-inverse
+  snapshot ("[PyTorch] Refactor FP8 workspaces in linear modules").
+* :class:`DelayedScalingState` -- packed amax histories, current amaxes,
+  scales and scale-inverses of T tensors (the fp8_meta of te.Linear and the
+  packed amax tensor of "support delayed scaling of weight in float8
+  all-gather"), with the DelayedScaling recipe of "CPU Overhead of te.Linear
+  FP8 Layers" (history 16, "max").
+* ``fp8_cast_transpose_amax``, ``fp8_scale_update``, ``fp8_linear_fwd``,
+  ``fp8_linear_dgrad``, ``fp8_linear_wgrad`` -- the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "DTYPE_BF16", "DTYPE_FP32", "Fp8Error", "Float8Tensor",
+    "DelayedScalingState", "fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
+    "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
+    "library_path", "lib",
+]
+
+E4M3 = 0
+E5M2 = 1
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libfp8dsl.so")
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fp8_status_string(status)} ({status})")
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    """Mirror of fp8_tensor_t."""
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("data_t", ctypes.c_void_p),
+        ("scale_inv", ctypes.c_void_p),
+        ("fmt", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp8dsl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(
+                f"{library_path} is missing: build it with "
+                "`python -m delayed_scaling_linear_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(library_path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        dp = ctypes.POINTER(_Desc)
+        L.fp8_scale_update.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.fp8_cast_transpose_amax.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp]
+        L.fp8_linear_fwd.argtypes = [dp, dp, vp, vp, vp]
+        L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
+        L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
+        for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_linear_fwd,
+                  L.fp8_linear_dgrad, L.fp8_linear_wgrad):
+            f.restype = ctypes.c_int
+        L.fp8_status_string.argtypes = [ctypes.c_int]
+        L.fp8_status_string.restype = ctypes.c_char_p
+        L.fp8_abi_version.argtypes = []
+        L.fp8_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def fp8_status_string(status: int) -> str:
+    return lib().fp8_status_string(status).decode()
+
+
+def fp8_abi_version() -> int:
+    return lib().fp8_abi_version()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise Fp8Error(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, what: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+@dataclass
+class Float8Tensor:
+    """FP8 codes [rows, cols] (optional), their transpose [cols, rows]
+    (optional) and the scale-inverse [1] in force when they were written."""
+    data: Optional[torch.Tensor]
+    data_t: Optional[torch.Tensor]
+    scale_inv: torch.Tensor
+    fmt: int
+    rows: int
+    cols: int
+
+    @staticmethod
+    def empty(rows: int, cols: int, fmt: int, *, data: bool = True, transpose: bool = True,
+              device="cuda") -> "Float8Tensor":
+        d = torch.empty((rows, cols), dtype=torch.uint8, device=device) if data else None
+        dt = torch.empty((cols, rows), dtype=torch.uint8, device=device) if transpose else None
+        si = torch.ones(1, dtype=torch.float32, device=device)
+        return Float8Tensor(d, dt, si, fmt, rows, cols)
+
+    def desc(self) -> _Desc:
+        return _Desc(_ptr(self.data, torch.uint8, "data"), _ptr(self.data_t, torch.uint8, "data_t"),
+                     _ptr(self.scale_inv, torch.float32, "scale_inv"), self.fmt, 0, self.rows,
+                     self.cols)
+
+
+class DelayedScalingState:
+    """Packed delayed-scaling state of T tensors (device memory, caller-owned).
+
+    amax_history [T, H], amax_cur [T], scale [T], scale_inv [T] (fp32) and
+    fmt [T] (uint8).  Initial state: empty history, amax 0, scale 1.
+    """
+
+    def __init__(self, fmts, history_len: int = 16, margin: int = 0, device="cuda"):
+        T = len(fmts)
+        self.T, self.H, self.margin = T, history_len, margin
+        self.amax_history = torch.zeros((T, history_len), dtype=torch.float32, device=device)
+        self.amax_cur = torch.zeros(T, dtype=torch.float32, device=device)
+        self.scale = torch.ones(T, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(T, dtype=torch.float32, device=device)
+        self.fmt = torch.tensor(list(fmts), dtype=torch.uint8, device=device)
+
+    def update(self, stream=None) -> None:
+        fp8_scale_update(self.amax_history, self.amax_cur, self.scale, self.scale_inv, self.fmt,
+                         margin=self.margin, stream=stream)
+
+
+def fp8_scale_update(amax_history: torch.Tensor, amax_cur: torch.Tensor, scale: torch.Tensor,
+                     scale_inv: torch.Tensor, fmt: torch.Tensor, margin: int = 0, algo: int = 0,
+                     stream=None) -> None:
+    T, H = amax_history.shape
+    for t, n in ((amax_cur, "amax_cur"), (scale, "scale"), (scale_inv, "scale_inv"), (fmt, "fmt")):
+        if t.numel() != T:
+            raise ValueError(f"{n} must have {T} entries")
+    _check(lib().fp8_scale_update(_ptr(amax_history, torch.float32, "amax_history"),
+                                  _ptr(amax_cur, torch.float32, "amax_cur"),
+                                  _ptr(scale, torch.float32, "scale"),
+                                  _ptr(scale_inv, torch.float32, "scale_inv"),
+                                  _ptr(fmt, torch.uint8, "fmt"), T, H, margin, algo,
+                                  _stream(stream)), "fp8_scale_update")
+
+
+def fp8_cast_transpose_amax(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,
+                            amax_cur: Optional[torch.Tensor] = None,
+                            noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Cast x (bf16 or fp32, 2-D, unit stride in the last dim) into `out`.
+
+    `scale` and `amax_cur` are 1-element fp32 device tensors (views into a
+    DelayedScalingState are fine)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride in the last dimension")
+    if x.dtype == torch.bfloat16:
+        src = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        src = DTYPE_FP32
+    else:
+        raise TypeError("x must be bf16 or fp32")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    d = out.desc()
+    _check(lib().fp8_cast_transpose_amax(x.data_ptr(), src, x.shape[0], x.shape[1], x.stride(0),
+                                         _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
+                                         _ptr(amax_cur, torch.float32, "amax_cur"),
+                                         _ptr(noop_flag, torch.int32, "noop_flag"),
+                                         _stream(stream)), "fp8_cast_transpose_amax")
+
+
+def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],
+                   y: torch.Tensor, stream=None) -> None:
+    """y [M, N] bf16 = x.data [M, K] . w.data [N, K]^T * sinv + bias."""
+    dx, dw = x.desc(), w.desc()
+    _check(lib().fp8_linear_fwd(ctypes.byref(dx), ctypes.byref(dw),
+                                _ptr(bias, torch.bfloat16, "bias"), _ptr(y, torch.bfloat16, "y"),
+                                _stream(stream)), "fp8_linear_fwd")
+
+
+def fp8_linear_dgrad(dy: Float8Tensor, w: Float8Tensor, dx: torch.Tensor, stream=None) -> None:
+    """dx [M, K] bf16 = dy.data [M, N] . w.data_t [K, N]^T * sinv."""
+    d1, d2 = dy.desc(), w.desc()
+    _check(lib().fp8_linear_dgrad(ctypes.byref(d1), ctypes.byref(d2),
+                                  _ptr(dx, torch.bfloat16, "dx"), _stream(stream)),
+           "fp8_linear_dgrad")
+
+
+def fp8_linear_wgrad(dy: Float8Tensor, x: Float8Tensor, dw: torch.Tensor, stream=None) -> None:
+    """dw [N, K] (fp32 or bf16) = dy.data_t [N, M] . x.data_t [K, M]^T * sinv."""
+    if dw.dtype == torch.float32:
+        od = DTYPE_FP32
+    elif dw.dtype == torch.bfloat16:
+        od = DTYPE_BF16
+    else:
+        raise TypeError("dw must be fp32 or bf16")
+    d1, d2 = dy.desc(), x.desc()
+    _check(lib().fp8_linear_wgrad(ctypes.byref(d1), ctypes.byref(d2), _ptr(dw, None, "dw"), od,
+                                  _stream(stream)), "fp8_linear_wgrad")

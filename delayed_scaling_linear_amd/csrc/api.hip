@@ -1,0 +1,159 @@
+// C-ABI entry points of the delayed-scaling FP8 linear library.
+//
+// This layer only validates arguments and picks a launcher; every step of
+// the computation runs in the HIP kernels.  It allocates nothing, never
+// synchronises and never reads device memory, so every call is capturable in
+// a HIP graph (the class of bug "[PyTorch] Refactor FP8 workspaces in linear
+// modules" describes for transpose caches filled outside the captured region
+// cannot arise: the cast always writes the transpose it is asked for).
+#include <string.h>
+
+#include "fp8dsl_internal.h"
+
+using namespace fp8dsl;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool valid_fmt(int32_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+
+// The current device must be a gfx950 (checked once per device).
+int check_device() {
+    static int state[64];   // 0 unknown, 1 good, 2 bad
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8_ERR_DEVICE;
+    if (state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8_ERR_DEVICE;
+        state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    return state[dev] == 1 ? FP8_OK : FP8_ERR_DEVICE;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
+
+// Shared checks of one GEMM: A [M, K], B [N, K], C [M, N].
+int check_gemm(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
+               const float *sa, const float *sb, const void *C, int64_t out_align_elems) {
+    if (M < 0 || N < 0 || K < 0 || (K % 16) != 0 || (N % out_align_elems) != 0)
+        return FP8_ERR_SHAPE;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8_OK;
+    if (C == nullptr || sa == nullptr || sb == nullptr) return FP8_ERR_NULL;
+    if (K > 0 && (A == nullptr || B == nullptr)) return FP8_ERR_NULL;
+    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B)))) return FP8_ERR_ALIGN;
+    return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8DSL_ABI_VERSION; }
+
+const char *fp8_status_string(int status) {
+    switch (status) {
+        case FP8_OK: return "FP8_OK";
+        case FP8_ERR_NULL: return "FP8_ERR_NULL: a required pointer is NULL";
+        case FP8_ERR_SHAPE: return "FP8_ERR_SHAPE: size out of range or not a required multiple";
+        case FP8_ERR_ALIGN: return "FP8_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+        case FP8_ERR_FORMAT: return "FP8_ERR_FORMAT: FP8 format not accepted here";
+        case FP8_ERR_ARG: return "FP8_ERR_ARG: argument out of range";
+        case FP8_ERR_LAUNCH: return "FP8_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+        case FP8_ERR_DEVICE: return "FP8_ERR_DEVICE: the current device is not a gfx950 GPU";
+        default: return "unknown fp8dsl status";
+    }
+}
+
+int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *scale_inv,
+                     const uint8_t *fmt, int32_t T, int32_t H, int32_t margin, int32_t algo,
+                     fp8_stream_t stream) {
+    if (T < 0 || H < 1 || H > 1024 || margin < -126 || margin > 126 ||
+        algo != FP8_AMAX_ALGO_MAX)
+        return FP8_ERR_ARG;
+    if (T == 0) return FP8_OK;
+    if (!amax_history || !amax_cur || !scale || !scale_inv || !fmt) return FP8_ERR_NULL;
+    if (int d = check_device()) return d;
+    return status_of(launch_scale_update(amax_history, amax_cur, scale, scale_inv, fmt, T, H,
+                                         margin, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
+                            const float *scale, const fp8_tensor_t *out, float *amax_cur,
+                            const int32_t *noop_flag, fp8_stream_t stream) {
+    if (out == nullptr) return FP8_ERR_NULL;
+    if (src != FP8_DTYPE_BF16 && src != FP8_DTYPE_FP32) return FP8_ERR_ARG;
+    if (!valid_fmt(out->fmt)) return FP8_ERR_FORMAT;
+    if (out->reserved != 0) return FP8_ERR_ARG;
+    if (rows < 0 || cols < 0 || (rows % 16) != 0 || (cols % 16) != 0 || ld < cols ||
+        (ld % (src == FP8_DTYPE_BF16 ? 8 : 4)) != 0 || out->rows != rows || out->cols != cols)
+        return FP8_ERR_SHAPE;
+    const int64_t tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
+    if (tiles > INT32_MAX) return FP8_ERR_SHAPE;
+    if (scale == nullptr) return FP8_ERR_NULL;
+    const bool empty = (rows == 0 || cols == 0);
+    // Nothing to cast in an empty tensor; the scale-inverse snapshot is still taken.
+    if (empty && out->scale_inv == nullptr) return FP8_OK;
+    if (!empty && (x == nullptr || (out->data == nullptr && out->data_t == nullptr)))
+        return FP8_ERR_NULL;
+    if ((x && !aligned16(x)) || (out->data && !aligned16(out->data)) ||
+        (out->data_t && !aligned16(out->data_t)))
+        return FP8_ERR_ALIGN;
+    if (int d = check_device()) return d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (empty) return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
+    return status_of(launch_cast_transpose_amax(x, src, rows, cols, ld, scale, out->fmt,
+                                                out->data, out->data_t, amax_cur, out->scale_inv,
+                                                noop_flag, s));
+}
+
+int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                   uint16_t *y, fp8_stream_t stream) {
+    if (!x || !w) return FP8_ERR_NULL;
+    if (!valid_fmt(x->fmt) || !valid_fmt(w->fmt)) return FP8_ERR_FORMAT;
+    const int64_t M = x->rows, K = x->cols, N = w->rows;
+    if (w->cols != K) return FP8_ERR_SHAPE;
+    if (int e = check_gemm(x->data, w->data, M, N, K, x->scale_inv, w->scale_inv, y, 8)) return e;
+    if (M == 0 || N == 0) return FP8_OK;
+    if (bias && !aligned16(bias)) return FP8_ERR_ALIGN;
+    if (int d = check_device()) return d;
+    return status_of(launch_gemm_nt(x->data, x->fmt, w->data, w->fmt, M, N, K, x->scale_inv,
+                                    w->scale_inv, bias, FP8_DTYPE_BF16, y,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
+                     fp8_stream_t stream) {
+    if (!dy || !w) return FP8_ERR_NULL;
+    if (!valid_fmt(dy->fmt) || !valid_fmt(w->fmt)) return FP8_ERR_FORMAT;
+    // dx [M, K] = dy [M, N] . (w_t [K, N])^T
+    const int64_t M = dy->rows, N = dy->cols, K = w->cols;
+    if (w->rows != N) return FP8_ERR_SHAPE;
+    if (int e = check_gemm(dy->data, w->data_t, M, K, N, dy->scale_inv, w->scale_inv, dx, 8))
+        return e;
+    if (M == 0 || K == 0) return FP8_OK;
+    if (int d = check_device()) return d;
+    return status_of(launch_gemm_nt(dy->data, dy->fmt, w->data_t, w->fmt, M, K, N, dy->scale_inv,
+                                    w->scale_inv, nullptr, FP8_DTYPE_BF16, dx,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, int32_t out_dtype,
+                     fp8_stream_t stream) {
+    if (!dy || !x) return FP8_ERR_NULL;
+    if (!valid_fmt(dy->fmt) || !valid_fmt(x->fmt)) return FP8_ERR_FORMAT;
+    if (out_dtype != FP8_DTYPE_BF16 && out_dtype != FP8_DTYPE_FP32) return FP8_ERR_ARG;
+    // dw [N, K] = dy_t [N, M] . (x_t [K, M])^T
+    const int64_t M = dy->rows, N = dy->cols, K = x->cols;
+    if (x->rows != M) return FP8_ERR_SHAPE;
+    if (int e = check_gemm(dy->data_t, x->data_t, N, K, M, dy->scale_inv, x->scale_inv, dw,
+                           out_dtype == FP8_DTYPE_BF16 ? 8 : 4))
+        return e;
+    if (N == 0 || K == 0) return FP8_OK;
+    if (int d = check_device()) return d;
+    return status_of(launch_gemm_nt(dy->data_t, dy->fmt, x->data_t, x->fmt, N, K, M,
+                                    dy->scale_inv, x->scale_inv, nullptr, out_dtype, dw,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,319 @@
+// Fused scaled cast + cached transpose + amax: one HBM pass over a bf16/fp32
+// tensor.
+//
+// What is computed follows the FP8 casts of "Accelerating PyTorch Training
+// Workloads with FP8 -- Part 2" (round to nearest even onto the
+// float8_e4m3fn / float8_e5m2 grids of its finfo table, here with
+// saturation), the Float8Tensor of "[PyTorch] Refactor FP8 workspaces in
+// linear modules" (codes, a transpose cache and a private scale-inverse
+// snapshot), and the per-tensor amax of "support delayed scaling of weight in
+// float8 all-gather" (taken on the unscaled source, in the same read as the
+// cast, which is why delayed scaling needs fewer memory reads than dynamic
+// scaling).
+//
+// Work decomposition (gfx950, wave64):
+//   * one 256-thread workgroup per 128 x 128 tile;
+//   * lane l of wave w owns rows 4*rg .. 4*rg+3 (rg = 8w + l/8) and columns
+//     16*cc .. 16*cc+15 (cc = l%8) of the tile: 16-byte global loads, 8
+//     lanes per 256-byte bf16 row segment;
+//   * each lane scales, clamps to +-fp8_max and converts with the hardware
+//     OCP FP8 converter (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, round to
+//     nearest even), writes its four 16-byte row-major code rows directly,
+//     transposes its 4x16 byte block in registers (v_perm_b32) into sixteen
+//     4-row column words and stores them to LDS;
+//   * the tile is read back from LDS as 16-row column segments (ds_read_b128)
+//     and written as 128-byte transposed row segments;
+//   * amax: packed 16-bit max over sign-cleared bf16 patterns (or 32-bit max
+//     for fp32), wave reduction, LDS across waves, one atomicMax per
+//     workgroup into the fp32 amax (order-preserving on non-negative floats).
+//
+// LDS layout of the transposed tile: 128 columns x 32 words (4 rows / word),
+// word index of (column c, row group g) = c*32 + (g ^ 4*(c/16)): the XOR keeps
+// the sixteen-lane groups that write one column word apiece in distinct banks
+// and leaves each 16-byte, 16-row read contiguous and in order.
+#include "fp8dsl_internal.h"
+
+namespace fp8dsl {
+namespace {
+
+constexpr int TILE = 128;
+constexpr int THREADS = 256;
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int FMT>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<FP8_E4M3> {
+    static constexpr float kMax = 448.0f;
+    template <bool HI>
+    __device__ static __forceinline__ int cvt(float a, float b, int old) {
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+    }
+};
+template <>
+struct Fp8Traits<FP8_E5M2> {
+    static constexpr float kMax = 57344.0f;
+    template <bool HI>
+    __device__ static __forceinline__ int cvt(float a, float b, int old) {
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    }
+};
+
+// Four scaled, clamped values -> one word of four codes (byte i = value i).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float s) {
+    using T = Fp8Traits<FMT>;
+    a = __builtin_amdgcn_fmed3f(a * s, -T::kMax, T::kMax);
+    b = __builtin_amdgcn_fmed3f(b * s, -T::kMax, T::kMax);
+    c = __builtin_amdgcn_fmed3f(c * s, -T::kMax, T::kMax);
+    d = __builtin_amdgcn_fmed3f(d * s, -T::kMax, T::kMax);
+    int w = T::template cvt<false>(a, b, 0);
+    w = T::template cvt<true>(c, d, w);
+    return (uint32_t)w;
+}
+
+// Rare path: a NaN product gets 0x7F | (sign(x) ^ sign(s)).  Only lanes that
+// saw a NaN source (or every lane, when the scale is 0, inf or NaN) run it.
+__device__ __forceinline__ uint32_t patch_nan4(uint32_t w, const float x[4], float s) {
+    const uint32_t sbits = __float_as_uint(s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float v = x[i] * s;
+        if (v != v) {
+            const uint32_t code = 0x7Fu | (((__float_as_uint(x[i]) ^ sbits) >> 24) & 0x80u);
+            w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
+        }
+    }
+    return w;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// 4x4 byte transpose: in[r] holds bytes (r, c=0..3); out[c] holds (r=0..3, c).
+__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// SRC: FP8_DTYPE_BF16 or FP8_DTYPE_FP32.
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) void cast_transpose_amax_kernel(
+    const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
+    const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
+    float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
+    const int32_t *__restrict__ noop, int64_t tiles_c) {
+    if (noop != nullptr && *noop != 0) return;
+
+    __shared__ uint32_t lds_t[TILE * (TILE / 4)];   // transposed tile, 16 KiB
+    __shared__ uint32_t lds_amax[THREADS / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t tile_r = blockIdx.x / tiles_c;
+    const int64_t tile_c = blockIdx.x - tile_r * tiles_c;
+    const int64_t row0 = tile_r * TILE;
+    const int64_t col0 = tile_c * TILE;
+
+    const float s = *scale_ptr;
+    // NaN products from a non-NaN source only arise when s is 0, inf or NaN.
+    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
+    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
+
+    const int cc = lane & 7;                 // 16-column chunk of the tile
+    const int rg = wave * 8 + (lane >> 3);   // 4-row group of the tile
+    const int64_t r = row0 + 4 * rg;
+    const int64_t c = col0 + 16 * cc;
+    const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
+
+    uint32_t key = 0;                        // sign-cleared max, fp32 bit order
+    uint32_t codes[4][4];                    // [row][word of 4 columns]
+
+    if (valid) {
+        float x[4][16];
+        if constexpr (SRC == FP8_DTYPE_BF16) {
+            const uint16_t *xb = static_cast<const uint16_t *>(xv);
+            u32x4 raw[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(xb + (r + i) * ld + c);
+                raw[i][0] = __builtin_nontemporal_load(p);
+                raw[i][1] = __builtin_nontemporal_load(p + 1);
+            }
+            ushort2_t m2 = {0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t d[4] = {raw[i][h].x, raw[i][h].y, raw[i][h].z, raw[i][h].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t a = d[j] & 0x7FFF7FFFu;
+                        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(ushort2_t, a));
+                        x[i][8 * h + 2 * j] = bf16_lo(d[j]);
+                        x[i][8 * h + 2 * j + 1] = bf16_hi(d[j]);
+                    }
+                }
+            }
+            key = (uint32_t)max(m2.x, m2.y) << 16;
+        } else {
+            const float *xf = static_cast<const float *>(xv);
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(xf + (r + i) * ld + c);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const f32x4 v = __builtin_nontemporal_load(p + h);
+                    x[i][4 * h + 0] = v.x;
+                    x[i][4 * h + 1] = v.y;
+                    x[i][4 * h + 2] = v.z;
+                    x[i][4 * h + 3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(x[i][j]) & 0x7FFFFFFFu);
+            }
+            key = m;
+        }
+
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                codes[i][j] = encode4<FMT>(x[i][4 * j], x[i][4 * j + 1], x[i][4 * j + 2],
+                                           x[i][4 * j + 3], s);
+
+        if (s_special || key > 0x7F800000u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) codes[i][j] = patch_nan4(codes[i][j], &x[i][4 * j], s);
+        }
+
+        if constexpr (WANT_Q) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(q + (r + i) * cols + c);
+                *dst = u32x4{codes[i][0], codes[i][1], codes[i][2], codes[i][3]};
+            }
+        }
+        if constexpr (WANT_QT) {
+            const int swz = 4 * cc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t in[4] = {codes[0][j], codes[1][j], codes[2][j], codes[3][j]};
+                uint32_t out[4];
+                transpose4x4(in, out);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int tc = 16 * cc + 4 * j + b;          // tile column
+                    lds_t[tc * 32 + (rg ^ swz)] = out[b];
+                }
+            }
+        }
+    }
+
+    if (amax_cur != nullptr) {
+        key = wave_max_u32(key);
+        if (lane == 0) lds_amax[wave] = key;
+    }
+    __syncthreads();
+
+    if constexpr (WANT_QT) {
+        // 8 lanes per column (16 rows each): 128-byte transposed segments.
+        const int qd = lane & 7;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int tc = (lane >> 3) + 8 * (wave + 4 * k);
+            const int64_t gc = col0 + tc;
+            const int64_t gr = row0 + 16 * qd;
+            if (gc < cols && gr < rows) {
+                const int word = tc * 32 + ((4 * qd) ^ (4 * (tc >> 4)));
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(&lds_t[word]);
+                *reinterpret_cast<u32x4 *>(qt + gc * rows + gr) = v;
+            }
+        }
+    }
+
+    if (amax_cur != nullptr && tid == 0) {
+        uint32_t k = lds_amax[0];
+#pragma unroll
+        for (int w = 1; w < THREADS / 64; ++w) k = max(k, lds_amax[w]);
+        if (k != 0) atomicMax(reinterpret_cast<unsigned int *>(amax_cur), k);
+    }
+}
+
+template <int SRC, int FMT>
+hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
+                          const float *scale, uint8_t *q, uint8_t *qt, float *amax_cur,
+                          float *scale_inv_out, const int32_t *noop, hipStream_t stream) {
+    const int64_t tiles_r = (rows + TILE - 1) / TILE;
+    const int64_t tiles_c = (cols + TILE - 1) / TILE;
+    const dim3 grid((unsigned)(tiles_r * tiles_c));
+    if (q && qt)
+        hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, true, true>), grid, dim3(THREADS),
+                           0, stream, x, rows, cols, ld, scale, q, qt, amax_cur, scale_inv_out,
+                           noop, tiles_c);
+    else if (q)
+        hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, true, false>), grid,
+                           dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt, amax_cur,
+                           scale_inv_out, noop, tiles_c);
+    else
+        hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, false, true>), grid,
+                           dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt, amax_cur,
+                           scale_inv_out, noop, tiles_c);
+    return hipGetLastError();
+}
+
+// An empty source still takes the scale-inverse snapshot.
+__global__ void scale_inv_only_kernel(const float *__restrict__ scale_ptr,
+                                      float *__restrict__ scale_inv_out,
+                                      const int32_t *__restrict__ noop) {
+    if (noop != nullptr && *noop != 0) return;
+    *scale_inv_out = 1.0f / *scale_ptr;
+}
+
+}  // namespace
+
+hipError_t launch_scale_inv_only(const float *scale, float *scale_inv_out, const int32_t *noop,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(scale_inv_only_kernel, dim3(1), dim3(1), 0, stream, scale, scale_inv_out,
+                       noop);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
+                                      int64_t ld, const float *scale, int fmt, uint8_t *q,
+                                      uint8_t *qt, float *amax_cur, float *scale_inv_out,
+                                      const int32_t *noop, hipStream_t stream) {
+    if (src == FP8_DTYPE_BF16) {
+        if (fmt == FP8_E4M3)
+            return launch_src_fmt<FP8_DTYPE_BF16, FP8_E4M3>(x, rows, cols, ld, scale, q, qt,
+                                                            amax_cur, scale_inv_out, noop, stream);
+        return launch_src_fmt<FP8_DTYPE_BF16, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
+                                                        scale_inv_out, noop, stream);
+    }
+    if (fmt == FP8_E4M3)
+        return launch_src_fmt<FP8_DTYPE_FP32, FP8_E4M3>(x, rows, cols, ld, scale, q, qt, amax_cur,
+                                                        scale_inv_out, noop, stream);
+    return launch_src_fmt<FP8_DTYPE_FP32, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
+                                                    scale_inv_out, noop, stream);
+}
+
+}  // namespace fp8dsl

@@ -1,0 +1,33 @@
+// Internal declarations shared by the kernels and the C-ABI layer of the
+// delayed-scaling FP8 linear library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8dsl.h"
+
+namespace fp8dsl {
+
+// Launchers: each validates nothing (the C-ABI layer has done that), enqueues
+// one kernel on `stream` and returns the launch status.
+hipError_t launch_scale_update(float *hist, float *amax_cur, float *scale, float *scale_inv,
+                               const uint8_t *fmt, int T, int H, int margin,
+                               hipStream_t stream);
+
+hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
+                                      int64_t ld, const float *scale, int fmt, uint8_t *q,
+                                      uint8_t *qt, float *amax_cur, float *scale_inv_out,
+                                      const int32_t *noop, hipStream_t stream);
+
+hipError_t launch_scale_inv_only(const float *scale, float *scale_inv_out, const int32_t *noop,
+                                 hipStream_t stream);
+
+// C[i, j] = out( sum_k dec(A[i, k]) dec(B[j, k]) * (*sinv_a) * (*sinv_b) + bias[j] )
+// A [M, K], B [N, K] row-major FP8; C [M, N] row-major, bf16 (out_dtype 0) or
+// fp32 (1).  bias is bf16 [N] or nullptr.
+hipError_t launch_gemm_nt(const uint8_t *A, int fa, const uint8_t *B, int fb, int64_t M,
+                          int64_t N, int64_t K, const float *sinv_a, const float *sinv_b,
+                          const uint16_t *bias, int out_dtype, void *C, hipStream_t stream);
+
+}  // namespace fp8dsl

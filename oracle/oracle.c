@@ -41,6 +41,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_E4M3 0
@@ -259,12 +260,19 @@ static void orc_store_out(void *out, int out_kind, int64_t idx, double y) {
         ((float *)out)[idx] = (float)y;
 }
 
-/* One output of C = A . B^T with A [*, K] (lda), B [*, K] (ldb), both FP8. */
-static double orc_dot(const uint8_t *A, int fa, int64_t lda, const uint8_t *B,
-                      int fb, int64_t ldb, int64_t i, int64_t j, int64_t K) {
+/* Decoded copy of rows [0, n) of an FP8 matrix with K columns (stride ld). */
+static double *orc_decode_rows(const uint8_t *X, int fmt, int64_t ld, int64_t n, int64_t K) {
+    double *d = (double *)malloc((size_t)(n * K > 0 ? n * K : 1) * sizeof(double));
+    if (!d) return NULL;
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = 0; k < K; ++k) d[i * K + k] = orc_fp8_decode(X[i * ld + k], fmt);
+    return d;
+}
+
+/* sum_k a[k] * b[k], k ascending, in fp64 (FP8 x FP8 products are exact). */
+static double orc_dot(const double *a, const double *b, int64_t K) {
     double acc = 0.0;
-    for (int64_t k = 0; k < K; ++k)
-        acc += orc_fp8_decode(A[i * lda + k], fa) * orc_fp8_decode(B[j * ldb + k], fb);
+    for (int64_t k = 0; k < K; ++k) acc += a[k] * b[k];
     return acc;
 }
 
@@ -284,12 +292,17 @@ int orc_gemm_nt(const uint8_t *A, int fa, int64_t lda, const uint8_t *B, int fb,
     if (orc_get_fmt(fa, &f) || orc_get_fmt(fb, &f) || M < 0 || N < 0 || K < 0 ||
         (out_kind != 0 && out_kind != 1))
         return -1;
+    double *da = orc_decode_rows(A, fa, lda, M, K);
+    double *db = orc_decode_rows(B, fb, ldb, N, K);
+    if (!da || !db) { free(da); free(db); return -1; }
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j) {
-            double acc = orc_dot(A, fa, lda, B, fb, ldb, i, j, K);
+            double acc = orc_dot(da + i * K, db + j * K, K);
             double y = acc * (double)sinv_a * (double)sinv_b + orc_bias_at(bias, j);
             orc_store_out(out, out_kind, i * ldo + j, y);
         }
+    free(da);
+    free(db);
     return 0;
 }
 
@@ -303,10 +316,19 @@ int orc_gemm_nt_sampled(const uint8_t *A, int fa, int64_t lda, const uint8_t *B,
     if (orc_get_fmt(fa, &f) || orc_get_fmt(fb, &f) || K < 0 || count < 0 ||
         (out_kind != 0 && out_kind != 1))
         return -1;
+    double *da = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    double *db = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    if (!da || !db) { free(da); free(db); return -1; }
     for (int64_t s = 0; s < count; ++s) {
-        double acc = orc_dot(A, fa, lda, B, fb, ldb, rows[s], cols[s], K);
+        for (int64_t k = 0; k < K; ++k) {
+            da[k] = orc_fp8_decode(A[rows[s] * lda + k], fa);
+            db[k] = orc_fp8_decode(B[cols[s] * ldb + k], fb);
+        }
+        double acc = orc_dot(da, db, K);
         double y = acc * (double)sinv_a * (double)sinv_b + orc_bias_at(bias, cols[s]);
         orc_store_out(out, out_kind, s, y);
     }
+    free(da);
+    free(db);
     return 0;
 }

@@ -1,0 +1,101 @@
+"""The C-ABI library loads on the CPU host and exports every declared symbol;
+argument validation rejects bad calls before anything touches a device.
+No compute call is made here (there is no GPU on the build host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delayed_scaling_linear_amd as dsl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fp8_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
+                 "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(dsl.library_path)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_host_only_calls():
+    assert dsl.fp8_abi_version() == 1
+    assert dsl.fp8_status_string(0) == "FP8_OK"
+    assert "SHAPE" in dsl.fp8_status_string(-2)
+    assert "unknown" in dsl.fp8_status_string(-99)
+
+
+def _desc(rows, cols, fmt=0, data=0x1000, data_t=0x2000, sinv=0x3000):
+    return dsl._Desc(data, data_t, sinv, fmt, 0, rows, cols)
+
+
+def test_validation_rejects_before_device_use():
+    L = dsl.lib()
+    byref = ctypes.byref
+    # scale update: bad H, margin, algo, T; NULL pointers.
+    assert L.fp8_scale_update(1, 1, 1, 1, 1, 4, 0, 0, 0, None) == -5
+    assert L.fp8_scale_update(1, 1, 1, 1, 1, 4, 16, 200, 0, None) == -5
+    assert L.fp8_scale_update(1, 1, 1, 1, 1, 4, 16, 0, 1, None) == -5
+    assert L.fp8_scale_update(1, 1, 1, 1, 1, -1, 16, 0, 0, None) == -5
+    assert L.fp8_scale_update(None, 1, 1, 1, 1, 4, 16, 0, 0, None) == -1
+    assert L.fp8_scale_update(None, None, None, None, None, 0, 16, 0, 0, None) == 0
+    # cast: shape multiples, ld, format, alignment, NULLs.
+    d = _desc(32, 48)
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 40, 48, 0x10, byref(_desc(32, 40)), 0, None, None) == -2
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 40, 0x10, byref(d), 0, None, None) == -2
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 52, 0x10, byref(d), 0, None, None) == -2
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 48, 0x10, byref(_desc(16, 48)), 0, None, None) == -2
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 48, 0x10, byref(_desc(32, 48, fmt=2)), 0, None, None) == -4
+    assert L.fp8_cast_transpose_amax(0x4000, 2, 32, 48, 48, 0x10, byref(d), 0, None, None) == -5
+    assert L.fp8_cast_transpose_amax(0x4001, 0, 32, 48, 48, 0x10, byref(d), 0, None, None) == -3
+    assert L.fp8_cast_transpose_amax(None, 0, 32, 48, 48, 0x10, byref(d), 0, None, None) == -1
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 48, None, byref(d), 0, None, None) == -1
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 48, 0x10, byref(_desc(32, 48, data=0, data_t=0)), 0, None, None) == -1
+    assert L.fp8_cast_transpose_amax(0x4000, 0, 32, 48, 48, 0x10, None, 0, None, None) == -1
+    # GEMMs: K multiple of 16, output row multiple of 8, matching inner dims.
+    x, w = _desc(64, 40), _desc(32, 40)
+    assert L.fp8_linear_fwd(byref(x), byref(w), None, 0x5000, None) == -2
+    x, w = _desc(64, 48), _desc(36, 48)
+    assert L.fp8_linear_fwd(byref(x), byref(w), None, 0x5000, None) == -2
+    x, w = _desc(64, 48), _desc(32, 64)
+    assert L.fp8_linear_fwd(byref(x), byref(w), None, 0x5000, None) == -2
+    x, w = _desc(64, 48), _desc(32, 48, fmt=3)
+    assert L.fp8_linear_fwd(byref(x), byref(w), None, 0x5000, None) == -4
+    x, w = _desc(64, 48), _desc(32, 48)
+    assert L.fp8_linear_fwd(byref(x), byref(w), None, None, None) == -1
+    assert L.fp8_linear_fwd(byref(x), byref(w), None, 0x5008, None) == -3
+    assert L.fp8_linear_fwd(byref(x), byref(w), 0x6002, 0x5000, None) == -3
+    assert L.fp8_linear_fwd(byref(_desc(0, 48)), byref(w), None, None, None) == 0
+    dy, wt = _desc(64, 32), _desc(32, 48)
+    assert L.fp8_linear_dgrad(byref(dy), byref(_desc(48, 48)), 0x5000, None) == -2
+    assert L.fp8_linear_dgrad(byref(dy), byref(_desc(32, 44)), 0x5000, None) == -2
+    assert L.fp8_linear_wgrad(byref(dy), byref(_desc(64, 48)), 0x5000, 2, None) == -5
+    assert L.fp8_linear_wgrad(byref(dy), byref(_desc(48, 48)), 0x5000, 1, None) == -2
+    assert L.fp8_linear_wgrad(byref(_desc(40, 32)), byref(_desc(40, 48)), 0x5000, 1, None) == -2
+
+
+def test_binding_checks_tensor_arguments():
+    import torch
+    with pytest.raises(ValueError):
+        dsl.fp8_cast_transpose_amax(torch.zeros(16, 16, dtype=torch.bfloat16),
+                                    torch.ones(1), dsl.Float8Tensor(None, None, torch.ones(1), 0, 16, 16))
+    with pytest.raises(TypeError):
+        dsl.fp8_cast_transpose_amax(torch.zeros(16, 16, dtype=torch.float16),
+                                    torch.ones(1), dsl.Float8Tensor(None, None, torch.ones(1), 0, 16, 16))

@@ -1,0 +1,159 @@
+"""GPU parity: fp8_cast_transpose_amax against the oracle, bit-exact (codes,
+transposed codes, amax and scale-inverse), through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import delayed_scaling_linear_amd as dsl
+import oracle
+import workloads
+from tests.gpu_util import DEV, bits16, bits8, f32_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_cast(x_dev, scale, fmt, *, q=True, qt=True, amax_in=0.0, noop=None):
+    R, C = x_dev.shape
+    out = dsl.Float8Tensor.empty(R, C, fmt, data=q, transpose=qt, device=DEV)
+    if q:
+        out.data.fill_(0xAA)
+    if qt:
+        out.data_t.fill_(0xAA)
+    s = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    amax = torch.tensor([amax_in], dtype=torch.float32, device=DEV)
+    dsl.fp8_cast_transpose_amax(x_dev, s, out, amax, noop_flag=noop)
+    torch.cuda.synchronize()
+    return out, amax
+
+
+def _oracle_src(x_cpu):
+    if x_cpu.dtype == torch.bfloat16:
+        return bits16(x_cpu)
+    return x_cpu.numpy()
+
+
+def _check(x_cpu, scale, fmt, q=True, qt=True, amax_in=0.0):
+    out, amax = _gpu_cast(x_cpu.to(DEV), scale, fmt, q=q, qt=qt, amax_in=amax_in)
+    oq, oqt, oamax, osinv = oracle.cast_transpose_amax(_oracle_src(x_cpu), scale, fmt,
+                                                       want_q=q, want_qt=qt, amax_in=amax_in)
+    if q:
+        np.testing.assert_array_equal(bits8(out.data), oq)
+    if qt:
+        np.testing.assert_array_equal(bits8(out.data_t), oqt)
+    assert f32_bits(amax)[0] == np.float32(oamax).view(np.uint32), (float(amax[0]), oamax)
+    if np.isnan(osinv):
+        assert np.isnan(f32_bits(out.scale_inv).view(np.float32)[0])
+    else:
+        assert f32_bits(out.scale_inv)[0] == np.float32(osinv).view(np.uint32)
+
+
+SCALES = [1.0, 448.0, 0.0009765625, 3.3333333, 57344.0, 1.7e-3, 2.0 ** -20, 1e30]
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+@pytest.mark.parametrize("scale", SCALES)
+def test_every_bf16_pattern(fmt, scale):
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    x = bits.reshape(256, 256).contiguous()
+    _check(x, scale, fmt)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+@pytest.mark.parametrize("scale", [0.0, float("inf"), float("nan"), -2.0])
+def test_special_scales(fmt, scale):
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    _check(bits.reshape(256, 256).contiguous(), scale, fmt)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_random_fp32_patterns(fmt):
+    g = torch.Generator().manual_seed(17)
+    raw = torch.randint(-2 ** 31, 2 ** 31 - 1, (512, 1024), generator=g, dtype=torch.int64)
+    x = raw.to(torch.int32).view(torch.float32)
+    # half of the rows concentrated on the FP8 grid
+    e = torch.empty(256, 1024).uniform_(-24, 20, generator=g)
+    x[:256] = (2.0 ** e) * torch.randn(256, 1024, generator=g)
+    for scale in (1.0, 0.37, 1024.0):
+        _check(x, scale, fmt)
+
+
+def test_worked_values_fp32_source():
+    # Part 2 blog, worked cast table: fp32 source values.
+    v = torch.tensor([2.073093891143, -0.78251332044, -0.47084918620, -1.32557279110],
+                     dtype=torch.float32)
+    x = torch.zeros(16, 16, dtype=torch.float32)
+    x[0, :4] = v
+    out4, _ = _gpu_cast(x.to(DEV), 1.0, oracle.E4M3)
+    out5, _ = _gpu_cast(x.to(DEV), 1.0, oracle.E5M2)
+    assert list(oracle.fp8_decode(bits8(out4.data)[0, :4], oracle.E4M3)) == [2.0, -0.8125, -0.46875, -1.375]
+    assert list(oracle.fp8_decode(bits8(out5.data)[0, :4], oracle.E5M2)) == [2.0, -0.75, -0.5, -1.25]
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (128, 256), (400, 272), (272, 400), (144, 1040),
+                                   (512, 128)])
+@pytest.mark.parametrize("src", ["bf16", "fp32"])
+def test_shapes_and_ragged_tiles(shape, src):
+    g = torch.Generator().manual_seed(shape[0] * 7 + shape[1])
+    x = torch.randn(*shape, generator=g) * 3
+    x = x.to(torch.bfloat16) if src == "bf16" else x
+    _check(x, 41.5, oracle.E4M3)
+    _check(x, 41.5, oracle.E5M2, q=False)
+    _check(x, 41.5, oracle.E4M3, qt=False)
+
+
+def test_leading_dimension_and_amax_accumulation():
+    g = torch.Generator().manual_seed(5)
+    big = (torch.randn(96, 200, generator=g) * 2).to(torch.bfloat16).to(DEV)
+    view = big[:, 16:176]           # ld = 200, cols = 160, 32-byte offset
+    assert view.stride(0) == 200
+    out, amax = _gpu_cast(view, 7.0, oracle.E4M3, amax_in=1e4)
+    oq, oqt, oamax, _ = oracle.cast_transpose_amax(bits16(view.contiguous()), 7.0, oracle.E4M3,
+                                                   amax_in=1e4)
+    np.testing.assert_array_equal(bits8(out.data), oq)
+    np.testing.assert_array_equal(bits8(out.data_t), oqt)
+    assert float(amax[0]) == 1e4 == oamax
+    # several casts of one tensor in a step accumulate the max
+    s = torch.tensor([1.0], device=DEV)
+    a = torch.zeros(1, device=DEV)
+    t1 = dsl.Float8Tensor.empty(16, 32, 0, device=DEV)
+    dsl.fp8_cast_transpose_amax(torch.full((16, 32), 3.0, device=DEV), s, t1, a)
+    dsl.fp8_cast_transpose_amax(torch.full((16, 32), -5.0, device=DEV), s, t1, a)
+    dsl.fp8_cast_transpose_amax(torch.full((16, 32), 4.0, device=DEV), s, t1, a)
+    torch.cuda.synchronize()
+    assert float(a[0]) == 5.0
+
+
+def test_noop_flag_skips_everything():
+    x = torch.ones(32, 32, dtype=torch.bfloat16, device=DEV)
+    flag = torch.ones(1, dtype=torch.int32, device=DEV)
+    out, amax = _gpu_cast(x, 2.0, oracle.E4M3, amax_in=0.0, noop=flag)
+    assert (bits8(out.data) == 0xAA).all() and (bits8(out.data_t) == 0xAA).all()
+    assert float(amax[0]) == 0.0 and float(out.scale_inv[0]) == 1.0
+    flag.zero_()
+    out, amax = _gpu_cast(x, 2.0, oracle.E4M3, noop=flag)
+    assert (bits8(out.data) == 0x40).all()      # 2.0 in E4M3
+    assert float(amax[0]) == 1.0 and float(out.scale_inv[0]) == 0.5
+
+
+def test_empty_tensor_takes_scale_inv_only():
+    x = torch.empty(0, 32, dtype=torch.bfloat16, device=DEV)
+    out = dsl.Float8Tensor.empty(0, 32, 0, device=DEV)
+    s = torch.tensor([4.0], device=DEV)
+    a = torch.zeros(1, device=DEV)
+    dsl.fp8_cast_transpose_amax(x, s, out, a)
+    torch.cuda.synchronize()
+    assert float(out.scale_inv[0]) == 0.25 and float(a[0]) == 0.0
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_full_size_cast_workload(fmt):
+    """[4096, 4096] bf16 N(0,1) with 0.1% outliers x1e3: the measured cast."""
+    x = workloads.cast_only()
+    scale = 448.0 / 3920.0 if fmt == oracle.E4M3 else 57344.0 / 3920.0
+    _check(x, scale, fmt)
+
+
+def test_full_size_gradient_cast():
+    """dY [8192, 8192] ~N(0, 1e-3) to E5M2 with both layouts."""
+    x = workloads.mlp_grad()
+    _check(x, 57344.0 / 0.005, oracle.E5M2)

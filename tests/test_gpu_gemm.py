@@ -1,0 +1,155 @@
+"""GPU parity: the FP8 GEMM entry points against the oracle (relative
+tolerance 1e-2 on identical FP8 operands), through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import delayed_scaling_linear_amd as dsl
+import oracle
+import workloads
+from tests.gpu_util import DEV, assert_gemm_close, bf16_values, bits16, f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _f8(codes: torch.Tensor, fmt: int, sinv: float, transpose_only=False) -> dsl.Float8Tensor:
+    rows, cols = codes.shape
+    d = codes.to(DEV).contiguous()
+    si = torch.tensor([sinv], dtype=torch.float32, device=DEV)
+    if transpose_only:
+        # `codes` is given as the transpose [cols', rows'] of the logical tensor.
+        return dsl.Float8Tensor(None, d, si, fmt, cols, rows)
+    return dsl.Float8Tensor(d, None, si, fmt, rows, cols)
+
+
+def _bias(n, seed):
+    return workloads.normal_bf16((n,), 0.5, seed)
+
+
+def _ref(A, fa, B, fb, sa, sb, bias=None, out_kind=oracle.OUT_BF16):
+    r = oracle.gemm_nt(A.numpy(), fa, B.numpy(), fb, sa, sb,
+                       bias=None if bias is None else bits16(bias), out_kind=out_kind)
+    return bf16_values(r) if out_kind == oracle.OUT_BF16 else r.astype(np.float64)
+
+
+SHAPES = [(128, 512, 256),       # the tiny forward layer
+          (256, 256, 128),
+          (200, 264, 272),       # ragged M, N and a K tail
+          (16, 8, 16),
+          (300, 776, 2064),
+          (1, 1024, 48),
+          (520, 136, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fwd_shapes_formats(M, N, K, fa, fb):
+    A = workloads.random_fp8_codes((M, K), M + K + fa, fa)
+    B = workloads.random_fp8_codes((N, K), N + K + 7 * fb, fb)
+    bias = _bias(N, N)
+    sa, sb = 1.0 / 37.0, 3.0 / 448.0
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_fwd(_f8(A, fa, sa), _f8(B, fb, sb), bias.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = _ref(A, fa, B, fb, np.float32(sa), np.float32(sb), bias)
+    assert_gemm_close(bf16_values(bits16(y)), ref, f"fwd {M}x{N}x{K} {fa}{fb}")
+
+
+def test_fwd_without_bias_and_k_zero():
+    A = workloads.random_fp8_codes((64, 128), 1, 0)
+    B = workloads.random_fp8_codes((32, 128), 2, 0)
+    y = torch.empty(64, 32, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_fwd(_f8(A, 0, 0.5), _f8(B, 0, 0.25), None, y)
+    torch.cuda.synchronize()
+    assert_gemm_close(bf16_values(bits16(y)), _ref(A, 0, B, 0, 0.5, 0.25), "fwd no bias")
+    # K == 0: the output is the bias
+    bias = _bias(32, 9)
+    A0 = torch.empty(64, 0, dtype=torch.uint8)
+    B0 = torch.empty(32, 0, dtype=torch.uint8)
+    dsl.fp8_linear_fwd(dsl.Float8Tensor(None, None, torch.ones(1, device=DEV), 0, 64, 0),
+                       dsl.Float8Tensor(None, None, torch.ones(1, device=DEV), 0, 32, 0),
+                       bias.to(DEV), y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits16(y), np.broadcast_to(bits16(bias), (64, 32)))
+    del A0, B0
+
+
+def test_exact_cases():
+    """All-ones operands give acc = K exactly; an FP8 identity operand gives
+    y = dec(A) * sinv_a * sinv_b exactly (power-of-two scale-inverses)."""
+    K = 2048
+    A = torch.full((256, K), 0x38, dtype=torch.uint8)     # 1.0 in E4M3
+    B = torch.full((128, K), 0x3C, dtype=torch.uint8)     # 1.0 in E5M2
+    yb = torch.empty(256, 128, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_fwd(_f8(A, 0, 1.0), _f8(B, 1, 1.0), None, yb)
+    eye = torch.zeros(256, 256, dtype=torch.uint8)
+    eye.fill_diagonal_(0x38)
+    A2 = workloads.random_fp8_codes((64, 256), 11, 0)
+    y2 = torch.empty(64, 256, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_fwd(_f8(A2, 0, 0.5), _f8(eye, 0, 0.25), None, y2)
+    torch.cuda.synchronize()
+    assert (bf16_values(bits16(yb)) == K).all()
+    want = oracle.fp8_decode(A2.numpy(), 0) * 0.125
+    np.testing.assert_array_equal(bf16_values(bits16(y2)), want)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 512, 256), (272, 208, 152), (8192, 8192, 2048)])
+def test_dgrad_and_wgrad_entry_points(M, N, K):
+    """dgrad reads W's transpose, wgrad both transposes; the oracle composes
+    the same products from the untransposed codes."""
+    dY = workloads.random_fp8_codes((M, N), 3, 1)
+    W = workloads.random_fp8_codes((N, K), 4, 0)
+    X = workloads.random_fp8_codes((M, K), 5, 0)
+    s_dy, s_w, s_x = 1.0 / 4096.0, 1.0 / 300.0, 1.0 / 7.0
+    dev = {k: v.to(DEV) for k, v in (("dY", dY), ("W", W), ("X", X))}
+    dyT = dsl.Float8Tensor(dev["dY"], dev["dY"].t().contiguous(),
+                           torch.tensor([s_dy], device=DEV), 1, M, N)
+    wT = dsl.Float8Tensor(None, dev["W"].t().contiguous(), torch.tensor([s_w], device=DEV), 0, N, K)
+    xT = dsl.Float8Tensor(None, dev["X"].t().contiguous(), torch.tensor([s_x], device=DEV), 0, M, K)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    dw = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    dwb = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_dgrad(dyT, wT, dx)
+    dsl.fp8_linear_wgrad(dyT, xT, dw)
+    dsl.fp8_linear_wgrad(dyT, xT, dwb)
+    torch.cuda.synchronize()
+    s_dy, s_w, s_x = np.float32(s_dy), np.float32(s_w), np.float32(s_x)
+    dYn, Wn, Xn = dY.numpy(), W.numpy(), X.numpy()
+    if M * N * K <= 2 ** 27:
+        ref_dx = oracle.gemm_nt(dYn, 1, np.ascontiguousarray(Wn.T), 0, s_dy, s_w)
+        assert_gemm_close(bf16_values(bits16(dx)), bf16_values(ref_dx), "dgrad")
+        ref_dw = oracle.gemm_nt(np.ascontiguousarray(dYn.T), 1, np.ascontiguousarray(Xn.T), 0,
+                                s_dy, s_x, out_kind=oracle.OUT_FP32)
+        assert_gemm_close(f32(dw).astype(np.float64), ref_dw.astype(np.float64), "wgrad fp32")
+        ref_dwb = oracle.gemm_nt(np.ascontiguousarray(dYn.T), 1, np.ascontiguousarray(Xn.T), 0,
+                                 s_dy, s_x)
+        assert_gemm_close(bf16_values(bits16(dwb)), bf16_values(ref_dwb), "wgrad bf16")
+    else:
+        rng = np.random.default_rng(1)
+        n = 1500
+        r, c = rng.integers(0, M, n), rng.integers(0, K, n)
+        WT = np.ascontiguousarray(Wn.T)
+        ref = oracle.gemm_nt_sampled(dYn, 1, WT, 0, s_dy, s_w, r, c)
+        assert_gemm_close(bf16_values(bits16(dx))[r, c], bf16_values(ref), "dgrad sampled")
+        rn, ck = rng.integers(0, N, n), rng.integers(0, K, n)
+        dYT, XT = np.ascontiguousarray(dYn.T), np.ascontiguousarray(Xn.T)
+        ref = oracle.gemm_nt_sampled(dYT, 1, XT, 0, s_dy, s_x, rn, ck, out_kind=oracle.OUT_FP32)
+        assert_gemm_close(f32(dw)[rn, ck].astype(np.float64), ref.astype(np.float64), "wgrad sampled")
+
+
+def test_full_size_forward_sampled():
+    """M8192 K2048 N8192 (the toy-block MLP shape), sampled outputs plus
+    whole rows and columns, including the corners of the last tile."""
+    M, N, K = 8192, 8192, 2048
+    A = workloads.random_fp8_codes((M, K), 21, 0)
+    B = workloads.random_fp8_codes((N, K), 22, 0)
+    bias = _bias(N, 23)
+    sa, sb = np.float32(1 / 448.0), np.float32(1 / 3.0)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_fwd(_f8(A, 0, float(sa)), _f8(B, 0, float(sb)), bias.to(DEV), y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    r = np.concatenate([rng.integers(0, M, 3000), np.full(64, M - 1), np.arange(64)])
+    c = np.concatenate([rng.integers(0, N, 3000), np.arange(N - 64, N), np.full(64, N - 1)])
+    ref = oracle.gemm_nt_sampled(A.numpy(), 0, B.numpy(), 0, sa, sb, r, c, bias=bits16(bias))
+    assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), "fwd full sampled")
