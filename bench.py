@@ -114,11 +114,11 @@ def cast_bandwidth(dsl, workloads, iters: int):
     return ms, gbs
 
 
-def cpu_baseline(workloads):
-    """The oracle (plain single-threaded C) on a bounded sample of the step:
-    the full X and W casts, 512 of the 8192 rows of the dY cast, and 32 of the
-    8192 output rows of each of the three GEMMs; extrapolated linearly to one
-    full step."""
+def cpu_baseline(workloads, rows: int = 128):
+    """The oracle (plain single-threaded C) on a bounded sample of one step:
+    the full X and W casts, 512 of the 8192 rows of the dY cast, and `rows` of
+    the output rows of each of the three GEMMs (operands cast by the oracle
+    itself); extrapolated linearly to one full step."""
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -128,21 +128,19 @@ def cpu_baseline(workloads):
 
     x, w, _ = workloads.mlp_forward(0)
     dy = workloads.mlp_grad()
-    xb, wb, dyb = b16(x), b16(w), b16(dy[:512])
     t0 = time.perf_counter()
-    qx, qxt, _, _ = oracle.cast_transpose_amax(xb, 100.0, 0)
-    qw, qwt, _, _ = oracle.cast_transpose_amax(wb, 4000.0, 0)
+    qx, qxt, ax, _ = oracle.cast_transpose_amax(b16(x), 448.0, 0)
+    qw, qwt, aw, _ = oracle.cast_transpose_amax(b16(w), 4000.0, 0)
     t_cast_xw = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.cast_transpose_amax(dyb, 5e6, 1)
+    qdy, _, _, _ = oracle.cast_transpose_amax(b16(dy[:512]), 5.0e6, 1, want_qt=False)
     t_cast_dy = (time.perf_counter() - t0) * (M / 512)
-    rows = 32
-    qdy = np.ascontiguousarray(qx[:, :2048].repeat(4, axis=1)[:rows])   # stand-in E5M2 codes
+    # rows of dY^T (= columns of dY), for the wgrad sample
+    _, qdyt, _, _ = oracle.cast_transpose_amax(b16(dy[:, :rows]), 5.0e6, 1, want_q=False)
     t0 = time.perf_counter()
-    oracle.gemm_nt(qx[:rows], 0, qw, 0, 1.0, 1.0)                      # fwd rows
-    oracle.gemm_nt(qdy, 1, qwt, 0, 1.0, 1.0)                           # dgrad rows
-    oracle.gemm_nt(np.ascontiguousarray(qwt[:rows].repeat(4, axis=1)), 1, qxt, 0, 1.0, 1.0,
-                   out_kind=oracle.OUT_FP32)                           # wgrad rows
+    oracle.gemm_nt(qx[:rows], 0, qw, 0, 1.0, 1.0)                          # fwd rows
+    oracle.gemm_nt(qdy[:rows], 1, qwt, 0, 1.0, 1.0)                        # dgrad rows
+    oracle.gemm_nt(qdyt, 1, qxt, 0, 1.0, 1.0, out_kind=oracle.OUT_FP32)    # wgrad rows
     t_gemm = (time.perf_counter() - t0) * (M / rows)
     t_step = t_cast_xw + t_cast_dy + t_gemm
     sample_s = t_cast_xw + t_cast_dy * 512 / M + t_gemm * rows / M
