@@ -93,6 +93,69 @@ __device__ __forceinline__ uint32_t patch_nan4(uint32_t w, const float x[4], flo
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
+// Sixteen consecutive source elements of one row, as loaded (16-byte loads).
+template <int SRC>
+struct SrcRow;
+
+template <>
+struct SrcRow<FP8_DTYPE_BF16> {
+    u32x4 v[2];
+    __device__ __forceinline__ void load(const void *x, int64_t elem) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(x) + elem);
+        v[0] = __builtin_nontemporal_load(p);
+        v[1] = __builtin_nontemporal_load(p + 1);
+    }
+    // Elements 4j .. 4j+3 as fp32 (exact widening).
+    __device__ __forceinline__ void get4(int j, float o[4]) const {
+        const u32x4 &q = v[j >> 1];
+        const uint32_t d0 = (j & 1) ? q.z : q.x;
+        const uint32_t d1 = (j & 1) ? q.w : q.y;
+        o[0] = bf16_lo(d0);
+        o[1] = bf16_hi(d0);
+        o[2] = bf16_lo(d1);
+        o[3] = bf16_hi(d1);
+    }
+    // Largest sign-cleared pattern, widened to the fp32 bit order.
+    __device__ __forceinline__ uint32_t amax_key() const {
+        ushort2_t m2 = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t d[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(ushort2_t, d[j] & 0x7FFF7FFFu));
+        }
+        return (uint32_t)max(m2.x, m2.y) << 16;
+    }
+};
+
+template <>
+struct SrcRow<FP8_DTYPE_FP32> {
+    f32x4 v[4];
+    __device__ __forceinline__ void load(const void *x, int64_t elem) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(x) + elem);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) v[h] = __builtin_nontemporal_load(p + h);
+    }
+    __device__ __forceinline__ void get4(int j, float o[4]) const {
+        o[0] = v[j].x;
+        o[1] = v[j].y;
+        o[2] = v[j].z;
+        o[3] = v[j].w;
+    }
+    __device__ __forceinline__ uint32_t amax_key() const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            m = max(m, __float_as_uint(v[h].x) & 0x7FFFFFFFu);
+            m = max(m, __float_as_uint(v[h].y) & 0x7FFFFFFFu);
+            m = max(m, __float_as_uint(v[h].z) & 0x7FFFFFFFu);
+            m = max(m, __float_as_uint(v[h].w) & 0x7FFFFFFFu);
+        }
+        return m;
+    }
+};
+
 // 4x4 byte transpose: in[r] holds bytes (r, c=0..3); out[c] holds (r=0..3, c).
 __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
     const uint32_t lo01 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
@@ -113,7 +176,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // SRC: FP8_DTYPE_BF16 or FP8_DTYPE_FP32.
 template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
-__global__ __launch_bounds__(THREADS) void cast_transpose_amax_kernel(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
+cast_transpose_amax_kernel(
     const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
     float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
@@ -131,79 +195,44 @@ __global__ __launch_bounds__(THREADS) void cast_transpose_amax_kernel(
     const int64_t row0 = tile_r * TILE;
     const int64_t col0 = tile_c * TILE;
 
-    const float s = *scale_ptr;
-    // NaN products from a non-NaN source only arise when s is 0, inf or NaN.
-    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
-    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
-
     const int cc = lane & 7;                 // 16-column chunk of the tile
     const int rg = wave * 8 + (lane >> 3);   // 4-row group of the tile
     const int64_t r = row0 + 4 * rg;
     const int64_t c = col0 + 16 * cc;
     const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
 
-    uint32_t key = 0;                        // sign-cleared max, fp32 bit order
-    uint32_t codes[4][4];                    // [row][word of 4 columns]
-
+    SrcRow<SRC> src[4];
     if (valid) {
-        float x[4][16];
-        if constexpr (SRC == FP8_DTYPE_BF16) {
-            const uint16_t *xb = static_cast<const uint16_t *>(xv);
-            u32x4 raw[4][2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 *p = reinterpret_cast<const u32x4 *>(xb + (r + i) * ld + c);
-                raw[i][0] = __builtin_nontemporal_load(p);
-                raw[i][1] = __builtin_nontemporal_load(p + 1);
+        for (int i = 0; i < 4; ++i) src[i].load(xv, (r + i) * ld + c);
+    }
+
+    const float s = *scale_ptr;
+    // NaN products from a non-NaN source only arise when s is 0, inf or NaN.
+    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
+    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
+
+    uint32_t key = 0;                        // sign-cleared max, fp32 bit order
+    if (valid) {
+        uint32_t codes[4][4];                // [row][word of 4 columns]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t row_key = src[i].amax_key();
+            key = max(key, row_key);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x4[4];
+                src[i].get4(j, x4);
+                codes[i][j] = encode4<FMT>(x4[0], x4[1], x4[2], x4[3], s);
             }
-            ushort2_t m2 = {0, 0};
+            if (s_special || row_key > 0x7F800000u) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t d[4] = {raw[i][h].x, raw[i][h].y, raw[i][h].z, raw[i][h].w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t a = d[j] & 0x7FFF7FFFu;
-                        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(ushort2_t, a));
-                        x[i][8 * h + 2 * j] = bf16_lo(d[j]);
-                        x[i][8 * h + 2 * j + 1] = bf16_hi(d[j]);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    float x4[4];
+                    src[i].get4(j, x4);
+                    codes[i][j] = patch_nan4(codes[i][j], x4, s);
                 }
             }
-            key = (uint32_t)max(m2.x, m2.y) << 16;
-        } else {
-            const float *xf = static_cast<const float *>(xv);
-            uint32_t m = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 *p = reinterpret_cast<const f32x4 *>(xf + (r + i) * ld + c);
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const f32x4 v = __builtin_nontemporal_load(p + h);
-                    x[i][4 * h + 0] = v.x;
-                    x[i][4 * h + 1] = v.y;
-                    x[i][4 * h + 2] = v.z;
-                    x[i][4 * h + 3] = v.w;
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) m = max(m, __float_as_uint(x[i][j]) & 0x7FFFFFFFu);
-            }
-            key = m;
-        }
-
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                codes[i][j] = encode4<FMT>(x[i][4 * j], x[i][4 * j + 1], x[i][4 * j + 2],
-                                           x[i][4 * j + 3], s);
-
-        if (s_special || key > 0x7F800000u) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) codes[i][j] = patch_nan4(codes[i][j], &x[i][4 * j], s);
         }
 
         if constexpr (WANT_Q) {
@@ -255,7 +284,10 @@ __global__ __launch_bounds__(THREADS) void cast_transpose_amax_kernel(
         uint32_t k = lds_amax[0];
 #pragma unroll
         for (int w = 1; w < THREADS / 64; ++w) k = max(k, lds_amax[w]);
-        if (k != 0) atomicMax(reinterpret_cast<unsigned int *>(amax_cur), k);
+        // amax_cur only grows while casts run, so a value already at least
+        // this block's maximum makes the atomic a no-op: skip it.
+        unsigned int *a = reinterpret_cast<unsigned int *>(amax_cur);
+        if (k > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, k);
     }
 }
 

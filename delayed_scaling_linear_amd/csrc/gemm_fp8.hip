@@ -25,6 +25,8 @@
 //     (bf16) or 16-byte (fp32) vectors;
 //   * M and N tails: out-of-range operand rows are clamped to the last valid
 //     row for loading and never stored; a K tail (K % 128 != 0) is zero-filled.
+#include <algorithm>
+
 #include "fp8dsl_internal.h"
 
 namespace fp8dsl {
@@ -32,8 +34,10 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;
 
@@ -43,11 +47,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Tile index of workgroup b.  Workgroups are dealt round-robin to the eight
+// XCDs (b % 8); when the tile count allows, each XCD gets a contiguous range
+// of tiles, walked in groups of GROUP_M tile rows, so that the workgroups
+// sharing an XCD's L2 also share A and B slabs.
+__device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
+    constexpr int XCDS = 8;
+    constexpr int GROUP_M = 4;
+    const int T = tiles_m * tiles_n;
+    int t = b;
+    if (T % XCDS == 0) t = (b % XCDS) * (T / XCDS) + b / XCDS;
+    const int per_group = GROUP_M * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * GROUP_M;
+    const int rows_here = min(GROUP_M, tiles_m - first_m);
+    const int r = t - g * per_group;
+    tm = first_m + r % rows_here;
+    tn = r / rows_here;
+}
+
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool HAS_BIAS>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
     const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
-    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_n) {
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n) {
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM;            // wave tile rows
     constexpr int WTN = BN / WN;            // wave tile cols
@@ -68,15 +91,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
     const int wm = wave / WN;
     const int wn = wave % WN;
 
-    const int tile_m = blockIdx.x / tiles_n;
-    const int tile_n = blockIdx.x - tile_m * tiles_n;
+    int tile_m, tile_n;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM;
     const int n0 = tile_n * BN;
 
     // Loader bookkeeping: chunk id = tid + i*NT -> (row = id / 8, kc = id % 8).
+    // Rows past M (N) are clamped to the last row: loaded, never stored.
     const uint8_t *a_src[LA];
     const uint8_t *b_src[LB];
-    int a_lds[LA], b_lds[LB], a_kc[LA], b_kc[LB];
+    int a_lds[LA], b_lds[LB];
+    const int kc16 = (tid & 7) * 16;        // same K chunk for every i (NT % 8 == 0)
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
         const int id = tid + i * NT;
@@ -84,7 +109,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
         const int grow = min(m0 + row, M - 1);
         a_src[i] = A + (int64_t)grow * K + kc * 16;
         a_lds[i] = row * BK + ((kc ^ (row & 7)) << 4);
-        a_kc[i] = kc * 16;
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
@@ -93,25 +117,30 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
         const int grow = min(n0 + row, N - 1);
         b_src[i] = B + (int64_t)grow * K + kc * 16;
         b_lds[i] = BM * BK + row * BK + ((kc ^ (row & 7)) << 4);
-        b_kc[i] = kc * 16;
     }
 
     u32x4 ra[LA], rb[LB];
-    auto load_global = [&](int k0) {
-        const bool full = (k0 + BK) <= K;
+    // Full K step: unconditional 16-byte loads.
+    auto load_full = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + k0);
+    };
+    // Last, partial K step: chunks at or past K read as zero (the address is
+    // pulled back in range and the value discarded).
+    auto load_tail = [&](int k0) {
+        const bool in = k0 + kc16 < K;
+        const int k = in ? k0 : 0;
 #pragma unroll
         for (int i = 0; i < LA; ++i) {
-            if (full || k0 + a_kc[i] < K)
-                ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
-            else
-                ra[i] = u32x4{0, 0, 0, 0};
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(a_src[i] + k);
+            ra[i] = in ? v : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < LB; ++i) {
-            if (full || k0 + b_kc[i] < K)
-                rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + k0);
-            else
-                rb[i] = u32x4{0, 0, 0, 0};
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(b_src[i] + k);
+            rb[i] = in ? v : u32x4{0, 0, 0, 0};
         }
     };
     auto store_lds = [&](int stage) {
@@ -137,15 +166,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
     const int off1 = (((fc0 + 1) ^ sw) << 4);
 
     const int nk = (K + BK - 1) / BK;
+    const int nfull = K / BK;               // steps with no K tail
     if (nk > 0) {
-        load_global(0);
+        if (nfull > 0) load_full(0); else load_tail(0);
         store_lds(0);
     }
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
         const int stage = kt & 1;
-        if (kt + 1 < nk) load_global((kt + 1) * BK);
+        if (kt + 1 < nfull) load_full((kt + 1) * BK);
+        else if (kt + 1 < nk) load_tail((kt + 1) * BK);
 
         const uint8_t *As = lds + stage * STAGE + (wm * WTM + frow) * BK;
         const uint8_t *Bs = lds + stage * STAGE + BM * BK + (wn * WTN + frow) * BK;
@@ -213,6 +244,300 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
     }
 }
 
+// Large-problem kernel: persistent, one 256-thread workgroup per CU.
+//
+//   * Each workgroup walks the 256 x 256 output tiles blockIdx.x,
+//     blockIdx.x + gridDim.x, ... as one continuous stream of 64-byte K
+//     stages, so the loads of the next tile's first stages are already in
+//     flight while the current tile's epilogue runs.
+//   * Four waves (one per SIMD) of 128 x 128, each a 4 x 4 grid of
+//     v_mfma_f32_32x32x64_f8f6f4 tiles (this instruction runs measurably
+//     faster per FLOP on gfx950 than 16x16x128); 256 fp32 accumulators per
+//     lane in AGPRs.
+//   * Stages live in three LDS buffers.  With one wave per SIMD nothing else
+//     can issue matrix-core work while a wave sits in a memory instruction,
+//     so every memory instruction of a stage is threaded between its 16
+//     matrix-core instructions:
+//        slots 0-7  : MFMA, then one LDS write committing stage k+2 and one
+//                     buffer load fetching stage k+3 into registers;
+//        barrier    : stage k+2 is in LDS for everyone;
+//        slots 8-15 : MFMA, then two LDS reads of stage k+1's fragments
+//                     (double-buffered fragment registers).
+//     Three buffers make one barrier per stage enough: stage k+2 overwrites
+//     the buffer of stage k-1, whose fragments were read before the previous
+//     barrier.  The loop has no data-dependent branches, so the compiler's
+//     wait counters stay exact (a conditional memory instruction makes it
+//     fall back to waiting for everything).
+//   * Operands come in with buffer loads (an SGPR descriptor per operand, a
+//     32-bit offset per lane); rows past M or N, K past the end and stages
+//     past the last tile fall outside the descriptor and read as zero.
+//   * LDS rows are 64 bytes; 16-byte chunk c of row r sits at chunk
+//     c ^ ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)): fragment reads (lanes on
+//     consecutive rows) and staging writes (4 lanes per row) are free of bank
+//     conflicts with 32 or with 64 banks.
+//
+// Fragment layout of v_mfma_f32_32x32x64_f8f6f4: lane l holds row l % 32 and
+// 32 K-bytes of half (l / 32) of the 64-byte K slice; A and B use the same
+// K assignment, so any consistent choice of bytes gives the same sum.  With
+// the B fragment passed first, lane l ends up with output row l % 32 and, for
+// register r, output column 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ int big_swz(int r) { return ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)); }
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void gemm_nt_big_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
+    const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int KS = 64;                  // K bytes per stage
+    constexpr int WT = 128;                 // wave tile (square)
+    constexpr int F = WT / 32;              // 4 x 4 fragments of 32 x 32
+    constexpr int LPT = BM * KS / 16 / 256; // 4 chunk loads per thread per operand
+    constexpr int STAGE = (BM + BN) * KS;   // 32 KiB
+    constexpr int OOB = 0x7FFFFFF0;         // an offset outside every descriptor
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int T = tiles_m * tiles_n;
+    if ((int)blockIdx.x >= T) return;
+    const int my_tiles = (T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(A), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, N * K, 0x00020000);
+
+    // Loader: thread -> (row = tid/4 + 64 i, chunk kc = tid % 4) of a stage;
+    // the 8 chunk loads of a stage alternate A, B, A, B, ...
+    const int kc = tid & 3;
+    const int lrow = tid >> 2;
+    const int rowstep = 64 * K;
+    const int st_off = lrow * KS + ((kc ^ big_swz(lrow)) << 4);   // + 4096 i (swizzle repeats)
+    // Per-lane operand offsets of tile number r of this workgroup (OOB when
+    // r is past its last tile).
+    auto tile_offsets = [&](int r, int &oa, int &ob) {
+        if (r < my_tiles) {
+            int tm, tn;
+            tile_of_block((int)blockIdx.x + r * (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+            oa = (tm * BM + lrow) * K + kc * 16;
+            ob = (tn * BN + lrow) * K + kc * 16;
+        } else {
+            oa = OOB;
+            ob = OOB;
+        }
+    };
+
+    u32x4 reg[2][2 * LPT];                  // two staging sets of one stage
+    // Load chunk q of a stage whose per-lane base offsets are (oa, ob), K
+    // byte offset k0, into staging set `set`.
+    auto load_one = [&](int set, int q, int oa, int ob, int k0) {
+        const bool in = k0 + kc * 16 < K;
+        const int i = q >> 1;
+        if (q & 1) {
+            const int o = (in && ob != OOB) ? ob + i * rowstep + k0 : OOB;
+            reg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, o, 0, 0));
+        } else {
+            const int o = (in && oa != OOB) ? oa + i * rowstep + k0 : OOB;
+            reg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, o, 0, 0));
+        }
+    };
+    auto store_one = [&](int set, int q, int buf_off) {
+        const int i = q >> 1;
+        uint8_t *dst = lds + buf_off + st_off + 4096 * i + ((q & 1) ? BM * KS : 0);
+        *reinterpret_cast<u32x4 *>(dst) = reg[set][q];
+    };
+
+    // Fragment reads: row (lane % 32) of each 32-row fragment, chunks
+    // 2*(lane/32) and +1.
+    const int frow = lane & 31;
+    const int fsw = big_swz(frow);
+    const int c0 = 2 * (lane >> 5);
+    const int fo0 = frow * KS + ((c0 ^ fsw) << 4);
+    const int fo1 = frow * KS + (((c0 + 1) ^ fsw) << 4);
+    const int a_fbase = wm * WT * KS;
+    const int b_fbase = BM * KS + wn * WT * KS;
+
+    v8i af[2][F], bf[2][F];
+    auto read_half = [&](v8i &dst, int off, int h) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + off + (h ? fo1 : fo0));
+        if (h == 0) { dst[0] = (int)v.x; dst[1] = (int)v.y; dst[2] = (int)v.z; dst[3] = (int)v.w; }
+        else        { dst[4] = (int)v.x; dst[5] = (int)v.y; dst[6] = (int)v.z; dst[7] = (int)v.w; }
+    };
+
+    v16f acc[F][F];
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Stages per tile, padded to even (a padded stage lies past K and adds
+    // nothing); the caller guarantees nk >= 4, so stage k+3 is in this tile
+    // or the next one.
+    const int nk = ((K + KS - 1) / KS + 1) & ~1;
+
+    int cur_a, cur_b, nxt_a, nxt_b;         // tile offsets: this tile, next tile
+    tile_offsets(0, cur_a, cur_b);
+    tile_offsets(1, nxt_a, nxt_b);
+
+    // Prologue: stages 0 and 1 committed, stage 2 in flight (set 0), the
+    // fragments of stage 0 in registers.
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2 * LPT; ++q) load_one(p, q, cur_a, cur_b, p * KS);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2 * LPT; ++q) store_one(p, q, p * STAGE);
+#pragma unroll
+    for (int q = 0; q < 2 * LPT; ++q) load_one(0, q, cur_a, cur_b, 2 * KS);
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            read_half(af[0][f], a_fbase + f * 32 * KS, h);
+            read_half(bf[0][f], b_fbase + f * 32 * KS, h);
+        }
+
+    const float s = (*sinv_a) * (*sinv_b);
+    const int half = lane >> 5;
+    int buf_next = STAGE;            // buffer of stage k+1
+    int buf_commit = 2 * STAGE;      // buffer of stage k+2
+
+    for (int r = 0; r < my_tiles; ++r) {
+        for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int k = kt + u;
+                const int cur = u, nxt = u ^ 1;
+                // Stage k+3: this tile, or the next tile's stage k+3-nk.
+                const bool same = k + 3 < nk;
+                const int ia = same ? cur_a : nxt_a;
+                const int ib = same ? cur_b : nxt_b;
+                const int ik = (same ? k + 3 : k + 3 - nk) * KS;
+#pragma unroll
+                for (int slot = 0; slot < 16; ++slot) {
+                    const int i = slot >> 2, j = slot & 3;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf[cur][j], af[cur][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+                    if (slot < 8) {
+                        store_one(cur, slot, buf_commit);        // stage k+2: set k%2
+                        load_one(nxt, slot, ia, ib, ik);         // stage k+3 -> set (k+1)%2
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+                        if (slot == 7) __syncthreads();
+                    } else {
+                        // Stage k+1's fragments, in the order the next stage's
+                        // first MFMAs need them: A0, B0..B3, A1..A3.
+                        const int f = slot - 8;
+                        if (f >= 1 && f <= 4) {
+                            read_half(bf[nxt][f - 1], buf_next + b_fbase + (f - 1) * 32 * KS, 0);
+                            read_half(bf[nxt][f - 1], buf_next + b_fbase + (f - 1) * 32 * KS, 1);
+                        } else {
+                            const int a = (f == 0) ? 0 : f - 4;
+                            read_half(af[nxt][a], buf_next + a_fbase + a * 32 * KS, 0);
+                            read_half(af[nxt][a], buf_next + a_fbase + a * 32 * KS, 1);
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+                    }
+                }
+                // Rotate the three buffers: next <- commit, commit <- current.
+                const int buf_cur = (buf_next == 0) ? 2 * STAGE : buf_next - STAGE;
+                buf_next = buf_commit;
+                buf_commit = buf_cur;
+            }
+        }
+
+        // Epilogue of tile r: lane holds row (lane % 32) of each fragment row
+        // block and, per group g of four registers, columns 8g + 4*(lane/32) .. +3.
+        int tm, tn;
+        tile_of_block((int)blockIdx.x + r * (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int gc = n0 + wn * WT + j * 32 + 8 * g + 4 * half;
+                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (HAS_BIAS) {
+                    if (gc < N) {
+                        const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
+                        bv[0] = __uint_as_float(b2.x << 16);
+                        bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                        bv[2] = __uint_as_float(b2.y << 16);
+                        bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < F; ++i) {
+                    const int gr = m0 + wm * WT + i * 32 + frow;
+                    const float y0 = acc[i][j][4 * g + 0] * s + bv[0];
+                    const float y1 = acc[i][j][4 * g + 1] * s + bv[1];
+                    const float y2 = acc[i][j][4 * g + 2] * s + bv[2];
+                    const float y3 = acc[i][j][4 * g + 3] * s + bv[3];
+                    if (gr < M && gc < N) {
+                        if constexpr (OUT == FP8_DTYPE_BF16) {
+                            uint16_t *C = static_cast<uint16_t *>(Cv);
+                            const bf16x4 o = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                            *reinterpret_cast<bf16x4 *>(C + (int64_t)gr * N + gc) = o;
+                        } else {
+                            float *C = static_cast<float *>(Cv);
+                            *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int j = 0; j < F; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        // The next tile becomes current; look one further ahead.
+        cur_a = nxt_a;
+        cur_b = nxt_b;
+        tile_offsets(r + 2, nxt_a, nxt_b);
+    }
+}
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_big(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
+                      const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
+    auto kern = gemm_nt_big_kernel<FA, FB, OUT, HAS_BIAS>;
+    constexpr int lds_bytes = 3 * (256 + 256) * 64;   // three 32 KiB stages
+    static bool attr_set[64];
+    static int cu_count[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const int tiles_m = (M + 255) / 256;
+    const int tiles_n = (N + 255) / 256;
+    const int grid = std::min(tiles_m * tiles_n, cu_count[dev]);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
+                       C, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
                       const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
@@ -233,7 +558,7 @@ hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(WM * WN * 64), lds_bytes, stream, A, B,
-                       M, N, K, sa, sb, bias, C, tiles_n);
+                       M, N, K, sa, sb, bias, C, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -241,10 +566,14 @@ template <int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
                       const float *sa, const float *sb, const uint16_t *bias, void *C,
                       hipStream_t stream) {
-    // Large problems: 256 x 256 tiles (128 x 128 per wave); small ones: 128 x 128.
-    if (M * N >= (int64_t)256 * 256 * 256)
-        return launch_cfg<256, 256, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa,
-                                                                 sb, bias, C, stream);
+    // Large problems: 256 x 256 tiles, four waves of 128 x 128 (32x32x64
+    // instructions); small ones: 128 x 128 tiles (16x16x128 instructions).
+    // The large kernel addresses operands with 32-bit buffer offsets.
+    // It also needs at least four 64-byte K stages.
+    const bool fits32 = (M + 256) * K < ((int64_t)1 << 31) && (N + 256) * K < ((int64_t)1 << 31);
+    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256)
+        return launch_big<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
+                                                 stream);
     return launch_cfg<128, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
                                                              bias, C, stream);
 }
