@@ -13,10 +13,12 @@ history 16):
 
 `value` is the step's GEMM throughput (3 x 2*8192*8192*2048 FLOP per step over
 the measured step time, casts and update included).  Per-kernel durations are
-taken with HIP events around each launch on the launch stream inside the
-timed region.  The cast-transpose-amax bandwidth is also measured on its own
-workload (bf16 [4096, 4096], 0.1% outliers) rotating over 640 MiB of buffers
-so that the 256 MiB last-level cache cannot serve it.
+taken with HIP events around each launch on the launch stream inside a second
+timed pass.  The roofline figures come from back-to-back launches between one
+event pair (the forward GEMM at the step's shape; the cast-transpose-amax on
+its own workload, bf16 [4096, 4096] with 0.1% outliers, rotating over 640 MiB
+of buffers so that the 256 MiB last-level cache cannot serve it), next to a
+measured device-to-device copy ceiling.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -88,8 +90,10 @@ def gpu_step(dsl, st, t: Timer | None):
 
 
 def cast_bandwidth(dsl, workloads, iters: int):
-    """configs: bf16 [4096, 4096] -> E4M3 codes + transpose + amax, rotating
-    over 10 buffer sets (640 MiB)."""
+    """bf16 [4096, 4096] -> E4M3 codes + transpose + amax, rotating over 10
+    buffer sets (640 MiB, more than the 256 MiB last-level cache).  One event
+    pair brackets `iters` back-to-back launches (an event pair around each
+    launch would add its own few microseconds to every call)."""
     dev = "cuda"
     src = workloads.cast_only().to(dev)
     nsets = 10
@@ -100,18 +104,58 @@ def cast_bandwidth(dsl, workloads, iters: int):
     for i in range(nsets):                                   # warm-up
         dsl.fp8_cast_transpose_amax(xs[i], scale, outs[i], amax)
     torch.cuda.synchronize()
-    t = Timer()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(iters):
-        j = i % nsets
-        tok = t.start("cast")
-        dsl.fp8_cast_transpose_amax(xs[j], scale, outs[j], amax)
-        t.stop(tok)
+        dsl.fp8_cast_transpose_amax(xs[i % nsets], scale, outs[i % nsets], amax)
+    e1.record()
     torch.cuda.synchronize()
-    ms = t.avg_ms("cast")
+    ms = e0.elapsed_time(e1) / iters
     gbs = CAST_BYTES / (ms * 1e-3) / 1e9
     del xs, outs
     torch.cuda.empty_cache()
     return ms, gbs
+
+
+def gemm_fwd_back_to_back(dsl, st, iters: int):
+    """The forward GEMM alone, `iters` back-to-back launches between one event
+    pair on the launch stream: its average duration per launch."""
+    for _ in range(2):
+        dsl.fp8_linear_fwd(st["qx"], st["qw"], st["b"], st["y"])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dsl.fp8_linear_fwd(st["qx"], st["qw"], st["b"], st["y"])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def copy_ceiling(mib: int = 256, iters: int = 20):
+    """Measured HBM ceiling: a device-to-device copy of `mib` MiB (read +
+    write bytes per second), rotating two buffer pairs."""
+    n = mib << 20
+    bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"),
+             torch.empty(n, dtype=torch.uint8, device="cuda")) for _ in range(2)]
+    for a, b in bufs:
+        a.fill_(1)
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        a, b = bufs[i % 2]
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del bufs
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(workloads, rows: int = 128):
@@ -212,9 +256,10 @@ def main():
             k["GB/s"] = round(4 * M * K / (ms * 1e-3) / 1e9, 1)
         kernels[name] = k
 
-    cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
-    fwd_ms = timer.avg_ms("gemm_fwd")
+    fwd_ms = gemm_fwd_back_to_back(dsl, st, max(args.steps, 10))
     fwd_tflops = GEMM_FLOP / (fwd_ms * 1e-3) / 1e12
+    cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
+    copy_gbs = copy_ceiling()
 
     result = {
         "metric": "FP8 GEMM TFLOP/s (M8192 K2048 N8192) + cast-transpose-amax HBM GB/s",
@@ -234,6 +279,8 @@ def main():
                    "M": M, "N": N, "K": K, "global_batch": 8, "seq_len": 1024,
                    "parallelism": "none (1 GPU)"},
         "gemm_fwd_tflops": round(fwd_tflops, 1),
+        "gemm_fwd_us": round(fwd_ms * 1e3, 2),
+        "hbm_copy_ceiling_gbs": round(copy_gbs, 1),
         "cast_transpose_amax_gbs": round(cast_gbs, 1),
         "cast_transpose_amax_us": round(cast_ms * 1e3, 2),
         "kernels": kernels,
@@ -243,7 +290,8 @@ def main():
                      "traffic": None},
         "roofline_cast": {"bound": "hbm", "kernel": "fp8_cast_transpose_amax bf16 [4096,4096]",
                           "achieved": round(cast_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(cast_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                          "frac": round(cast_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                          "measured_copy_ceiling_gbs": round(copy_gbs, 1)},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -90,6 +90,8 @@ int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t co
         return FP8_ERR_SHAPE;
     const int64_t tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
     if (tiles > INT32_MAX) return FP8_ERR_SHAPE;
+    // A 128-row tile of the source is addressed with 32-bit byte offsets.
+    if (128 * ld * (src == FP8_DTYPE_BF16 ? 2 : 4) >= ((int64_t)1 << 31)) return FP8_ERR_SHAPE;
     if (scale == nullptr) return FP8_ERR_NULL;
     const bool empty = (rows == 0 || cols == 0);
     // Nothing to cast in an empty tensor; the scale-inverse snapshot is still taken.

@@ -31,6 +31,8 @@
 // word index of (column c, row group g) = c*32 + (g ^ 4*(c/16)): the XOR keeps
 // the sixteen-lane groups that write one column word apiece in distinct banks
 // and leaves each 16-byte, 16-row read contiguous and in order.
+#include <algorithm>
+
 #include "fp8dsl_internal.h"
 
 namespace fp8dsl {
@@ -99,11 +101,13 @@ struct SrcRow;
 
 template <>
 struct SrcRow<FP8_DTYPE_BF16> {
+    static constexpr int kBytes = 2;
     u32x4 v[2];
-    __device__ __forceinline__ void load(const void *x, int64_t elem) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(x) + elem);
-        v[0] = __builtin_nontemporal_load(p);
-        v[1] = __builtin_nontemporal_load(p + 1);
+    // 16 elements at byte offset `off` of the descriptor (an offset outside
+    // it reads zeros and touches no memory).
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+        v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+        v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, 0));
     }
     // Elements 4j .. 4j+3 as fp32 (exact widening).
     __device__ __forceinline__ void get4(int j, float o[4]) const {
@@ -131,11 +135,12 @@ struct SrcRow<FP8_DTYPE_BF16> {
 
 template <>
 struct SrcRow<FP8_DTYPE_FP32> {
+    static constexpr int kBytes = 4;
     f32x4 v[4];
-    __device__ __forceinline__ void load(const void *x, int64_t elem) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(x) + elem);
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
 #pragma unroll
-        for (int h = 0; h < 4; ++h) v[h] = __builtin_nontemporal_load(p + h);
+        for (int h = 0; h < 4; ++h)
+            v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16 * h, 0, 0));
     }
     __device__ __forceinline__ void get4(int j, float o[4]) const {
         o[0] = v[j].x;
@@ -174,98 +179,119 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// SRC: FP8_DTYPE_BF16 or FP8_DTYPE_FP32.
+// Encode this lane's 4 x 16 block of the tile held in `src`, store its
+// row-major codes and its transposed 4-row words into the LDS tile `lt`.
 template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
-cast_transpose_amax_kernel(
-    const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
-    const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
-    float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
-    const int32_t *__restrict__ noop, int64_t tiles_c) {
-    if (noop != nullptr && *noop != 0) return;
-
-    __shared__ uint32_t lds_t[TILE * (TILE / 4)];   // transposed tile, 16 KiB
-    __shared__ uint32_t lds_amax[THREADS / 64];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int64_t tile_r = blockIdx.x / tiles_c;
-    const int64_t tile_c = blockIdx.x - tile_r * tiles_c;
-    const int64_t row0 = tile_r * TILE;
-    const int64_t col0 = tile_c * TILE;
-
-    const int cc = lane & 7;                 // 16-column chunk of the tile
-    const int rg = wave * 8 + (lane >> 3);   // 4-row group of the tile
-    const int64_t r = row0 + 4 * rg;
-    const int64_t c = col0 + 16 * cc;
-    const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
-
-    SrcRow<SRC> src[4];
-    if (valid) {
+__device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float s, bool s_special,
+                                             bool valid, uint8_t *__restrict__ q, int64_t r,
+                                             int64_t c, int64_t cols, int cc, int rg,
+                                             uint32_t *lt, uint32_t &key) {
+    uint32_t codes[4][4];                    // [row][word of 4 columns]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) src[i].load(xv, (r + i) * ld + c);
-    }
-
-    const float s = *scale_ptr;
-    // NaN products from a non-NaN source only arise when s is 0, inf or NaN.
-    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
-    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
-
-    uint32_t key = 0;                        // sign-cleared max, fp32 bit order
-    if (valid) {
-        uint32_t codes[4][4];                // [row][word of 4 columns]
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t row_key = src[i].amax_key();
+        key = max(key, row_key);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t row_key = src[i].amax_key();
-            key = max(key, row_key);
+        for (int j = 0; j < 4; ++j) {
+            float x4[4];
+            src[i].get4(j, x4);
+            codes[i][j] = encode4<FMT>(x4[0], x4[1], x4[2], x4[3], s);
+        }
+        if (s_special || row_key > 0x7F800000u) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float x4[4];
                 src[i].get4(j, x4);
-                codes[i][j] = encode4<FMT>(x4[0], x4[1], x4[2], x4[3], s);
-            }
-            if (s_special || row_key > 0x7F800000u) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float x4[4];
-                    src[i].get4(j, x4);
-                    codes[i][j] = patch_nan4(codes[i][j], x4, s);
-                }
+                codes[i][j] = patch_nan4(codes[i][j], x4, s);
             }
         }
-
-        if constexpr (WANT_Q) {
+    }
+    if constexpr (WANT_Q) {
+        if (valid) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 u32x4 *dst = reinterpret_cast<u32x4 *>(q + (r + i) * cols + c);
                 *dst = u32x4{codes[i][0], codes[i][1], codes[i][2], codes[i][3]};
             }
         }
-        if constexpr (WANT_QT) {
-            const int swz = 4 * cc;
+    }
+    if constexpr (WANT_QT) {
+        const int swz = 4 * cc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t in[4] = {codes[0][j], codes[1][j], codes[2][j], codes[3][j]};
-                uint32_t out[4];
-                transpose4x4(in, out);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t in[4] = {codes[0][j], codes[1][j], codes[2][j], codes[3][j]};
+            uint32_t out[4];
+            transpose4x4(in, out);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int tc = 16 * cc + 4 * j + b;          // tile column
-                    lds_t[tc * 32 + (rg ^ swz)] = out[b];
-                }
+            for (int b = 0; b < 4; ++b) {
+                const int tc = 16 * cc + 4 * j + b;          // tile column
+                lt[tc * 32 + (rg ^ swz)] = out[b];
             }
         }
     }
+}
 
-    if (amax_cur != nullptr) {
-        key = wave_max_u32(key);
-        if (lane == 0) lds_amax[wave] = key;
-    }
-    __syncthreads();
+// Persistent: workgroup b casts tiles b, b + gridDim.x, ... with the loads of
+// its next tile in flight while the current one is encoded and stored, and
+// a double-buffered LDS transpose tile (one barrier per tile).
+// SRC: FP8_DTYPE_BF16 or FP8_DTYPE_FP32.
+// Resident workgroups per CU: the double-buffered source needs 64 (bf16) or
+// 128 (fp32) registers per lane.
+template <int SRC>
+constexpr int kWavesPerSimd = (SRC == FP8_DTYPE_BF16) ? 3 : 2;
 
-    if constexpr (WANT_QT) {
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<SRC>))) void
+cast_transpose_amax_kernel(
+    const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
+    const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
+    float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
+    const int32_t *__restrict__ noop, int64_t tiles_c, int64_t ntiles) {
+    if (noop != nullptr && *noop != 0) return;
+
+    __shared__ uint32_t lds_t[2][TILE * (TILE / 4)];   // transposed tiles, 2 x 16 KiB
+    __shared__ uint32_t lds_amax[THREADS / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cc = lane & 7;                 // 16-column chunk of the tile
+    const int rg = wave * 8 + (lane >> 3);   // 4-row group of the tile
+    constexpr int EB = SrcRow<SRC>::kBytes;
+    const int64_t total_bytes = ((rows - 1) * ld + cols) * EB;
+
+    const float s = *scale_ptr;
+    // NaN products from a non-NaN source only arise when s is 0, inf or NaN.
+    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
+    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
+
+    // Source descriptor of tile t (empty when t is past the last tile) and
+    // this lane's byte offset in it.
+    auto tile_rsrc = [&](int64_t t, __amdgpu_buffer_rsrc_t &rs, uint32_t &off, int64_t &r,
+                         int64_t &c, bool &valid) {
+        const int64_t tr = t / tiles_c, tcn = t - (t / tiles_c) * tiles_c;
+        const int64_t row0 = tr * TILE, col0 = tcn * TILE;
+        r = row0 + 4 * rg;
+        c = col0 + 16 * cc;
+        valid = (t < ntiles) && (r < rows) && (c < cols);
+        const int64_t base = (t < ntiles) ? (row0 * ld + col0) * EB : 0;
+        const int64_t avail = (t < ntiles) ? total_bytes - base : 0;
+        const int32_t nrec = (int32_t)min(avail, (int64_t)0x7FFFFFFF);
+        rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(static_cast<const uint8_t *>(xv)) + base, (short)0, nrec,
+            0x00020000);
+        off = valid ? (uint32_t)(((4 * rg) * ld + 16 * cc) * EB) : 0x80000000u;
+    };
+    const uint32_t row_step = (uint32_t)(ld * EB);
+    auto load_tile = [&](SrcRow<SRC> (&dst)[4], __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dst[i].load(rs, off == 0x80000000u ? off : off + i * row_step);
+    };
+    auto store_t = [&](const uint32_t *lt, int64_t t) {
         // 8 lanes per column (16 rows each): 128-byte transposed segments.
+        const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
+        const int64_t row0 = tr * TILE, col0 = tcn * TILE;
         const int qd = lane & 7;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -274,20 +300,54 @@ cast_transpose_amax_kernel(
             const int64_t gr = row0 + 16 * qd;
             if (gc < cols && gr < rows) {
                 const int word = tc * 32 + ((4 * qd) ^ (4 * (tc >> 4)));
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(&lds_t[word]);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(&lt[word]);
                 *reinterpret_cast<u32x4 *>(qt + gc * rows + gr) = v;
+            }
+        }
+    };
+
+    uint32_t key = 0;                        // sign-cleared max, fp32 bit order
+    SrcRow<SRC> src[2][4];
+    __amdgpu_buffer_rsrc_t rs_cur, rs_nxt;
+    uint32_t off_cur, off_nxt;
+    int64_t r_cur, c_cur, r_nxt, c_nxt;
+    bool v_cur, v_nxt;
+    int64_t t = blockIdx.x;
+    tile_rsrc(t, rs_cur, off_cur, r_cur, c_cur, v_cur);
+    load_tile(src[0], rs_cur, off_cur);
+
+    for (; t < ntiles;) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (t < ntiles) {
+                const int64_t tn = t + gridDim.x;
+                tile_rsrc(tn, rs_nxt, off_nxt, r_nxt, c_nxt, v_nxt);
+                load_tile(src[u ^ 1], rs_nxt, off_nxt);           // empty past the end
+                encode_block<SRC, FMT, WANT_Q, WANT_QT>(src[u], s, s_special, v_cur, q, r_cur,
+                                                        c_cur, cols, cc, rg, lds_t[u], key);
+                __syncthreads();
+                if constexpr (WANT_QT) store_t(lds_t[u], t);
+                t = tn;
+                r_cur = r_nxt;
+                c_cur = c_nxt;
+                v_cur = v_nxt;
             }
         }
     }
 
-    if (amax_cur != nullptr && tid == 0) {
-        uint32_t k = lds_amax[0];
+    if (amax_cur != nullptr) {
+        key = wave_max_u32(key);
+        if (lane == 0) lds_amax[wave] = key;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t k = lds_amax[0];
 #pragma unroll
-        for (int w = 1; w < THREADS / 64; ++w) k = max(k, lds_amax[w]);
-        // amax_cur only grows while casts run, so a value already at least
-        // this block's maximum makes the atomic a no-op: skip it.
-        unsigned int *a = reinterpret_cast<unsigned int *>(amax_cur);
-        if (k > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, k);
+            for (int w = 1; w < THREADS / 64; ++w) k = max(k, lds_amax[w]);
+            // amax_cur only grows while casts run, so a value already at least
+            // this block's maximum makes the atomic a no-op: skip it.
+            unsigned int *a = reinterpret_cast<unsigned int *>(amax_cur);
+            if (k > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, k);
+        }
     }
 }
 
@@ -295,21 +355,32 @@ template <int SRC, int FMT>
 hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
                           const float *scale, uint8_t *q, uint8_t *qt, float *amax_cur,
                           float *scale_inv_out, const int32_t *noop, hipStream_t stream) {
+    static int cu_count[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cu_count[dev] == 0) {
+        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
     const int64_t tiles_r = (rows + TILE - 1) / TILE;
     const int64_t tiles_c = (cols + TILE - 1) / TILE;
-    const dim3 grid((unsigned)(tiles_r * tiles_c));
+    const int64_t ntiles = tiles_r * tiles_c;
+    // As many workgroups as fit on the chip at once, each looping over tiles.
+    const dim3 grid((unsigned)std::min<int64_t>(ntiles, (int64_t)cu_count[dev] * kWavesPerSimd<SRC>));
     if (q && qt)
         hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, true, true>), grid, dim3(THREADS),
                            0, stream, x, rows, cols, ld, scale, q, qt, amax_cur, scale_inv_out,
-                           noop, tiles_c);
+                           noop, tiles_c, ntiles);
     else if (q)
         hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, true, false>), grid,
                            dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt, amax_cur,
-                           scale_inv_out, noop, tiles_c);
+                           scale_inv_out, noop, tiles_c, ntiles);
     else
         hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, false, true>), grid,
                            dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt, amax_cur,
-                           scale_inv_out, noop, tiles_c);
+                           scale_inv_out, noop, tiles_c, ntiles);
     return hipGetLastError();
 }
 

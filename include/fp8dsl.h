@@ -151,7 +151,8 @@ int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *
  * noop_flag NULL, or a device int32: when it is non-zero at kernel time the
  *         call does nothing (weight caching under graph replay).
  * Constraints: rows, cols >= 0 and multiples of 16; x, data, data_t 16-byte
- * aligned; ld a multiple of 8 (bf16) or 4 (fp32).
+ * aligned; ld a multiple of 8 (bf16) or 4 (fp32); 128 * ld * element size
+ * below 2^31 bytes.
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_FORMAT,
  * FP8_ERR_ARG, FP8_ERR_LAUNCH.
  */
