@@ -47,6 +47,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cast-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--probe-kernels", action="store_true",
+                   help="launch the forward GEMM, the [4096,4096] cast and a 64 MiB device copy "
+                        "once each (after a warm-up) and exit: the command profiled for HBM "
+                        "traffic counters")
     return p.parse_args()
 
 
@@ -195,6 +199,47 @@ def cpu_baseline(workloads, rows: int = 128):
                        f"extrapolated to one step = {t_step:.0f} s")}
 
 
+def probe_kernels(dsl, workloads, st):
+    """One launch each of the kernels whose HBM traffic is reported, after a
+    warm-up, with a synchronisation between them (so counter collection sees
+    one dispatch each), plus a plain 64 MiB device copy whose traffic is known
+    exactly and calibrates the counters."""
+    src = workloads.cast_only().to("cuda")
+    out = dsl.Float8Tensor.empty(CAST_R, CAST_C, 0, device="cuda")
+    scale = torch.tensor([448.0 / 3920.0], device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    a = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        dsl.fp8_linear_fwd(st["qx"], st["qw"], st["b"], st["y"])
+        dsl.fp8_cast_transpose_amax(src, scale, out, amax)
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dsl.fp8_linear_fwd(st["qx"], st["qw"], st["b"], st["y"])
+    torch.cuda.synchronize()
+    dsl.fp8_cast_transpose_amax(src, scale, out, amax)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print("probe-kernels: fwd GEMM 8192x8192x2048, cast bf16 [4096,4096], copy 64 MiB", flush=True)
+
+
+def traffic_record(root: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    kernel sources, or None when the sources changed since the measurement."""
+    import hashlib
+    path = os.path.join(root, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    srcs = {}
+    for name in ("gemm_fp8.hip", "cast_transpose_amax.hip"):
+        with open(os.path.join(root, "delayed_scaling_linear_amd", "csrc", name), "rb") as f:
+            srcs[name] = hashlib.sha256(f.read()).hexdigest()[:16]
+    return {k: v for k, v in rec["kernels"].items() if rec["source_sha256"].get(v["source"]) == srcs[v["source"]]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -225,6 +270,9 @@ def main():
     for _ in range(args.warmup):
         gpu_step(dsl, st, None)
     torch.cuda.synchronize()
+    if args.probe_kernels:
+        probe_kernels(dsl, workloads, st)
+        return
 
     # Whole-step timing (no per-kernel events inside).
     t0 = time.perf_counter()
@@ -261,6 +309,7 @@ def main():
     cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
     copy_gbs = copy_ceiling()
 
+    traffic = traffic_record(root)
     result = {
         "metric": "FP8 GEMM TFLOP/s (M8192 K2048 N8192) + cast-transpose-amax HBM GB/s",
         "value": round(3 * GEMM_FLOP / (ms_step * 1e-3) / 1e12, 1),
@@ -287,10 +336,11 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_fwd (fp8_linear_fwd)",
                      "achieved": round(fwd_tflops, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": (traffic or {}).get("gemm_fwd", {}).get("bytes")},
         "roofline_cast": {"bound": "hbm", "kernel": "fp8_cast_transpose_amax bf16 [4096,4096]",
                           "achieved": round(cast_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(cast_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                          "frac": round(cast_gbs / HBM_PEAK_GBS, 4),
+                          "traffic": (traffic or {}).get("cast", {}).get("bytes"),
                           "measured_copy_ceiling_gbs": round(copy_gbs, 1)},
         "wall_s_timed": round(wall, 3),
     }

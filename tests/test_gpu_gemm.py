@@ -153,3 +153,22 @@ def test_full_size_forward_sampled():
     c = np.concatenate([rng.integers(0, N, 3000), np.arange(N - 64, N), np.full(64, N - 1)])
     ref = oracle.gemm_nt_sampled(A.numpy(), 0, B.numpy(), 0, sa, sb, r, c, bias=bits16(bias))
     assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), "fwd full sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 272),      # large-tile path with a K tail
+                                   (4104, 4104, 320),      # ragged M and N on the large-tile path
+                                   (8200, 2056, 2064)])    # ragged everything, several tiles per CU
+def test_large_path_tails_sampled(M, N, K):
+    A = workloads.random_fp8_codes((M, K), M + 1, 0)
+    B = workloads.random_fp8_codes((N, K), N + 2, 1)
+    bias = _bias(N, K)
+    sa, sb = np.float32(1 / 97.0), np.float32(1 / 5.0)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    dsl.fp8_linear_fwd(_f8(A, 0, float(sa)), _f8(B, 1, float(sb)), bias.to(DEV), y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    # random samples plus the last rows/columns (the ragged edges)
+    r = np.concatenate([rng.integers(0, M, 2000), np.full(200, M - 1), rng.integers(M - 8, M, 200)])
+    c = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 200), np.full(200, N - 1)])
+    ref = oracle.gemm_nt_sampled(A.numpy(), 0, B.numpy(), 1, sa, sb, r, c, bias=bits16(bias))
+    assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), f"fwd {M}x{N}x{K}")
