@@ -244,6 +244,63 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
     }
 }
 
+// Epilogue of one wave's 128 x 128 accumulator tile, 4 x 4 fragments of
+// v_mfma_f32_32x32x64 with the B fragment passed first: lane l holds output
+// row r0 + 32 i + l % 32 of fragment row block i and, for register group g
+// (registers 4g .. 4g+3) of fragment column block j, the four consecutive
+// columns c0 + 32 j + 8 g + 4 (l / 32) .. +3.  Writes out(acc * s + bias) for
+// the in-range elements as one 8-byte (bf16) or 16-byte (fp32) vector per
+// row and group (N % 8 == 0 keeps every vector inside the row), then clears
+// the accumulators for the next tile.
+template <int OUT, bool HAS_BIAS>
+__device__ __forceinline__ void store_wave_tile(v16f (&acc)[4][4], void *__restrict__ Cv,
+                                                const uint16_t *__restrict__ bias, int M, int N,
+                                                int r0, int c0, int lane, float s) {
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int gc = c0 + j * 32 + 8 * g + 4 * half;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_BIAS) {
+                if (gc < N) {
+                    const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
+                    bv[0] = __uint_as_float(b2.x << 16);
+                    bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                    bv[2] = __uint_as_float(b2.y << 16);
+                    bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int gr = r0 + i * 32 + frow;
+                const float y0 = acc[i][j][4 * g + 0] * s + bv[0];
+                const float y1 = acc[i][j][4 * g + 1] * s + bv[1];
+                const float y2 = acc[i][j][4 * g + 2] * s + bv[2];
+                const float y3 = acc[i][j][4 * g + 3] * s + bv[3];
+                if (gr < M && gc < N) {
+                    if constexpr (OUT == FP8_DTYPE_BF16) {
+                        uint16_t *C = static_cast<uint16_t *>(Cv);
+                        const bf16x4 o = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                        *reinterpret_cast<bf16x4 *>(C + (int64_t)gr * N + gc) = o;
+                    } else {
+                        float *C = static_cast<float *>(Cv);
+                        *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+}
+
 // Large-problem kernel: persistent, one 256-thread workgroup per CU.
 //
 //   * Each workgroup walks the 256 x 256 output tiles blockIdx.x,
@@ -408,7 +465,6 @@ __global__ __launch_bounds__(256) void gemm_nt_big_kernel(
         }
 
     const float s = (*sinv_a) * (*sinv_b);
-    const int half = lane >> 5;
     int buf_next = STAGE;            // buffer of stage k+1
     int buf_commit = 2 * STAGE;      // buffer of stage k+2
 
@@ -458,56 +514,268 @@ __global__ __launch_bounds__(256) void gemm_nt_big_kernel(
             }
         }
 
-        // Epilogue of tile r: lane holds row (lane % 32) of each fragment row
-        // block and, per group g of four registers, columns 8g + 4*(lane/32) .. +3.
         int tm, tn;
         tile_of_block((int)blockIdx.x + r * (int)gridDim.x, tiles_m, tiles_n, tm, tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-#pragma unroll
-        for (int j = 0; j < F; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int gc = n0 + wn * WT + j * 32 + 8 * g + 4 * half;
-                float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (HAS_BIAS) {
-                    if (gc < N) {
-                        const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
-                        bv[0] = __uint_as_float(b2.x << 16);
-                        bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-                        bv[2] = __uint_as_float(b2.y << 16);
-                        bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < F; ++i) {
-                    const int gr = m0 + wm * WT + i * 32 + frow;
-                    const float y0 = acc[i][j][4 * g + 0] * s + bv[0];
-                    const float y1 = acc[i][j][4 * g + 1] * s + bv[1];
-                    const float y2 = acc[i][j][4 * g + 2] * s + bv[2];
-                    const float y3 = acc[i][j][4 * g + 3] * s + bv[3];
-                    if (gr < M && gc < N) {
-                        if constexpr (OUT == FP8_DTYPE_BF16) {
-                            uint16_t *C = static_cast<uint16_t *>(Cv);
-                            const bf16x4 o = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
-                            *reinterpret_cast<bf16x4 *>(C + (int64_t)gr * N + gc) = o;
-                        } else {
-                            float *C = static_cast<float *>(Cv);
-                            *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < F; ++i)
-#pragma unroll
-            for (int j = 0; j < F; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        store_wave_tile<OUT, HAS_BIAS>(acc, Cv, bias, M, N, tm * BM + wm * WT, tn * BN + wn * WT,
+                                       lane, s);
         // The next tile becomes current; look one further ahead.
         cur_a = nxt_a;
         cur_b = nxt_b;
         tile_offsets(r + 2, nxt_a, nxt_b);
+    }
+}
+
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's
+// 16 bytes at byte offset `voff` of the buffer land at LDS address
+// m0 + 16 l, so one instruction fills 1 KiB of LDS in lane order.  Offsets
+// at or past the descriptor's record count read as zero and move no data.
+// Issued from inline assembly so that the compiler neither waits for it
+// before unrelated LDS reads nor tracks it at all: the kernel that uses it
+// places every vmcnt wait itself (nothing else in that kernel touches M0;
+// gfx9 LDS instructions do not read it).  An SALU write of M0 needs one wait
+// state before an LDS-DMA load reads it, hence the s_nop.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 128-byte-row LDS swizzle: chunk c (16 bytes) of row r sits at chunk
+// c ^ dma_swz(r).  Fragment reads touch 16 consecutive rows at one logical
+// chunk per 256-byte LDS cycle (or 8 rows per 128 bytes): the rows' (r & 1,
+// chunk) pairs are all distinct, so neither layout has bank conflicts.
+__device__ __forceinline__ int dma_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// bf16 epilogue of one wave's 128 x 128 tile through LDS (32 KiB at `stg`):
+// out(acc * s + bias) is written in the matrix-core layout (8 bytes per lane,
+// one output row per lane) into 256-byte staging rows whose 16-byte chunk c
+// of row q sits at chunk c ^ (q & 15); the wave then reads the rows back 16
+// lanes per row and stores them with 16-byte stores, so every instruction
+// writes four whole 256-byte row segments.  Clears the accumulators.
+template <bool HAS_BIAS>
+__device__ __forceinline__ void store_wave_tile_bf16_lds(v16f (&acc)[4][4], uint8_t *stg,
+                                                         uint16_t *__restrict__ C,
+                                                         const uint16_t *__restrict__ bias, int M,
+                                                         int N, int r0, int c0, int lane, float s) {
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int gc = c0 + j * 32 + 8 * g + 4 * half;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_BIAS) {
+                if (gc < N) {
+                    const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
+                    bv[0] = __uint_as_float(b2.x << 16);
+                    bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                    bv[2] = __uint_as_float(b2.y << 16);
+                    bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+                }
+            }
+            const int c = 4 * j + g;                     // 16-byte chunk of the staging row
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = i * 32 + frow;
+                const bf16x4 o = {(__bf16)(acc[i][j][4 * g + 0] * s + bv[0]),
+                                  (__bf16)(acc[i][j][4 * g + 1] * s + bv[1]),
+                                  (__bf16)(acc[i][j][4 * g + 2] * s + bv[2]),
+                                  (__bf16)(acc[i][j][4 * g + 3] * s + bv[3])};
+                *reinterpret_cast<bf16x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4) + 8 * half) = o;
+            }
+        }
+    }
+    const int c = lane & 15;
+    const int gc = c0 + 8 * c;
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+        const int q = 4 * it + (lane >> 4);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
+        const int gr = r0 + q;
+        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+}
+
+// Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
+// 256-thread workgroup per CU, four waves of 128 x 128 with
+// v_mfma_f32_32x32x64_f8f6f4) whose operand stages are written into LDS by
+// the load unit itself (buffer loads with the LDS flag), not through
+// registers.
+//   * Stages are 128 K-bytes (64 KiB for A and B), so every operand row
+//     segment is one whole 128-byte line, double-buffered in 128 KiB of LDS;
+//     no staging registers and no LDS write instructions in the main loop.
+//   * Wave w fetches rows 128 w .. 128 w + 127 of the 512-row stage (A rows
+//     for waves 0-1, B rows for 2-3): 16 instructions of 8 rows, lane l
+//     taking row l / 8 of the eight and the logical chunk that lands at
+//     chunk position l % 8 under the swizzle.
+//   * One barrier per stage, in its middle.  Stage k runs 16 MFMAs on the
+//     fragments of its first 64 K-bytes (read earlier) while reading those
+//     of its second 64; then every wave waits for its own loads of stage k+1
+//     and meets the others at the barrier, after which stage k's buffer is
+//     free (all its fragments are in registers) and stage k+1's is complete.
+//     The second 16 MFMAs then carry the loads of stage k+2 into the freed
+//     buffer (one per MFMA, which paces them at the load unit's rate) and
+//     the reads of stage k+1's first fragments.
+//   * Tile boundaries drain the pipeline: the bf16 epilogue stages the
+//     output through the then idle stage buffers and leaves as whole
+//     256-byte row segments; the next tile's first two stages are requested
+//     right after, so their latency overlaps the drain of the stores.
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
+    const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int KS = 128;                     // K bytes per stage
+    constexpr int WT = 128;                     // wave tile (square)
+    constexpr int F = WT / 32;                  // 4 x 4 fragments of 32 x 32
+    constexpr uint32_t STAGE = (BM + BN) * KS;  // 64 KiB
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int T = tiles_m * tiles_n;
+    if ((int)blockIdx.x >= T) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(A), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, N * K, 0x00020000);
+    const bool loads_b = wave >= 2;
+    const __amdgpu_buffer_rsrc_t ld_rsrc = loads_b ? rb_rsrc : ra_rsrc;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    const uint32_t ld_lds = lds0 + (uint32_t)wave * (128 * KS);   // this wave's 128 rows
+
+    // Per-lane part of the load offsets: row l / 8 of an 8-row group, the
+    // logical chunk stored at position l % 8 (the swizzle of rows 8i..8i+7
+    // is (l / 8) ^ (i & 1)).
+    const int lr = lane >> 3;
+    const uint32_t voff_e = (uint32_t)(lr * K + 16 * ((lane & 7) ^ lr));
+    const uint32_t voff_o = (uint32_t)(lr * K + 16 * ((lane & 7) ^ lr ^ 1));
+    // Load instruction i (0..15) of a stage: rows 8i..8i+7 of this wave's
+    // 128, starting at operand byte offset `base` (+ k0 along K).
+    auto load_one = [&](int i, uint32_t base, uint32_t k0, uint32_t buf) {
+        const uint32_t so = base + (uint32_t)(8 * i) * (uint32_t)K + k0;
+        dma_b128(ld_rsrc, so + ((i & 1) ? voff_o : voff_e), ld_lds + buf + (uint32_t)i * 1024u);
+    };
+
+    // Fragment reads: row (lane % 32) of a 32-row fragment, 16-byte chunks
+    // 4 s + 2 (lane / 32) and + 1 for K half s of the stage.
+    const int frow = lane & 31;
+    const int fsw = dma_swz(frow);
+    const int c0 = 2 * (lane >> 5);
+    uint32_t fo[2][2];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fo[sh][h] = frow * KS + (((4 * sh + c0 + h) ^ fsw) << 4);
+    const uint32_t a_fbase = (uint32_t)(wm * WT * KS);
+    const uint32_t b_fbase = (uint32_t)(BM * KS + wn * WT * KS);
+
+    v8i af[2][F], bf[2][F];                     // [K half][fragment]
+    auto read_half = [&](v8i &dst, uint32_t off, int h) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + off);
+        dst[4 * h + 0] = (int)v.x; dst[4 * h + 1] = (int)v.y;
+        dst[4 * h + 2] = (int)v.z; dst[4 * h + 3] = (int)v.w;
+    };
+    // Fragment n (0..7) of a K half in read order A0, B0..B3, A1..A3, half h.
+    auto read_frag = [&](int sh, int n, int h, uint32_t buf) {
+        if (n >= 1 && n <= 4)
+            read_half(bf[sh][n - 1], buf + b_fbase + (n - 1) * 32 * KS + fo[sh][h], h);
+        else {
+            const int a = (n == 0) ? 0 : n - 4;
+            read_half(af[sh][a], buf + a_fbase + a * 32 * KS + fo[sh][h], h);
+        }
+    };
+
+    v16f acc[F][F];
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // One stage: MFMAs on both K halves around the barrier.  DMA: issue the
+    // loads of stage k+2 (at `ld_k0`) into this stage's buffer; RD: read the
+    // next stage's first fragments.
+    auto stage = [&](uint32_t buf, bool dma, bool rd, uint32_t base, uint32_t ld_k0) {
+        const uint32_t nbuf = buf ^ STAGE;
+#pragma unroll
+        for (int slot = 0; slot < 16; ++slot) {
+            const int i = slot >> 2, j = slot & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[0][j], af[0][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            if (slot < 8) {
+                read_frag(1, slot, 0, buf);
+                read_frag(1, slot, 1, buf);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Stage k+1 has landed (own loads) and is visible (barrier); nobody
+        // reads this stage's buffer any more.
+        wait_vmem_all();
+        __syncthreads();
+#pragma unroll
+        for (int slot = 0; slot < 16; ++slot) {
+            const int i = slot >> 2, j = slot & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[1][j], af[1][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            if (dma) load_one(slot, base, ld_k0, buf);
+            if (rd) read_frag(0, slot >> 1, slot & 1, nbuf);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = K / KS;                      // >= 2 (caller guarantees)
+    const float s = (*sinv_a) * (*sinv_b);
+    for (int r = (int)blockIdx.x; r < T; r += (int)gridDim.x) {
+        int tm, tn;
+        tile_of_block(r, tiles_m, tiles_n, tm, tn);
+        const uint32_t base =
+            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+        // Stages 0 and 1 into buffers 0 and 1 (this also drains the previous
+        // tile's stores), then stage 0's first fragments.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load_one(i, base, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load_one(i, base, KS, STAGE);
+        wait_vmem_all();
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) read_frag(0, n, h, 0);
+
+        uint32_t buf = 0;
+        for (int k = 0; k + 2 < nk; ++k) {
+            stage(buf, true, true, base, (uint32_t)((k + 2) * KS));
+            buf ^= STAGE;
+        }
+        stage(buf, false, true, 0, 0);          // stage nk-2
+        buf ^= STAGE;
+        stage(buf, false, false, 0, 0);         // stage nk-1: LDS idle after its barrier
+
+        const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
+        if constexpr (OUT == FP8_DTYPE_BF16)
+            store_wave_tile_bf16_lds<HAS_BIAS>(acc, lds + wave * 32768,
+                                               static_cast<uint16_t *>(Cv), bias, M, N, r0, cc0,
+                                               lane, s);
+        else
+            store_wave_tile<OUT, HAS_BIAS>(acc, Cv, bias, M, N, r0, cc0, lane, s);
+        __syncthreads();                        // staging read back before the next loads
     }
 }
 
@@ -516,6 +784,33 @@ hipError_t launch_big(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
                       const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
     auto kern = gemm_nt_big_kernel<FA, FB, OUT, HAS_BIAS>;
     constexpr int lds_bytes = 3 * (256 + 256) * 64;   // three 32 KiB stages
+    static bool attr_set[64];
+    static int cu_count[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const int tiles_m = (M + 255) / 256;
+    const int tiles_n = (N + 255) / 256;
+    const int grid = std::min(tiles_m * tiles_n, cu_count[dev]);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
+                       C, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
+                      const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
+    auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS>;
+    constexpr int lds_bytes = 2 * (256 + 256) * 128;   // two 64 KiB stages
     static bool attr_set[64];
     static int cu_count[64];
     int dev = 0;
@@ -571,6 +866,9 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
     // The large kernel addresses operands with 32-bit buffer offsets.
     // It also needs at least four 64-byte K stages.
     const bool fits32 = (M + 256) * K < ((int64_t)1 << 31) && (N + 256) * K < ((int64_t)1 << 31);
+    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256 && K % 128 == 0)
+        return launch_dma<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
+                                                 stream);
     if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256)
         return launch_big<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
                                                  stream);

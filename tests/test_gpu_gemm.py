@@ -172,3 +172,39 @@ def test_large_path_tails_sampled(M, N, K):
     c = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 200), np.full(200, N - 1)])
     ref = oracle.gemm_nt_sampled(A.numpy(), 0, B.numpy(), 1, sa, sb, r, c, bias=bits16(bias))
     assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), f"fwd {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb,out", [
+    (4096, 4096, 256, 0, 0, "bf16"),     # two K stages per tile (the minimum)
+    (4104, 4104, 384, 1, 0, "bf16"),     # odd stage count, ragged M and N
+    (8200, 2056, 2048, 0, 1, "bf16"),    # ragged, several tiles per workgroup
+    (4096, 4352, 640, 1, 1, "fp32"),     # fp32 output, five stages
+])
+def test_dma_path_rows_and_columns(M, N, K, fa, fb, out):
+    """K % 128 == 0 at large M x N: whole output rows and columns at fragment
+    and tile boundaries plus random samples, against the oracle."""
+    A = workloads.random_fp8_codes((M, K), M + K, fa)
+    B = workloads.random_fp8_codes((N, K), N + K + 1, fb)
+    bias = _bias(N, K + 1) if out == "bf16" else None
+    sa, sb = np.float32(1 / 61.0), np.float32(1 / 9.0)
+    if out == "bf16":
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        dsl.fp8_linear_fwd(_f8(A, fa, float(sa)), _f8(B, fb, float(sb)), bias.to(DEV), y)
+    else:
+        y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+        # wgrad computes dW = dY^T X from the transposes: A^T is dY, B^T is X.
+        dsl.fp8_linear_wgrad(_f8(A, fa, float(sa), transpose_only=True),
+                             _f8(B, fb, float(sb), transpose_only=True), y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    rows = [0, 1, 31, 32, 255, 256, M - 1]
+    cols = [0, 127, 128, 255, N - 1]
+    r = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 2000)])
+    c = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 2000)])
+    if out == "bf16":
+        ref = oracle.gemm_nt_sampled(A.numpy(), fa, B.numpy(), fb, sa, sb, r, c, bias=bits16(bias))
+        assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), f"dma {M}x{N}x{K}")
+    else:
+        ref = oracle.gemm_nt_sampled(A.numpy(), fa, B.numpy(), fb, sa, sb, r, c,
+                                     out_kind=oracle.OUT_FP32)
+        assert_gemm_close(f32(y)[r, c].astype(np.float64), ref.astype(np.float64), f"dma {M}x{N}x{K}")
