@@ -258,6 +258,19 @@ __device__ __forceinline__ void store_wave_tile(v16f (&acc)[4][4], void *__restr
                                                 int r0, int c0, int lane, float s) {
     const int frow = lane & 31;
     const int half = lane >> 5;
+    // All bias loads first (one latency, not sixteen); columns past N read
+    // as zero through the descriptor's range check.
+    u32x2 bq[4][4];
+    if constexpr (HAS_BIAS) {
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(bias), (short)0, 2 * N, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bq[j][g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                    brs, 2 * (c0 + j * 32 + 8 * g + 4 * half), 0, 0));
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -265,13 +278,11 @@ __device__ __forceinline__ void store_wave_tile(v16f (&acc)[4][4], void *__restr
             const int gc = c0 + j * 32 + 8 * g + 4 * half;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (HAS_BIAS) {
-                if (gc < N) {
-                    const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
-                    bv[0] = __uint_as_float(b2.x << 16);
-                    bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-                    bv[2] = __uint_as_float(b2.y << 16);
-                    bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
-                }
+                const u32x2 b2 = bq[j][g];
+                bv[0] = __uint_as_float(b2.x << 16);
+                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(b2.y << 16);
+                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -552,28 +563,28 @@ __device__ __forceinline__ int dma_swz(int r) { return (r & 7) ^ ((r >> 3) & 1);
 // one output row per lane) into 256-byte staging rows whose 16-byte chunk c
 // of row q sits at chunk c ^ (q & 15); the wave then reads the rows back 16
 // lanes per row and stores them with 16-byte stores, so every instruction
-// writes four whole 256-byte row segments.  Clears the accumulators.
+// writes four whole 256-byte row segments.  The bias of the wave's 128
+// columns is read from LDS (`bias_lds`, bf16, column c0 first; zero past N).
+// Clears the accumulators.
 template <bool HAS_BIAS>
 __device__ __forceinline__ void store_wave_tile_bf16_lds(v16f (&acc)[4][4], uint8_t *stg,
                                                          uint16_t *__restrict__ C,
-                                                         const uint16_t *__restrict__ bias, int M,
-                                                         int N, int r0, int c0, int lane, float s) {
+                                                         const uint8_t *bias_lds, int M, int N,
+                                                         int r0, int c0, int lane, float s) {
     const int frow = lane & 31;
     const int half = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int gc = c0 + j * 32 + 8 * g + 4 * half;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (HAS_BIAS) {
-                if (gc < N) {
-                    const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
-                    bv[0] = __uint_as_float(b2.x << 16);
-                    bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-                    bv[2] = __uint_as_float(b2.y << 16);
-                    bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
-                }
+                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
+                    bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
+                bv[0] = __uint_as_float(b2.x << 16);
+                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(b2.y << 16);
+                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
             }
             const int c = 4 * j + g;                     // 16-byte chunk of the staging row
 #pragma unroll
@@ -627,7 +638,9 @@ __device__ __forceinline__ void store_wave_tile_bf16_lds(v16f (&acc)[4][4], uint
 //   * Tile boundaries drain the pipeline: the bf16 epilogue stages the
 //     output through the then idle stage buffers and leaves as whole
 //     256-byte row segments; the next tile's first two stages are requested
-//     right after, so their latency overlaps the drain of the stores.
+//     right after, so their latency overlaps the drain of the stores.  The
+//     tile's bias comes in with its first stages (1 KiB of LDS past them),
+//     so the epilogue never waits on a global load.
 template <int FA, int FB, int OUT, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
@@ -657,6 +670,8 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const __amdgpu_buffer_rsrc_t ld_rsrc = loads_b ? rb_rsrc : ra_rsrc;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
     const uint32_t ld_lds = lds0 + (uint32_t)wave * (128 * KS);   // this wave's 128 rows
+    // The tile's 256 bias values (512 bytes) live past the two stages.
+    uint8_t *const bias_lds = lds + 2 * STAGE;
 
     // Per-lane part of the load offsets: row l / 8 of an 8-row group, the
     // logical chunk stored at position l % 8 (the swizzle of rows 8i..8i+7
@@ -747,7 +762,14 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         const uint32_t base =
             (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
         // Stages 0 and 1 into buffers 0 and 1 (this also drains the previous
-        // tile's stores), then stage 0's first fragments.
+        // tile's stores), the tile's bias, then stage 0's first fragments.
+        if constexpr (HAS_BIAS) {
+            if (wave == 0) {
+                const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t *>(bias), (short)0, 2 * N, 0x00020000);
+                dma_b128(brs, (uint32_t)(2 * tn * BN + 16 * lane), lds0 + 2 * STAGE);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) load_one(i, base, 0, 0);
 #pragma unroll
@@ -771,8 +793,8 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
         if constexpr (OUT == FP8_DTYPE_BF16)
             store_wave_tile_bf16_lds<HAS_BIAS>(acc, lds + wave * 32768,
-                                               static_cast<uint16_t *>(Cv), bias, M, N, r0, cc0,
-                                               lane, s);
+                                               static_cast<uint16_t *>(Cv),
+                                               bias_lds + 2 * wn * WT, M, N, r0, cc0, lane, s);
         else
             store_wave_tile<OUT, HAS_BIAS>(acc, Cv, bias, M, N, r0, cc0, lane, s);
         __syncthreads();                        // staging read back before the next loads
@@ -810,7 +832,7 @@ template <int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
                       const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
     auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS>;
-    constexpr int lds_bytes = 2 * (256 + 256) * 128;   // two 64 KiB stages
+    constexpr int lds_bytes = 2 * (256 + 256) * 128 + 1024;   // two 64 KiB stages, bias
     static bool attr_set[64];
     static int cu_count[64];
     int dev = 0;
