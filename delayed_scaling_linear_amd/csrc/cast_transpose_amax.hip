@@ -12,7 +12,9 @@
 // scaling).
 //
 // Work decomposition (gfx950, wave64):
-//   * one 256-thread workgroup per 128 x 128 tile;
+//   * 128 x 128 tiles, 256 threads per tile; persistent workgroups (up to
+//     three per CU for bf16, two for fp32) walk the tiles with the next
+//     tile's loads in flight while the current one is encoded and stored;
 //   * lane l of wave w owns rows 4*rg .. 4*rg+3 (rg = 8w + l/8) and columns
 //     16*cc .. 16*cc+15 (cc = l%8) of the tile: 16-byte global loads, 8
 //     lanes per 256-byte bf16 row segment;
