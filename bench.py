@@ -14,13 +14,14 @@ history 16):
 `value` is the step's GEMM throughput (3 x 2*8192*8192*2048 FLOP per step over
 the measured step time, casts and update included).  Per-kernel durations are
 taken with HIP events around each launch on the launch stream inside a second
-timed pass.  The roofline figures come from back-to-back launches between one
+timed pass and reported as median, p10, p90 and mean over the steps (each
+event pair adds a few microseconds of its own).  The roofline figures come from back-to-back launches between one
 event pair (the forward GEMM at the step's shape; the cast-transpose-amax on
 its own workload, bf16 [4096, 4096] with 0.1% outliers, rotating over 640 MiB
 of buffers so that the 256 MiB last-level cache cannot serve it), next to a
 measured device-to-device copy ceiling.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -43,8 +44,8 @@ FP8_PEAK_TFLOPS = 5000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--cast-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--probe-kernels", action="store_true",
@@ -71,9 +72,11 @@ class Timer:
         e.record()
         self.pairs.setdefault(name, []).append((s, e))
 
-    def avg_ms(self, name):
-        v = [s.elapsed_time(e) for s, e in self.pairs[name]]
-        return sum(v) / len(v)
+    def stats_ms(self, name):
+        """Median, p10, p90 and mean of the per-call durations (ms)."""
+        v = sorted(s.elapsed_time(e) for s, e in self.pairs[name])
+        q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+        return q(0.5), q(0.1), q(0.9), sum(v) / len(v)
 
 
 def gpu_step(dsl, st, t: Timer | None):
@@ -162,7 +165,7 @@ def copy_ceiling(mib: int = 256, iters: int = 20):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(workloads, rows: int = 128):
+def cpu_baseline(workloads, rows: int = 512):
     """The oracle (plain single-threaded C) on a bounded sample of one step:
     the full X and W casts, 512 of the 8192 rows of the dY cast, and `rows` of
     the output rows of each of the three GEMMs (operands cast by the oracle
@@ -294,8 +297,9 @@ def main():
     kernels = {}
     for name in ("cast_x", "cast_w", "gemm_fwd", "cast_dy", "gemm_dgrad", "gemm_wgrad",
                  "scale_update"):
-        ms = timer.avg_ms(name)
-        k = {"us": round(ms * 1e3, 2)}
+        ms, p10, p90, mean = timer.stats_ms(name)
+        k = {"us": round(ms * 1e3, 2), "us_p10": round(p10 * 1e3, 2),
+             "us_p90": round(p90 * 1e3, 2), "us_mean": round(mean * 1e3, 2)}
         if name.startswith("gemm"):
             k["TFLOP/s"] = round(GEMM_FLOP / (ms * 1e-3) / 1e12, 1)
         elif name == "cast_dy":
