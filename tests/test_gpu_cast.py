@@ -157,3 +157,17 @@ def test_full_size_gradient_cast():
     """dY [8192, 8192] ~N(0, 1e-3) to E5M2 with both layouts."""
     x = workloads.mlp_grad()
     _check(x, 57344.0 / 0.005, oracle.E5M2)
+
+
+@pytest.mark.parametrize("shape,src,fmt,q,qt", [
+    ((5008, 5024), "bf16", oracle.E4M3, True, True),      # ragged, 1600 tiles
+    ((4096, 6144), "fp32", oracle.E5M2, True, False),     # fp32 source, 1536 tiles, codes only
+    ((5024, 5008), "bf16", oracle.E5M2, False, True),     # ragged, transpose only
+])
+def test_large_tensors_one_workgroup_per_tile(shape, src, fmt, q, qt):
+    """Tensors with more than two tiles per resident workgroup take the
+    non-temporal, one-workgroup-per-tile launch: same bits as the oracle."""
+    g = torch.Generator().manual_seed(shape[0] + shape[1])
+    x = torch.randn(*shape, generator=g) * 2
+    x = x.to(torch.bfloat16) if src == "bf16" else x
+    _check(x, 97.0, fmt, q=q, qt=qt)
