@@ -558,19 +558,16 @@ __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(
 // chunk) pairs are all distinct, so neither layout has bank conflicts.
 __device__ __forceinline__ int dma_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// bf16 epilogue of one wave's 128 x 128 tile through LDS (32 KiB at `stg`):
-// out(acc * s + bias) is written in the matrix-core layout (8 bytes per lane,
-// one output row per lane) into 256-byte staging rows whose 16-byte chunk c
-// of row q sits at chunk c ^ (q & 15); the wave then reads the rows back 16
-// lanes per row and stores them with 16-byte stores, so every instruction
-// writes four whole 256-byte row segments.  The bias of the wave's 128
-// columns is read from LDS (`bias_lds`, bf16, column c0 first; zero past N).
-// Clears the accumulators.
+// bf16 epilogue of one wave's 128 x 128 tile through LDS (32 KiB at `stg`),
+// in three steps so that the caller can put other work between them.
+// stage_wave_tile_bf16: out(acc * s + bias) is written in the matrix-core
+// layout (8 bytes per lane, one output row per lane) into 256-byte staging
+// rows whose 16-byte chunk c of row q sits at chunk c ^ (q & 15); the bias of
+// the wave's 128 columns is read from LDS (`bias_lds`, bf16, column c0
+// first; zero past N).  Clears the accumulators.
 template <bool HAS_BIAS>
-__device__ __forceinline__ void store_wave_tile_bf16_lds(v16f (&acc)[4][4], uint8_t *stg,
-                                                         uint16_t *__restrict__ C,
-                                                         const uint8_t *bias_lds, int M, int N,
-                                                         int r0, int c0, int lane, float s) {
+__device__ __forceinline__ void stage_wave_tile_bf16(v16f (&acc)[4][4], uint8_t *stg,
+                                                     const uint8_t *bias_lds, int lane, float s) {
     const int frow = lane & 31;
     const int half = lane >> 5;
 #pragma unroll
@@ -598,21 +595,35 @@ __device__ __forceinline__ void store_wave_tile_bf16_lds(v16f (&acc)[4][4], uint
             }
         }
     }
-    const int c = lane & 15;
-    const int gc = c0 + 8 * c;
-#pragma unroll
-    for (int it = 0; it < 32; ++it) {
-        const int q = 4 * it + (lane >> 4);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
-        const int gr = r0 + q;
-        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v;
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+}
+
+// Read the staged tile back, 16 lanes per 256-byte row: v[it] is row
+// 4 it + lane / 16, columns 8 (lane % 16) .. +7.
+__device__ __forceinline__ void read_staged_rows(const uint8_t *stg, int lane, u32x4 (&v)[32]) {
+    const int c = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+        const int q = 4 * it + (lane >> 4);
+        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
+    }
+}
+
+// Store the rows of read_staged_rows: every instruction writes four whole
+// 256-byte row segments (in-range rows and 8-column groups only).
+__device__ __forceinline__ void store_staged_rows(uint16_t *__restrict__ C, const u32x4 (&v)[32],
+                                                  int M, int N, int r0, int c0, int lane) {
+    const int gc = c0 + 8 * (lane & 15);
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+        const int gr = r0 + 4 * it + (lane >> 4);
+        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+    }
 }
 
 // Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
@@ -635,12 +646,14 @@ __device__ __forceinline__ void store_wave_tile_bf16_lds(v16f (&acc)[4][4], uint
 //     The second 16 MFMAs then carry the loads of stage k+2 into the freed
 //     buffer (one per MFMA, which paces them at the load unit's rate) and
 //     the reads of stage k+1's first fragments.
-//   * Tile boundaries drain the pipeline: the bf16 epilogue stages the
-//     output through the then idle stage buffers and leaves as whole
-//     256-byte row segments; the next tile's first two stages are requested
-//     right after, so their latency overlaps the drain of the stores.  The
-//     tile's bias comes in with its first stages (1 KiB of LDS past them),
-//     so the epilogue never waits on a global load.
+//   * Tile boundaries drain the pipeline.  The bf16 epilogue stages each
+//     wave's output in the then idle stage buffers and reads it back as
+//     whole 256-byte row segments into the (now free) fragment registers;
+//     the next tile's first two stages and its bias (1 KiB of LDS past the
+//     stages) are requested before the output stores are issued, so those
+//     loads land while the store burst drains.  (fp32 output skips the
+//     staging and stores straight from the accumulators, also after the
+//     next tile's loads.)
 template <int FA, int FB, int OUT, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
@@ -756,13 +769,12 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
 
     const int nk = K / KS;                      // >= 2 (caller guarantees)
     const float s = (*sinv_a) * (*sinv_b);
-    for (int r = (int)blockIdx.x; r < T; r += (int)gridDim.x) {
+    // Loads of tile r's stages 0 and 1 into buffers 0 and 1, and its bias.
+    auto issue_prologue = [&](int r) {
         int tm, tn;
         tile_of_block(r, tiles_m, tiles_n, tm, tn);
         const uint32_t base =
             (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
-        // Stages 0 and 1 into buffers 0 and 1 (this also drains the previous
-        // tile's stores), the tile's bias, then stage 0's first fragments.
         if constexpr (HAS_BIAS) {
             if (wave == 0) {
                 const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
@@ -774,13 +786,25 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         for (int i = 0; i < 16; ++i) load_one(i, base, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) load_one(i, base, KS, STAGE);
+    };
+    // Everything requested so far has landed (this also drains the previous
+    // tile's stores); stage 0's first fragments into registers.
+    auto finish_prologue = [&]() {
         wait_vmem_all();
         __syncthreads();
 #pragma unroll
         for (int n = 0; n < 8; ++n)
 #pragma unroll
             for (int h = 0; h < 2; ++h) read_frag(0, n, h, 0);
+    };
 
+    issue_prologue((int)blockIdx.x);
+    finish_prologue();
+    for (int r = (int)blockIdx.x; r < T; r += (int)gridDim.x) {
+        int tm, tn;
+        tile_of_block(r, tiles_m, tiles_n, tm, tn);
+        const uint32_t base =
+            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
         uint32_t buf = 0;
         for (int k = 0; k + 2 < nk; ++k) {
             stage(buf, true, true, base, (uint32_t)((k + 2) * KS));
@@ -790,14 +814,22 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         buf ^= STAGE;
         stage(buf, false, false, 0, 0);         // stage nk-1: LDS idle after its barrier
 
+        const int rn = r + (int)gridDim.x;
+        const bool more = rn < T;
         const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
-        if constexpr (OUT == FP8_DTYPE_BF16)
-            store_wave_tile_bf16_lds<HAS_BIAS>(acc, lds + wave * 32768,
-                                               static_cast<uint16_t *>(Cv),
-                                               bias_lds + 2 * wn * WT, M, N, r0, cc0, lane, s);
-        else
+        if constexpr (OUT == FP8_DTYPE_BF16) {
+            uint8_t *stg = lds + wave * 32768;
+            stage_wave_tile_bf16<HAS_BIAS>(acc, stg, bias_lds + 2 * wn * WT, lane, s);
+            u32x4 rows_out[32];
+            read_staged_rows(stg, lane, rows_out);
+            __syncthreads();                    // staging and bias read by every wave
+            if (more) issue_prologue(rn);
+            store_staged_rows(static_cast<uint16_t *>(Cv), rows_out, M, N, r0, cc0, lane);
+        } else {
+            if (more) issue_prologue(rn);       // the stages' LDS is idle, bias is not in LDS
             store_wave_tile<OUT, HAS_BIAS>(acc, Cv, bias, M, N, r0, cc0, lane, s);
-        __syncthreads();                        // staging read back before the next loads
+        }
+        if (more) finish_prologue();
     }
 }
 
