@@ -626,6 +626,63 @@ __device__ __forceinline__ void store_staged_rows(uint16_t *__restrict__ C, cons
     }
 }
 
+// fp32 epilogue of one wave's tile through LDS, one 32-row fragment block i
+// at a time: 32 staging rows of 512 bytes (16 KiB at `stg`), 16-byte chunk c
+// of row q at chunk c ^ (q & 15).  Lane l holds row (l % 32) of the block
+// and, per register group g of fragment column block j, the four columns
+// 32 j + 8 g + 4 (l / 32) .. +3, i.e. chunk 8 j + 2 g + l / 32.  Bias as in
+// stage_wave_tile_bf16.
+template <bool HAS_BIAS>
+__device__ __forceinline__ void stage_wave_block_f32(const v16f (&acc)[4][4], uint8_t *stg,
+                                                     const uint8_t *bias_lds, int lane, float s,
+                                                     int i) {
+    const int q = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_BIAS) {
+                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
+                    bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
+                bv[0] = __uint_as_float(b2.x << 16);
+                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(b2.y << 16);
+                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+            }
+            const int c = 8 * j + 2 * g + half;
+            const v4f o = {acc[i][j][4 * g + 0] * s + bv[0], acc[i][j][4 * g + 1] * s + bv[1],
+                           acc[i][j][4 * g + 2] * s + bv[2], acc[i][j][4 * g + 3] * s + bv[3]};
+            *reinterpret_cast<v4f *>(stg + q * 512 + ((c ^ (q & 15)) << 4)) = o;
+        }
+    }
+}
+
+// Read a staged fp32 block back, 32 lanes per 512-byte row: v[it] is row
+// 2 it + lane / 32 of the block, columns 4 (lane % 32) .. +3.
+__device__ __forceinline__ void read_staged_block_f32(const uint8_t *stg, int lane,
+                                                      u32x4 (&v)[16]) {
+    const int c = lane & 31;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int q = 2 * it + (lane >> 5);
+        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 512 + ((c ^ (q & 15)) << 4));
+    }
+}
+
+// Store a block read by read_staged_block_f32 (rows r0 .. r0 + 31): every
+// instruction writes two whole 512-byte row segments.
+__device__ __forceinline__ void store_staged_block_f32(float *__restrict__ C, const u32x4 (&v)[16],
+                                                       int M, int N, int r0, int c0, int lane) {
+    const int gc = c0 + 4 * (lane & 31);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int gr = r0 + 2 * it + (lane >> 5);
+        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+    }
+}
+
 // Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
 // 256-thread workgroup per CU, four waves of 128 x 128 with
 // v_mfma_f32_32x32x64_f8f6f4) whose operand stages are written into LDS by
@@ -651,9 +708,8 @@ __device__ __forceinline__ void store_staged_rows(uint16_t *__restrict__ C, cons
 //     whole 256-byte row segments into the (now free) fragment registers;
 //     the next tile's first two stages and its bias (1 KiB of LDS past the
 //     stages) are requested before the output stores are issued, so those
-//     loads land while the store burst drains.  (fp32 output skips the
-//     staging and stores straight from the accumulators, also after the
-//     next tile's loads.)
+//     loads land while the store burst drains.  fp32 output goes through
+//     the same staging in four 32-row blocks (512-byte row segments).
 template <int FA, int FB, int OUT, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
@@ -826,8 +882,26 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
             if (more) issue_prologue(rn);
             store_staged_rows(static_cast<uint16_t *>(Cv), rows_out, M, N, r0, cc0, lane);
         } else {
-            if (more) issue_prologue(rn);       // the stages' LDS is idle, bias is not in LDS
-            store_wave_tile<OUT, HAS_BIAS>(acc, Cv, bias, M, N, r0, cc0, lane, s);
+            // fp32: four 32-row blocks through the wave's own 16 KiB of staging.
+            uint8_t *stg = lds + wave * 32768;
+            float *C = static_cast<float *>(Cv);
+            u32x4 rows_out[16];
+#pragma unroll
+            for (int i = 0; i < F; ++i) {
+                stage_wave_block_f32<HAS_BIAS>(acc, stg, bias_lds + 2 * wn * WT, lane, s, i);
+                read_staged_block_f32(stg, lane, rows_out);
+                if (i == F - 1) {
+                    __syncthreads();            // staging and bias read by every wave
+                    if (more) issue_prologue(rn);
+                }
+                store_staged_block_f32(C, rows_out, M, N, r0 + 32 * i, cc0, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < F; ++i)
+#pragma unroll
+                for (int j = 0; j < F; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         }
         if (more) finish_prologue();
     }
