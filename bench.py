@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--cast-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-toy-stack", action="store_true",
+                   help="skip the 32-block toy-stack forward timing (eager vs HIP graph)")
     p.add_argument("--probe-kernels", action="store_true",
                    help="launch the forward GEMM, the [4096,4096] cast and a 64 MiB device copy "
                         "once each (after a warm-up) and exit: the command profiled for HBM "
@@ -163,6 +165,110 @@ def copy_ceiling(mib: int = 256, iters: int = 20):
     del bufs
     torch.cuda.empty_cache()
     return 2 * n / (ms * 1e-3) / 1e9
+
+
+def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
+    """The 32-block toy transformer forward (hidden 2048, batch 8, seq 1024;
+    per block the linears 2048->12288 +b, 2048->6144, 2048->2048,
+    2048->4096, 2048->8192 +b and 8192->2048 +b with the shift/scale and
+    residual glue in torch), one scale update over all 384 records per
+    forward.  Timed eagerly and as one captured HIP graph, each with the
+    weights re-cast and with cached FP8 weights (the weight casts see a
+    device no-op flag, so the same graph serves both), next to the same
+    stack in plain torch bf16.  Two interleaved rounds, best of each."""
+    dev = "cuda"
+    H, Mt = workloads.HIDDEN, workloads.TOKENS
+    lin = workloads.toy_block_linears()
+    gen = torch.Generator(device=dev).manual_seed(20)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = dsl.DelayedScalingState([0] * (12 * blocks), device=dev)
+    layers = []
+    for bi in range(blocks):
+        ls = []
+        for fin, fout, hb in lin:
+            w = (torch.randn(fout, fin, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            b = (torch.randn(fout, generator=gen, device=dev) * 0.02).to(torch.bfloat16) if hb else None
+            ls.append((w, b, dsl.Float8Tensor.empty(fout, fin, 0, device=dev)))
+        layers.append(ls)
+    # FP8 inputs and outputs of linear l are reused by every block (each
+    # block consumes them before the next one overwrites them).
+    qxs = [dsl.Float8Tensor.empty(Mt, fin, 0, device=dev) for fin, _, _ in lin]
+    ys = [torch.empty(Mt, fout, dtype=torch.bfloat16, device=dev) for _, fout, _ in lin]
+    x0 = workloads.uniform_bf16((Mt, H), workloads.SEED_X).to(dev)
+    xin = torch.empty_like(x0)
+
+    def linear(bi, l, inp):
+        w, b, qw = layers[bi][l]
+        qx, y = qxs[l], ys[l]
+        tx, tw = 12 * bi + 2 * l, 12 * bi + 2 * l + 1
+        dsl.fp8_cast_transpose_amax(inp, st.scale[tx:tx + 1], qx, st.amax_cur[tx:tx + 1])
+        dsl.fp8_cast_transpose_amax(w, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1],
+                                    noop_flag=flag)
+        dsl.fp8_linear_fwd(qx, qw, b, y)
+        return y
+
+    def forward(x):
+        for bi in range(blocks):
+            mod = linear(bi, 0, x)
+            x = torch.nan_to_num((mod[:, :H].float() * x.float() / mod[:, H:2 * H].float())
+                                 .to(torch.bfloat16), nan=0.0, posinf=0.0, neginf=0.0)
+            x = x + linear(bi, 1, x)[:, :H]
+            x = x + linear(bi, 2, x) + linear(bi, 3, x)[:, :H]
+            h = linear(bi, 4, x)
+            x = x + linear(bi, 5, h)
+        st.update()
+        return x
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, (time.perf_counter() - t0) * 1e3 / reps
+
+    def forward_bf16(x):
+        """The same stack with plain torch bf16 linears (no FP8): context for
+        the FP8-vs-BF16 forward comparison of the toy model's page."""
+        for bi in range(blocks):
+            lw = layers[bi]
+            f = lambda l, inp: torch.nn.functional.linear(inp, lw[l][0], lw[l][1])
+            mod = f(0, x)
+            x = torch.nan_to_num((mod[:, :H].float() * x.float() / mod[:, H:2 * H].float())
+                                 .to(torch.bfloat16), nan=0.0, posinf=0.0, neginf=0.0)
+            x = x + f(1, x)[:, :H]
+            x = x + f(2, x) + f(3, x)[:, :H]
+            x = x + f(5, f(4, x))
+        return x
+
+    xin.copy_(x0)
+    forward(xin)                              # first launches (kernel attributes) outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        forward(xin)
+    modes = {"eager": (lambda: forward(xin), 0), "eager_cached_weights": (lambda: forward(xin), 1),
+             "graph": (graph.replay, 0), "graph_cached_weights": (graph.replay, 1),
+             "bf16_torch_eager": (lambda: forward_bf16(xin), 0)}
+    res = {}
+    for _ in range(2):                        # interleaved rounds, best of each mode
+        for name, (fn, fl) in modes.items():
+            flag.fill_(fl)
+            ms, wall = timed(fn)
+            if name + "_ms" not in res or ms < res[name + "_ms"]:
+                res[name + "_ms"], res[name + "_wall_ms"] = ms, wall
+    flop = 2 * Mt * sum(fin * fout for fin, fout, _ in lin) * blocks
+    out = {k: round(v, 3) for k, v in res.items()}
+    out.update({"blocks": blocks, "gemm_flop": flop, "library_launches_per_forward": blocks * 18 + 1,
+                "graph_cached_weights_gemm_tflops": round(flop / (res["graph_cached_weights_ms"] * 1e-3) / 1e12, 1)})
+    del graph, layers, qxs, ys
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(workloads, rows: int = 512):
@@ -313,6 +419,7 @@ def main():
     cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
     copy_gbs = copy_ceiling()
 
+    toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
     traffic = traffic_record(root)
     result = {
         "metric": "FP8 GEMM TFLOP/s (M8192 K2048 N8192) + cast-transpose-amax HBM GB/s",
@@ -348,6 +455,8 @@ def main():
                           "measured_copy_ceiling_gbs": round(copy_gbs, 1)},
         "wall_s_timed": round(wall, 3),
     }
+    if toy is not None:
+        result["toy_stack_forward"] = toy
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(workloads)
     print(json.dumps(result), flush=True)

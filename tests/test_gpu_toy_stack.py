@@ -162,3 +162,91 @@ def test_graph_capture_replays_match_eager():
         for name in ("amax_history", "amax_cur", "scale", "scale_inv"):
             assert torch.equal(getattr(g_st, name), getattr(e_st, name)), f"replay {rep}: {name}"
     assert float(g_st.scale[0]) != 1.0                  # the state did evolve
+
+
+class _CachedWeightStack:
+    """Toy-block forward whose FP8 weights persist across micro-batches: the
+    weight casts take a device no-op flag (0 = cast, 1 = keep the cached
+    codes, transpose and scale-inverse), so one captured graph serves both."""
+
+    def __init__(self, blocks):
+        H = workloads.HIDDEN
+        self.flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.st = dsl.DelayedScalingState([0] * (12 * blocks), device=DEV)
+        self.blocks = []
+        for bi in range(blocks):
+            lins = []
+            for (w, b), (fin, fout, _) in zip(_block_weights(bi), workloads.toy_block_linears()):
+                qw = dsl.Float8Tensor.empty(fout, fin, 0, device=DEV)
+                qx = dsl.Float8Tensor.empty(M, fin, 0, device=DEV)
+                lins.append((w, b, qw, qx, torch.empty(M, fout, dtype=torch.bfloat16, device=DEV)))
+            self.blocks.append(lins)
+        self.H = H
+
+    def _lin(self, bi, l, inp):
+        w, b, qw, qx, y = self.blocks[bi][l]
+        tx, tw = 12 * bi + 2 * l, 12 * bi + 2 * l + 1
+        st = self.st
+        dsl.fp8_cast_transpose_amax(inp, st.scale[tx:tx + 1], qx, st.amax_cur[tx:tx + 1])
+        dsl.fp8_cast_transpose_amax(w, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1],
+                                    noop_flag=self.flag)
+        dsl.fp8_linear_fwd(qx, qw, b, y)
+        return y
+
+    def forward(self, x):
+        H = self.H
+        for bi in range(len(self.blocks)):
+            mod = self._lin(bi, 0, x)
+            x = torch.nan_to_num((mod[:, :H].float() * x.float() / mod[:, H:2 * H].float())
+                                 .to(torch.bfloat16), nan=0.0, posinf=0.0, neginf=0.0)
+            x = x + self._lin(bi, 1, x)[:, :H]
+            x = x + self._lin(bi, 2, x) + self._lin(bi, 3, x)[:, :H]
+            h = self._lin(bi, 4, x)
+            x = x + self._lin(bi, 5, h)
+        self.st.update()
+        return x
+
+
+def test_cached_weights_and_whole_forward_graph():
+    """Two micro-batches of a 2-block forward (weights cast on the first,
+    kept on the second by the device flag), eager and as one captured graph
+    replayed with the flag flipped on the device: identical bits, and the
+    cached FP8 weights are left untouched by the second micro-batch."""
+    x1 = workloads.uniform_bf16((M, workloads.HIDDEN), 11).to(DEV)
+    x2 = workloads.uniform_bf16((M, workloads.HIDDEN), 12).to(DEV)
+
+    eager = _CachedWeightStack(2)
+    eager.flag.fill_(0)
+    e1 = eager.forward(x1).clone()
+    torch.cuda.synchronize()
+    cached = [(qw.data.clone(), qw.data_t.clone(), qw.scale_inv.clone())
+              for lins in eager.blocks for (_, _, qw, _, _) in lins]
+    eager.flag.fill_(1)
+    e2 = eager.forward(x2).clone()
+    torch.cuda.synchronize()
+    after = [(qw.data, qw.data_t, qw.scale_inv) for lins in eager.blocks for (_, _, qw, _, _) in lins]
+    for (d0, t0, s0), (d1, t1, s1) in zip(cached, after):
+        assert torch.equal(d0, d1) and torch.equal(t0, t1) and torch.equal(s0, s1)
+    # weights amax: recorded on the first micro-batch only
+    assert float(eager.st.amax_history[1, 0]) == 0.0 and float(eager.st.amax_history[1, 1]) > 0.0
+
+    g = _CachedWeightStack(2)
+    xin = torch.empty_like(x1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                 # warm-up launches on a side stream
+        w = _CachedWeightStack(1)
+        w.forward(x1)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gout = g.forward(xin)
+    for rep, (xv, flag, want) in enumerate(((x1, 0, e1), (x2, 1, e2))):
+        xin.copy_(xv)
+        g.flag.fill_(flag)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gout.view(torch.int16), want.view(torch.int16)), f"micro-batch {rep + 1}"
+    for name in ("amax_history", "scale", "scale_inv"):
+        assert torch.equal(getattr(g.st, name), getattr(eager.st, name)), name
