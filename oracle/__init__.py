@@ -16,6 +16,9 @@ of the pages it follows:
   modules": the FP8 tensor keeps a private scale-inverse and a transpose
   cache) and the per-tensor amax ("support delayed scaling of weight in float8
   all-gather": amax buffers packed per tensor).
+* ``dbias`` -- the bias gradient (column sums of the output gradient) that the
+  training loop of "CPU Overhead of te.Linear FP8 Layers" needs for its biased
+  linears (fp32, exact fp64 sum rounded once).
 * ``scale_update`` -- the DelayedScaling recipe (history length 16, algorithm
   "max") of "CPU Overhead of te.Linear FP8 Layers".
 * ``gemm_nt`` / ``gemm_nt_sampled`` -- the per-tensor-scaled FP8 product with
@@ -77,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.orc_cast_transpose_amax.argtypes = [vp, c.c_int, i64, i64, i64, c.c_float, c.c_int,
                                               vp, vp, f32p, f32p]
         L.orc_cast_transpose_amax.restype = c.c_int
+        L.orc_dbias.argtypes = [vp, c.c_int, i64, i64, i64, f32p]
+        L.orc_dbias.restype = c.c_int
         L.orc_scale_update.argtypes = [vp, vp, vp, vp, vp, c.c_int, c.c_int, c.c_int, c.c_int]
         L.orc_scale_update.restype = c.c_int
         L.orc_gemm_nt.argtypes = [vp, c.c_int, i64, vp, c.c_int, i64, i64, i64, i64,
@@ -172,6 +177,25 @@ def cast_transpose_amax(x: np.ndarray, scale: float, fmt: int, *, want_q: bool =
     if rc != 0:
         raise ValueError("oracle cast rejected its arguments")
     return q, qt, np.float32(amax.value), np.float32(sinv.value)
+
+
+def dbias(x: np.ndarray) -> np.ndarray:
+    """Column sums [C] (float32) of a 2-D source (uint16 = bf16 bits, or
+    float32): the bias gradient, exact in fp64, rounded once."""
+    if x.dtype == np.uint16:
+        src = SRC_BF16
+    elif x.dtype == np.float32:
+        src = SRC_FP32
+    else:
+        raise TypeError("source must be bf16 bits (uint16) or float32")
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    out = np.empty(cols, dtype=np.float32)
+    rc = lib().orc_dbias(_ptr(x), src, rows, cols, cols,
+                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    if rc != 0:
+        raise ValueError("oracle dbias rejected its arguments")
+    return out
 
 
 # --------------------------------------------------------- scale update ----

@@ -204,6 +204,28 @@ int orc_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
     return 0;
 }
 
+/*
+ * Bias gradient of y = x W^T + b over a row-major [rows, cols] output
+ * gradient dY with leading dimension ld (elements): dbias[c] = sum over r of
+ * dY[r, c], of the unscaled source.  The training loop of "CPU Overhead of
+ * te.Linear FP8 Layers" (reproduction script: biased linears, fp32
+ * parameters in the FP8 run, loss.backward()) needs it for every biased
+ * linear.  The sum is accumulated in fp64 (exact whenever the inputs'
+ * exponent span and count fit in fp64's 53-bit significand, as for every
+ * test input; otherwise the fp64 sum is the reference) and rounded once to
+ * fp32.  src: 0 = bf16, 1 = fp32.
+ * Returns 0, or -1 for a bad argument.
+ */
+int orc_dbias(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, float *dbias) {
+    if ((src != 0 && src != 1) || rows < 0 || cols < 0 || ld < cols || !dbias) return -1;
+    for (int64_t c = 0; c < cols; ++c) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < rows; ++r) acc += (double)orc_load_src(x, src, r * ld + c);
+        dbias[c] = (float)acc;
+    }
+    return 0;
+}
+
 /* ---- amax history and scale update ----------------------------------- */
 
 /*
