@@ -167,6 +167,35 @@ def copy_ceiling(mib: int = 256, iters: int = 20):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def dbias_cast_cost(dsl, st, iters: int = 20):
+    """The dY [8192, 8192] E5M2 cast (codes + transpose + amax) back to back,
+    plain and with the bias gradient fused in (fp8_cast_transpose_amax_dbias):
+    what the fused column sums cost on top of the cast."""
+    g = st["state"]
+    dy, qdy = st["dy"], st["qdy"]
+    dbias = torch.empty(N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsl.fp8_cast_dbias_workspace_bytes(M, N), dtype=torch.uint8, device="cuda")
+    plain = lambda: dsl.fp8_cast_transpose_amax(dy, g.scale[2:3], qdy, g.amax_cur[2:3])
+    fused = lambda: dsl.fp8_cast_transpose_amax_dbias(dy, g.scale[2:3], qdy, g.amax_cur[2:3],
+                                                      dbias, ws)
+    res = {}
+    for _ in range(2):                        # interleaved rounds, best of each
+        for name, fn in (("cast_us", plain), ("cast_dbias_us", fused)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / iters * 1e3
+            res[name] = min(res.get(name, us), us)
+    return {k: round(v, 2) for k, v in res.items()}
+
+
 def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     """The 32-block toy transformer forward (hidden 2048, batch 8, seq 1024;
     per block the linears 2048->12288 +b, 2048->6144, 2048->2048,
@@ -419,6 +448,7 @@ def main():
     cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
     copy_gbs = copy_ceiling()
 
+    dbias_cost = dbias_cast_cost(dsl, st)
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
     traffic = traffic_record(root)
     result = {
@@ -455,6 +485,7 @@ def main():
                           "measured_copy_ceiling_gbs": round(copy_gbs, 1)},
         "wall_s_timed": round(wall, 3),
     }
+    result["dy_cast_dbias"] = dbias_cost
     if toy is not None:
         result["toy_stack_forward"] = toy
     if not args.no_cpu_baseline:

@@ -33,6 +33,7 @@ __all__ = [
     "E4M3", "E5M2", "DTYPE_BF16", "DTYPE_FP32", "Fp8Error", "Float8Tensor",
     "DelayedScalingState", "fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
     "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
+    "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
     "library_path", "lib",
 ]
 
@@ -81,11 +82,15 @@ def lib() -> ctypes.CDLL:
         dp = ctypes.POINTER(_Desc)
         L.fp8_scale_update.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
         L.fp8_cast_transpose_amax.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp]
+        L.fp8_cast_transpose_amax_dbias.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp,
+                                                    i64, vp, vp]
+        L.fp8_cast_dbias_workspace_bytes.argtypes = [i64, i64]
+        L.fp8_cast_dbias_workspace_bytes.restype = i64
         L.fp8_linear_fwd.argtypes = [dp, dp, vp, vp, vp]
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
-        for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_linear_fwd,
-                  L.fp8_linear_dgrad, L.fp8_linear_wgrad):
+        for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
+                  L.fp8_linear_fwd, L.fp8_linear_dgrad, L.fp8_linear_wgrad):
             f.restype = ctypes.c_int
         L.fp8_status_string.argtypes = [ctypes.c_int]
         L.fp8_status_string.restype = ctypes.c_char_p
@@ -212,6 +217,42 @@ def fp8_cast_transpose_amax(x: torch.Tensor, scale: torch.Tensor, out: Float8Ten
                                          _ptr(amax_cur, torch.float32, "amax_cur"),
                                          _ptr(noop_flag, torch.int32, "noop_flag"),
                                          _stream(stream)), "fp8_cast_transpose_amax")
+
+
+def fp8_cast_dbias_workspace_bytes(rows: int, cols: int) -> int:
+    """Bytes of device workspace fp8_cast_transpose_amax_dbias needs."""
+    n = lib().fp8_cast_dbias_workspace_bytes(rows, cols)
+    if n < 0:
+        raise Fp8Error(n, "fp8_cast_dbias_workspace_bytes")
+    return n
+
+
+def fp8_cast_transpose_amax_dbias(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,
+                                  amax_cur: Optional[torch.Tensor], dbias: torch.Tensor,
+                                  workspace: torch.Tensor,
+                                  noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """fp8_cast_transpose_amax plus dbias [cols] (fp32) = column sums of x.
+    `workspace` is a device uint8 tensor of at least
+    fp8_cast_dbias_workspace_bytes(rows, cols) bytes."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride in the last dimension")
+    if x.dtype == torch.bfloat16:
+        src = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        src = DTYPE_FP32
+    else:
+        raise TypeError("x must be bf16 or fp32")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if dbias.numel() != x.shape[1]:
+        raise ValueError("dbias must have cols elements")
+    d = out.desc()
+    _check(lib().fp8_cast_transpose_amax_dbias(
+        x.data_ptr(), src, x.shape[0], x.shape[1], x.stride(0), _ptr(scale, torch.float32, "scale"),
+        ctypes.byref(d), _ptr(amax_cur, torch.float32, "amax_cur"),
+        _ptr(dbias, torch.float32, "dbias"), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)),
+        "fp8_cast_transpose_amax_dbias")
 
 
 def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],

@@ -45,6 +45,30 @@ int check_gemm(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t
     return FP8_OK;
 }
 
+// Shared checks of the two cast entry points (shape, format, alignment).
+int check_cast(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
+               const float *scale, const fp8_tensor_t *out) {
+    if (out == nullptr) return FP8_ERR_NULL;
+    if (src != FP8_DTYPE_BF16 && src != FP8_DTYPE_FP32) return FP8_ERR_ARG;
+    if (!valid_fmt(out->fmt)) return FP8_ERR_FORMAT;
+    if (out->reserved != 0) return FP8_ERR_ARG;
+    if (rows < 0 || cols < 0 || (rows % 16) != 0 || (cols % 16) != 0 || ld < cols ||
+        (ld % (src == FP8_DTYPE_BF16 ? 8 : 4)) != 0 || out->rows != rows || out->cols != cols)
+        return FP8_ERR_SHAPE;
+    const int64_t tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
+    if (tiles > INT32_MAX) return FP8_ERR_SHAPE;
+    // A 128-row tile of the source is addressed with 32-bit byte offsets.
+    if (128 * ld * (src == FP8_DTYPE_BF16 ? 2 : 4) >= ((int64_t)1 << 31)) return FP8_ERR_SHAPE;
+    if (scale == nullptr) return FP8_ERR_NULL;
+    const bool empty = (rows == 0 || cols == 0);
+    if (!empty && (x == nullptr || (out->data == nullptr && out->data_t == nullptr)))
+        return FP8_ERR_NULL;
+    if ((x && !aligned16(x)) || (out->data && !aligned16(out->data)) ||
+        (out->data_t && !aligned16(out->data_t)))
+        return FP8_ERR_ALIGN;
+    return FP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,32 +105,56 @@ int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *
 int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
                             const float *scale, const fp8_tensor_t *out, float *amax_cur,
                             const int32_t *noop_flag, fp8_stream_t stream) {
-    if (out == nullptr) return FP8_ERR_NULL;
-    if (src != FP8_DTYPE_BF16 && src != FP8_DTYPE_FP32) return FP8_ERR_ARG;
-    if (!valid_fmt(out->fmt)) return FP8_ERR_FORMAT;
-    if (out->reserved != 0) return FP8_ERR_ARG;
-    if (rows < 0 || cols < 0 || (rows % 16) != 0 || (cols % 16) != 0 || ld < cols ||
-        (ld % (src == FP8_DTYPE_BF16 ? 8 : 4)) != 0 || out->rows != rows || out->cols != cols)
-        return FP8_ERR_SHAPE;
-    const int64_t tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
-    if (tiles > INT32_MAX) return FP8_ERR_SHAPE;
-    // A 128-row tile of the source is addressed with 32-bit byte offsets.
-    if (128 * ld * (src == FP8_DTYPE_BF16 ? 2 : 4) >= ((int64_t)1 << 31)) return FP8_ERR_SHAPE;
-    if (scale == nullptr) return FP8_ERR_NULL;
+    if (int e = check_cast(x, src, rows, cols, ld, scale, out)) return e;
     const bool empty = (rows == 0 || cols == 0);
     // Nothing to cast in an empty tensor; the scale-inverse snapshot is still taken.
     if (empty && out->scale_inv == nullptr) return FP8_OK;
-    if (!empty && (x == nullptr || (out->data == nullptr && out->data_t == nullptr)))
-        return FP8_ERR_NULL;
-    if ((x && !aligned16(x)) || (out->data && !aligned16(out->data)) ||
-        (out->data_t && !aligned16(out->data_t)))
-        return FP8_ERR_ALIGN;
     if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (empty) return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
     return status_of(launch_cast_transpose_amax(x, src, rows, cols, ld, scale, out->fmt,
                                                 out->data, out->data_t, amax_cur, out->scale_inv,
-                                                noop_flag, s));
+                                                noop_flag, nullptr, 0, s));
+}
+
+int64_t fp8_cast_dbias_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return FP8_ERR_SHAPE;
+    return ((rows + 127) / 128) * ((cols + 127) / 128) * 128 * (int64_t)sizeof(float);
+}
+
+int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int64_t cols,
+                                  int64_t ld, const float *scale, const fp8_tensor_t *out,
+                                  float *amax_cur, float *dbias, void *workspace,
+                                  int64_t workspace_bytes, const int32_t *noop_flag,
+                                  fp8_stream_t stream) {
+    if (int e = check_cast(x, src, rows, cols, ld, scale, out)) return e;
+    if (cols > 0 && dbias == nullptr) return FP8_ERR_NULL;
+    if (dbias && (reinterpret_cast<uintptr_t>(dbias) & 3) != 0) return FP8_ERR_ALIGN;
+    const bool empty = (rows == 0 || cols == 0);
+    const int64_t tiles_r = (rows + 127) / 128, tiles_c = (cols + 127) / 128;
+    if (!empty) {
+        if (workspace == nullptr) return FP8_ERR_NULL;
+        if (workspace_bytes < fp8_cast_dbias_workspace_bytes(rows, cols)) return FP8_ERR_SHAPE;
+        if (!aligned16(workspace)) return FP8_ERR_ALIGN;
+    }
+    if (cols == 0 && out->scale_inv == nullptr) return FP8_OK;
+    if (int d = check_device()) return d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (empty) {
+        // No rows: the bias gradient is zero; the scale-inverse snapshot is still taken.
+        if (out->scale_inv) {
+            if (int e = status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s)))
+                return e;
+        }
+        return status_of(launch_dbias_reduce(nullptr, 0, 0, cols, dbias, noop_flag, s));
+    }
+    float *ws = static_cast<float *>(workspace);
+    if (int e = status_of(launch_cast_transpose_amax(x, src, rows, cols, ld, scale, out->fmt,
+                                                     out->data, out->data_t, amax_cur,
+                                                     out->scale_inv, noop_flag, ws,
+                                                     128 * tiles_c, s)))
+        return e;
+    return status_of(launch_dbias_reduce(ws, tiles_r, 128 * tiles_c, cols, dbias, noop_flag, s));
 }
 
 int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,

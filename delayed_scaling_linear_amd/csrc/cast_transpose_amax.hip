@@ -247,20 +247,28 @@ __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float 
 // from 59 to 54 us, while the same settings slow [4096, 4096] down.
 // Resident workgroups per CU: the double-buffered source needs 64 (bf16) or
 // 128 (fp32) registers per lane.
-template <int SRC>
-constexpr int kWavesPerSimd = (SRC == FP8_DTYPE_BF16) ? 3 : 2;
+// The bias-gradient variant needs its 16 column sums on top: two per CU.
+template <int SRC, bool DBIAS>
+constexpr int kWavesPerSimd = (SRC == FP8_DTYPE_BF16 && !DBIAS) ? 3 : 2;
 
-template <int SRC, int FMT, bool WANT_Q, bool WANT_QT, bool STREAM>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<SRC>))) void
+// DBIAS: also the bias gradient's per-tile column sums of the unscaled source
+// (fp32): each lane adds its four rows in order, the eight row groups of a
+// wave meet in a butterfly of lane exchanges, the four waves in LDS in wave
+// order; tile (tr, tc) writes its 128 sums to dbias_ws[tr * ws_ld + 128 tc ..].
+// Every step has a fixed order, so the result is the same on every run.
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT, bool STREAM, bool DBIAS>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<SRC, DBIAS>))) void
 cast_transpose_amax_kernel(
     const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
     float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
-    const int32_t *__restrict__ noop, int64_t tiles_c, int64_t ntiles) {
+    const int32_t *__restrict__ noop, int64_t tiles_c, int64_t ntiles,
+    float *__restrict__ dbias_ws, int64_t ws_ld) {
     if (noop != nullptr && *noop != 0) return;
 
     __shared__ uint32_t lds_t[2][TILE * (TILE / 4)];   // transposed tiles, 2 x 16 KiB
     __shared__ uint32_t lds_amax[THREADS / 64];
+    __shared__ float lds_db[DBIAS ? 2 * (THREADS / 64) * TILE : 1];   // [buffer][wave][column]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -335,8 +343,46 @@ cast_transpose_amax_kernel(
                 load_tile(src[u ^ 1], rs_nxt, off_nxt);           // empty past the end
                 encode_block<SRC, FMT, WANT_Q, WANT_QT>(src[u], s, s_special, v_cur, q, r_cur,
                                                         c_cur, cols, cc, rg, lds_t[u], key);
+                if constexpr (DBIAS) {
+                    // Rows past the tensor were loaded as zeros and add nothing.
+                    float cs[16];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float o[4];
+                        src[u][0].get4(j, o);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) cs[4 * j + k] = o[k];
+                    }
+#pragma unroll
+                    for (int i = 1; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            float o[4];
+                            src[u][i].get4(j, o);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) cs[4 * j + k] += o[k];
+                        }
+#pragma unroll
+                    for (int m = 8; m < 64; m *= 2)
+#pragma unroll
+                        for (int k = 0; k < 16; ++k) cs[k] += __shfl_xor(cs[k], m);
+                    if ((lane >> 3) == 0) {
+                        float *d = &lds_db[(u * (THREADS / 64) + wave) * TILE + 16 * cc];
+#pragma unroll
+                        for (int k = 0; k < 16; k += 4)
+                            *reinterpret_cast<f32x4 *>(d + k) = f32x4{cs[k], cs[k + 1], cs[k + 2], cs[k + 3]};
+                    }
+                }
                 __syncthreads();
                 if constexpr (WANT_QT) store_t(lds_t[u], t);
+                if constexpr (DBIAS) {
+                    if (tid < TILE) {
+                        const float *d = &lds_db[u * (THREADS / 64) * TILE + tid];
+                        const float sum = ((d[0] + d[TILE]) + d[2 * TILE]) + d[3 * TILE];
+                        const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
+                        dbias_ws[tr * ws_ld + tcn * TILE + tid] = sum;
+                    }
+                }
                 t = tn;
                 r_cur = r_nxt;
                 c_cur = c_nxt;
@@ -364,7 +410,8 @@ cast_transpose_amax_kernel(
 template <int SRC, int FMT>
 hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
                           const float *scale, uint8_t *q, uint8_t *qt, float *amax_cur,
-                          float *scale_inv_out, const int32_t *noop, hipStream_t stream) {
+                          float *scale_inv_out, const int32_t *noop, float *dbias_ws,
+                          int64_t ws_ld, hipStream_t stream) {
     static int cu_count[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -379,25 +426,30 @@ hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
     const int64_t ntiles = tiles_r * tiles_c;
     // As many workgroups as fit on the chip at once, each looping over tiles;
     // large tensors: one workgroup per tile.
-    const int64_t resident = (int64_t)cu_count[dev] * kWavesPerSimd<SRC>;
+    const int64_t resident =
+        (int64_t)cu_count[dev] * (dbias_ws ? kWavesPerSimd<SRC, true> : kWavesPerSimd<SRC, false>);
     const bool stream_mode = ntiles > 2 * resident;
     const dim3 grid((unsigned)(stream_mode ? ntiles : std::min<int64_t>(ntiles, resident)));
-    auto launch = [&](auto wq, auto wqt, auto st) {
+    auto launch = [&](auto wq, auto wqt, auto st, auto db) {
         hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, decltype(wq)::value,
-                                                       decltype(wqt)::value, decltype(st)::value>),
+                                                       decltype(wqt)::value, decltype(st)::value,
+                                                       decltype(db)::value>),
                            grid, dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt,
-                           amax_cur, scale_inv_out, noop, tiles_c, ntiles);
+                           amax_cur, scale_inv_out, noop, tiles_c, ntiles, dbias_ws, ws_ld);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
+    auto by_layout = [&](auto st, auto db) {
+        if (q && qt) launch(T_{}, T_{}, st, db);
+        else if (q) launch(T_{}, F_{}, st, db);
+        else launch(F_{}, T_{}, st, db);
+    };
     if (stream_mode) {
-        if (q && qt) launch(T_{}, T_{}, T_{});
-        else if (q) launch(T_{}, F_{}, T_{});
-        else launch(F_{}, T_{}, T_{});
+        if (dbias_ws) by_layout(T_{}, T_{});
+        else by_layout(T_{}, F_{});
     } else {
-        if (q && qt) launch(T_{}, T_{}, F_{});
-        else if (q) launch(T_{}, F_{}, F_{});
-        else launch(F_{}, T_{}, F_{});
+        if (dbias_ws) by_layout(F_{}, T_{});
+        else by_layout(F_{}, F_{});
     }
     return hipGetLastError();
 }
@@ -422,19 +474,64 @@ hipError_t launch_scale_inv_only(const float *scale, float *scale_inv_out, const
 hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
                                       int64_t ld, const float *scale, int fmt, uint8_t *q,
                                       uint8_t *qt, float *amax_cur, float *scale_inv_out,
-                                      const int32_t *noop, hipStream_t stream) {
+                                      const int32_t *noop, float *dbias_ws, int64_t ws_ld,
+                                      hipStream_t stream) {
     if (src == FP8_DTYPE_BF16) {
         if (fmt == FP8_E4M3)
             return launch_src_fmt<FP8_DTYPE_BF16, FP8_E4M3>(x, rows, cols, ld, scale, q, qt,
-                                                            amax_cur, scale_inv_out, noop, stream);
+                                                            amax_cur, scale_inv_out, noop,
+                                                            dbias_ws, ws_ld, stream);
         return launch_src_fmt<FP8_DTYPE_BF16, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
-                                                        scale_inv_out, noop, stream);
+                                                        scale_inv_out, noop, dbias_ws, ws_ld,
+                                                        stream);
     }
     if (fmt == FP8_E4M3)
         return launch_src_fmt<FP8_DTYPE_FP32, FP8_E4M3>(x, rows, cols, ld, scale, q, qt, amax_cur,
-                                                        scale_inv_out, noop, stream);
+                                                        scale_inv_out, noop, dbias_ws, ws_ld,
+                                                        stream);
     return launch_src_fmt<FP8_DTYPE_FP32, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
-                                                    scale_inv_out, noop, stream);
+                                                    scale_inv_out, noop, dbias_ws, ws_ld, stream);
+}
+
+// Bias gradient, second pass: dbias[c] = sum over tile rows tr of
+// ws[tr * ws_ld + c].  A workgroup takes 64 columns; its four 64-thread
+// parts add the tile rows of four contiguous ranges (loads issued sixteen at
+// a time, added in row order) and part 0 adds the four part sums in part
+// order, so the order is fixed.  tiles_r = 0 writes zeros.
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *__restrict__ ws,
+                                                           int64_t tiles_r, int64_t ws_ld,
+                                                           int64_t cols, float *__restrict__ dbias,
+                                                           const int32_t *__restrict__ noop) {
+    if (noop != nullptr && *noop != 0) return;
+    __shared__ float part_sum[4][64];
+    const int cl = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + cl;
+    const int64_t per = (tiles_r + 3) / 4;
+    const int64_t r0 = min(tiles_r, part * per), r1 = min(tiles_r, r0 + per);
+    float acc = 0.0f;
+    if (c < cols) {
+        int64_t r = r0;
+        for (; r + 16 <= r1; r += 16) {
+            float v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = ws[(r + k) * ws_ld + c];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) acc += v[k];
+        }
+        for (; r < r1; ++r) acc += ws[r * ws_ld + c];
+    }
+    part_sum[part][cl] = acc;
+    __syncthreads();
+    if (part == 0 && c < cols)
+        dbias[c] = ((part_sum[0][cl] + part_sum[1][cl]) + part_sum[2][cl]) + part_sum[3][cl];
+}
+
+hipError_t launch_dbias_reduce(const float *ws, int64_t tiles_r, int64_t ws_ld, int64_t cols,
+                               float *dbias, const int32_t *noop, hipStream_t stream) {
+    if (cols == 0) return hipSuccess;
+    hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(256), 0,
+                       stream, ws, tiles_r, ws_ld, cols, dbias, noop);
+    return hipGetLastError();
 }
 
 }  // namespace fp8dsl

@@ -15,10 +15,17 @@ hipError_t launch_scale_update(float *hist, float *amax_cur, float *scale, float
                                const uint8_t *fmt, int T, int H, int margin,
                                hipStream_t stream);
 
+// dbias_ws: nullptr, or the bias-gradient workspace [tiles_r, ws_ld] fp32
+// (ws_ld = 128 * tiles_c) that receives each tile's column sums.
 hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
                                       int64_t ld, const float *scale, int fmt, uint8_t *q,
                                       uint8_t *qt, float *amax_cur, float *scale_inv_out,
-                                      const int32_t *noop, hipStream_t stream);
+                                      const int32_t *noop, float *dbias_ws, int64_t ws_ld,
+                                      hipStream_t stream);
+
+// dbias[c] = sum over tr < tiles_r of ws[tr * ws_ld + c] (tile-row order).
+hipError_t launch_dbias_reduce(const float *ws, int64_t tiles_r, int64_t ws_ld, int64_t cols,
+                               float *dbias, const int32_t *noop, hipStream_t stream);
 
 hipError_t launch_scale_inv_only(const float *scale, float *scale_inv_out, const int32_t *noop,
                                  hipStream_t stream);

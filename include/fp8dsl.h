@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 1
+#define FP8DSL_ABI_VERSION 2
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -159,6 +159,47 @@ int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *
 int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
                             const float *scale, const fp8_tensor_t *out, float *amax_cur,
                             const int32_t *noop_flag, fp8_stream_t stream);
+
+/*
+ * fp8_cast_dbias_workspace_bytes -- device workspace (bytes) that
+ * fp8_cast_transpose_amax_dbias needs for a [rows, cols] source:
+ * ceil(rows / 128) * ceil(cols / 128) * 128 * sizeof(float).  Returns a
+ * negative status for negative or oversized sizes.
+ */
+int64_t fp8_cast_dbias_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * fp8_cast_transpose_amax_dbias -- fp8_cast_transpose_amax plus the bias
+ * gradient in the same pass over the source.
+ *
+ * The training loop of "CPU Overhead of te.Linear FP8 Layers" (reproduction
+ * script: biased linears, fp32 parameters in its FP8 run, loss.backward())
+ * needs, for a biased linear y = x W^T + b, the gradient of b, i.e. the
+ * column sums of the output gradient dY:
+ *
+ *   dbias[c] = sum over r of x[r, c]       (unscaled source, fp32 result)
+ *
+ * Everything fp8_cast_transpose_amax writes is written identically (same
+ * codes, transpose, amax, scale-inverse).  The sum is taken in fp32 in a
+ * fixed order: per 128 x 128 tile, then over tiles in tile-row order (a
+ * second small kernel), so repeated calls give identical bits; its error is
+ * at most (ceil(rows / 128) + 12) * 2^-24 * sum over r of |x[r, c]|.
+ *
+ * dbias     device, [cols] fp32, overwritten; 4-byte aligned.
+ * workspace device scratch of at least
+ *           fp8_cast_dbias_workspace_bytes(rows, cols) bytes, 16-byte
+ *           aligned, owned by the caller; its contents on entry do not
+ *           matter and on return are unspecified.  Two calls that overlap
+ *           on one workspace race.
+ * rows == 0 writes dbias = 0 (cols > 0) and the scale-inverse snapshot;
+ * noop_flag skips the whole call, dbias included.
+ * Other arguments, constraints and errors as fp8_cast_transpose_amax.
+ */
+int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int64_t cols,
+                                  int64_t ld, const float *scale, const fp8_tensor_t *out,
+                                  float *amax_cur, float *dbias, void *workspace,
+                                  int64_t workspace_bytes, const int32_t *noop_flag,
+                                  fp8_stream_t stream);
 
 /*
  * fp8_linear_fwd -- Y = X W^T + bias on FP8 operands.

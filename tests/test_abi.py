@@ -25,7 +25,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
-                 "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version"):
+                 "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
+                 "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes"):
         assert want in names
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 1
+    assert dsl.fp8_abi_version() == 2
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -99,3 +100,29 @@ def test_binding_checks_tensor_arguments():
     with pytest.raises(TypeError):
         dsl.fp8_cast_transpose_amax(torch.zeros(16, 16, dtype=torch.float16),
                                     torch.ones(1), dsl.Float8Tensor(None, None, torch.ones(1), 0, 16, 16))
+
+
+def test_dbias_workspace_size_and_validation():
+    L = dsl.lib()
+    byref = ctypes.byref
+    assert dsl.fp8_cast_dbias_workspace_bytes(8192, 8192) == 64 * 64 * 128 * 4
+    assert dsl.fp8_cast_dbias_workspace_bytes(16, 48) == 1 * 1 * 128 * 4
+    assert dsl.fp8_cast_dbias_workspace_bytes(0, 48) == 0
+    assert L.fp8_cast_dbias_workspace_bytes(-1, 16) == -2
+    d = _desc(32, 48)
+    ws = 0x10000
+    # NULL dbias, NULL / short / misaligned workspace, misaligned dbias
+    assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 32, 48, 48, 0x5000, byref(d), None, None,
+                                           ws, 512, None, None) == -1
+    assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 32, 48, 48, 0x5000, byref(d), None, 0x6000,
+                                           None, 512, None, None) == -1
+    assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 32, 48, 48, 0x5000, byref(d), None, 0x6000,
+                                           ws, 511, None, None) == -2
+    assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 32, 48, 48, 0x5000, byref(d), None, 0x6000,
+                                           ws + 8, 512, None, None) == -3
+    assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 32, 48, 48, 0x5000, byref(d), None, 0x6002,
+                                           ws, 512, None, None) == -3
+    # the cast's own checks still apply (rows not a multiple of 16)
+    d2 = _desc(30, 48)
+    assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 30, 48, 48, 0x5000, byref(d2), None, 0x6000,
+                                           ws, 512, None, None) == -2
