@@ -19,6 +19,9 @@ of the pages it follows:
 * ``dbias`` -- the bias gradient (column sums of the output gradient) that the
   training loop of "CPU Overhead of te.Linear FP8 Layers" needs for its biased
   linears (fp32, exact fp64 sum rounded once).
+* ``produce_cast`` -- the toy block's elementwise producers (``shift * x /
+  scale`` with its nan_to_num, and the residual add) rounded to bf16 and
+  followed by the cast ("CPU Overhead of te.Linear FP8 Layers").
 * ``scale_update`` -- the DelayedScaling recipe (history length 16, algorithm
   "max") of "CPU Overhead of te.Linear FP8 Layers".
 * ``gemm_nt`` / ``gemm_nt_sampled`` -- the per-tensor-scaled FP8 product with
@@ -80,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.orc_cast_transpose_amax.argtypes = [vp, c.c_int, i64, i64, i64, c.c_float, c.c_int,
                                               vp, vp, f32p, f32p]
         L.orc_cast_transpose_amax.restype = c.c_int
+        L.orc_produce_cast.argtypes = [c.c_int, vp, i64, vp, i64, vp, i64, i64, i64, c.c_float,
+                                       c.c_int, vp, vp, vp, f32p, f32p]
+        L.orc_produce_cast.restype = c.c_int
         L.orc_dbias.argtypes = [vp, c.c_int, i64, i64, i64, f32p]
         L.orc_dbias.restype = c.c_int
         L.orc_scale_update.argtypes = [vp, vp, vp, vp, vp, c.c_int, c.c_int, c.c_int, c.c_int]
@@ -177,6 +183,34 @@ def cast_transpose_amax(x: np.ndarray, scale: float, fmt: int, *, want_q: bool =
     if rc != 0:
         raise ValueError("oracle cast rejected its arguments")
     return q, qt, np.float32(amax.value), np.float32(sinv.value)
+
+
+PROD_MODULATE = 1
+PROD_ADD = 2
+
+
+def produce_cast(op: int, x: np.ndarray, a: np.ndarray, b: np.ndarray | None, scale: float,
+                 fmt: int, *, want_q: bool = True, want_qt: bool = True):
+    """y = op(x, a, b) in bf16, then the cast of y.  x, a, b: 2-D uint16 (bf16
+    bits) arrays of one shape, any row stride (views are fine).  Returns
+    (y [R,C] uint16, q or None, qt or None, amax float32, scale_inv float32)."""
+    for t in (x, a) + ((b,) if b is not None else ()):
+        if t.dtype != np.uint16 or t.ndim != 2 or t.strides[1] != 2:
+            raise TypeError("inputs must be 2-D bf16 bit arrays with unit column stride")
+    rows, cols = x.shape
+    ld = lambda t: t.strides[0] // 2
+    y = np.empty((rows, cols), dtype=np.uint16)
+    q = np.empty((rows, cols), dtype=np.uint8) if want_q else None
+    qt = np.empty((cols, rows), dtype=np.uint8) if want_qt else None
+    amax = ctypes.c_float(0.0)
+    sinv = ctypes.c_float(0.0)
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.ctypes.data)
+    rc = lib().orc_produce_cast(op, vp(x), ld(x), vp(a), ld(a), vp(b), ld(b) if b is not None else 0,
+                                rows, cols, ctypes.c_float(scale), fmt, _ptr(y), _ptr(q), _ptr(qt),
+                                ctypes.byref(amax), ctypes.byref(sinv))
+    if rc != 0:
+        raise ValueError("oracle produce_cast rejected its arguments")
+    return y, q, qt, np.float32(amax.value), np.float32(sinv.value)
 
 
 def dbias(x: np.ndarray) -> np.ndarray:

@@ -226,6 +226,53 @@ int orc_dbias(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, fl
     return 0;
 }
 
+/*
+ * Producer-fused cast: the elementwise operation that produces a linear's
+ * input in the toy block of "CPU Overhead of te.Linear FP8 Layers"
+ * (reproduction script: x = shift * x / scale after the modulation linear,
+ * and the residual adds x = x + ...), rounded to bf16, followed by the cast of
+ * its result.  All arithmetic in fp32, as torch does for bf16 tensors:
+ *   op 1 (modulate): y = bf16(a * x / b), one multiply then one correctly
+ *        rounded division, round to nearest even; then an infinite or NaN y
+ *        becomes +0 (the torch.nan_to_num that follows in that script);
+ *   op 2 (residual add): y = bf16(x + a); a NaN result is 0x7FC0.
+ * x, a, b are bf16 [rows, cols] with leading dimensions ldx, lda, ldb (b is
+ * only read by op 1); y is bf16 [rows, cols], row-major.  The cast is then
+ * exactly orc_cast_transpose_amax of y.  Returns 0, or -1 for a bad argument.
+ */
+static uint16_t orc_f32_to_bf16_canon(float f) {
+    if (isnan(f)) return 0x7FC0;
+    return orc_f64_to_bf16((double)f);   /* f is exact in fp64: one rounding */
+}
+
+int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, int64_t lda,
+                     const uint16_t *b, int64_t ldb, int64_t rows, int64_t cols, float scale,
+                     int fmt, uint16_t *y, uint8_t *q, uint8_t *qt, float *amax_inout,
+                     float *scale_inv_out) {
+    if ((op != 1 && op != 2) || rows < 0 || cols < 0 || ldx < cols || lda < cols || !y ||
+        (op == 1 && (!b || ldb < cols)))
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            float xv = orc_bf16_to_f32(x[r * ldx + c]);
+            float av = orc_bf16_to_f32(a[r * lda + c]);
+            uint16_t out;
+            if (op == 1) {
+                float bv = orc_bf16_to_f32(b[r * ldb + c]);
+                float prod = av * xv;
+                float v = prod / bv;
+                out = orc_f32_to_bf16_canon(v);
+                if ((out & 0x7F80u) == 0x7F80u) out = 0x0000;   /* inf or NaN -> +0 */
+            } else {
+                out = orc_f32_to_bf16_canon(xv + av);
+            }
+            y[r * cols + c] = out;
+        }
+    }
+    return orc_cast_transpose_amax(y, 0, rows, cols, cols, scale, fmt, q, qt, amax_inout,
+                                   scale_inv_out);
+}
+
 /* ---- amax history and scale update ----------------------------------- */
 
 /*
