@@ -196,6 +196,56 @@ def dbias_cast_cost(dsl, st, iters: int = 20):
     return {k: round(v, 2) for k, v in res.items()}
 
 
+def producer_cast_cost(dsl, workloads, iters: int = 20):
+    """The toy block's glue in front of a linear at its real shapes, as torch
+    elementwise code followed by the cast, and fused into one pass
+    (fp8_produce_cast_transpose_amax): x = nan_to_num(shift * x / scale) with
+    shift/scale column slices of the [8192, 12288] modulation output, and the
+    residual add x + qkv[:, :2048]; E4M3 codes + transpose + amax of the
+    result each time."""
+    dev = "cuda"
+    H, Mt = workloads.HIDDEN, workloads.TOKENS
+    g = torch.Generator(device=dev).manual_seed(30)
+    mod = (torch.randn(Mt, 6 * H, generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    qkv = (torch.randn(Mt, 3 * H, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    x = torch.rand(Mt, H, generator=g, device=dev).to(torch.bfloat16)
+    shift, scale_m, r = mod[:, :H], mod[:, H:2 * H], qkv[:, :H]
+    y = torch.empty_like(x)
+    out = dsl.Float8Tensor.empty(Mt, H, 0, device=dev)
+    s = torch.tensor([3.5], device=dev)
+    amax = torch.zeros(1, device=dev)
+
+    def torch_mod():
+        t = torch.nan_to_num((shift.float() * x.float() / scale_m.float()).to(torch.bfloat16),
+                             nan=0.0, posinf=0.0, neginf=0.0)
+        dsl.fp8_cast_transpose_amax(t, s, out, amax)
+
+    def torch_add():
+        dsl.fp8_cast_transpose_amax(x + r, s, out, amax)
+
+    fused_mod = lambda: dsl.fp8_produce_cast_transpose_amax(dsl.PRODUCE_MODULATE, x, shift,
+                                                            scale_m, y, s, out, amax)
+    fused_add = lambda: dsl.fp8_produce_cast_transpose_amax(dsl.PRODUCE_ADD, x, r, None, y, s,
+                                                            out, amax)
+    res = {}
+    for _ in range(2):
+        for name, fn in (("modulate_torch_then_cast_us", torch_mod), ("modulate_fused_us", fused_mod),
+                         ("add_torch_then_cast_us", torch_add), ("add_fused_us", fused_add)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / iters * 1e3
+            res[name] = min(res.get(name, us), us)
+    return {k: round(v, 2) for k, v in res.items()}
+
+
 def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     """The 32-block toy transformer forward (hidden 2048, batch 8, seq 1024;
     per block the linears 2048->12288 +b, 2048->6144, 2048->2048,
@@ -203,8 +253,9 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     residual glue in torch), one scale update over all 384 records per
     forward.  Timed eagerly and as one captured HIP graph, each with the
     weights re-cast and with cached FP8 weights (the weight casts see a
-    device no-op flag, so the same graph serves both), next to the same
-    stack in plain torch bf16.  Two interleaved rounds, best of each."""
+    device no-op flag, so the same graph serves both); as a graph with the
+    modulation and residual adds fused into the following casts; and the
+    same stack in plain torch bf16.  Two interleaved rounds, best of each."""
     dev = "cuda"
     H, Mt = workloads.HIDDEN, workloads.TOKENS
     lin = workloads.toy_block_linears()
@@ -261,6 +312,45 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps, (time.perf_counter() - t0) * 1e3 / reps
 
+    def cast_in(bi, l, inp):
+        tx = 12 * bi + 2 * l
+        dsl.fp8_cast_transpose_amax(inp, st.scale[tx:tx + 1], qxs[l], st.amax_cur[tx:tx + 1])
+
+    def produce_in(bi, l, op, x, a, b):
+        tx = 12 * bi + 2 * l
+        y = torch.empty_like(x)
+        dsl.fp8_produce_cast_transpose_amax(op, x, a, b, y, st.scale[tx:tx + 1], qxs[l],
+                                            st.amax_cur[tx:tx + 1])
+        return y
+
+    def w_gemm(bi, l):
+        w, b, qw = layers[bi][l]
+        tw = 12 * bi + 2 * l + 1
+        dsl.fp8_cast_transpose_amax(w, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1],
+                                    noop_flag=flag)
+        dsl.fp8_linear_fwd(qxs[l], qw, b, ys[l])
+        return ys[l]
+
+    def forward_fused(x):
+        """forward() with the modulation and the residual adds fused into the
+        casts of the inputs they produce (fp8_produce_cast_transpose_amax)."""
+        cast_in(0, 0, x)
+        for bi in range(blocks):
+            mod = w_gemm(bi, 0)
+            x = produce_in(bi, 1, dsl.PRODUCE_MODULATE, x, mod[:, :H], mod[:, H:2 * H])
+            sa = w_gemm(bi, 1)
+            x = produce_in(bi, 2, dsl.PRODUCE_ADD, x, sa[:, :H], None)
+            cast_in(bi, 3, x)
+            ca_q = w_gemm(bi, 2)
+            ca_k = w_gemm(bi, 3)
+            x = produce_in(bi, 4, dsl.PRODUCE_ADD, x + ca_q, ca_k[:, :H], None)
+            h = w_gemm(bi, 4)
+            cast_in(bi, 5, h)
+            o = w_gemm(bi, 5)
+            x = produce_in(bi + 1, 0, dsl.PRODUCE_ADD, x, o, None) if bi + 1 < blocks else x + o
+        st.update()
+        return x
+
     def forward_bf16(x):
         """The same stack with plain torch bf16 linears (no FP8): context for
         the FP8-vs-BF16 forward comparison of the toy model's page."""
@@ -278,11 +368,17 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     xin.copy_(x0)
     forward(xin)                              # first launches (kernel attributes) outside capture
     torch.cuda.synchronize()
+    forward_fused(xin)
+    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         forward(xin)
+    graph_fused = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_fused):
+        forward_fused(xin)
     modes = {"eager": (lambda: forward(xin), 0), "eager_cached_weights": (lambda: forward(xin), 1),
              "graph": (graph.replay, 0), "graph_cached_weights": (graph.replay, 1),
+             "graph_fused_producers": (graph_fused.replay, 0),
              "bf16_torch_eager": (lambda: forward_bf16(xin), 0)}
     res = {}
     for _ in range(2):                        # interleaved rounds, best of each mode
@@ -294,8 +390,9 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     flop = 2 * Mt * sum(fin * fout for fin, fout, _ in lin) * blocks
     out = {k: round(v, 3) for k, v in res.items()}
     out.update({"blocks": blocks, "gemm_flop": flop, "library_launches_per_forward": blocks * 18 + 1,
-                "graph_cached_weights_gemm_tflops": round(flop / (res["graph_cached_weights_ms"] * 1e-3) / 1e12, 1)})
-    del graph, layers, qxs, ys
+                "graph_fused_producers_gemm_tflops":
+                    round(flop / (res["graph_fused_producers_ms"] * 1e-3) / 1e12, 1)})
+    del graph, graph_fused, layers, qxs, ys
     torch.cuda.empty_cache()
     return out
 
@@ -449,6 +546,7 @@ def main():
     copy_gbs = copy_ceiling()
 
     dbias_cost = dbias_cast_cost(dsl, st)
+    producer_cost = producer_cast_cost(dsl, workloads)
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
     traffic = traffic_record(root)
     result = {
@@ -486,6 +584,7 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     result["dy_cast_dbias"] = dbias_cost
+    result["producer_fused_cast"] = producer_cost
     if toy is not None:
         result["toy_stack_forward"] = toy
     if not args.no_cpu_baseline:

@@ -34,6 +34,7 @@ __all__ = [
     "DelayedScalingState", "fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
     "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
     "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
+    "fp8_produce_cast_transpose_amax", "PRODUCE_MODULATE", "PRODUCE_ADD",
     "library_path", "lib",
 ]
 
@@ -41,6 +42,8 @@ E4M3 = 0
 E5M2 = 1
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
+PRODUCE_MODULATE = 1
+PRODUCE_ADD = 2
 FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -84,12 +87,15 @@ def lib() -> ctypes.CDLL:
         L.fp8_cast_transpose_amax.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp]
         L.fp8_cast_transpose_amax_dbias.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp,
                                                     i64, vp, vp]
+        L.fp8_produce_cast_transpose_amax.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64,
+                                                      i64, vp, dp, vp, vp, vp]
         L.fp8_cast_dbias_workspace_bytes.argtypes = [i64, i64]
         L.fp8_cast_dbias_workspace_bytes.restype = i64
         L.fp8_linear_fwd.argtypes = [dp, dp, vp, vp, vp]
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
         for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
+                  L.fp8_produce_cast_transpose_amax,
                   L.fp8_linear_fwd, L.fp8_linear_dgrad, L.fp8_linear_wgrad):
             f.restype = ctypes.c_int
         L.fp8_status_string.argtypes = [ctypes.c_int]
@@ -253,6 +259,32 @@ def fp8_cast_transpose_amax_dbias(x: torch.Tensor, scale: torch.Tensor, out: Flo
         _ptr(dbias, torch.float32, "dbias"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)),
         "fp8_cast_transpose_amax_dbias")
+
+
+def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
+                                    b: Optional[torch.Tensor], y: torch.Tensor,
+                                    scale: torch.Tensor, out: Float8Tensor,
+                                    amax_cur: Optional[torch.Tensor] = None,
+                                    noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """y = op(x, a, b) in bf16 (PRODUCE_MODULATE: a * x / b with inf/NaN -> 0;
+    PRODUCE_ADD: x + a), then y cast into `out`.  x, a, b: bf16 2-D device
+    tensors of one shape with unit column stride (column slices are fine);
+    y: contiguous bf16 of that shape."""
+    ins = [x, a] + ([b] if b is not None else [])
+    for t in ins + [y]:
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+            raise ValueError("x, a, b, y must be 2-D bf16 device tensors with unit column stride")
+        if t.shape != x.shape:
+            raise ValueError("x, a, b, y must have one shape")
+    if not y.is_contiguous():
+        raise ValueError("y must be contiguous")
+    d = out.desc()
+    _check(lib().fp8_produce_cast_transpose_amax(
+        op, x.data_ptr(), x.stride(0), a.data_ptr(), a.stride(0),
+        None if b is None else b.data_ptr(), 0 if b is None else b.stride(0), y.data_ptr(),
+        x.shape[0], x.shape[1], _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
+        _ptr(amax_cur, torch.float32, "amax_cur"), _ptr(noop_flag, torch.int32, "noop_flag"),
+        _stream(stream)), "fp8_produce_cast_transpose_amax")
 
 
 def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],

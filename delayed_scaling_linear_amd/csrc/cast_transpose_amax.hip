@@ -237,6 +237,42 @@ __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float 
     }
 }
 
+// Transposed store of one tile from its LDS transpose `lt`: 8 lanes per
+// tile column (16 rows each), 128-byte transposed row segments.
+__device__ __forceinline__ void store_transposed(const uint32_t *lt, uint8_t *__restrict__ qt,
+                                                 int64_t rows, int64_t cols, int64_t row0,
+                                                 int64_t col0, int lane, int wave) {
+    const int qd = lane & 7;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int tc = (lane >> 3) + 8 * (wave + 4 * k);
+        const int64_t gc = col0 + tc;
+        const int64_t gr = row0 + 16 * qd;
+        if (gc < cols && gr < rows) {
+            const int word = tc * 32 + ((4 * qd) ^ (4 * (tc >> 4)));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(&lt[word]);
+            *reinterpret_cast<u32x4 *>(qt + gc * rows + gr) = v;
+        }
+    }
+}
+
+// Fold this workgroup's sign-cleared maximum `key` into *amax_cur: wave
+// reduction, LDS across waves, one atomicMax (skipped when the stored value
+// already covers it: amax_cur only grows while casts run).
+__device__ __forceinline__ void flush_amax(uint32_t key, float *amax_cur, uint32_t *lds_amax,
+                                           int lane, int wave, int tid) {
+    key = wave_max_u32(key);
+    if (lane == 0) lds_amax[wave] = key;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t k = lds_amax[0];
+#pragma unroll
+        for (int w = 1; w < THREADS / 64; ++w) k = max(k, lds_amax[w]);
+        unsigned int *a = reinterpret_cast<unsigned int *>(amax_cur);
+        if (k > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, k);
+    }
+}
+
 // Persistent: workgroup b casts tiles b, b + gridDim.x, ... with the loads of
 // its next tile in flight while the current one is encoded and stored, and
 // a double-buffered LDS transpose tile (one barrier per tile).
@@ -307,21 +343,8 @@ cast_transpose_amax_kernel(
             dst[i].template load<STREAM ? 2 : 0>(rs, off == 0x80000000u ? off : off + i * row_step);
     };
     auto store_t = [&](const uint32_t *lt, int64_t t) {
-        // 8 lanes per column (16 rows each): 128-byte transposed segments.
         const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
-        const int64_t row0 = tr * TILE, col0 = tcn * TILE;
-        const int qd = lane & 7;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int tc = (lane >> 3) + 8 * (wave + 4 * k);
-            const int64_t gc = col0 + tc;
-            const int64_t gr = row0 + 16 * qd;
-            if (gc < cols && gr < rows) {
-                const int word = tc * 32 + ((4 * qd) ^ (4 * (tc >> 4)));
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(&lt[word]);
-                *reinterpret_cast<u32x4 *>(qt + gc * rows + gr) = v;
-            }
-        }
+        store_transposed(lt, qt, rows, cols, tr * TILE, tcn * TILE, lane, wave);
     };
 
     uint32_t key = 0;                        // sign-cleared max, fp32 bit order
@@ -391,20 +414,7 @@ cast_transpose_amax_kernel(
         }
     }
 
-    if (amax_cur != nullptr) {
-        key = wave_max_u32(key);
-        if (lane == 0) lds_amax[wave] = key;
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t k = lds_amax[0];
-#pragma unroll
-            for (int w = 1; w < THREADS / 64; ++w) k = max(k, lds_amax[w]);
-            // amax_cur only grows while casts run, so a value already at least
-            // this block's maximum makes the atomic a no-op: skip it.
-            unsigned int *a = reinterpret_cast<unsigned int *>(amax_cur);
-            if (k > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, k);
-        }
-    }
+    if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
 }
 
 template <int SRC, int FMT>
@@ -493,6 +503,132 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
                                                     scale_inv_out, noop, dbias_ws, ws_ld, stream);
 }
 
+// Producer-fused cast.  The toy block of "CPU Overhead of te.Linear FP8
+// Layers" computes each linear's input with an elementwise operation in
+// torch (x = shift * x / scale after the modulation linear, then
+// nan_to_num; residual adds) and only then casts it.  Here one pass reads the
+// operands, writes the bf16 result y and casts y exactly as
+// cast_transpose_amax_kernel would:
+//   OP 1 (modulate): y = bf16(a * x / b) (fp32 multiply, correctly rounded
+//        fp32 division, round to nearest even), inf or NaN -> +0;
+//   OP 2 (residual add): y = bf16(x + a); a NaN sum becomes 0x7FC0.
+// One workgroup per 128 x 128 tile, the lane layout of the cast (4 rows x 16
+// columns, 16-byte loads and stores).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // finite or inf input
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t produce_pair(uint32_t xw, uint32_t aw, uint32_t bw) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float xv = __uint_as_float(h ? (xw & 0xFFFF0000u) : (xw << 16));
+        const float av = __uint_as_float(h ? (aw & 0xFFFF0000u) : (aw << 16));
+        uint32_t y;
+        if constexpr (OP == FP8_PRODUCE_MODULATE) {
+            const float bv = __uint_as_float(h ? (bw & 0xFFFF0000u) : (bw << 16));
+            const float v = (av * xv) / bv;
+            y = (v != v) ? 0u : f32_to_bf16_bits_rne(v);
+            if ((y & 0x7F80u) == 0x7F80u) y = 0u;
+        } else {
+            const float v = xv + av;
+            y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);
+        }
+        out |= y << (16 * h);
+    }
+    return out;
+}
+
+template <int OP, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) void produce_cast_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ a, int64_t lda,
+    const uint16_t *__restrict__ b, int64_t ldb, uint16_t *__restrict__ y, int64_t rows,
+    int64_t cols, const float *__restrict__ scale_ptr, uint8_t *__restrict__ q,
+    uint8_t *__restrict__ qt, float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
+    const int32_t *__restrict__ noop, int64_t tiles_c) {
+    if (noop != nullptr && *noop != 0) return;
+    __shared__ uint32_t lds_t[TILE * (TILE / 4)];
+    __shared__ uint32_t lds_amax[THREADS / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cc = lane & 7;
+    const int rg = wave * 8 + (lane >> 3);
+    const float s = *scale_ptr;
+    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
+    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
+
+    const int64_t t = blockIdx.x;
+    const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
+    const int64_t row0 = tr * TILE, col0 = tcn * TILE;
+    const int64_t r = row0 + 4 * rg, c = col0 + 16 * cc;
+    const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
+
+    SrcRow<FP8_DTYPE_BF16> ys[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ys[i].v[0] = u32x4{0u, 0u, 0u, 0u};
+        ys[i].v[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (valid) {
+        u32x4 xv[4][2], av[4][2], bv[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                xv[i][h] = *reinterpret_cast<const u32x4 *>(x + (r + i) * ldx + c + 8 * h);
+                av[i][h] = *reinterpret_cast<const u32x4 *>(a + (r + i) * lda + c + 8 * h);
+                if constexpr (OP == FP8_PRODUCE_MODULATE)
+                    bv[i][h] = *reinterpret_cast<const u32x4 *>(b + (r + i) * ldb + c + 8 * h);
+                else
+                    bv[i][h] = u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 X = xv[i][h], A = av[i][h], B = bv[i][h];
+                const u32x4 Y = {produce_pair<OP>(X.x, A.x, B.x), produce_pair<OP>(X.y, A.y, B.y),
+                                 produce_pair<OP>(X.z, A.z, B.z), produce_pair<OP>(X.w, A.w, B.w)};
+                ys[i].v[h] = Y;
+                *reinterpret_cast<u32x4 *>(y + (r + i) * cols + c + 8 * h) = Y;
+            }
+        }
+    }
+    uint32_t key = 0;
+    encode_block<FP8_DTYPE_BF16, FMT, WANT_Q, WANT_QT>(ys, s, s_special, valid, q, r, c, cols, cc,
+                                                       rg, lds_t, key);
+    __syncthreads();
+    if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
+    if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
+}
+
+template <int OP, int FMT>
+hipError_t launch_produce_op_fmt(const uint16_t *x, int64_t ldx, const uint16_t *a, int64_t lda,
+                                 const uint16_t *b, int64_t ldb, uint16_t *y, int64_t rows,
+                                 int64_t cols, const float *scale, uint8_t *q, uint8_t *qt,
+                                 float *amax_cur, float *scale_inv_out, const int32_t *noop,
+                                 hipStream_t stream) {
+    const int64_t tiles_c = (cols + TILE - 1) / TILE;
+    const dim3 grid((unsigned)(((rows + TILE - 1) / TILE) * tiles_c));
+    if (q && qt)
+        hipLaunchKernelGGL((produce_cast_kernel<OP, FMT, true, true>), grid, dim3(THREADS), 0,
+                           stream, x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur,
+                           scale_inv_out, noop, tiles_c);
+    else if (q)
+        hipLaunchKernelGGL((produce_cast_kernel<OP, FMT, true, false>), grid, dim3(THREADS), 0,
+                           stream, x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur,
+                           scale_inv_out, noop, tiles_c);
+    else
+        hipLaunchKernelGGL((produce_cast_kernel<OP, FMT, false, true>), grid, dim3(THREADS), 0,
+                           stream, x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur,
+                           scale_inv_out, noop, tiles_c);
+    return hipGetLastError();
+}
+
 // Bias gradient, second pass: dbias[c] = sum over tile rows tr of
 // ws[tr * ws_ld + c].  A workgroup takes 64 columns; its four 64-thread
 // parts add the tile rows of four contiguous ranges (loads issued sixteen at
@@ -532,6 +668,29 @@ hipError_t launch_dbias_reduce(const float *ws, int64_t tiles_r, int64_t ws_ld, 
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(256), 0,
                        stream, ws, tiles_r, ws_ld, cols, dbias, noop);
     return hipGetLastError();
+}
+
+hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a,
+                               int64_t lda, const uint16_t *b, int64_t ldb, uint16_t *y,
+                               int64_t rows, int64_t cols, const float *scale, int fmt,
+                               uint8_t *q, uint8_t *qt, float *amax_cur, float *scale_inv_out,
+                               const int32_t *noop, hipStream_t stream) {
+    if (op == FP8_PRODUCE_MODULATE) {
+        if (fmt == FP8_E4M3)
+            return launch_produce_op_fmt<FP8_PRODUCE_MODULATE, FP8_E4M3>(
+                x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+                stream);
+        return launch_produce_op_fmt<FP8_PRODUCE_MODULATE, FP8_E5M2>(
+            x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+            stream);
+    }
+    if (fmt == FP8_E4M3)
+        return launch_produce_op_fmt<FP8_PRODUCE_ADD, FP8_E4M3>(
+            x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+            stream);
+    return launch_produce_op_fmt<FP8_PRODUCE_ADD, FP8_E5M2>(x, ldx, a, lda, b, ldb, y, rows, cols,
+                                                            scale, q, qt, amax_cur, scale_inv_out,
+                                                            noop, stream);
 }
 
 }  // namespace fp8dsl

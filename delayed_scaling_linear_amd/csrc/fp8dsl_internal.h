@@ -23,6 +23,13 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
                                       const int32_t *noop, float *dbias_ws, int64_t ws_ld,
                                       hipStream_t stream);
 
+// y = op(x, a, b) in bf16 (row-major [rows, cols]), then the cast of y.
+hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a,
+                               int64_t lda, const uint16_t *b, int64_t ldb, uint16_t *y,
+                               int64_t rows, int64_t cols, const float *scale, int fmt,
+                               uint8_t *q, uint8_t *qt, float *amax_cur, float *scale_inv_out,
+                               const int32_t *noop, hipStream_t stream);
+
 // dbias[c] = sum over tr < tiles_r of ws[tr * ws_ld + c] (tile-row order).
 hipError_t launch_dbias_reduce(const float *ws, int64_t tiles_r, int64_t ws_ld, int64_t cols,
                                float *dbias, const int32_t *noop, hipStream_t stream);

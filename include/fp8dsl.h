@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 2
+#define FP8DSL_ABI_VERSION 3
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -70,6 +70,9 @@ typedef enum { FP8_DTYPE_BF16 = 0, FP8_DTYPE_FP32 = 1 } fp8_dtype_t;
 
 /* Amax-history reduction; "max" is the only one the recipe on the pages uses. */
 typedef enum { FP8_AMAX_ALGO_MAX = 0 } fp8_amax_algo_t;
+
+/* Elementwise producer fused in front of a cast (fp8_produce_cast_transpose_amax). */
+typedef enum { FP8_PRODUCE_MODULATE = 1, FP8_PRODUCE_ADD = 2 } fp8_produce_op_t;
 
 /*
  * An FP8 tensor: codes, optional cached transpose and the scale-inverse that
@@ -200,6 +203,40 @@ int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int6
                                   float *amax_cur, float *dbias, void *workspace,
                                   int64_t workspace_bytes, const int32_t *noop_flag,
                                   fp8_stream_t stream);
+
+/*
+ * fp8_produce_cast_transpose_amax -- the elementwise operation that produces
+ * a linear's input, fused with that input's cast.
+ *
+ * In the toy block of "CPU Overhead of te.Linear FP8 Layers" (reproduction
+ * script) the input of a linear is made by torch elementwise code right
+ * before the linear: x = shift * x / scale (shift and scale are column slices
+ * of the modulation linear's output) followed by torch.nan_to_num, and the
+ * residual adds x = x + ... .  This call computes it and casts it in one pass:
+ *
+ *   op FP8_PRODUCE_MODULATE: y = bf16(a * x / b)   (fp32 multiply, correctly
+ *                            rounded fp32 division, round to nearest even);
+ *                            an infinite or NaN y becomes +0
+ *   op FP8_PRODUCE_ADD:      y = bf16(x + a)       (fp32 add, round to nearest
+ *                            even); a NaN y is written as 0x7FC0
+ *
+ * then writes y (bf16, row-major [rows, cols], ld = cols) and exactly what
+ * fp8_cast_transpose_amax writes for the bf16 source y with this scale.
+ *
+ * x, a, b   device bf16 [rows, cols] with row strides ldx, lda, ldb
+ *           (elements, each >= cols and a multiple of 8; 16-byte aligned); b
+ *           is only read by MODULATE (NULL otherwise).  Column slices of a
+ *           wider tensor are fine.
+ * y         device bf16 [rows, cols], 16-byte aligned; must not overlap the
+ *           inputs.
+ * Other arguments, constraints (rows, cols multiples of 16) and errors as
+ * fp8_cast_transpose_amax; FP8_ERR_ARG for an unknown op.
+ */
+int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
+                                    const uint16_t *a, int64_t lda, const uint16_t *b,
+                                    int64_t ldb, uint16_t *y, int64_t rows, int64_t cols,
+                                    const float *scale, const fp8_tensor_t *out, float *amax_cur,
+                                    const int32_t *noop_flag, fp8_stream_t stream);
 
 /*
  * fp8_linear_fwd -- Y = X W^T + bias on FP8 operands.

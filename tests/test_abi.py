@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
                  "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
-                 "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes"):
+                 "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
+                 "fp8_produce_cast_transpose_amax"):
         assert want in names
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 2
+    assert dsl.fp8_abi_version() == 3
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -126,3 +127,21 @@ def test_dbias_workspace_size_and_validation():
     d2 = _desc(30, 48)
     assert L.fp8_cast_transpose_amax_dbias(0x4000, 0, 30, 48, 48, 0x5000, byref(d2), None, 0x6000,
                                            ws, 512, None, None) == -2
+
+
+def test_produce_cast_validation():
+    L = dsl.lib()
+    byref = ctypes.byref
+    d = _desc(32, 48)
+    X, A, B, Y = 0x10000, 0x20000, 0x30000, 0x40000
+    ok = dict(ldx=48, lda=48, ldb=48)
+    call = lambda op, ldx=48, lda=48, ldb=48, b=B, x=X, y=Y, desc=d: L.fp8_produce_cast_transpose_amax(
+        op, x, ldx, A, lda, b, ldb, y, desc.rows, desc.cols, 0x5000, byref(desc), None, None, None)
+    assert call(3) == -5                          # unknown op
+    assert call(1, b=None) == -1                  # modulate needs b
+    assert call(1, ldx=40) == -2                  # ld < cols
+    assert call(1, lda=52) == -2                  # ld not a multiple of 8
+    assert call(1, ldb=44) == -2
+    assert call(1, x=X + 8) == -3                 # misaligned input
+    assert call(2, y=Y + 4) == -3                 # misaligned output
+    assert call(2, desc=_desc(30, 48)) == -2      # rows not a multiple of 16

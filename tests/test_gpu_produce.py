@@ -1,0 +1,115 @@
+"""GPU parity of the producer-fused cast (fp8_produce_cast_transpose_amax):
+the toy block's elementwise producers rounded to bf16 and the cast of the
+result, bit-exact against the oracle (y, codes, transpose, amax,
+scale-inverse), through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import delayed_scaling_linear_amd as dsl
+import oracle
+from tests.gpu_util import DEV, bits8, bits16, f32_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits_view(t: torch.Tensor) -> np.ndarray:
+    """bf16 bits of a (possibly strided) CPU tensor as a numpy view with the same strides."""
+    base = t.contiguous() if t.storage_offset() == 0 and t.is_contiguous() else None
+    if base is not None:
+        return base.view(torch.int16).numpy().view(np.uint16)
+    full = t._base if t._base is not None else t
+    fb = full.view(torch.int16).numpy().view(np.uint16)
+    r0, c0 = divmod(t.storage_offset(), full.stride(0))
+    return fb[r0:r0 + t.shape[0], c0:c0 + t.shape[1]]
+
+
+def _run_and_check(op, x, a, b, scale, fmt, q=True, qt=True):
+    """x, a, b: CPU bf16 tensors (b may be None); views of wider tensors allowed."""
+    rows, cols = x.shape
+    # move the underlying storage once so device views keep the host strides
+    def to_dev(t):
+        if t is None:
+            return None
+        if t._base is not None:
+            full = t._base.to(DEV)
+            r0, c0 = divmod(t.storage_offset(), t._base.stride(0))
+            return full[r0:r0 + t.shape[0], c0:c0 + t.shape[1]]
+        return t.to(DEV)
+    xd, ad, bd = to_dev(x), to_dev(a), to_dev(b)
+    y = torch.full((rows, cols), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = dsl.Float8Tensor.empty(rows, cols, fmt, data=q, transpose=qt, device=DEV)
+    s = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+    dsl.fp8_produce_cast_transpose_amax(op, xd, ad, bd, y, s, out, amax)
+    torch.cuda.synchronize()
+    oy, oq, oqt, oamax, osinv = oracle.produce_cast(
+        op, _bits_view(x), _bits_view(a), None if b is None else _bits_view(b), scale, fmt,
+        want_q=q, want_qt=qt)
+    np.testing.assert_array_equal(bits16(y), oy)
+    if q:
+        np.testing.assert_array_equal(bits8(out.data), oq)
+    if qt:
+        np.testing.assert_array_equal(bits8(out.data_t), oqt)
+    assert f32_bits(amax)[0] == np.float32(oamax).view(np.uint32)
+    assert f32_bits(out.scale_inv)[0] == np.float32(osinv).view(np.uint32)
+    return y
+
+
+def _rand(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (400, 272), (272, 400), (1024, 2048)])
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_modulate_shapes(shape, fmt):
+    x, a, b = _rand(shape, 1), _rand(shape, 2), _rand(shape, 3, 0.7)
+    _run_and_check(oracle.PROD_MODULATE, x, a, b, 41.0, fmt)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (400, 272), (1024, 2048)])
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_add_shapes(shape, fmt):
+    x, a = _rand(shape, 4), _rand(shape, 5, 3.0)
+    _run_and_check(oracle.PROD_ADD, x, a, None, 41.0, fmt)
+
+
+def test_toy_block_shapes_with_column_slices():
+    """shift, scale = columns [0, 2048) and [2048, 4096) of the modulation
+    output [8192, 12288]; the qkv residual = columns [0, 2048) of [8192, 6144]."""
+    mod = _rand((8192, 12288), 6, 0.5)
+    x = (torch.rand(8192, 2048, generator=torch.Generator().manual_seed(7))).to(torch.bfloat16)
+    y = _run_and_check(oracle.PROD_MODULATE, x, mod[:, :2048], mod[:, 2048:4096], 3.5, oracle.E4M3)
+    qkv = _rand((8192, 6144), 8, 0.02)
+    _run_and_check(oracle.PROD_ADD, y.cpu(), qkv[:, :2048], None, 3.5, oracle.E4M3, qt=False)
+
+
+def test_special_values():
+    x, a, b = _rand((64, 64), 9), _rand((64, 64), 10), _rand((64, 64), 11)
+    b[0, :] = 0.0                        # a*x/0 -> inf -> 0
+    x[1, :] = 0.0
+    b[1, :] = 0.0                        # 0/0 -> NaN -> 0
+    x[2, :] = 3.0e38
+    a[2, :] = 3.0e38                     # overflow -> 0
+    y = _run_and_check(oracle.PROD_MODULATE, x, a, b, 1.0, oracle.E5M2)
+    assert (bits16(y)[:3] == 0).all()
+    x2, a2 = _rand((64, 64), 12), _rand((64, 64), 13)
+    x2[0, 0], a2[1, 1] = float("nan"), float("inf")
+    x2[2, 2], a2[2, 2] = float("-inf"), float("inf")
+    y = _run_and_check(oracle.PROD_ADD, x2, a2, None, 1.0, oracle.E5M2)
+    v = bits16(y)
+    assert v[0, 0] == 0x7FC0 and v[2, 2] == 0x7FC0 and v[1, 1] == 0x7F80
+
+
+def test_noop_flag_writes_nothing():
+    x, a = _rand((64, 64), 14).to(DEV), _rand((64, 64), 15).to(DEV)
+    y = torch.full((64, 64), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = dsl.Float8Tensor.empty(64, 64, 0, device=DEV)
+    out.data.fill_(0xAA)
+    flag = torch.ones(1, dtype=torch.int32, device=DEV)
+    amax = torch.zeros(1, device=DEV)
+    dsl.fp8_produce_cast_transpose_amax(dsl.PRODUCE_ADD, x, a, None, y,
+                                        torch.ones(1, device=DEV), out, amax, noop_flag=flag)
+    torch.cuda.synchronize()
+    assert (y.float() == -7.0).all() and (out.data == 0xAA).all() and float(amax[0]) == 0.0

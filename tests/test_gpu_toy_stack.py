@@ -193,6 +193,53 @@ class _CachedWeightStack:
         dsl.fp8_linear_fwd(qx, qw, b, y)
         return y
 
+    def _cast_w_gemm(self, bi, l):
+        """Weight cast (flag-gated) and GEMM of linear l, its input already cast in qx."""
+        w, b, qw, qx, y = self.blocks[bi][l]
+        tw = 12 * bi + 2 * l + 1
+        dsl.fp8_cast_transpose_amax(w, self.st.scale[tw:tw + 1], qw, self.st.amax_cur[tw:tw + 1],
+                                    noop_flag=self.flag)
+        dsl.fp8_linear_fwd(qx, qw, b, y)
+        return y
+
+    def _cast_in(self, bi, l, inp):
+        tx = 12 * bi + 2 * l
+        dsl.fp8_cast_transpose_amax(inp, self.st.scale[tx:tx + 1], self.blocks[bi][l][3],
+                                    self.st.amax_cur[tx:tx + 1])
+
+    def _produce_in(self, bi, l, op, x, a, b, y):
+        tx = 12 * bi + 2 * l
+        dsl.fp8_produce_cast_transpose_amax(op, x, a, b, y, self.st.scale[tx:tx + 1],
+                                            self.blocks[bi][l][3], self.st.amax_cur[tx:tx + 1])
+        return y
+
+    def forward_fused(self, x):
+        """forward() with each linear's input produced and cast in one pass
+        where the glue allows (modulation, residual adds)."""
+        H = self.H
+        nb = len(self.blocks)
+        self._cast_in(0, 0, x)
+        for bi in range(nb):
+            mod = self._cast_w_gemm(bi, 0)
+            x = self._produce_in(bi, 1, dsl.PRODUCE_MODULATE, x, mod[:, :H], mod[:, H:2 * H],
+                                 torch.empty_like(x))
+            sa = self._cast_w_gemm(bi, 1)
+            x = self._produce_in(bi, 2, dsl.PRODUCE_ADD, x, sa[:, :H], None, torch.empty_like(x))
+            self._cast_in(bi, 3, x)
+            ca_q = self._cast_w_gemm(bi, 2)
+            ca_k = self._cast_w_gemm(bi, 3)
+            x = self._produce_in(bi, 4, dsl.PRODUCE_ADD, x + ca_q, ca_k[:, :H], None,
+                                 torch.empty_like(x))
+            h = self._cast_w_gemm(bi, 4)
+            self._cast_in(bi, 5, h)
+            o = self._cast_w_gemm(bi, 5)
+            if bi + 1 < nb:
+                x = self._produce_in(bi + 1, 0, dsl.PRODUCE_ADD, x, o, None, torch.empty_like(x))
+            else:
+                x = x + o
+        self.st.update()
+        return x
+
     def forward(self, x):
         H = self.H
         for bi in range(len(self.blocks)):
@@ -250,3 +297,19 @@ def test_cached_weights_and_whole_forward_graph():
         assert torch.equal(gout.view(torch.int16), want.view(torch.int16)), f"micro-batch {rep + 1}"
     for name in ("amax_history", "scale", "scale_inv"):
         assert torch.equal(getattr(g.st, name), getattr(eager.st, name)), name
+
+
+def test_fused_producers_forward_matches_torch_glue():
+    """The 2-block forward with the modulation and the residual adds fused into
+    the following casts gives the same bits as the forward with torch glue
+    followed by separate casts (same scales, same weights): outputs, and the
+    whole delayed-scaling state after the update."""
+    x = workloads.uniform_bf16((M, workloads.HIDDEN), 21).to(DEV)
+    a, b = _CachedWeightStack(2), _CachedWeightStack(2)
+    for _ in range(2):                         # two steps: the second uses updated scales
+        ya = a.forward(x)
+        yb = b.forward_fused(x)
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+    for name in ("amax_history", "scale", "scale_inv"):
+        assert torch.equal(getattr(a.st, name), getattr(b.st, name)), name
