@@ -22,6 +22,9 @@ of the pages it follows:
 * ``produce_cast`` -- the toy block's elementwise producers (``shift * x /
   scale`` with its nan_to_num, and the residual add) rounded to bf16 and
   followed by the cast ("CPU Overhead of te.Linear FP8 Layers").
+* ``dynamic_cast`` -- dynamic scaling, the comparator the float8 all-gather
+  page contrasts delayed scaling with (amax of the tensor itself, then the
+  cast with fp8_max / amax).
 * ``scale_update`` -- the DelayedScaling recipe (history length 16, algorithm
   "max") of "CPU Overhead of te.Linear FP8 Layers".
 * ``gemm_nt`` / ``gemm_nt_sampled`` -- the per-tensor-scaled FP8 product with
@@ -86,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.orc_produce_cast.argtypes = [c.c_int, vp, i64, vp, i64, vp, i64, i64, i64, c.c_float,
                                        c.c_int, vp, vp, vp, f32p, f32p]
         L.orc_produce_cast.restype = c.c_int
+        L.orc_dynamic_cast.argtypes = [vp, c.c_int, i64, i64, i64, c.c_int, c.c_int, f32p, vp, vp,
+                                       f32p, f32p]
+        L.orc_dynamic_cast.restype = c.c_int
         L.orc_dbias.argtypes = [vp, c.c_int, i64, i64, i64, f32p]
         L.orc_dbias.restype = c.c_int
         L.orc_scale_update.argtypes = [vp, vp, vp, vp, vp, c.c_int, c.c_int, c.c_int, c.c_int]
@@ -211,6 +217,30 @@ def produce_cast(op: int, x: np.ndarray, a: np.ndarray, b: np.ndarray | None, sc
     if rc != 0:
         raise ValueError("oracle produce_cast rejected its arguments")
     return y, q, qt, np.float32(amax.value), np.float32(sinv.value)
+
+
+def dynamic_cast(x: np.ndarray, fmt: int, *, margin: int = 0, fallback_scale: float = 1.0,
+                 want_q: bool = True, want_qt: bool = True):
+    """Dynamic scaling of a 2-D source (uint16 = bf16 bits, or float32):
+    returns (q or None, qt or None, amax, scale, scale_inv), float32 scalars."""
+    if x.dtype == np.uint16:
+        src = SRC_BF16
+    elif x.dtype == np.float32:
+        src = SRC_FP32
+    else:
+        raise TypeError("source must be bf16 bits (uint16) or float32")
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), dtype=np.uint8) if want_q else None
+    qt = np.empty((cols, rows), dtype=np.uint8) if want_qt else None
+    scale = ctypes.c_float(fallback_scale)
+    amax = ctypes.c_float(0.0)
+    sinv = ctypes.c_float(0.0)
+    rc = lib().orc_dynamic_cast(_ptr(x), src, rows, cols, cols, margin, fmt, ctypes.byref(scale),
+                                _ptr(q), _ptr(qt), ctypes.byref(amax), ctypes.byref(sinv))
+    if rc != 0:
+        raise ValueError("oracle dynamic_cast rejected its arguments")
+    return q, qt, np.float32(amax.value), np.float32(scale.value), np.float32(sinv.value)
 
 
 def dbias(x: np.ndarray) -> np.ndarray:

@@ -273,6 +273,43 @@ int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, 
                                    scale_inv_out);
 }
 
+/*
+ * Dynamic scaling, the comparator of delayed scaling: "support delayed
+ * scaling of weight in float8 all-gather" contrasts the two recipes
+ * (dynamic scaling reads a tensor twice -- once for its amax, once for the
+ * cast -- where delayed scaling takes the amax in the cast's own read).  Here:
+ *   amax  = max |x| of this very tensor (sign-cleared fp32 bit order);
+ *   scale = fp8_max / (amax * 2^margin) in fp32, with the scale update's
+ *           guard: *scale_inout is kept when amax is zero or not finite or
+ *           the quotient is not a finite positive number;
+ * then the cast of x with that scale, as orc_cast_transpose_amax (no amax
+ * accumulation).  Writes *amax_out, *scale_inout and *scale_inv_out.
+ * Returns 0, or -1 for a bad argument.
+ */
+int orc_dynamic_cast(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, int margin,
+                     int fmt, float *scale_inout, uint8_t *q, uint8_t *qt, float *amax_out,
+                     float *scale_inv_out) {
+    orc_fmt f;
+    if (orc_get_fmt(fmt, &f) || (src != 0 && src != 1) || rows < 0 || cols < 0 || ld < cols ||
+        !scale_inout || !amax_out)
+        return -1;
+    uint32_t best = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            uint32_t k = orc_abs_key(orc_load_src(x, src, r * ld + c));
+            if (k > best) best = k;
+        }
+    float amax = orc_bits_f32(best);
+    *amax_out = amax;
+    if (isfinite(amax) && amax > 0.0f) {
+        float fp8_max = (float)orc_fp8_max(fmt);
+        float s = fp8_max / ldexpf(amax, margin);   /* fp32, correctly rounded */
+        if (isfinite(s) && s > 0.0f) *scale_inout = s;
+    }
+    return orc_cast_transpose_amax(x, src, rows, cols, ld, *scale_inout, fmt, q, qt, NULL,
+                                   scale_inv_out);
+}
+
 /* ---- amax history and scale update ----------------------------------- */
 
 /*
