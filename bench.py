@@ -196,6 +196,40 @@ def dbias_cast_cost(dsl, st, iters: int = 20):
     return {k: round(v, 2) for k, v in res.items()}
 
 
+def dynamic_vs_delayed(dsl, st, iters: int = 20):
+    """Delayed scaling (one cast pass: codes + transpose + amax with the scale
+    from earlier amaxes) against dynamic scaling (amax pass, scale, then the
+    cast pass) on the step's X [8192, 2048] (E4M3) and dY [8192, 8192] (E5M2)
+    casts, back to back."""
+    g = st["state"]
+    scale = torch.ones(1, device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    cases = {
+        "x": (lambda: dsl.fp8_cast_transpose_amax(st["x"], g.scale[0:1], st["qx"], g.amax_cur[0:1]),
+              lambda: dsl.fp8_cast_transpose_dynamic(st["x"], scale, st["qx"], amax)),
+        "dy": (lambda: dsl.fp8_cast_transpose_amax(st["dy"], g.scale[2:3], st["qdy"], g.amax_cur[2:3]),
+               lambda: dsl.fp8_cast_transpose_dynamic(st["dy"], scale, st["qdy"], amax)),
+    }
+    res = {}
+    for _ in range(2):
+        for name, (delayed, dynamic) in cases.items():
+            for kind, fn in (("delayed", delayed), ("dynamic", dynamic)):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(iters):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / iters * 1e3
+                key = f"{name}_{kind}_us"
+                res[key] = min(res.get(key, us), us)
+    return {k: round(v, 2) for k, v in res.items()}
+
+
 def producer_cast_cost(dsl, workloads, iters: int = 20):
     """The toy block's glue in front of a linear at its real shapes, as torch
     elementwise code followed by the cast, and fused into one pass
@@ -547,6 +581,7 @@ def main():
 
     dbias_cost = dbias_cast_cost(dsl, st)
     producer_cost = producer_cast_cost(dsl, workloads)
+    dyn_cost = dynamic_vs_delayed(dsl, st)
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
     traffic = traffic_record(root)
     result = {
@@ -585,6 +620,7 @@ def main():
     }
     result["dy_cast_dbias"] = dbias_cost
     result["producer_fused_cast"] = producer_cost
+    result["delayed_vs_dynamic_cast"] = dyn_cost
     if toy is not None:
         result["toy_stack_forward"] = toy
     if not args.no_cpu_baseline:

@@ -35,6 +35,7 @@ __all__ = [
     "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
     "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
     "fp8_produce_cast_transpose_amax", "PRODUCE_MODULATE", "PRODUCE_ADD",
+    "fp8_cast_transpose_dynamic",
     "library_path", "lib",
 ]
 
@@ -89,13 +90,14 @@ def lib() -> ctypes.CDLL:
                                                     i64, vp, vp]
         L.fp8_produce_cast_transpose_amax.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64,
                                                       i64, vp, dp, vp, vp, vp]
+        L.fp8_cast_transpose_dynamic.argtypes = [vp, i32, i64, i64, i64, i32, vp, dp, vp, vp, vp]
         L.fp8_cast_dbias_workspace_bytes.argtypes = [i64, i64]
         L.fp8_cast_dbias_workspace_bytes.restype = i64
         L.fp8_linear_fwd.argtypes = [dp, dp, vp, vp, vp]
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
         for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
-                  L.fp8_produce_cast_transpose_amax,
+                  L.fp8_produce_cast_transpose_amax, L.fp8_cast_transpose_dynamic,
                   L.fp8_linear_fwd, L.fp8_linear_dgrad, L.fp8_linear_wgrad):
             f.restype = ctypes.c_int
         L.fp8_status_string.argtypes = [ctypes.c_int]
@@ -285,6 +287,29 @@ def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
         x.shape[0], x.shape[1], _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
         _ptr(amax_cur, torch.float32, "amax_cur"), _ptr(noop_flag, torch.int32, "noop_flag"),
         _stream(stream)), "fp8_produce_cast_transpose_amax")
+
+
+def fp8_cast_transpose_dynamic(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,
+                               amax: torch.Tensor, margin: int = 0,
+                               noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Dynamic scaling: amax of x, scale = fp8_max / (amax * 2^margin) (scale
+    keeps its value for a zero or non-finite amax), then the cast into `out`.
+    `scale` (in/out) and `amax` (out) are 1-element fp32 device tensors."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride in the last dimension")
+    if x.dtype == torch.bfloat16:
+        src = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        src = DTYPE_FP32
+    else:
+        raise TypeError("x must be bf16 or fp32")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    d = out.desc()
+    _check(lib().fp8_cast_transpose_dynamic(
+        x.data_ptr(), src, x.shape[0], x.shape[1], x.stride(0), margin,
+        _ptr(scale, torch.float32, "scale"), ctypes.byref(d), _ptr(amax, torch.float32, "amax"),
+        _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)), "fp8_cast_transpose_dynamic")
 
 
 def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],

@@ -183,6 +183,28 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
                                          out->scale_inv, noop_flag, s));
 }
 
+int fp8_cast_transpose_dynamic(const void *x, int32_t src, int64_t rows, int64_t cols,
+                               int64_t ld, int32_t margin, float *scale, const fp8_tensor_t *out,
+                               float *amax, const int32_t *noop_flag, fp8_stream_t stream) {
+    if (int e = check_cast(x, src, rows, cols, ld, scale, out)) return e;
+    if (margin < -126 || margin > 126) return FP8_ERR_ARG;
+    if (amax == nullptr) return FP8_ERR_NULL;
+    if (int d = check_device()) return d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // amax of x and the scale derived from it, then the ordinary cast with
+    // that scale (no amax accumulation: the amax is already known).
+    if (int e = status_of(launch_dynamic_scale(x, src, rows, cols, ld, out->fmt, margin, amax,
+                                               scale, noop_flag, s)))
+        return e;
+    if (rows == 0 || cols == 0) {
+        if (out->scale_inv == nullptr) return FP8_OK;
+        return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
+    }
+    return status_of(launch_cast_transpose_amax(x, src, rows, cols, ld, scale, out->fmt,
+                                                out->data, out->data_t, nullptr, out->scale_inv,
+                                                noop_flag, nullptr, 0, s));
+}
+
 int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
                    uint16_t *y, fp8_stream_t stream) {
     if (!x || !w) return FP8_ERR_NULL;

@@ -30,6 +30,12 @@ hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uin
                                uint8_t *q, uint8_t *qt, float *amax_cur, float *scale_inv_out,
                                const int32_t *noop, hipStream_t stream);
 
+// Dynamic scaling: *amax = max |x| (cleared first), then *scale = fp8_max /
+// (amax * 2^margin) unless zero / non-finite (the scale update's guard).
+hipError_t launch_dynamic_scale(const void *x, int src, int64_t rows, int64_t cols, int64_t ld,
+                                int fmt, int margin, float *amax, float *scale,
+                                const int32_t *noop, hipStream_t stream);
+
 // dbias[c] = sum over tr < tiles_r of ws[tr * ws_ld + c] (tile-row order).
 hipError_t launch_dbias_reduce(const float *ws, int64_t tiles_r, int64_t ws_ld, int64_t cols,
                                float *dbias, const int32_t *noop, hipStream_t stream);

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 3
+#define FP8DSL_ABI_VERSION 4
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -237,6 +237,28 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
                                     int64_t ldb, uint16_t *y, int64_t rows, int64_t cols,
                                     const float *scale, const fp8_tensor_t *out, float *amax_cur,
                                     const int32_t *noop_flag, fp8_stream_t stream);
+
+/*
+ * fp8_cast_transpose_dynamic -- dynamic scaling, the comparator of delayed
+ * scaling ("support delayed scaling of weight in float8 all-gather" contrasts
+ * them: dynamic scaling reads the tensor twice, delayed scaling once).
+ *
+ *   *amax  = max |x|  of this tensor (sign-cleared fp32 bit order)
+ *   *scale = fp8_max / (*amax * 2^margin)   -- the fp8_scale_update formula;
+ *            the value in *scale on entry is kept when *amax is zero or not
+ *            finite or the quotient is not a finite positive number
+ * then exactly fp8_cast_transpose_amax with that scale (without amax
+ * accumulation).  Four launches on `stream`: clear *amax, an amax-only pass
+ * over x, the scale, the cast.
+ *
+ * scale   device, 1 float, in: fallback scale, out: the scale used.
+ * amax    device, 1 float, out.
+ * margin  -126 .. 126.
+ * Other arguments, constraints and errors as fp8_cast_transpose_amax.
+ */
+int fp8_cast_transpose_dynamic(const void *x, int32_t src, int64_t rows, int64_t cols,
+                               int64_t ld, int32_t margin, float *scale, const fp8_tensor_t *out,
+                               float *amax, const int32_t *noop_flag, fp8_stream_t stream);
 
 /*
  * fp8_linear_fwd -- Y = X W^T + bias on FP8 operands.

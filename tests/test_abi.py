@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     for want in ("fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
                  "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
                  "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
-                 "fp8_produce_cast_transpose_amax"):
+                 "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic"):
         assert want in names
 
 
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 3
+    assert dsl.fp8_abi_version() == 4
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -145,3 +145,18 @@ def test_produce_cast_validation():
     assert call(1, x=X + 8) == -3                 # misaligned input
     assert call(2, y=Y + 4) == -3                 # misaligned output
     assert call(2, desc=_desc(30, 48)) == -2      # rows not a multiple of 16
+
+
+def test_dynamic_cast_validation():
+    L = dsl.lib()
+    byref = ctypes.byref
+    d = _desc(32, 48)
+    assert L.fp8_cast_transpose_dynamic(0x4000, 0, 32, 48, 48, 200, 0x5000, byref(d), 0x6000,
+                                        None, None) == -5           # margin out of range
+    assert L.fp8_cast_transpose_dynamic(0x4000, 0, 32, 48, 48, 0, 0x5000, byref(d), None,
+                                        None, None) == -1           # amax NULL
+    assert L.fp8_cast_transpose_dynamic(0x4000, 0, 32, 48, 48, 0, None, byref(d), 0x6000,
+                                        None, None) == -1           # scale NULL
+    d2 = _desc(32, 40)
+    assert L.fp8_cast_transpose_dynamic(0x4000, 0, 32, 40, 40, 0, 0x5000, byref(d2), 0x6000,
+                                        None, None) == -2           # cols not a multiple of 16
