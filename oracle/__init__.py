@@ -29,6 +29,9 @@ of the pages it follows:
   "max") of "CPU Overhead of te.Linear FP8 Layers".
 * ``gemm_nt`` / ``gemm_nt_sampled`` -- the per-tensor-scaled FP8 product with
   bias of the ``torch._scaled_mm`` example (Part 2 blog).
+* ``gemm_nt_fp8out`` -- the same product with an FP8 output and its amax (the
+  ``torch._scaled_mm`` example's FP8 out_dtype, which also returns the
+  output amax): the fp32 product followed by the cast.
 
 Parity pins for every function are in ``tests/test_oracle_*.py``; there is no
 function here without one.
@@ -102,6 +105,10 @@ def lib() -> ctypes.CDLL:
         L.orc_gemm_nt_sampled.argtypes = [vp, c.c_int, i64, vp, c.c_int, i64, i64, c.c_float,
                                           c.c_float, vp, c.c_int, vp, vp, i64, vp]
         L.orc_gemm_nt_sampled.restype = c.c_int
+        L.orc_gemm_nt_fp8out.argtypes = [vp, c.c_int, i64, vp, c.c_int, i64, i64, i64, i64,
+                                         c.c_float, c.c_float, vp, c.c_float, c.c_int, vp, i64,
+                                         vp, f32p, f32p]
+        L.orc_gemm_nt_fp8out.restype = c.c_int
         _lib = L
     return _lib
 
@@ -300,6 +307,36 @@ def gemm_nt(A: np.ndarray, fa: int, B: np.ndarray, fb: int, sinv_a: float, sinv_
     if rc != 0:
         raise ValueError("oracle GEMM rejected its arguments")
     return out
+
+
+def gemm_nt_fp8out(A: np.ndarray, fa: int, B: np.ndarray, fb: int, sinv_a: float,
+                   sinv_b: float, scale_out: float, fo: int, bias: np.ndarray | None = None,
+                   amax_in: float = 0.0):
+    """torch._scaled_mm with an FP8 out_dtype: v = fp32(dec(A) @ dec(B).T *
+    sinv_a * sinv_b + bias), then the cast of v with scale_out.
+
+    Returns (codes [M, N] uint8, v [M, N] float32, amax float32 = max(amax_in,
+    max|v|) over the unscaled v, scale_inv float32 = 1 / scale_out).
+    """
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+        assert bias.shape == (N,)
+    codes = np.empty((M, N), dtype=np.uint8)
+    v = np.empty((M, N), dtype=np.float32)
+    amax = ctypes.c_float(amax_in)
+    sinv = ctypes.c_float(0.0)
+    rc = lib().orc_gemm_nt_fp8out(_ptr(A), fa, K, _ptr(B), fb, K, M, N, K,
+                                  ctypes.c_float(sinv_a), ctypes.c_float(sinv_b), _ptr(bias),
+                                  ctypes.c_float(scale_out), fo, _ptr(codes), N, _ptr(v),
+                                  ctypes.byref(amax), ctypes.byref(sinv))
+    if rc != 0:
+        raise ValueError("oracle GEMM rejected its arguments")
+    return codes, v, np.float32(amax.value), np.float32(sinv.value)
 
 
 def gemm_nt_sampled(A: np.ndarray, fa: int, B: np.ndarray, fb: int, sinv_a: float,

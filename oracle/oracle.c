@@ -412,6 +412,49 @@ int orc_gemm_nt(const uint8_t *A, int fa, int64_t lda, const uint8_t *B, int fb,
     return 0;
 }
 
+/*
+ * FP8-output form of the product: torch._scaled_mm called with an FP8
+ * out_dtype returns the FP8 output together with its amax (the example in
+ * the Part 2 blog, section on torch._scaled_mm).  The pages print the call,
+ * not its arithmetic; the reading taken here is "the fp32 product, then the
+ * ordinary cast of it":
+ *   v[i, j]   = fp32( acc * sinv_a * sinv_b + bias[j] ), rounded once, as the
+ *               fp32 output of orc_gemm_nt;
+ *   codes     = the cast of v with the output's own scale (one fp32 multiply,
+ *               saturating round-to-nearest-even, NaN -> sign|0x7F);
+ *   *amax_inout folds in max |v| over the UNSCALED v -- the amax that a
+ *               delayed-scaling history of the output records, as the cast
+ *               records the amax of its unscaled source;
+ *   *scale_inv_out = 1 / scale_out, the output's scale-inverse snapshot.
+ * codes is [M, N] row-major (ldo).  v_out (fp32 [M, N], row-major, may be
+ * NULL) receives v.  Returns 0 or -1.
+ */
+int orc_gemm_nt_fp8out(const uint8_t *A, int fa, int64_t lda, const uint8_t *B, int fb,
+                       int64_t ldb, int64_t M, int64_t N, int64_t K, float sinv_a,
+                       float sinv_b, const uint16_t *bias, float scale_out, int fo,
+                       uint8_t *codes, int64_t ldo, float *v_out, float *amax_inout,
+                       float *scale_inv_out) {
+    orc_fmt f;
+    if (orc_get_fmt(fo, &f) || M < 0 || N < 0 || ldo < N || !codes) return -1;
+    float *v = (float *)malloc((size_t)(M * N > 0 ? M * N : 1) * sizeof(float));
+    if (!v) return -1;
+    int rc = orc_gemm_nt(A, fa, lda, B, fb, ldb, M, N, K, sinv_a, sinv_b, bias, 1, v, N);
+    if (rc == 0) {
+        uint8_t *q = (uint8_t *)malloc((size_t)(M * N > 0 ? M * N : 1));
+        if (!q) rc = -1;
+        else {
+            rc = orc_cast_transpose_amax(v, 1, M, N, N, scale_out, fo, q, NULL, amax_inout,
+                                         scale_inv_out);
+            for (int64_t i = 0; rc == 0 && i < M; ++i)
+                memcpy(codes + i * ldo, q + i * N, (size_t)N);
+            free(q);
+        }
+        if (rc == 0 && v_out) memcpy(v_out, v, (size_t)(M * N) * sizeof(float));
+    }
+    free(v);
+    return rc;
+}
+
 /* The same definition evaluated only at the listed (rows[s], cols[s]) pairs;
  * out receives `count` values of the output type, in list order. */
 int orc_gemm_nt_sampled(const uint8_t *A, int fa, int64_t lda, const uint8_t *B,
