@@ -230,6 +230,41 @@ def dynamic_vs_delayed(dsl, st, iters: int = 20):
     return {k: round(v, 2) for k, v in res.items()}
 
 
+def fp8_output_forward(dsl, st, iters: int = 20):
+    """The forward product with an FP8 output and its amax (torch._scaled_mm
+    with an FP8 out_dtype) at the step's shape [8192, 2048] x [8192, 2048]^T,
+    against what it replaces: the bf16 output followed by a codes-only cast
+    of it (which takes the amax), back to back."""
+    M, N = st["y"].shape
+    g = st["state"]
+    qy = dsl.Float8Tensor.empty(M, N, 0, transpose=False, device="cuda")
+    scale = torch.tensor([448.0 / 6.0], device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    cases = {
+        "bf16_out_then_cast": lambda: (dsl.fp8_linear_fwd(st["qx"], st["qw"], st["b"], st["y"]),
+                                       dsl.fp8_cast_transpose_amax(st["y"], scale, qy, amax)),
+        "fp8_out_fused": lambda: dsl.fp8_linear_fwd_fp8out(st["qx"], st["qw"], st["b"], scale,
+                                                           qy, amax),
+    }
+    res = {}
+    for _ in range(2):
+        for name, fn in cases.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / iters * 1e3
+            res[name + "_us"] = min(res.get(name + "_us", us), us)
+    del g
+    return {k: round(v, 2) for k, v in res.items()}
+
+
 def producer_cast_cost(dsl, workloads, iters: int = 20):
     """The toy block's glue in front of a linear at its real shapes, as torch
     elementwise code followed by the cast, and fused into one pass
@@ -502,11 +537,17 @@ def traffic_record(root: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    srcs = {}
-    for name in ("gemm_fp8.hip", "cast_transpose_amax.hip"):
-        with open(os.path.join(root, "delayed_scaling_linear_amd", "csrc", name), "rb") as f:
-            srcs[name] = hashlib.sha256(f.read()).hexdigest()[:16]
-    return {k: v for k, v in rec["kernels"].items() if rec["source_sha256"].get(v["source"]) == srcs[v["source"]]}
+    def sha(name):
+        p = os.path.join(root, "delayed_scaling_linear_amd", "csrc", name)
+        if not os.path.exists(p):
+            return None
+        with open(p, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+
+    # A kernel's bytes count only while every source file it was built from
+    # is unchanged.
+    return {k: v for k, v in rec["kernels"].items()
+            if v.get("sources") and all(rec["source_sha256"].get(n) == sha(n) for n in v["sources"])}
 
 
 def main():
@@ -582,6 +623,7 @@ def main():
     dbias_cost = dbias_cast_cost(dsl, st)
     producer_cost = producer_cast_cost(dsl, workloads)
     dyn_cost = dynamic_vs_delayed(dsl, st)
+    fp8out_cost = fp8_output_forward(dsl, st)
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
     traffic = traffic_record(root)
     result = {
@@ -621,6 +663,7 @@ def main():
     result["dy_cast_dbias"] = dbias_cost
     result["producer_fused_cast"] = producer_cost
     result["delayed_vs_dynamic_cast"] = dyn_cost
+    result["fp8_output_forward"] = fp8out_cost
     if toy is not None:
         result["toy_stack_forward"] = toy
     if not args.no_cpu_baseline:

@@ -35,7 +35,7 @@ __all__ = [
     "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
     "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
     "fp8_produce_cast_transpose_amax", "PRODUCE_MODULATE", "PRODUCE_ADD",
-    "fp8_cast_transpose_dynamic",
+    "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
     "library_path", "lib",
 ]
 
@@ -94,11 +94,13 @@ def lib() -> ctypes.CDLL:
         L.fp8_cast_dbias_workspace_bytes.argtypes = [i64, i64]
         L.fp8_cast_dbias_workspace_bytes.restype = i64
         L.fp8_linear_fwd.argtypes = [dp, dp, vp, vp, vp]
+        L.fp8_linear_fwd_fp8out.argtypes = [dp, dp, vp, vp, dp, vp, vp]
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
         for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
                   L.fp8_produce_cast_transpose_amax, L.fp8_cast_transpose_dynamic,
-                  L.fp8_linear_fwd, L.fp8_linear_dgrad, L.fp8_linear_wgrad):
+                  L.fp8_linear_fwd, L.fp8_linear_fwd_fp8out, L.fp8_linear_dgrad,
+                  L.fp8_linear_wgrad):
             f.restype = ctypes.c_int
         L.fp8_status_string.argtypes = [ctypes.c_int]
         L.fp8_status_string.restype = ctypes.c_char_p
@@ -319,6 +321,20 @@ def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor
     _check(lib().fp8_linear_fwd(ctypes.byref(dx), ctypes.byref(dw),
                                 _ptr(bias, torch.bfloat16, "bias"), _ptr(y, torch.bfloat16, "y"),
                                 _stream(stream)), "fp8_linear_fwd")
+
+
+def fp8_linear_fwd_fp8out(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],
+                          scale_y: torch.Tensor, y: Float8Tensor, amax_y: Optional[torch.Tensor],
+                          stream=None) -> None:
+    """y.data [M, N] FP8 codes = the cast (scale_y) of v = x.data . w.data^T *
+    sinv + bias in fp32; amax_y folds in max|v|; y.scale_inv = 1 / scale_y.
+    y must have no transpose buffer."""
+    dx, dw, dy = x.desc(), w.desc(), y.desc()
+    _check(lib().fp8_linear_fwd_fp8out(ctypes.byref(dx), ctypes.byref(dw),
+                                       _ptr(bias, torch.bfloat16, "bias"),
+                                       _ptr(scale_y, torch.float32, "scale_y"), ctypes.byref(dy),
+                                       _ptr(amax_y, torch.float32, "amax_y"), _stream(stream)),
+           "fp8_linear_fwd_fp8out")
 
 
 def fp8_linear_dgrad(dy: Float8Tensor, w: Float8Tensor, dx: torch.Tensor, stream=None) -> None:

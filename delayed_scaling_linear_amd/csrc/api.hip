@@ -220,6 +220,29 @@ int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t 
                                     static_cast<hipStream_t>(stream)));
 }
 
+int fp8_linear_fwd_fp8out(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                          const float *scale_y, const fp8_tensor_t *y, float *amax_y,
+                          fp8_stream_t stream) {
+    if (!x || !w || !y || !scale_y) return FP8_ERR_NULL;
+    if (!valid_fmt(x->fmt) || !valid_fmt(w->fmt) || !valid_fmt(y->fmt)) return FP8_ERR_FORMAT;
+    if (y->reserved != 0 || y->data_t != nullptr) return FP8_ERR_ARG;
+    const int64_t M = x->rows, K = x->cols, N = w->rows;
+    if (w->cols != K || y->rows != M || y->cols != N) return FP8_ERR_SHAPE;
+    if (int e = check_gemm(x->data, w->data, M, N, K, x->scale_inv, w->scale_inv, y->data, 16))
+        return e;
+    if (int d = check_device()) return d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 0 || N == 0) {
+        // No output: the amax is untouched; the snapshot is still taken.
+        if (y->scale_inv == nullptr) return FP8_OK;
+        return status_of(launch_scale_inv_only(scale_y, y->scale_inv, nullptr, s));
+    }
+    if (bias && !aligned16(bias)) return FP8_ERR_ALIGN;
+    return status_of(launch_gemm_nt_fp8out(x->data, x->fmt, w->data, w->fmt, M, N, K,
+                                           x->scale_inv, w->scale_inv, bias, y->fmt, scale_y,
+                                           y->data, amax_y, y->scale_inv, s));
+}
+
 int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
                      fp8_stream_t stream) {
     if (!dy || !w) return FP8_ERR_NULL;

@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "fp8_codec.h"
 #include "fp8dsl_internal.h"
 
 namespace fp8dsl {
@@ -47,53 +48,6 @@ constexpr int THREADS = 256;
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int FMT>
-struct Fp8Traits;
-template <>
-struct Fp8Traits<FP8_E4M3> {
-    static constexpr float kMax = 448.0f;
-    template <bool HI>
-    __device__ static __forceinline__ int cvt(float a, float b, int old) {
-        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-    }
-};
-template <>
-struct Fp8Traits<FP8_E5M2> {
-    static constexpr float kMax = 57344.0f;
-    template <bool HI>
-    __device__ static __forceinline__ int cvt(float a, float b, int old) {
-        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
-    }
-};
-
-// Four scaled, clamped values -> one word of four codes (byte i = value i).
-template <int FMT>
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, float s) {
-    using T = Fp8Traits<FMT>;
-    a = __builtin_amdgcn_fmed3f(a * s, -T::kMax, T::kMax);
-    b = __builtin_amdgcn_fmed3f(b * s, -T::kMax, T::kMax);
-    c = __builtin_amdgcn_fmed3f(c * s, -T::kMax, T::kMax);
-    d = __builtin_amdgcn_fmed3f(d * s, -T::kMax, T::kMax);
-    int w = T::template cvt<false>(a, b, 0);
-    w = T::template cvt<true>(c, d, w);
-    return (uint32_t)w;
-}
-
-// Rare path: a NaN product gets 0x7F | (sign(x) ^ sign(s)).  Only lanes that
-// saw a NaN source (or every lane, when the scale is 0, inf or NaN) run it.
-__device__ __forceinline__ uint32_t patch_nan4(uint32_t w, const float x[4], float s) {
-    const uint32_t sbits = __float_as_uint(s);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float v = x[i] * s;
-        if (v != v) {
-            const uint32_t code = 0x7Fu | (((__float_as_uint(x[i]) ^ sbits) >> 24) & 0x80u);
-            w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
-        }
-    }
-    return w;
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }

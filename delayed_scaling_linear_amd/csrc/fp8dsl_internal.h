@@ -50,4 +50,13 @@ hipError_t launch_gemm_nt(const uint8_t *A, int fa, const uint8_t *B, int fb, in
                           int64_t N, int64_t K, const float *sinv_a, const float *sinv_b,
                           const uint16_t *bias, int out_dtype, void *C, hipStream_t stream);
 
+// The same product with an FP8 output (format fo): C [M, N] codes = the cast
+// of v = acc * (*sinv_a) * (*sinv_b) + bias[j] (fp32) with *scale_out;
+// *amax (non-negative or NaN; may be null) folds in max |v| of the unscaled
+// output; *scale_inv (may be null) = 1 / *scale_out.  N % 16 == 0.
+hipError_t launch_gemm_nt_fp8out(const uint8_t *A, int fa, const uint8_t *B, int fb, int64_t M,
+                                 int64_t N, int64_t K, const float *sinv_a, const float *sinv_b,
+                                 const uint16_t *bias, int fo, const float *scale_out,
+                                 uint8_t *C, float *amax, float *scale_inv, hipStream_t stream);
+
 }  // namespace fp8dsl

@@ -1,0 +1,1258 @@
+// Per-tensor-scaled FP8 GEMM, "NT" layout, on CDNA4 FP8 matrix cores.
+//
+//   C[i, j] = out( (sum_k dec(A[i, k]) * dec(B[j, k])) * sinv_a * sinv_b + bias[j] )
+//
+// out is bf16 or fp32 rounding, or (OUT_E4M3 / OUT_E5M2) the FP8 cast of the
+// fp32 value with the output's own scale, together with the amax of the
+// unscaled output: torch._scaled_mm called with an FP8 out_dtype returns that
+// amax beside the FP8 output.
+//
+// This is torch._scaled_mm of "Accelerating PyTorch Training Workloads with
+// FP8 -- Part 2" (row-major first operand, transposed second operand,
+// per-tensor scales held on the device, optional bf16 bias), used for the
+// forward, dgrad and wgrad products of te.Linear ("CPU Overhead of te.Linear
+// FP8 Layers").  Every FP8 x FP8 product is exact; the matrix core adds them
+// in groups of eight consecutive K positions aligned to the group's largest
+// product, dropping bits more than 13 binades below it (measured on gfx950:
+// a group loses less than 2^-10 of its largest product), and accumulates the
+// group sums in fp32.
+//
+// Design (gfx950, wave64):
+//   * v_mfma_f32_16x16x128_f8f6f4 with per-operand format select (E4M3 /
+//     E5M2), 8192 FLOP per instruction;
+//   * block tile BM x BN, K step 128 bytes, waves arranged WM x WN, each wave
+//     owning a (BM/WM) x (BN/WN) accumulator tile in AGPRs/VGPRs;
+//   * A and B K-slabs staged through LDS, double-buffered: the global loads
+//     of step k+1 are in flight while the matrix cores work on step k;
+//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+//     c ^ (r & 7), so both the row-wise stores and the fragment reads (8 lanes
+//     on 8 consecutive rows) touch 8 distinct chunks: no bank conflicts;
+//   * the B fragment is fed as the matrix core's first operand, so each lane
+//     ends up holding four consecutive output columns of one output row: the
+//     epilogue applies sinv_a * sinv_b and the bias in fp32 and writes 8-byte
+//     (bf16) or 16-byte (fp32) vectors;
+//   * M and N tails: out-of-range operand rows are clamped to the last valid
+//     row for loading and never stored; a K tail (K % 128 != 0) is zero-filled.
+//
+// The kernels and their launch templates live in this header; the library's
+// sources instantiate them per output kind (bf16 / fp32, FP8 codes) so that
+// the two sets compile in parallel.
+#pragma once
+
+#include <algorithm>
+
+#include "fp8_codec.h"
+#include "fp8dsl_internal.h"
+
+namespace fp8dsl {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 128;
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;   // NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Output kinds beyond FP8_DTYPE_BF16 / FP8_DTYPE_FP32: FP8 codes.
+constexpr int OUT_E4M3 = 2;
+constexpr int OUT_E5M2 = 3;
+template <int OUT>
+constexpr bool is_q_out() { return OUT == OUT_E4M3 || OUT == OUT_E5M2; }
+template <int OUT>
+constexpr int q_fmt() { return OUT == OUT_E5M2 ? FP8_E5M2 : FP8_E4M3; }
+
+// FP8 output of the product: codes = cast(v, *scale) with v = acc * s + bias
+// in fp32; *amax folds in max |v| of the UNSCALED output (one atomic per
+// workgroup); workgroup 0 writes *scale_inv = 1 / *scale.  amax and
+// scale_inv may be null.  Unused for bf16 / fp32 output.
+struct QOut {
+    const float *scale;
+    float *amax;
+    float *scale_inv;
+};
+
+// Codes of four consecutive outputs (byte i = y_i); their amax key
+// (sign-cleared fp32 pattern: a NaN dominates) is folded into `key`.
+template <int OUT>
+__device__ __forceinline__ uint32_t encode_out4(float y0, float y1, float y2, float y3, float so,
+                                                bool so_special, uint32_t &key) {
+    const uint32_t k = max(max(__float_as_uint(y0) & 0x7FFFFFFFu, __float_as_uint(y1) & 0x7FFFFFFFu),
+                           max(__float_as_uint(y2) & 0x7FFFFFFFu, __float_as_uint(y3) & 0x7FFFFFFFu));
+    key = max(key, k);
+    uint32_t w = encode4<q_fmt<OUT>()>(y0, y1, y2, y3, so);
+    if (so_special || k > 0x7F800000u) {
+        const float x[4] = {y0, y1, y2, y3};
+        w = patch_nan4(w, x, so);
+    }
+    return w;
+}
+
+// True when the output scale is 0, inf or NaN: every product may be NaN.
+__device__ __forceinline__ bool scale_is_special(float so) {
+    return !(fabsf(so) > 0.0f && fabsf(so) <= 3.402823466e38f);
+}
+
+// An output scale that can be folded into the epilogue's multiply-add
+// (v * so computed as acc * (s * so) + bias * so) without leaving fp32's
+// comfortable range; any other scale takes the cast's own order.
+__device__ __forceinline__ bool scale_is_foldable(float so) {
+    return fabsf(so) >= 0x1p-60f && fabsf(so) <= 0x1p60f;
+}
+
+// End of a 256-thread workgroup with an FP8 output: one atomic max of the
+// lanes' amax keys into *amax (which holds a non-negative value or NaN), and
+// the scale-inverse snapshot from workgroup 0.  With `scaled_key` the keys
+// are of |v * so| and the amax is recovered as max |v * so| / |so|.  `red`
+// is 16 bytes of LDS that no wave reads any more; every thread calls this.
+__device__ __forceinline__ void finish_q_out(uint32_t key, const QOut &qo, float so,
+                                             uint32_t *red, bool scaled_key = false) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) key = max(key, (uint32_t)__shfl_xor((int)key, off, 64));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t k = max(max(red[0], red[1]), max(red[2], red[3]));
+        if (scaled_key && k <= 0x7F800000u) k = __float_as_uint(__uint_as_float(k) / fabsf(so));
+        if (qo.amax != nullptr) {
+            unsigned int *a = reinterpret_cast<unsigned int *>(qo.amax);
+            if (k > __atomic_load_n(a, __ATOMIC_RELAXED)) atomicMax(a, k);
+        }
+        if (blockIdx.x == 0 && qo.scale_inv != nullptr) *qo.scale_inv = 1.0f / so;
+    }
+}
+
+// Tile index of workgroup b.  Workgroups are dealt round-robin to the eight
+// XCDs (b % 8); when the tile count allows, each XCD gets a contiguous range
+// of tiles, walked in groups of GROUP_M tile rows, so that the workgroups
+// sharing an XCD's L2 also share A and B slabs.
+__device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
+    constexpr int XCDS = 8;
+    constexpr int GROUP_M = 4;
+    const int T = tiles_m * tiles_n;
+    int t = b;
+    if (T % XCDS == 0) t = (b % XCDS) * (T / XCDS) + b / XCDS;
+    const int per_group = GROUP_M * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * GROUP_M;
+    const int rows_here = min(GROUP_M, tiles_m - first_m);
+    const int r = t - g * per_group;
+    tm = first_m + r % rows_here;
+    tn = r / rows_here;
+}
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
+    const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n, QOut qo) {
+    static_assert(!is_q_out<OUT>() || WM * WN == 4, "the FP8 output reduces over four waves");
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM;            // wave tile rows
+    constexpr int WTN = BN / WN;            // wave tile cols
+    constexpr int FM = WTM / 16;
+    constexpr int FN = WTN / 16;
+    constexpr int A_CHUNKS = BM * BK / 16;  // 16-byte chunks per stage
+    constexpr int B_CHUNKS = BN * BK / 16;
+    constexpr int LA = A_CHUNKS / NT;
+    constexpr int LB = B_CHUNKS / NT;
+    static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "loader shape");
+    constexpr int STAGE = (BM + BN) * BK;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+
+    int tile_m, tile_n;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+
+    // Loader bookkeeping: chunk id = tid + i*NT -> (row = id / 8, kc = id % 8).
+    // Rows past M (N) are clamped to the last row: loaded, never stored.
+    const uint8_t *a_src[LA];
+    const uint8_t *b_src[LB];
+    int a_lds[LA], b_lds[LB];
+    const int kc16 = (tid & 7) * 16;        // same K chunk for every i (NT % 8 == 0)
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int id = tid + i * NT;
+        const int row = id >> 3, kc = id & 7;
+        const int grow = min(m0 + row, M - 1);
+        a_src[i] = A + (int64_t)grow * K + kc * 16;
+        a_lds[i] = row * BK + ((kc ^ (row & 7)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int id = tid + i * NT;
+        const int row = id >> 3, kc = id & 7;
+        const int grow = min(n0 + row, N - 1);
+        b_src[i] = B + (int64_t)grow * K + kc * 16;
+        b_lds[i] = BM * BK + row * BK + ((kc ^ (row & 7)) << 4);
+    }
+
+    u32x4 ra[LA], rb[LB];
+    // Full K step: unconditional 16-byte loads.
+    auto load_full = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + k0);
+    };
+    // Last, partial K step: chunks at or past K read as zero (the address is
+    // pulled back in range and the value discarded).
+    auto load_tail = [&](int k0) {
+        const bool in = k0 + kc16 < K;
+        const int k = in ? k0 : 0;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(a_src[i] + k);
+            ra[i] = in ? v : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(b_src[i] + k);
+            rb[i] = in ? v : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_lds = [&](int stage) {
+        uint8_t *base = lds + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4 *>(base + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4 *>(base + b_lds[i]) = rb[i];
+    };
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment addressing: lane holds row (lane % 16) of a 16-row fragment and
+    // the 32 K-bytes of chunks 2*(lane/16) and 2*(lane/16)+1.
+    const int frow = lane & 15;
+    const int fc0 = (lane >> 4) * 2;
+    const int sw = frow & 7;   // fragment bases are multiples of 16 rows
+    const int off0 = ((fc0 ^ sw) << 4);
+    const int off1 = (((fc0 + 1) ^ sw) << 4);
+
+    const int nk = (K + BK - 1) / BK;
+    const int nfull = K / BK;               // steps with no K tail
+    if (nk > 0) {
+        if (nfull > 0) load_full(0); else load_tail(0);
+        store_lds(0);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < nfull) load_full((kt + 1) * BK);
+        else if (kt + 1 < nk) load_tail((kt + 1) * BK);
+
+        const uint8_t *As = lds + stage * STAGE + (wm * WTM + frow) * BK;
+        const uint8_t *Bs = lds + stage * STAGE + BM * BK + (wn * WTN + frow) * BK;
+        v8i bf[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(Bs + j * 16 * BK + off0);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(Bs + j * 16 * BK + off1);
+            bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(As + i * 16 * BK + off0);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(As + i * 16 * BK + off1);
+            const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                // B fragment first: lane (l%16, l/16) receives output row
+                // (l%16) of the A fragment, columns 4*(l/16) .. +3.
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf[j], af, acc[i][j], FB, FA, 0, 0, 0, 0);
+        }
+
+        if (kt + 1 < nk) store_lds(stage ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.
+    const float s = (*sinv_a) * (*sinv_b);
+    float so = 0.f;
+    bool so_special = false;
+    if constexpr (is_q_out<OUT>()) {
+        so = *qo.scale;
+        so_special = scale_is_special(so);
+    }
+    uint32_t key = 0;
+    const int orow = lane & 15;
+    const int ocol = (lane >> 4) * 4;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int gc = n0 + wn * WTN + j * 16 + ocol;
+        if (gc >= N) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_BIAS) {
+            const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
+            bv[0] = __uint_as_float(b2.x << 16);
+            bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+            bv[2] = __uint_as_float(b2.y << 16);
+            bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int gr = m0 + wm * WTM + i * 16 + orow;
+            if (gr >= M) continue;
+            const v4f a = acc[i][j];
+            const float y0 = a.x * s + bv[0];
+            const float y1 = a.y * s + bv[1];
+            const float y2 = a.z * s + bv[2];
+            const float y3 = a.w * s + bv[3];
+            if constexpr (OUT == FP8_DTYPE_BF16) {
+                uint16_t *C = static_cast<uint16_t *>(Cv);
+                const u32x2 o = u32x2{f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16),
+                                      f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16)};
+                *reinterpret_cast<u32x2 *>(C + (int64_t)gr * N + gc) = o;
+            } else if constexpr (is_q_out<OUT>()) {
+                uint8_t *C = static_cast<uint8_t *>(Cv);
+                *reinterpret_cast<uint32_t *>(C + (int64_t)gr * N + gc) =
+                    encode_out4<OUT>(y0, y1, y2, y3, so, so_special, key);
+            } else {
+                float *C = static_cast<float *>(Cv);
+                *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
+            }
+        }
+    }
+    if constexpr (is_q_out<OUT>()) finish_q_out(key, qo, so, reinterpret_cast<uint32_t *>(lds));
+}
+
+// Epilogue of one wave's 128 x 128 accumulator tile, 4 x 4 fragments of
+// v_mfma_f32_32x32x64 with the B fragment passed first: lane l holds output
+// row r0 + 32 i + l % 32 of fragment row block i and, for register group g
+// (registers 4g .. 4g+3) of fragment column block j, the four consecutive
+// columns c0 + 32 j + 8 g + 4 (l / 32) .. +3.  Writes out(acc * s + bias) for
+// the in-range elements as one 8-byte (bf16), 16-byte (fp32) or 4-byte (FP8
+// codes, scale so, amax key folded into `key`) vector per row and group
+// (N % 8 == 0 keeps every vector inside the row), then clears the
+// accumulators for the next tile.
+template <int OUT, bool HAS_BIAS>
+__device__ __forceinline__ void store_wave_tile(v16f (&acc)[4][4], void *__restrict__ Cv,
+                                                const uint16_t *__restrict__ bias, int M, int N,
+                                                int r0, int c0, int lane, float s, float so,
+                                                bool so_special, uint32_t &key) {
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+    // All bias loads first (one latency, not sixteen); columns past N read
+    // as zero through the descriptor's range check.
+    u32x2 bq[4][4];
+    if constexpr (HAS_BIAS) {
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(bias), (short)0, 2 * N, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bq[j][g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                    brs, 2 * (c0 + j * 32 + 8 * g + 4 * half), 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int gc = c0 + j * 32 + 8 * g + 4 * half;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_BIAS) {
+                const u32x2 b2 = bq[j][g];
+                bv[0] = __uint_as_float(b2.x << 16);
+                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(b2.y << 16);
+                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int gr = r0 + i * 32 + frow;
+                const float y0 = acc[i][j][4 * g + 0] * s + bv[0];
+                const float y1 = acc[i][j][4 * g + 1] * s + bv[1];
+                const float y2 = acc[i][j][4 * g + 2] * s + bv[2];
+                const float y3 = acc[i][j][4 * g + 3] * s + bv[3];
+                if (gr < M && gc < N) {
+                    if constexpr (OUT == FP8_DTYPE_BF16) {
+                        uint16_t *C = static_cast<uint16_t *>(Cv);
+                        const bf16x4 o = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                        *reinterpret_cast<bf16x4 *>(C + (int64_t)gr * N + gc) = o;
+                    } else if constexpr (is_q_out<OUT>()) {
+                        uint8_t *C = static_cast<uint8_t *>(Cv);
+                        *reinterpret_cast<uint32_t *>(C + (int64_t)gr * N + gc) =
+                            encode_out4<OUT>(y0, y1, y2, y3, so, so_special, key);
+                    } else {
+                        float *C = static_cast<float *>(Cv);
+                        *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+}
+
+// Large-problem kernel: persistent, one 256-thread workgroup per CU.
+//
+//   * Each workgroup walks the 256 x 256 output tiles blockIdx.x,
+//     blockIdx.x + gridDim.x, ... as one continuous stream of 64-byte K
+//     stages, so the loads of the next tile's first stages are already in
+//     flight while the current tile's epilogue runs.
+//   * Four waves (one per SIMD) of 128 x 128, each a 4 x 4 grid of
+//     v_mfma_f32_32x32x64_f8f6f4 tiles (this instruction runs measurably
+//     faster per FLOP on gfx950 than 16x16x128); 256 fp32 accumulators per
+//     lane in AGPRs.
+//   * Stages live in three LDS buffers.  With one wave per SIMD nothing else
+//     can issue matrix-core work while a wave sits in a memory instruction,
+//     so every memory instruction of a stage is threaded between its 16
+//     matrix-core instructions:
+//        slots 0-7  : MFMA, then one LDS write committing stage k+2 and one
+//                     buffer load fetching stage k+3 into registers;
+//        barrier    : stage k+2 is in LDS for everyone;
+//        slots 8-15 : MFMA, then two LDS reads of stage k+1's fragments
+//                     (double-buffered fragment registers).
+//     Three buffers make one barrier per stage enough: stage k+2 overwrites
+//     the buffer of stage k-1, whose fragments were read before the previous
+//     barrier.  The loop has no data-dependent branches, so the compiler's
+//     wait counters stay exact (a conditional memory instruction makes it
+//     fall back to waiting for everything).
+//   * Operands come in with buffer loads (an SGPR descriptor per operand, a
+//     32-bit offset per lane); rows past M or N, K past the end and stages
+//     past the last tile fall outside the descriptor and read as zero.
+//   * LDS rows are 64 bytes; 16-byte chunk c of row r sits at chunk
+//     c ^ ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)): fragment reads (lanes on
+//     consecutive rows) and staging writes (4 lanes per row) are free of bank
+//     conflicts with 32 or with 64 banks.
+//
+// Fragment layout of v_mfma_f32_32x32x64_f8f6f4: lane l holds row l % 32 and
+// 32 K-bytes of half (l / 32) of the 64-byte K slice; A and B use the same
+// K assignment, so any consistent choice of bytes gives the same sum.  With
+// the B fragment passed first, lane l ends up with output row l % 32 and, for
+// register r, output column 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ int big_swz(int r) { return ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)); }
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void gemm_nt_big_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
+    const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n, QOut qo) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int KS = 64;                  // K bytes per stage
+    constexpr int WT = 128;                 // wave tile (square)
+    constexpr int F = WT / 32;              // 4 x 4 fragments of 32 x 32
+    constexpr int LPT = BM * KS / 16 / 256; // 4 chunk loads per thread per operand
+    constexpr int STAGE = (BM + BN) * KS;   // 32 KiB
+    constexpr int OOB = 0x7FFFFFF0;         // an offset outside every descriptor
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int T = tiles_m * tiles_n;
+    if ((int)blockIdx.x >= T) return;
+    const int my_tiles = (T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(A), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, N * K, 0x00020000);
+
+    // Loader: thread -> (row = tid/4 + 64 i, chunk kc = tid % 4) of a stage;
+    // the 8 chunk loads of a stage alternate A, B, A, B, ...
+    const int kc = tid & 3;
+    const int lrow = tid >> 2;
+    const int rowstep = 64 * K;
+    const int st_off = lrow * KS + ((kc ^ big_swz(lrow)) << 4);   // + 4096 i (swizzle repeats)
+    // Per-lane operand offsets of tile number r of this workgroup (OOB when
+    // r is past its last tile).
+    auto tile_offsets = [&](int r, int &oa, int &ob) {
+        if (r < my_tiles) {
+            int tm, tn;
+            tile_of_block((int)blockIdx.x + r * (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+            oa = (tm * BM + lrow) * K + kc * 16;
+            ob = (tn * BN + lrow) * K + kc * 16;
+        } else {
+            oa = OOB;
+            ob = OOB;
+        }
+    };
+
+    u32x4 reg[2][2 * LPT];                  // two staging sets of one stage
+    // Load chunk q of a stage whose per-lane base offsets are (oa, ob), K
+    // byte offset k0, into staging set `set`.
+    auto load_one = [&](int set, int q, int oa, int ob, int k0) {
+        const bool in = k0 + kc * 16 < K;
+        const int i = q >> 1;
+        if (q & 1) {
+            const int o = (in && ob != OOB) ? ob + i * rowstep + k0 : OOB;
+            reg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, o, 0, 0));
+        } else {
+            const int o = (in && oa != OOB) ? oa + i * rowstep + k0 : OOB;
+            reg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, o, 0, 0));
+        }
+    };
+    auto store_one = [&](int set, int q, int buf_off) {
+        const int i = q >> 1;
+        uint8_t *dst = lds + buf_off + st_off + 4096 * i + ((q & 1) ? BM * KS : 0);
+        *reinterpret_cast<u32x4 *>(dst) = reg[set][q];
+    };
+
+    // Fragment reads: row (lane % 32) of each 32-row fragment, chunks
+    // 2*(lane/32) and +1.
+    const int frow = lane & 31;
+    const int fsw = big_swz(frow);
+    const int c0 = 2 * (lane >> 5);
+    const int fo0 = frow * KS + ((c0 ^ fsw) << 4);
+    const int fo1 = frow * KS + (((c0 + 1) ^ fsw) << 4);
+    const int a_fbase = wm * WT * KS;
+    const int b_fbase = BM * KS + wn * WT * KS;
+
+    v8i af[2][F], bf[2][F];
+    auto read_half = [&](v8i &dst, int off, int h) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + off + (h ? fo1 : fo0));
+        if (h == 0) { dst[0] = (int)v.x; dst[1] = (int)v.y; dst[2] = (int)v.z; dst[3] = (int)v.w; }
+        else        { dst[4] = (int)v.x; dst[5] = (int)v.y; dst[6] = (int)v.z; dst[7] = (int)v.w; }
+    };
+
+    v16f acc[F][F];
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Stages per tile, padded to even (a padded stage lies past K and adds
+    // nothing); the caller guarantees nk >= 4, so stage k+3 is in this tile
+    // or the next one.
+    const int nk = ((K + KS - 1) / KS + 1) & ~1;
+
+    int cur_a, cur_b, nxt_a, nxt_b;         // tile offsets: this tile, next tile
+    tile_offsets(0, cur_a, cur_b);
+    tile_offsets(1, nxt_a, nxt_b);
+
+    // Prologue: stages 0 and 1 committed, stage 2 in flight (set 0), the
+    // fragments of stage 0 in registers.
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2 * LPT; ++q) load_one(p, q, cur_a, cur_b, p * KS);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2 * LPT; ++q) store_one(p, q, p * STAGE);
+#pragma unroll
+    for (int q = 0; q < 2 * LPT; ++q) load_one(0, q, cur_a, cur_b, 2 * KS);
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            read_half(af[0][f], a_fbase + f * 32 * KS, h);
+            read_half(bf[0][f], b_fbase + f * 32 * KS, h);
+        }
+
+    const float s = (*sinv_a) * (*sinv_b);
+    float so = 0.f;
+    bool so_special = false;
+    if constexpr (is_q_out<OUT>()) {
+        so = *qo.scale;
+        so_special = scale_is_special(so);
+    }
+    uint32_t key = 0;
+    int buf_next = STAGE;            // buffer of stage k+1
+    int buf_commit = 2 * STAGE;      // buffer of stage k+2
+
+    for (int r = 0; r < my_tiles; ++r) {
+        for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int k = kt + u;
+                const int cur = u, nxt = u ^ 1;
+                // Stage k+3: this tile, or the next tile's stage k+3-nk.
+                const bool same = k + 3 < nk;
+                const int ia = same ? cur_a : nxt_a;
+                const int ib = same ? cur_b : nxt_b;
+                const int ik = (same ? k + 3 : k + 3 - nk) * KS;
+#pragma unroll
+                for (int slot = 0; slot < 16; ++slot) {
+                    const int i = slot >> 2, j = slot & 3;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf[cur][j], af[cur][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+                    if (slot < 8) {
+                        store_one(cur, slot, buf_commit);        // stage k+2: set k%2
+                        load_one(nxt, slot, ia, ib, ik);         // stage k+3 -> set (k+1)%2
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+                        if (slot == 7) __syncthreads();
+                    } else {
+                        // Stage k+1's fragments, in the order the next stage's
+                        // first MFMAs need them: A0, B0..B3, A1..A3.
+                        const int f = slot - 8;
+                        if (f >= 1 && f <= 4) {
+                            read_half(bf[nxt][f - 1], buf_next + b_fbase + (f - 1) * 32 * KS, 0);
+                            read_half(bf[nxt][f - 1], buf_next + b_fbase + (f - 1) * 32 * KS, 1);
+                        } else {
+                            const int a = (f == 0) ? 0 : f - 4;
+                            read_half(af[nxt][a], buf_next + a_fbase + a * 32 * KS, 0);
+                            read_half(af[nxt][a], buf_next + a_fbase + a * 32 * KS, 1);
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+                    }
+                }
+                // Rotate the three buffers: next <- commit, commit <- current.
+                const int buf_cur = (buf_next == 0) ? 2 * STAGE : buf_next - STAGE;
+                buf_next = buf_commit;
+                buf_commit = buf_cur;
+            }
+        }
+
+        int tm, tn;
+        tile_of_block((int)blockIdx.x + r * (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+        store_wave_tile<OUT, HAS_BIAS>(acc, Cv, bias, M, N, tm * BM + wm * WT, tn * BN + wn * WT,
+                                       lane, s, so, so_special, key);
+        // The next tile becomes current; look one further ahead.
+        cur_a = nxt_a;
+        cur_b = nxt_b;
+        tile_offsets(r + 2, nxt_a, nxt_b);
+    }
+    if constexpr (is_q_out<OUT>()) finish_q_out(key, qo, so, reinterpret_cast<uint32_t *>(lds));
+}
+
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's
+// 16 bytes at byte offset `voff` of the buffer land at LDS address
+// m0 + 16 l, so one instruction fills 1 KiB of LDS in lane order.  Offsets
+// at or past the descriptor's record count read as zero and move no data.
+// Issued from inline assembly so that the compiler neither waits for it
+// before unrelated LDS reads nor tracks it at all: the kernel that uses it
+// places every vmcnt wait itself (nothing else in that kernel touches M0;
+// gfx9 LDS instructions do not read it).  An SALU write of M0 needs one wait
+// state before an LDS-DMA load reads it, hence the s_nop.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 128-byte-row LDS swizzle: chunk c (16 bytes) of row r sits at chunk
+// c ^ dma_swz(r).  Fragment reads touch 16 consecutive rows at one logical
+// chunk per 256-byte LDS cycle (or 8 rows per 128 bytes): the rows' (r & 1,
+// chunk) pairs are all distinct, so neither layout has bank conflicts.
+__device__ __forceinline__ int dma_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// bf16 epilogue of one wave's 128 x 128 tile through LDS (32 KiB at `stg`),
+// in three steps so that the caller can put other work between them.
+// stage_wave_tile_bf16: out(acc * s + bias) is written in the matrix-core
+// layout (8 bytes per lane, one output row per lane) into 256-byte staging
+// rows whose 16-byte chunk c of row q sits at chunk c ^ (q & 15); the bias of
+// the wave's 128 columns is read from LDS (`bias_lds`, bf16, column c0
+// first; zero past N).  Clears the accumulators.
+template <bool HAS_BIAS>
+__device__ __forceinline__ void stage_wave_tile_bf16(v16f (&acc)[4][4], uint8_t *stg,
+                                                     const uint8_t *bias_lds, int lane, float s) {
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_BIAS) {
+                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
+                    bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
+                bv[0] = __uint_as_float(b2.x << 16);
+                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(b2.y << 16);
+                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+            }
+            const int c = 4 * j + g;                     // 16-byte chunk of the staging row
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = i * 32 + frow;
+                const bf16x4 o = {(__bf16)(acc[i][j][4 * g + 0] * s + bv[0]),
+                                  (__bf16)(acc[i][j][4 * g + 1] * s + bv[1]),
+                                  (__bf16)(acc[i][j][4 * g + 2] * s + bv[2]),
+                                  (__bf16)(acc[i][j][4 * g + 3] * s + bv[3])};
+                *reinterpret_cast<bf16x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4) + 8 * half) = o;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+}
+
+// Read the staged tile back, 16 lanes per 256-byte row: v[it] is row
+// 4 it + lane / 16, columns 8 (lane % 16) .. +7.
+__device__ __forceinline__ void read_staged_rows(const uint8_t *stg, int lane, u32x4 (&v)[32]) {
+    const int c = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+        const int q = 4 * it + (lane >> 4);
+        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
+    }
+}
+
+// Store the rows of read_staged_rows: every instruction writes four whole
+// 256-byte row segments (in-range rows and 8-column groups only).
+__device__ __forceinline__ void store_staged_rows(uint16_t *__restrict__ C, const u32x4 (&v)[32],
+                                                  int M, int N, int r0, int c0, int lane) {
+    const int gc = c0 + 8 * (lane & 15);
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+        const int gr = r0 + 4 * it + (lane >> 4);
+        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+    }
+}
+
+// fp32 epilogue of one wave's tile through LDS, one 32-row fragment block i
+// at a time: 32 staging rows of 512 bytes (16 KiB at `stg`), 16-byte chunk c
+// of row q at chunk c ^ (q & 15).  Lane l holds row (l % 32) of the block
+// and, per register group g of fragment column block j, the four columns
+// 32 j + 8 g + 4 (l / 32) .. +3, i.e. chunk 8 j + 2 g + l / 32.  Bias as in
+// stage_wave_tile_bf16.
+template <bool HAS_BIAS>
+__device__ __forceinline__ void stage_wave_block_f32(const v16f (&acc)[4][4], uint8_t *stg,
+                                                     const uint8_t *bias_lds, int lane, float s,
+                                                     int i) {
+    const int q = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_BIAS) {
+                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
+                    bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
+                bv[0] = __uint_as_float(b2.x << 16);
+                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+                bv[2] = __uint_as_float(b2.y << 16);
+                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+            }
+            const int c = 8 * j + 2 * g + half;
+            const v4f o = {acc[i][j][4 * g + 0] * s + bv[0], acc[i][j][4 * g + 1] * s + bv[1],
+                           acc[i][j][4 * g + 2] * s + bv[2], acc[i][j][4 * g + 3] * s + bv[3]};
+            *reinterpret_cast<v4f *>(stg + q * 512 + ((c ^ (q & 15)) << 4)) = o;
+        }
+    }
+}
+
+// Read a staged fp32 block back, 32 lanes per 512-byte row: v[it] is row
+// 2 it + lane / 32 of the block, columns 4 (lane % 32) .. +3.
+__device__ __forceinline__ void read_staged_block_f32(const uint8_t *stg, int lane,
+                                                      u32x4 (&v)[16]) {
+    const int c = lane & 31;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int q = 2 * it + (lane >> 5);
+        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 512 + ((c ^ (q & 15)) << 4));
+    }
+}
+
+// Store a block read by read_staged_block_f32 (rows r0 .. r0 + 31): every
+// instruction writes two whole 512-byte row segments.
+__device__ __forceinline__ void store_staged_block_f32(float *__restrict__ C, const u32x4 (&v)[16],
+                                                       int M, int N, int r0, int c0, int lane) {
+    const int gc = c0 + 4 * (lane & 31);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int gr = r0 + 2 * it + (lane >> 5);
+        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+    }
+}
+
+// FP8-code epilogue of one wave's tile through LDS (16 KiB at `stg`): 128
+// staging rows of 128 bytes, 16-byte chunk c of row q at chunk c ^ (q & 7).
+// Lane l holds row (l % 32) of fragment row block i and, per register group
+// g of fragment column block j, the four columns 32 j + 8 g + 4 (l / 32) ..
+// +3: one code word at byte 16 (2 j + g / 2) + 8 (g % 2) + 4 (l / 32) of its
+// row.  Bias as in stage_wave_tile_bf16.  Clears the accumulators.
+//   fold: t = acc * (s * so) + bias * so, the scaled value itself, is clamped
+//     and converted, and the amax keys are of |t| (the caller divides by
+//     |so| once at the end).  Otherwise t = v = acc * s + bias and the encode
+//     multiplies by so, exactly as the cast does (the only order in which a
+//     0, inf or NaN scale gives the cast's results).  `fold` is wave-uniform;
+//     one copy of the code serves both (two inlined copies push the kernel
+//     past its register budget).
+// Returns this lane's amax key of the tile's in-range outputs.  Keys are
+// two maxima of t's raw bit patterns per fragment row block: signed (the
+// largest positive t, NaN above inf) and unsigned (the most negative t); a
+// block's key is max(kpos, kneg & 0x7FFFFFFF).  Columns past N hold t = 0
+// (operand rows and bias read as zero there), so only rows past M (t =
+// bias) are masked, once per block.  A NaN t gets 0x7F | sign on the rare
+// path of the group of four that holds it (or, unfolded, always: the scale
+// itself may make NaN products).
+template <int OUT, bool HAS_BIAS>
+__device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t *stg,
+                                                      const uint8_t *bias_lds, int lane, float s,
+                                                      float so, bool fold, int M, int r0) {
+    constexpr int FMT = q_fmt<OUT>();
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+    const float sm = fold ? s * so : s;       // multiplier of the accumulator
+    const float se = fold ? 1.0f : so;        // the encode's own scale
+    const float sb = fold ? so : 1.0f;        // multiplier of the bias
+    auto bias4 = [&](int j, int g, float (&bv)[4]) {
+        bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
+        if constexpr (HAS_BIAS) {
+            const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
+                bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
+            bv[0] = __uint_as_float(b2.x << 16) * sb;
+            bv[1] = __uint_as_float(b2.x & 0xFFFF0000u) * sb;
+            bv[2] = __uint_as_float(b2.y << 16) * sb;
+            bv[3] = __uint_as_float(b2.y & 0xFFFF0000u) * sb;
+        }
+    };
+    auto word_addr = [&](int i, int j, int g) {
+        const int q = i * 32 + frow;
+        return stg + q * 128 + (((2 * j + (g >> 1)) ^ (q & 7)) << 4) + 8 * (g & 1) + 4 * half;
+    };
+    int32_t kpos[4] = {0, 0, 0, 0};
+    uint32_t kneg[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float bv[4];
+            bias4(j, g, bv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float t[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) t[q] = acc[i][j][4 * g + q] * sm + bv[q];
+                uint32_t w = encode4<FMT>(t[0], t[1], t[2], t[3], se);
+                const int32_t p = max(max((int32_t)__float_as_uint(t[0]), (int32_t)__float_as_uint(t[1])),
+                                      max((int32_t)__float_as_uint(t[2]), (int32_t)__float_as_uint(t[3])));
+                const uint32_t n = max(max(__float_as_uint(t[0]), __float_as_uint(t[1])),
+                                       max(__float_as_uint(t[2]), __float_as_uint(t[3])));
+                if (!fold || p > 0x7F800000 || n > 0xFF800000u) w = patch_nan4(w, t, se);
+                *reinterpret_cast<uint32_t *>(word_addr(i, j, g)) = w;
+                kpos[i] = max(kpos[i], p);
+                kneg[i] = max(kneg[i], n);
+            }
+        }
+    }
+    uint32_t key = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (r0 + i * 32 + frow < M) key = max(key, max((uint32_t)kpos[i], kneg[i] & 0x7FFFFFFFu));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    return key;
+}
+
+// Largest key of the wave, as a wave-uniform value (held in a scalar
+// register, so that it takes no vector register across the main loop).
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t k) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) k = max(k, (uint32_t)__shfl_xor((int)k, off, 64));
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)k);
+}
+
+// Read the staged codes back, 8 lanes per 128-byte row: v[it] is row
+// 8 it + lane / 8, columns 16 (lane % 8) .. +15.
+__device__ __forceinline__ void read_staged_rows_q(const uint8_t *stg, int lane, u32x4 (&v)[16]) {
+    const int c = lane & 7;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int q = 8 * it + (lane >> 3);
+        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 128 + ((c ^ (q & 7)) << 4));
+    }
+}
+
+// Store the rows of read_staged_rows_q: every instruction writes eight whole
+// 128-byte row segments (in-range rows and 16-column groups only; N % 16 == 0
+// keeps every group inside the row).
+__device__ __forceinline__ void store_staged_rows_q(uint8_t *__restrict__ C, const u32x4 (&v)[16],
+                                                    int M, int N, int r0, int c0, int lane) {
+    const int gc = c0 + 16 * (lane & 7);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int gr = r0 + 8 * it + (lane >> 3);
+        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+    }
+}
+
+// Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
+// 256-thread workgroup per CU, four waves of 128 x 128 with
+// v_mfma_f32_32x32x64_f8f6f4) whose operand stages are written into LDS by
+// the load unit itself (buffer loads with the LDS flag), not through
+// registers.
+//   * Stages are 128 K-bytes (64 KiB for A and B), so every operand row
+//     segment is one whole 128-byte line, double-buffered in 128 KiB of LDS;
+//     no staging registers and no LDS write instructions in the main loop.
+//   * Wave w fetches rows 128 w .. 128 w + 127 of the 512-row stage (A rows
+//     for waves 0-1, B rows for 2-3): 16 instructions of 8 rows, lane l
+//     taking row l / 8 of the eight and the logical chunk that lands at
+//     chunk position l % 8 under the swizzle.
+//   * One barrier per stage, in its middle.  Stage k runs 16 MFMAs on the
+//     fragments of its first 64 K-bytes (read earlier) while reading those
+//     of its second 64; then every wave waits for its own loads of stage k+1
+//     and meets the others at the barrier, after which stage k's buffer is
+//     free (all its fragments are in registers) and stage k+1's is complete.
+//     The second 16 MFMAs then carry the loads of stage k+2 into the freed
+//     buffer (one per MFMA, which paces them at the load unit's rate) and
+//     the reads of stage k+1's first fragments.
+//   * Tile boundaries drain the pipeline.  The bf16 epilogue stages each
+//     wave's output in the then idle stage buffers and reads it back as
+//     whole 256-byte row segments into the (now free) fragment registers;
+//     the next tile's first two stages and its bias (1 KiB of LDS past the
+//     stages) are requested before the output stores are issued, so those
+//     loads land while the store burst drains.  fp32 output goes through
+//     the same staging in four 32-row blocks (512-byte row segments), FP8
+//     codes through 128-byte staging rows.
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
+    const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n, QOut qo) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int KS = 128;                     // K bytes per stage
+    constexpr int WT = 128;                     // wave tile (square)
+    constexpr int F = WT / 32;                  // 4 x 4 fragments of 32 x 32
+    constexpr uint32_t STAGE = (BM + BN) * KS;  // 64 KiB
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int T = tiles_m * tiles_n;
+    if ((int)blockIdx.x >= T) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(A), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, N * K, 0x00020000);
+    const bool loads_b = wave >= 2;
+    const __amdgpu_buffer_rsrc_t ld_rsrc = loads_b ? rb_rsrc : ra_rsrc;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    const uint32_t ld_lds = lds0 + (uint32_t)wave * (128 * KS);   // this wave's 128 rows
+    // The tile's 256 bias values (512 bytes) live past the two stages.
+    uint8_t *const bias_lds = lds + 2 * STAGE;
+
+    // Per-lane part of the load offsets: row l / 8 of an 8-row group, the
+    // logical chunk stored at position l % 8 (the swizzle of rows 8i..8i+7
+    // is (l / 8) ^ (i & 1)).
+    const int lr = lane >> 3;
+    const uint32_t voff_e = (uint32_t)(lr * K + 16 * ((lane & 7) ^ lr));
+    const uint32_t voff_o = (uint32_t)(lr * K + 16 * ((lane & 7) ^ lr ^ 1));
+    // Load instruction i (0..15) of a stage: rows 8i..8i+7 of this wave's
+    // 128, starting at operand byte offset `base` (+ k0 along K).
+    auto load_one = [&](int i, uint32_t base, uint32_t k0, uint32_t buf) {
+        const uint32_t so = base + (uint32_t)(8 * i) * (uint32_t)K + k0;
+        dma_b128(ld_rsrc, so + ((i & 1) ? voff_o : voff_e), ld_lds + buf + (uint32_t)i * 1024u);
+    };
+
+    // Fragment reads: row (lane % 32) of a 32-row fragment, 16-byte chunks
+    // 4 s + 2 (lane / 32) and + 1 for K half s of the stage.
+    const int frow = lane & 31;
+    const int fsw = dma_swz(frow);
+    const int c0 = 2 * (lane >> 5);
+    uint32_t fo[2][2];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fo[sh][h] = frow * KS + (((4 * sh + c0 + h) ^ fsw) << 4);
+    const uint32_t a_fbase = (uint32_t)(wm * WT * KS);
+    const uint32_t b_fbase = (uint32_t)(BM * KS + wn * WT * KS);
+
+    v8i af[2][F], bf[2][F];                     // [K half][fragment]
+    auto read_half = [&](v8i &dst, uint32_t off, int h) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + off);
+        dst[4 * h + 0] = (int)v.x; dst[4 * h + 1] = (int)v.y;
+        dst[4 * h + 2] = (int)v.z; dst[4 * h + 3] = (int)v.w;
+    };
+    // Fragment n (0..7) of a K half in read order A0, B0..B3, A1..A3, half h.
+    auto read_frag = [&](int sh, int n, int h, uint32_t buf) {
+        if (n >= 1 && n <= 4)
+            read_half(bf[sh][n - 1], buf + b_fbase + (n - 1) * 32 * KS + fo[sh][h], h);
+        else {
+            const int a = (n == 0) ? 0 : n - 4;
+            read_half(af[sh][a], buf + a_fbase + a * 32 * KS + fo[sh][h], h);
+        }
+    };
+
+    v16f acc[F][F];
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // One stage: MFMAs on both K halves around the barrier.  DMA: issue the
+    // loads of stage k+2 (at `ld_k0`) into this stage's buffer; RD: read the
+    // next stage's first fragments.
+    auto stage = [&](uint32_t buf, bool dma, bool rd, uint32_t base, uint32_t ld_k0) {
+        const uint32_t nbuf = buf ^ STAGE;
+#pragma unroll
+        for (int slot = 0; slot < 16; ++slot) {
+            const int i = slot >> 2, j = slot & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[0][j], af[0][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            if (slot < 8) {
+                read_frag(1, slot, 0, buf);
+                read_frag(1, slot, 1, buf);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Stage k+1 has landed (own loads) and is visible (barrier); nobody
+        // reads this stage's buffer any more.
+        wait_vmem_all();
+        __syncthreads();
+#pragma unroll
+        for (int slot = 0; slot < 16; ++slot) {
+            const int i = slot >> 2, j = slot & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[1][j], af[1][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            if (dma) load_one(slot, base, ld_k0, buf);
+            if (rd) read_frag(0, slot >> 1, slot & 1, nbuf);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = K / KS;                      // >= 2 (caller guarantees)
+    const float s = (*sinv_a) * (*sinv_b);
+    float so = 0.f;
+    bool so_fold = false;
+    if constexpr (is_q_out<OUT>()) {
+        so = *qo.scale;
+        so_fold = scale_is_foldable(so);
+    }
+    uint32_t wkey = 0;                          // FP8 output: the wave's amax key
+    // Loads of tile r's stages 0 and 1 into buffers 0 and 1, and its bias.
+    auto issue_prologue = [&](int r) {
+        int tm, tn;
+        tile_of_block(r, tiles_m, tiles_n, tm, tn);
+        const uint32_t base =
+            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+        if constexpr (HAS_BIAS) {
+            if (wave == 0) {
+                const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t *>(bias), (short)0, 2 * N, 0x00020000);
+                dma_b128(brs, (uint32_t)(2 * tn * BN + 16 * lane), lds0 + 2 * STAGE);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load_one(i, base, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load_one(i, base, KS, STAGE);
+    };
+    // Everything requested so far has landed (this also drains the previous
+    // tile's stores); stage 0's first fragments into registers.
+    auto finish_prologue = [&]() {
+        wait_vmem_all();
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) read_frag(0, n, h, 0);
+    };
+
+    issue_prologue((int)blockIdx.x);
+    finish_prologue();
+    for (int r = (int)blockIdx.x; r < T; r += (int)gridDim.x) {
+        int tm, tn;
+        tile_of_block(r, tiles_m, tiles_n, tm, tn);
+        const uint32_t base =
+            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+        uint32_t buf = 0;
+        for (int k = 0; k + 2 < nk; ++k) {
+            stage(buf, true, true, base, (uint32_t)((k + 2) * KS));
+            buf ^= STAGE;
+        }
+        stage(buf, false, true, 0, 0);          // stage nk-2
+        buf ^= STAGE;
+        stage(buf, false, false, 0, 0);         // stage nk-1: LDS idle after its barrier
+
+        const int rn = r + (int)gridDim.x;
+        const bool more = rn < T;
+        const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
+        if constexpr (OUT == FP8_DTYPE_BF16) {
+            uint8_t *stg = lds + wave * 32768;
+            stage_wave_tile_bf16<HAS_BIAS>(acc, stg, bias_lds + 2 * wn * WT, lane, s);
+            u32x4 rows_out[32];
+            read_staged_rows(stg, lane, rows_out);
+            __syncthreads();                    // staging and bias read by every wave
+            if (more) issue_prologue(rn);
+            store_staged_rows(static_cast<uint16_t *>(Cv), rows_out, M, N, r0, cc0, lane);
+        } else if constexpr (is_q_out<OUT>()) {
+            uint8_t *stg = lds + wave * 32768;
+            const uint32_t tk = stage_wave_tile_q<OUT, HAS_BIAS>(
+                acc, stg, bias_lds + 2 * wn * WT, lane, s, so, so_fold, M, r0);
+            wkey = max(wkey, wave_max_key(tk));
+            u32x4 rows_out[16];
+            read_staged_rows_q(stg, lane, rows_out);
+            __syncthreads();                    // staging and bias read by every wave
+            if (more) issue_prologue(rn);
+            store_staged_rows_q(static_cast<uint8_t *>(Cv), rows_out, M, N, r0, cc0, lane);
+        } else {
+            // fp32: four 32-row blocks through the wave's own 16 KiB of staging.
+            uint8_t *stg = lds + wave * 32768;
+            float *C = static_cast<float *>(Cv);
+            u32x4 rows_out[16];
+#pragma unroll
+            for (int i = 0; i < F; ++i) {
+                stage_wave_block_f32<HAS_BIAS>(acc, stg, bias_lds + 2 * wn * WT, lane, s, i);
+                read_staged_block_f32(stg, lane, rows_out);
+                if (i == F - 1) {
+                    __syncthreads();            // staging and bias read by every wave
+                    if (more) issue_prologue(rn);
+                }
+                store_staged_block_f32(C, rows_out, M, N, r0 + 32 * i, cc0, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < F; ++i)
+#pragma unroll
+                for (int j = 0; j < F; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        }
+        if (more) finish_prologue();
+    }
+    if constexpr (is_q_out<OUT>())
+        finish_q_out(wkey, qo, so, reinterpret_cast<uint32_t *>(lds), so_fold);
+}
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_big(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
+                      const float *sb, const uint16_t *bias, void *C, const QOut &qo,
+                      hipStream_t stream) {
+    auto kern = gemm_nt_big_kernel<FA, FB, OUT, HAS_BIAS>;
+    constexpr int lds_bytes = 3 * (256 + 256) * 64;   // three 32 KiB stages
+    static bool attr_set[64];
+    static int cu_count[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const int tiles_m = (M + 255) / 256;
+    const int tiles_n = (N + 255) / 256;
+    const int grid = std::min(tiles_m * tiles_n, cu_count[dev]);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
+                       C, tiles_m, tiles_n, qo);
+    return hipGetLastError();
+}
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
+                      const float *sb, const uint16_t *bias, void *C, const QOut &qo,
+                      hipStream_t stream) {
+    auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS>;
+    constexpr int lds_bytes = 2 * (256 + 256) * 128 + 1024;   // two 64 KiB stages, bias
+    static bool attr_set[64];
+    static int cu_count[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const int tiles_m = (M + 255) / 256;
+    const int tiles_n = (N + 255) / 256;
+    const int grid = std::min(tiles_m * tiles_n, cu_count[dev]);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
+                       C, tiles_m, tiles_n, qo);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
+                      const float *sb, const uint16_t *bias, void *C, const QOut &qo,
+                      hipStream_t stream) {
+    auto kern = gemm_nt_kernel<BM, BN, WM, WN, FA, FB, OUT, HAS_BIAS>;
+    constexpr int lds_bytes = 2 * (BM + BN) * BK;
+    // Dynamic LDS above 64 KiB must be enabled once per device and kernel.
+    static bool attr_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set[dev] = true;
+    }
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(WM * WN * 64), lds_bytes, stream, A, B,
+                       M, N, K, sa, sb, bias, C, tiles_m, tiles_n, qo);
+    return hipGetLastError();
+}
+
+template <int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
+                      const float *sa, const float *sb, const uint16_t *bias, void *C,
+                      const QOut &qo, hipStream_t stream) {
+    // Large problems: 256 x 256 tiles, four waves of 128 x 128 (32x32x64
+    // instructions); small ones: 128 x 128 tiles (16x16x128 instructions).
+    // The large kernel addresses operands with 32-bit buffer offsets.
+    // It also needs at least four 64-byte K stages.
+    const bool fits32 = (M + 256) * K < ((int64_t)1 << 31) && (N + 256) * K < ((int64_t)1 << 31);
+    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256 && K % 128 == 0)
+        return launch_dma<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
+                                                 qo, stream);
+    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256)
+        return launch_big<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
+                                                 qo, stream);
+    return launch_cfg<128, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
+                                                             bias, C, qo, stream);
+}
+
+}  // namespace
+}  // namespace fp8dsl

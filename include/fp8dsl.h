@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 4
+#define FP8DSL_ABI_VERSION 5
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -280,6 +280,37 @@ int fp8_cast_transpose_dynamic(const void *x, int32_t src, int64_t rows, int64_t
  */
 int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
                    uint16_t *y, fp8_stream_t stream);
+
+/*
+ * fp8_linear_fwd_fp8out -- Y = X W^T + bias with an FP8 output and its amax.
+ *
+ * torch._scaled_mm called with an FP8 out_dtype returns the FP8 output
+ * together with the output's amax ("Accelerating PyTorch Training Workloads
+ * with FP8 -- Part 2", the torch._scaled_mm example).  The product is the one
+ * of fp8_linear_fwd, kept in fp32, and then cast as fp8_cast_transpose_amax
+ * casts, with the output tensor's own delayed scale:
+ *
+ *   v[m, n]  = fp32( (sum_k dec(x[m,k]) dec(w[n,k])) * x_sinv * w_sinv + bias[n] )
+ *   y->data[m, n] = the cast of v with *scale_y (one fp32 multiply, saturating
+ *                   round to nearest even, NaN -> 0x7F | sign)
+ *   *amax_y  = max(*amax_y, |v[m, n]|)   (UNSCALED v, sign-cleared fp32 bit
+ *                                          order: the value the output's amax
+ *                                          history records)
+ *   *y->scale_inv = 1 / *scale_y          (if y->scale_inv is non-NULL)
+ *
+ * x, w, bias as fp8_linear_fwd.  scale_y device, 1 float.  y host descriptor:
+ * y->data device [M, N] codes in y->fmt (E4M3 or E5M2), y->rows == M,
+ * y->cols == N, y->data_t must be NULL (no transposed output).  amax_y device,
+ * 1 float, max-accumulated atomically; must hold a non-negative value (e.g. 0
+ * after fp8_scale_update); may be NULL to skip the amax.  With M or N zero
+ * only the scale-inverse snapshot is written.
+ * Constraints: as fp8_linear_fwd, with N a multiple of 16.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_FORMAT,
+ * FP8_ERR_ARG (y->data_t set), FP8_ERR_LAUNCH.
+ */
+int fp8_linear_fwd_fp8out(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                          const float *scale_y, const fp8_tensor_t *y, float *amax_y,
+                          fp8_stream_t stream);
 
 /*
  * fp8_linear_dgrad -- dX = dY W on FP8 operands, using W's cached transpose.

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     for want in ("fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
                  "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
                  "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
-                 "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic"):
+                 "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic",
+                 "fp8_linear_fwd_fp8out"):
         assert want in names
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 4
+    assert dsl.fp8_abi_version() == 5
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -85,6 +86,25 @@ def test_validation_rejects_before_device_use():
     assert L.fp8_linear_fwd(byref(x), byref(w), None, 0x5008, None) == -3
     assert L.fp8_linear_fwd(byref(x), byref(w), 0x6002, 0x5000, None) == -3
     assert L.fp8_linear_fwd(byref(_desc(0, 48)), byref(w), None, None, None) == 0
+    # FP8-output forward: N a multiple of 16, no transposed output, shapes of y.
+    def y_desc(rows, cols, fmt=1, data=0x7000, data_t=0):
+        return _desc(rows, cols, fmt=fmt, data=data, data_t=data_t, sinv=0x7800)
+    fwdq = L.fp8_linear_fwd_fp8out
+    x, w = _desc(64, 48), _desc(40, 48)
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(64, 40)), 0x6100, None) == -2
+    x, w = _desc(64, 48), _desc(32, 48)
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(64, 32, data_t=0x2000)), 0x6100,
+                None) == -5
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(64, 48)), 0x6100, None) == -2
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(32, 32)), 0x6100, None) == -2
+    assert fwdq(byref(x), byref(w), None, None, byref(y_desc(64, 32)), 0x6100, None) == -1
+    assert fwdq(byref(x), byref(w), None, 0x6000, None, 0x6100, None) == -1
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(64, 32, fmt=2)), 0x6100,
+                None) == -4
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(64, 32, data=0)), 0x6100,
+                None) == -1
+    assert fwdq(byref(x), byref(w), None, 0x6000, byref(y_desc(64, 32, data=0x7004)), 0x6100,
+                None) == -3
     dy, wt = _desc(64, 32), _desc(32, 48)
     assert L.fp8_linear_dgrad(byref(dy), byref(_desc(48, 48)), 0x5000, None) == -2
     assert L.fp8_linear_dgrad(byref(dy), byref(_desc(32, 44)), 0x5000, None) == -2
