@@ -135,6 +135,13 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, what: str = "tensor") -> Optiona
     return t.data_ptr()
 
 
+def _row_stride(t: torch.Tensor) -> int:
+    """Row stride (elements) of a 2-D source.  torch gives an empty tensor an
+    arbitrary stride; no memory is read for it, so its column count is
+    passed instead."""
+    return t.stride(0) if t.numel() > 0 else t.shape[1]
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -222,7 +229,7 @@ def fp8_cast_transpose_amax(x: torch.Tensor, scale: torch.Tensor, out: Float8Ten
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
     d = out.desc()
-    _check(lib().fp8_cast_transpose_amax(x.data_ptr(), src, x.shape[0], x.shape[1], x.stride(0),
+    _check(lib().fp8_cast_transpose_amax(x.data_ptr(), src, x.shape[0], x.shape[1], _row_stride(x),
                                          _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
                                          _ptr(amax_cur, torch.float32, "amax_cur"),
                                          _ptr(noop_flag, torch.int32, "noop_flag"),
@@ -258,7 +265,7 @@ def fp8_cast_transpose_amax_dbias(x: torch.Tensor, scale: torch.Tensor, out: Flo
         raise ValueError("dbias must have cols elements")
     d = out.desc()
     _check(lib().fp8_cast_transpose_amax_dbias(
-        x.data_ptr(), src, x.shape[0], x.shape[1], x.stride(0), _ptr(scale, torch.float32, "scale"),
+        x.data_ptr(), src, x.shape[0], x.shape[1], _row_stride(x), _ptr(scale, torch.float32, "scale"),
         ctypes.byref(d), _ptr(amax_cur, torch.float32, "amax_cur"),
         _ptr(dbias, torch.float32, "dbias"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)),
@@ -284,8 +291,8 @@ def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
         raise ValueError("y must be contiguous")
     d = out.desc()
     _check(lib().fp8_produce_cast_transpose_amax(
-        op, x.data_ptr(), x.stride(0), a.data_ptr(), a.stride(0),
-        None if b is None else b.data_ptr(), 0 if b is None else b.stride(0), y.data_ptr(),
+        op, x.data_ptr(), _row_stride(x), a.data_ptr(), _row_stride(a),
+        None if b is None else b.data_ptr(), 0 if b is None else _row_stride(b), y.data_ptr(),
         x.shape[0], x.shape[1], _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
         _ptr(amax_cur, torch.float32, "amax_cur"), _ptr(noop_flag, torch.int32, "noop_flag"),
         _stream(stream)), "fp8_produce_cast_transpose_amax")
@@ -309,7 +316,7 @@ def fp8_cast_transpose_dynamic(x: torch.Tensor, scale: torch.Tensor, out: Float8
         raise ValueError("x must be a device tensor")
     d = out.desc()
     _check(lib().fp8_cast_transpose_dynamic(
-        x.data_ptr(), src, x.shape[0], x.shape[1], x.stride(0), margin,
+        x.data_ptr(), src, x.shape[0], x.shape[1], _row_stride(x), margin,
         _ptr(scale, torch.float32, "scale"), ctypes.byref(d), _ptr(amax, torch.float32, "amax"),
         _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)), "fp8_cast_transpose_dynamic")
 
