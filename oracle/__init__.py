@@ -20,8 +20,9 @@ of the pages it follows:
   training loop of "CPU Overhead of te.Linear FP8 Layers" needs for its biased
   linears (fp32, exact fp64 sum rounded once).
 * ``produce_cast`` -- the toy block's elementwise producers (``shift * x /
-  scale`` with its nan_to_num, and the residual add) rounded to bf16 and
-  followed by the cast ("CPU Overhead of te.Linear FP8 Layers").
+  scale`` with its nan_to_num, the residual add, and the residual add of two
+  terms, each sum rounded) rounded to bf16 and followed by the cast ("CPU
+  Overhead of te.Linear FP8 Layers").
 * ``dynamic_cast`` -- dynamic scaling, the comparator the float8 all-gather
   page contrasts delayed scaling with (amax of the tensor itself, then the
   cast with fp8_max / amax).
@@ -200,6 +201,7 @@ def cast_transpose_amax(x: np.ndarray, scale: float, fmt: int, *, want_q: bool =
 
 PROD_MODULATE = 1
 PROD_ADD = 2
+PROD_ADD2 = 3
 
 
 def produce_cast(op: int, x: np.ndarray, a: np.ndarray, b: np.ndarray | None, scale: float,

@@ -235,9 +235,12 @@ int orc_dbias(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, fl
  *   op 1 (modulate): y = bf16(a * x / b), one multiply then one correctly
  *        rounded division, round to nearest even; then an infinite or NaN y
  *        becomes +0 (the torch.nan_to_num that follows in that script);
- *   op 2 (residual add): y = bf16(x + a); a NaN result is 0x7FC0.
+ *   op 2 (residual add): y = bf16(x + a); a NaN result is 0x7FC0;
+ *   op 3 (two residual terms, the block's x = x + attn_q + attn_k[:, :H]):
+ *        y = bf16(bf16(x + a) + b), the two bf16 adds torch performs one
+ *        after the other, each rounded; a NaN at either step is 0x7FC0.
  * x, a, b are bf16 [rows, cols] with leading dimensions ldx, lda, ldb (b is
- * only read by op 1); y is bf16 [rows, cols], row-major.  The cast is then
+ * read by ops 1 and 3); y is bf16 [rows, cols], row-major.  The cast is then
  * exactly orc_cast_transpose_amax of y.  Returns 0, or -1 for a bad argument.
  */
 static uint16_t orc_f32_to_bf16_canon(float f) {
@@ -249,8 +252,8 @@ int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, 
                      const uint16_t *b, int64_t ldb, int64_t rows, int64_t cols, float scale,
                      int fmt, uint16_t *y, uint8_t *q, uint8_t *qt, float *amax_inout,
                      float *scale_inv_out) {
-    if ((op != 1 && op != 2) || rows < 0 || cols < 0 || ldx < cols || lda < cols || !y ||
-        (op == 1 && (!b || ldb < cols)))
+    if ((op != 1 && op != 2 && op != 3) || rows < 0 || cols < 0 || ldx < cols || lda < cols ||
+        !y || (op != 2 && (!b || ldb < cols)))
         return -1;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t c = 0; c < cols; ++c) {
@@ -263,8 +266,12 @@ int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, 
                 float v = prod / bv;
                 out = orc_f32_to_bf16_canon(v);
                 if ((out & 0x7F80u) == 0x7F80u) out = 0x0000;   /* inf or NaN -> +0 */
-            } else {
+            } else if (op == 2) {
                 out = orc_f32_to_bf16_canon(xv + av);
+            } else {
+                float t = orc_bf16_to_f32(orc_f32_to_bf16_canon(xv + av));
+                float bv = orc_bf16_to_f32(b[r * ldb + c]);
+                out = orc_f32_to_bf16_canon(t + bv);
             }
             y[r * cols + c] = out;
         }

@@ -45,6 +45,35 @@ def test_add_against_torch_including_nan():
     assert y[1, 1] == 0x7F80
 
 
+def test_add2_against_torch_including_nan():
+    """Two residual terms: torch adds them one after the other, rounding each
+    sum to bf16."""
+    x, a, b = _rand_bf16((64, 48), 12), _rand_bf16((64, 48), 13, 10.0), _rand_bf16((64, 48), 14, 0.01)
+    x[0, 0] = float("nan")
+    a[1, 1] = float("inf")
+    b[2, 2] = float("-inf")
+    a[3, 3] = float("inf")
+    b[3, 3] = float("-inf")                       # inf + -inf = NaN at the second add
+    y, *_ = oracle.produce_cast(oracle.PROD_ADD2, _bits(x), _bits(a), _bits(b), 1.0, oracle.E4M3)
+    want = (x + a) + b
+    nan = torch.isnan(want).numpy()
+    np.testing.assert_array_equal(y[~nan], _bits(want)[~nan])
+    assert (y[nan] == 0x7FC0).all() and nan[0, 0] and nan[3, 3]
+    assert y[1, 1] == 0x7F80 and y[2, 2] == 0xFF80
+
+
+def test_add2_rounds_twice():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 and rounds to even (1); adding
+    # 2^-8 again gives 1 again.  One rounding of the exact sum 1 + 2^-7 would
+    # give 1 + 2^-7 (0x3F81).
+    one = torch.ones(16, 16, dtype=torch.bfloat16)
+    e = torch.full((16, 16), 2.0 ** -8, dtype=torch.bfloat16)
+    y, *_ = oracle.produce_cast(oracle.PROD_ADD2, _bits(one), _bits(e), _bits(e), 1.0, oracle.E4M3)
+    assert (y == 0x3F80).all()
+    y, *_ = oracle.produce_cast(oracle.PROD_ADD, _bits(one), _bits(e + e), None, 1.0, oracle.E4M3)
+    assert (y == 0x3F81).all()
+
+
 def test_strided_views_match_torch():
     # shift and scale are column slices of the modulation linear's output,
     # the residual term a column slice of the qkv output.
@@ -57,6 +86,9 @@ def test_strided_views_match_torch():
     np.testing.assert_array_equal(y, _bits(_torch_modulate(shift, x, scale)))
     y, *_ = oracle.produce_cast(oracle.PROD_ADD, _bits(x), mb[:, 64:96], None, 1.0, oracle.E4M3)
     np.testing.assert_array_equal(y, _bits(x + mod[:, 64:96]))
+    y, *_ = oracle.produce_cast(oracle.PROD_ADD2, _bits(x), mb[:, 64:96], mb[:, :32], 1.0,
+                                oracle.E4M3)
+    np.testing.assert_array_equal(y, _bits((x + mod[:, 64:96]) + mod[:, :32]))
 
 
 def test_modulate_closed_forms():
@@ -92,4 +124,6 @@ def test_bad_arguments():
     with pytest.raises(ValueError):
         oracle.produce_cast(oracle.PROD_MODULATE, x, x, None, 1.0, oracle.E4M3)   # b missing
     with pytest.raises(ValueError):
-        oracle.produce_cast(3, x, x, x, 1.0, oracle.E4M3)
+        oracle.produce_cast(oracle.PROD_ADD2, x, x, None, 1.0, oracle.E4M3)       # b missing
+    with pytest.raises(ValueError):
+        oracle.produce_cast(4, x, x, x, 1.0, oracle.E4M3)
