@@ -412,7 +412,7 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
             cast_in(bi, 3, x)
             ca_q = w_gemm(bi, 2)
             ca_k = w_gemm(bi, 3)
-            x = produce_in(bi, 4, dsl.PRODUCE_ADD, x + ca_q, ca_k[:, :H], None)
+            x = produce_in(bi, 4, dsl.PRODUCE_ADD2, x, ca_q, ca_k[:, :H])
             h = w_gemm(bi, 4)
             cast_in(bi, 5, h)
             o = w_gemm(bi, 5)

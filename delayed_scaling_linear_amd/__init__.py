@@ -34,7 +34,7 @@ __all__ = [
     "DelayedScalingState", "fp8_scale_update", "fp8_cast_transpose_amax", "fp8_linear_fwd",
     "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
     "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
-    "fp8_produce_cast_transpose_amax", "PRODUCE_MODULATE", "PRODUCE_ADD",
+    "fp8_produce_cast_transpose_amax", "PRODUCE_MODULATE", "PRODUCE_ADD", "PRODUCE_ADD2",
     "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
     "library_path", "lib",
 ]
@@ -45,6 +45,7 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 PRODUCE_MODULATE = 1
 PRODUCE_ADD = 2
+PRODUCE_ADD2 = 3
 FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -278,7 +279,8 @@ def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
                                     amax_cur: Optional[torch.Tensor] = None,
                                     noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
     """y = op(x, a, b) in bf16 (PRODUCE_MODULATE: a * x / b with inf/NaN -> 0;
-    PRODUCE_ADD: x + a), then y cast into `out`.  x, a, b: bf16 2-D device
+    PRODUCE_ADD: x + a; PRODUCE_ADD2: (x + a) + b, each sum rounded), then y
+    cast into `out`.  x, a, b: bf16 2-D device
     tensors of one shape with unit column stride (column slices are fine);
     y: contiguous bf16 of that shape."""
     ins = [x, a] + ([b] if b is not None else [])

@@ -162,23 +162,24 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
                                     int64_t ldb, uint16_t *y, int64_t rows, int64_t cols,
                                     const float *scale, const fp8_tensor_t *out, float *amax_cur,
                                     const int32_t *noop_flag, fp8_stream_t stream) {
-    if (op != FP8_PRODUCE_MODULATE && op != FP8_PRODUCE_ADD) return FP8_ERR_ARG;
+    if (op != FP8_PRODUCE_MODULATE && op != FP8_PRODUCE_ADD && op != FP8_PRODUCE_ADD2)
+        return FP8_ERR_ARG;
     // The cast of y: same rules as a bf16 cast of a contiguous [rows, cols].
     if (int e = check_cast(y, FP8_DTYPE_BF16, rows, cols, cols, scale, out)) return e;
-    const bool modulate = (op == FP8_PRODUCE_MODULATE);
+    const bool reads_b = (op != FP8_PRODUCE_ADD);
     if (ldx < cols || lda < cols || (ldx % 8) != 0 || (lda % 8) != 0 ||
-        (modulate && (ldb < cols || (ldb % 8) != 0)))
+        (reads_b && (ldb < cols || (ldb % 8) != 0)))
         return FP8_ERR_SHAPE;
     const bool empty = (rows == 0 || cols == 0);
-    if (!empty && (x == nullptr || a == nullptr || y == nullptr || (modulate && b == nullptr)))
+    if (!empty && (x == nullptr || a == nullptr || y == nullptr || (reads_b && b == nullptr)))
         return FP8_ERR_NULL;
-    if ((x && !aligned16(x)) || (a && !aligned16(a)) || (modulate && b && !aligned16(b)))
+    if ((x && !aligned16(x)) || (a && !aligned16(a)) || (reads_b && b && !aligned16(b)))
         return FP8_ERR_ALIGN;
     if (empty && out->scale_inv == nullptr) return FP8_OK;
     if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (empty) return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
-    return status_of(launch_produce_cast(op, x, ldx, a, lda, modulate ? b : nullptr, ldb, y, rows,
+    return status_of(launch_produce_cast(op, x, ldx, a, lda, reads_b ? b : nullptr, ldb, y, rows,
                                          cols, scale, out->fmt, out->data, out->data_t, amax_cur,
                                          out->scale_inv, noop_flag, s));
 }

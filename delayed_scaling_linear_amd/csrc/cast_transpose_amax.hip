@@ -484,8 +484,15 @@ __device__ __forceinline__ uint32_t produce_pair(uint32_t xw, uint32_t aw, uint3
             const float v = (av * xv) / bv;
             y = (v != v) ? 0u : f32_to_bf16_bits_rne(v);
             if ((y & 0x7F80u) == 0x7F80u) y = 0u;
-        } else {
+        } else if constexpr (OP == FP8_PRODUCE_ADD) {
             const float v = xv + av;
+            y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);
+        } else {
+            // Two terms, added one at a time with a bf16 rounding after each.
+            const float bv = __uint_as_float(h ? (bw & 0xFFFF0000u) : (bw << 16));
+            const float v1 = xv + av;
+            const uint32_t t = (v1 != v1) ? 0x7FC0u : f32_to_bf16_bits_rne(v1);
+            const float v = __uint_as_float(t << 16) + bv;
             y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);
         }
         out |= y << (16 * h);
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(THREADS) void produce_cast_kernel(
             for (int h = 0; h < 2; ++h) {
                 xv[i][h] = *reinterpret_cast<const u32x4 *>(x + (r + i) * ldx + c + 8 * h);
                 av[i][h] = *reinterpret_cast<const u32x4 *>(a + (r + i) * lda + c + 8 * h);
-                if constexpr (OP == FP8_PRODUCE_MODULATE)
+                if constexpr (OP != FP8_PRODUCE_ADD)
                     bv[i][h] = *reinterpret_cast<const u32x4 *>(b + (r + i) * ldb + c + 8 * h);
                 else
                     bv[i][h] = u32x4{0u, 0u, 0u, 0u};
@@ -633,6 +640,15 @@ hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uin
                 x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
                 stream);
         return launch_produce_op_fmt<FP8_PRODUCE_MODULATE, FP8_E5M2>(
+            x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+            stream);
+    }
+    if (op == FP8_PRODUCE_ADD2) {
+        if (fmt == FP8_E4M3)
+            return launch_produce_op_fmt<FP8_PRODUCE_ADD2, FP8_E4M3>(
+                x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+                stream);
+        return launch_produce_op_fmt<FP8_PRODUCE_ADD2, FP8_E5M2>(
             x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
             stream);
     }

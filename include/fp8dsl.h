@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 5
+#define FP8DSL_ABI_VERSION 6
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -72,7 +72,11 @@ typedef enum { FP8_DTYPE_BF16 = 0, FP8_DTYPE_FP32 = 1 } fp8_dtype_t;
 typedef enum { FP8_AMAX_ALGO_MAX = 0 } fp8_amax_algo_t;
 
 /* Elementwise producer fused in front of a cast (fp8_produce_cast_transpose_amax). */
-typedef enum { FP8_PRODUCE_MODULATE = 1, FP8_PRODUCE_ADD = 2 } fp8_produce_op_t;
+typedef enum {
+    FP8_PRODUCE_MODULATE = 1,
+    FP8_PRODUCE_ADD = 2,
+    FP8_PRODUCE_ADD2 = 3
+} fp8_produce_op_t;
 
 /*
  * An FP8 tensor: codes, optional cached transpose and the scale-inverse that
@@ -219,13 +223,17 @@ int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int6
  *                            an infinite or NaN y becomes +0
  *   op FP8_PRODUCE_ADD:      y = bf16(x + a)       (fp32 add, round to nearest
  *                            even); a NaN y is written as 0x7FC0
+ *   op FP8_PRODUCE_ADD2:     y = bf16(bf16(x + a) + b)   (the block's residual
+ *                            x = x + attn_q + attn_k[:, :H], added one term at
+ *                            a time as torch does, each sum rounded; a NaN at
+ *                            either step is written as 0x7FC0)
  *
  * then writes y (bf16, row-major [rows, cols], ld = cols) and exactly what
  * fp8_cast_transpose_amax writes for the bf16 source y with this scale.
  *
  * x, a, b   device bf16 [rows, cols] with row strides ldx, lda, ldb
  *           (elements, each >= cols and a multiple of 8; 16-byte aligned); b
- *           is only read by MODULATE (NULL otherwise).  Column slices of a
+ *           is read by MODULATE and ADD2 (NULL for ADD).  Column slices of a
  *           wider tensor are fine.
  * y         device bf16 [rows, cols], 16-byte aligned; must not overlap the
  *           inputs.

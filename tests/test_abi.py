@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 5
+    assert dsl.fp8_abi_version() == 6
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -157,8 +157,10 @@ def test_produce_cast_validation():
     ok = dict(ldx=48, lda=48, ldb=48)
     call = lambda op, ldx=48, lda=48, ldb=48, b=B, x=X, y=Y, desc=d: L.fp8_produce_cast_transpose_amax(
         op, x, ldx, A, lda, b, ldb, y, desc.rows, desc.cols, 0x5000, byref(desc), None, None, None)
-    assert call(3) == -5                          # unknown op
+    assert call(4) == -5                          # unknown op
     assert call(1, b=None) == -1                  # modulate needs b
+    assert call(3, b=None) == -1                  # the two-term add needs b
+    assert call(3, ldb=44) == -2
     assert call(1, ldx=40) == -2                  # ld < cols
     assert call(1, lda=52) == -2                  # ld not a multiple of 8
     assert call(1, ldb=44) == -2

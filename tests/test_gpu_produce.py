@@ -75,6 +75,21 @@ def test_add_shapes(shape, fmt):
     _run_and_check(oracle.PROD_ADD, x, a, None, 41.0, fmt)
 
 
+@pytest.mark.parametrize("shape", [(16, 16), (400, 272), (1024, 2048)])
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_add2_shapes(shape, fmt):
+    x, a, b = _rand(shape, 16), _rand(shape, 17, 3.0), _rand(shape, 18, 0.05)
+    _run_and_check(oracle.PROD_ADD2, x, a, b, 41.0, fmt)
+
+
+def test_add2_rounds_after_each_term():
+    """1 + 2^-8 + 2^-8: each sum is a tie that rounds back to 1."""
+    one = torch.ones(32, 32, dtype=torch.bfloat16)
+    e = torch.full((32, 32), 2.0 ** -8, dtype=torch.bfloat16)
+    y = _run_and_check(oracle.PROD_ADD2, one, e, e, 1.0, oracle.E4M3)
+    assert (bits16(y) == 0x3F80).all()
+
+
 def test_toy_block_shapes_with_column_slices():
     """shift, scale = columns [0, 2048) and [2048, 4096) of the modulation
     output [8192, 12288]; the qkv residual = columns [0, 2048) of [8192, 6144]."""
@@ -83,6 +98,10 @@ def test_toy_block_shapes_with_column_slices():
     y = _run_and_check(oracle.PROD_MODULATE, x, mod[:, :2048], mod[:, 2048:4096], 3.5, oracle.E4M3)
     qkv = _rand((8192, 6144), 8, 0.02)
     _run_and_check(oracle.PROD_ADD, y.cpu(), qkv[:, :2048], None, 3.5, oracle.E4M3, qt=False)
+    # x + attn_q [8192, 2048] + attn_k[:, :2048] of [8192, 4096]
+    q_out = _rand((8192, 2048), 19, 0.02)
+    k_out = _rand((8192, 4096), 20, 0.02)
+    _run_and_check(oracle.PROD_ADD2, y.cpu(), q_out, k_out[:, :2048], 3.5, oracle.E4M3)
 
 
 def test_special_values():
@@ -100,6 +119,12 @@ def test_special_values():
     y = _run_and_check(oracle.PROD_ADD, x2, a2, None, 1.0, oracle.E5M2)
     v = bits16(y)
     assert v[0, 0] == 0x7FC0 and v[2, 2] == 0x7FC0 and v[1, 1] == 0x7F80
+    b2 = _rand((64, 64), 21)
+    b2[3, 3], a2[3, 3] = float("-inf"), float("inf")    # NaN at the second add
+    b2[4, 4] = float("nan")
+    y = _run_and_check(oracle.PROD_ADD2, x2, a2, b2, 1.0, oracle.E4M3)
+    v = bits16(y)
+    assert v[0, 0] == 0x7FC0 and v[3, 3] == 0x7FC0 and v[4, 4] == 0x7FC0
 
 
 def test_noop_flag_writes_nothing():

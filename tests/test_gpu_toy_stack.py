@@ -215,7 +215,8 @@ class _CachedWeightStack:
 
     def forward_fused(self, x):
         """forward() with each linear's input produced and cast in one pass
-        where the glue allows (modulation, residual adds)."""
+        (modulation, residual adds of one or two terms): no torch glue left
+        but the last block's residual add."""
         H = self.H
         nb = len(self.blocks)
         self._cast_in(0, 0, x)
@@ -228,7 +229,7 @@ class _CachedWeightStack:
             self._cast_in(bi, 3, x)
             ca_q = self._cast_w_gemm(bi, 2)
             ca_k = self._cast_w_gemm(bi, 3)
-            x = self._produce_in(bi, 4, dsl.PRODUCE_ADD, x + ca_q, ca_k[:, :H], None,
+            x = self._produce_in(bi, 4, dsl.PRODUCE_ADD2, x, ca_q, ca_k[:, :H],
                                  torch.empty_like(x))
             h = self._cast_w_gemm(bi, 4)
             self._cast_in(bi, 5, h)
