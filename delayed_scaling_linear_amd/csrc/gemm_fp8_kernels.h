@@ -669,15 +669,33 @@ __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(
 // chunk) pairs are all distinct, so neither layout has bank conflicts.
 __device__ __forceinline__ int dma_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// bf16 epilogue of one wave's 128 x 128 tile through LDS (32 KiB at `stg`),
-// in three steps so that the caller can put other work between them.
-// stage_wave_tile_bf16: out(acc * s + bias) is written in the matrix-core
-// layout (8 bytes per lane, one output row per lane) into 256-byte staging
-// rows whose 16-byte chunk c of row q sits at chunk c ^ (q & 15); the bias of
-// the wave's 128 columns is read from LDS (`bias_lds`, bf16, column c0
-// first; zero past N).  Clears the accumulators.
-template <bool HAS_BIAS>
-__device__ __forceinline__ void stage_wave_tile_bf16(v16f (&acc)[4][4], uint8_t *stg,
+// Output stores of the LDS-DMA kernel go through a buffer resource over the
+// wave's 128 output rows r0 .. r0 + 127 (those below M): a store at an
+// offset at or past the resource's size is dropped by the hardware.  So
+// every store instruction is issued whatever the tails, and the kernel can
+// count them in its vmcnt waits.  Column groups past N take OUT_OOB.  The
+// host guarantees 128 * N * EB < 2^31.
+constexpr uint32_t OUT_OOB = 0x80000000u;
+template <int EB>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows_rsrc(void *C, int M, int N, int r0) {
+    // Every input is wave-uniform, but the clamp compiles to a vector
+    // instruction; without readfirstlane the resource would sit in vector
+    // registers and the compiler would loop over its values at every store.
+    const int rows = min(128, max(0, M - r0));
+    const int nrec = __builtin_amdgcn_readfirstlane(rows * N * EB);
+    return __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t *>(C) + (int64_t)r0 * N * EB,
+                                             (short)0, nrec, 0x00020000);
+}
+
+// bf16 epilogue of one wave's 128 x 128 tile through 16 KiB of LDS at
+// `stg`, in two passes of 64 rows.  stage_wave_half_bf16<P>: out(acc * s +
+// bias) of fragment row blocks 2P and 2P + 1 is written in the matrix-core
+// layout (8 bytes per lane, one output row per lane) into 64 staging rows of
+// 256 bytes whose 16-byte chunk c of row q sits at chunk c ^ (q & 15); the
+// bias of the wave's 128 columns is read from LDS (`bias_lds`, bf16, column
+// c0 first; zero past N).  Clears those accumulators.
+template <int P, bool HAS_BIAS>
+__device__ __forceinline__ void stage_wave_half_bf16(v16f (&acc)[4][4], uint8_t *stg,
                                                      const uint8_t *bias_lds, int lane, float s) {
     const int frow = lane & 31;
     const int half = lane >> 5;
@@ -696,8 +714,9 @@ __device__ __forceinline__ void stage_wave_tile_bf16(v16f (&acc)[4][4], uint8_t 
             }
             const int c = 4 * j + g;                     // 16-byte chunk of the staging row
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = i * 32 + frow;
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * P + ii;
+                const int q = ii * 32 + frow;
                 const bf16x4 o = {(__bf16)(acc[i][j][4 * g + 0] * s + bv[0]),
                                   (__bf16)(acc[i][j][4 * g + 1] * s + bv[1]),
                                   (__bf16)(acc[i][j][4 * g + 2] * s + bv[2]),
@@ -707,33 +726,36 @@ __device__ __forceinline__ void stage_wave_tile_bf16(v16f (&acc)[4][4], uint8_t 
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+            for (int q = 0; q < 16; ++q) acc[2 * P + ii][j][q] = 0.f;
 }
 
-// Read the staged tile back, 16 lanes per 256-byte row: v[it] is row
-// 4 it + lane / 16, columns 8 (lane % 16) .. +7.
-__device__ __forceinline__ void read_staged_rows(const uint8_t *stg, int lane, u32x4 (&v)[32]) {
+// Read a staged half back, 16 lanes per 256-byte row: v[16 P + it] is tile
+// row 64 P + 4 it + lane / 16, columns 8 (lane % 16) .. +7.
+template <int P>
+__device__ __forceinline__ void read_staged_half(const uint8_t *stg, int lane, u32x4 (&v)[32]) {
     const int c = lane & 15;
 #pragma unroll
-    for (int it = 0; it < 32; ++it) {
+    for (int it = 0; it < 16; ++it) {
         const int q = 4 * it + (lane >> 4);
-        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
+        v[16 * P + it] = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
     }
 }
 
-// Store the rows of read_staged_rows: every instruction writes four whole
-// 256-byte row segments (in-range rows and 8-column groups only).
-__device__ __forceinline__ void store_staged_rows(uint16_t *__restrict__ C, const u32x4 (&v)[32],
-                                                  int M, int N, int r0, int c0, int lane) {
+// Store the rows of read_staged_half<0> and <1>: 32 instructions, each
+// writing four 256-byte row segments.
+__device__ __forceinline__ void store_rows_bf16(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[32],
+                                                int N, int c0, int lane) {
     const int gc = c0 + 8 * (lane & 15);
+    const uint32_t cb = gc < N ? (uint32_t)gc * 2u : OUT_OOB;   // + row offset < 2^31
 #pragma unroll
     for (int it = 0; it < 32; ++it) {
-        const int gr = r0 + 4 * it + (lane >> 4);
-        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+        const int row = 4 * it + (lane >> 4);
+        const uint32_t off = cb + (uint32_t)(row * N) * 2u;
+        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
     }
 }
 
@@ -782,15 +804,18 @@ __device__ __forceinline__ void read_staged_block_f32(const uint8_t *stg, int la
     }
 }
 
-// Store a block read by read_staged_block_f32 (rows r0 .. r0 + 31): every
-// instruction writes two whole 512-byte row segments.
-__device__ __forceinline__ void store_staged_block_f32(float *__restrict__ C, const u32x4 (&v)[16],
-                                                       int M, int N, int r0, int c0, int lane) {
+// Store a block read by read_staged_block_f32 (tile rows 32 i .. 32 i + 31
+// of the resource's 128): 16 instructions, each writing two 512-byte row
+// segments.
+__device__ __forceinline__ void store_block_f32(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[16],
+                                                int N, int i, int c0, int lane) {
     const int gc = c0 + 4 * (lane & 31);
+    const uint32_t cb = gc < N ? (uint32_t)gc * 4u : OUT_OOB;   // + row offset < 2^31
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int gr = r0 + 2 * it + (lane >> 5);
-        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+        const int row = 32 * i + 2 * it + (lane >> 5);
+        const uint32_t off = cb + (uint32_t)(row * N) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
     }
 }
 
@@ -897,17 +922,42 @@ __device__ __forceinline__ void read_staged_rows_q(const uint8_t *stg, int lane,
     }
 }
 
-// Store the rows of read_staged_rows_q: every instruction writes eight whole
-// 128-byte row segments (in-range rows and 16-column groups only; N % 16 == 0
-// keeps every group inside the row).
-__device__ __forceinline__ void store_staged_rows_q(uint8_t *__restrict__ C, const u32x4 (&v)[16],
-                                                    int M, int N, int r0, int c0, int lane) {
+// Store the rows of read_staged_rows_q: 16 instructions, each writing eight
+// 128-byte row segments (N % 16 == 0 keeps every 16-column group inside
+// the row).
+__device__ __forceinline__ void store_rows_q(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[16],
+                                             int N, int c0, int lane) {
     const int gc = c0 + 16 * (lane & 7);
+    const uint32_t cb = gc < N ? (uint32_t)gc : OUT_OOB;        // + row offset < 2^31
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int gr = r0 + 8 * it + (lane >> 3);
-        if (gr < M && gc < N) *reinterpret_cast<u32x4 *>(C + (int64_t)gr * N + gc) = v[it];
+        const int row = 8 * it + (lane >> 3);
+        const uint32_t off = cb + (uint32_t)(row * N);
+        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
     }
+}
+
+// vmcnt wait that leaves the last N vector memory instructions in flight.
+// Vector memory instructions of a wave complete in issue order (loads and
+// stores alike on gfx9), so this waits for everything issued before them.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+    static_assert(N == 16 || N == 32 || N == 48, "wait_vmem_but: unsupported count");
+    if constexpr (N == 16)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (N == 32)
+        asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+}
+
+// Lane index from an instruction the compiler cannot merge with others, so
+// that values derived from it are recomputed where they are used instead of
+// being kept live (or spilled) across the kernel.
+__device__ __forceinline__ int fresh_lane_id() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
 }
 
 // Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
@@ -930,14 +980,23 @@ __device__ __forceinline__ void store_staged_rows_q(uint8_t *__restrict__ C, con
 //     The second 16 MFMAs then carry the loads of stage k+2 into the freed
 //     buffer (one per MFMA, which paces them at the load unit's rate) and
 //     the reads of stage k+1's first fragments.
-//   * Tile boundaries drain the pipeline.  The bf16 epilogue stages each
-//     wave's output in the then idle stage buffers and reads it back as
-//     whole 256-byte row segments into the (now free) fragment registers;
-//     the next tile's first two stages and its bias (1 KiB of LDS past the
-//     stages) are requested before the output stores are issued, so those
-//     loads land while the store burst drains.  fp32 output goes through
-//     the same staging in four 32-row blocks (512-byte row segments), FP8
-//     codes through 128-byte staging rows.
+//   * Stages stream on across tile boundaries.  A tile's stage nk-2
+//     requests the next tile's stage 0 and bias (two 1 KiB bias slots past
+//     the stages); the epilogue stages each wave's output in its own 16 KiB
+//     quarter of the buffer freed by stage nk-1 and reads it back as whole
+//     row segments into the (now free) fragment registers: bf16 in two
+//     passes of 64 rows (256-byte segments), fp32 in four 32-row blocks
+//     (512-byte segments), FP8 codes in one pass (128-byte segments).  Then
+//     the next tile's stage 1 goes into that buffer, and only after it the
+//     output stores, as buffer stores that are always issued (the hardware
+//     drops the out-of-range ones).  Vector memory instructions of a wave
+//     complete in order, so the next tile waits with exact counts: for its
+//     stage 0 with stage 1 and the stores in flight, then at stage 0's
+//     middle for stage 1 with the stores in flight.
+//   * The per-lane load offsets and epilogue addresses are recomputed where
+//     they are used, from a lane index the compiler cannot hoist: kept live
+//     across the loop they spill, and a spill reload waits for every load
+//     in flight.
 template <int FA, int FB, int OUT, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
@@ -967,15 +1026,25 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const __amdgpu_buffer_rsrc_t ld_rsrc = loads_b ? rb_rsrc : ra_rsrc;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
     const uint32_t ld_lds = lds0 + (uint32_t)wave * (128 * KS);   // this wave's 128 rows
-    // The tile's 256 bias values (512 bytes) live past the two stages.
+    // Two 1 KiB bias slots past the two stages: a tile's 256 bias values
+    // (512 bytes; one load instruction moves 1 KiB) in slot t % 2 for the
+    // t-th tile of this workgroup, so the next tile's bias can land while
+    // the current tile's epilogue reads its own.
     uint8_t *const bias_lds = lds + 2 * STAGE;
 
     // Per-lane part of the load offsets: row l / 8 of an 8-row group, the
     // logical chunk stored at position l % 8 (the swizzle of rows 8i..8i+7
-    // is (l / 8) ^ (i & 1)).
-    const int lr = lane >> 3;
-    const uint32_t voff_e = (uint32_t)(lr * K + 16 * ((lane & 7) ^ lr));
-    const uint32_t voff_o = (uint32_t)(lr * K + 16 * ((lane & 7) ^ lr ^ 1));
+    // is (l / 8) ^ (i & 1)).  Recomputed at the top of every tile and before
+    // every request of a tile's first stages, so that they are never kept
+    // live (or spilled) across the epilogue: a spill reload there would wait
+    // for every load in flight.
+    uint32_t voff_e, voff_o;
+    auto set_voff = [&]() {
+        const int l = fresh_lane_id();
+        const int lr = l >> 3;
+        voff_e = (uint32_t)(lr * K + 16 * ((l & 7) ^ lr));
+        voff_o = (uint32_t)(lr * K + 16 * ((l & 7) ^ lr ^ 1));
+    };
     // Load instruction i (0..15) of a stage: rows 8i..8i+7 of this wave's
     // 128, starting at operand byte offset `base` (+ k0 along K).
     auto load_one = [&](int i, uint32_t base, uint32_t k0, uint32_t buf) {
@@ -1020,10 +1089,17 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // Output stores a tile leaves in flight past its last load request.
+    constexpr int NST = OUT == FP8_DTYPE_BF16 ? 32 : 16;
     // One stage: MFMAs on both K halves around the barrier.  DMA: issue the
-    // loads of stage k+2 (at `ld_k0`) into this stage's buffer; RD: read the
-    // next stage's first fragments.
-    auto stage = [&](uint32_t buf, bool dma, bool rd, uint32_t base, uint32_t ld_k0) {
+    // loads of stage k+2 (or of the next tile's stage 0, at `base` and
+    // `ld_k0`) into this stage's buffer; RD: read the next stage's first
+    // fragments.  WAIT, before the barrier: 0 = every load of this wave has
+    // landed (stage k+1 was requested last); 1 = the same, but the previous
+    // tile's NST output stores, the only memory instructions issued after
+    // stage k+1's loads, stay in flight; 2 = no wait (a tile's last stage:
+    // nothing of the tile is loading, only the next tile's first stage).
+    auto stage = [&](uint32_t buf, bool dma, bool rd, uint32_t base, uint32_t ld_k0, int wait) {
         const uint32_t nbuf = buf ^ STAGE;
 #pragma unroll
         for (int slot = 0; slot < 16; ++slot) {
@@ -1038,7 +1114,10 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         }
         // Stage k+1 has landed (own loads) and is visible (barrier); nobody
         // reads this stage's buffer any more.
-        wait_vmem_all();
+        if (wait == 0)
+            wait_vmem_all();
+        else if (wait == 1)
+            wait_vmem_but<NST>();
         __syncthreads();
 #pragma unroll
         for (int slot = 0; slot < 16; ++slot) {
@@ -1060,86 +1139,115 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         so_fold = scale_is_foldable(so);
     }
     uint32_t wkey = 0;                          // FP8 output: the wave's amax key
-    // Loads of tile r's stages 0 and 1 into buffers 0 and 1, and its bias.
-    auto issue_prologue = [&](int r) {
+    // Operand byte offset of this wave's 128 rows of tile r.
+    auto tile_base = [&](int r) {
         int tm, tn;
         tile_of_block(r, tiles_m, tiles_n, tm, tn);
-        const uint32_t base =
-            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+        return (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+    };
+    // Tile r's bias into bias slot `slot` (wave 0).
+    auto load_bias = [&](int r, int slot) {
         if constexpr (HAS_BIAS) {
             if (wave == 0) {
+                int tm, tn;
+                tile_of_block(r, tiles_m, tiles_n, tm, tn);
                 const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<uint16_t *>(bias), (short)0, 2 * N, 0x00020000);
-                dma_b128(brs, (uint32_t)(2 * tn * BN + 16 * lane), lds0 + 2 * STAGE);
+                dma_b128(brs, (uint32_t)(2 * tn * BN + 16 * fresh_lane_id()),
+                         lds0 + 2 * STAGE + 1024u * (uint32_t)slot);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) load_one(i, base, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) load_one(i, base, KS, STAGE);
     };
-    // Everything requested so far has landed (this also drains the previous
-    // tile's stores); stage 0's first fragments into registers.
-    auto finish_prologue = [&]() {
-        wait_vmem_all();
-        __syncthreads();
+    auto issue_stage = [&](uint32_t base, uint32_t k0, uint32_t buf) {
+        set_voff();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load_one(i, base, k0, buf);
+    };
+    // Stage 0's first fragments of the buffer `buf` into registers.
+    auto read_first = [&](uint32_t buf) {
 #pragma unroll
         for (int n = 0; n < 8; ++n)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) read_frag(0, n, h, 0);
+            for (int h = 0; h < 2; ++h) read_frag(0, n, h, buf);
     };
 
-    issue_prologue((int)blockIdx.x);
-    finish_prologue();
+    // The first tile: its bias and stages 0 and 1, waited for.
+    load_bias((int)blockIdx.x, 0);
+    issue_stage(tile_base((int)blockIdx.x), 0, 0);
+    issue_stage(tile_base((int)blockIdx.x), KS, STAGE);
+    wait_vmem_all();
+    __syncthreads();
+    read_first(0);
+
+    // Stages stream on across tiles: the buffer of a stage alternates with
+    // no reset at tile boundaries.  At the end of a tile, stage nk-2 requests
+    // the next tile's stage 0 (and its bias) into its freed buffer; stage
+    // nk-1's buffer, free after its barrier, stages the epilogue; once every
+    // wave has read the staging back, it receives the next tile's stage 1,
+    // and only then are the output stores issued.  The next tile waits for
+    // its stages with the NST stores still in flight; the first wait that
+    // needs a later load (stage 1's) also waits for them.
+    uint32_t buf = 0;
+    int slot = 0;
+    bool pend = false;                          // the previous tile's stores are in flight
     for (int r = (int)blockIdx.x; r < T; r += (int)gridDim.x) {
         int tm, tn;
+        set_voff();
         tile_of_block(r, tiles_m, tiles_n, tm, tn);
         const uint32_t base =
             (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
-        uint32_t buf = 0;
-        for (int k = 0; k + 2 < nk; ++k) {
-            stage(buf, true, true, base, (uint32_t)((k + 2) * KS));
-            buf ^= STAGE;
-        }
-        stage(buf, false, true, 0, 0);          // stage nk-2
-        buf ^= STAGE;
-        stage(buf, false, false, 0, 0);         // stage nk-1: LDS idle after its barrier
-
         const int rn = r + (int)gridDim.x;
         const bool more = rn < T;
+        const uint32_t nbase = more ? tile_base(rn) : 0u;
+        for (int k = 0; k + 2 < nk; ++k) {
+            stage(buf, true, true, base, (uint32_t)((k + 2) * KS), (k == 0 && pend) ? 1 : 0);
+            buf ^= STAGE;
+        }
+        stage(buf, more, true, nbase, 0, (nk == 2 && pend) ? 1 : 0);   // stage nk-2
+        if (more) load_bias(rn, slot ^ 1);
+        buf ^= STAGE;
+        stage(buf, false, false, 0, 0, 2);      // stage nk-1: its buffer is free after the barrier
+        const uint32_t sbuf = buf;              // staging; then the next tile's stage 1
+        buf ^= STAGE;                           // the next tile's stage 0
+
         const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
+        // The epilogue's per-lane addresses derive from a lane index read
+        // here, so the compiler cannot hoist them out of the tile loop (where
+        // they would be spilled and reloaded with a wait for every load).
+        const int el = fresh_lane_id();
+        uint8_t *stg = lds + sbuf + wave * 16384;
+        const uint8_t *bl = bias_lds + 1024 * slot + 2 * wn * WT;
         if constexpr (OUT == FP8_DTYPE_BF16) {
-            uint8_t *stg = lds + wave * 32768;
-            stage_wave_tile_bf16<HAS_BIAS>(acc, stg, bias_lds + 2 * wn * WT, lane, s);
             u32x4 rows_out[32];
-            read_staged_rows(stg, lane, rows_out);
+            stage_wave_half_bf16<0, HAS_BIAS>(acc, stg, bl, el, s);
+            read_staged_half<0>(stg, el, rows_out);
+            stage_wave_half_bf16<1, HAS_BIAS>(acc, stg, bl, el, s);
+            read_staged_half<1>(stg, el, rows_out);
             __syncthreads();                    // staging and bias read by every wave
-            if (more) issue_prologue(rn);
-            store_staged_rows(static_cast<uint16_t *>(Cv), rows_out, M, N, r0, cc0, lane);
+            if (more) issue_stage(nbase, KS, sbuf);
+            store_rows_bf16(out_rows_rsrc<2>(Cv, M, N, r0), rows_out, N, cc0, el);
         } else if constexpr (is_q_out<OUT>()) {
-            uint8_t *stg = lds + wave * 32768;
-            const uint32_t tk = stage_wave_tile_q<OUT, HAS_BIAS>(
-                acc, stg, bias_lds + 2 * wn * WT, lane, s, so, so_fold, M, r0);
+            const uint32_t tk = stage_wave_tile_q<OUT, HAS_BIAS>(acc, stg, bl, el, s, so,
+                                                                 so_fold, M, r0);
             wkey = max(wkey, wave_max_key(tk));
             u32x4 rows_out[16];
-            read_staged_rows_q(stg, lane, rows_out);
+            read_staged_rows_q(stg, el, rows_out);
             __syncthreads();                    // staging and bias read by every wave
-            if (more) issue_prologue(rn);
-            store_staged_rows_q(static_cast<uint8_t *>(Cv), rows_out, M, N, r0, cc0, lane);
+            if (more) issue_stage(nbase, KS, sbuf);
+            store_rows_q(out_rows_rsrc<1>(Cv, M, N, r0), rows_out, N, cc0, el);
         } else {
-            // fp32: four 32-row blocks through the wave's own 16 KiB of staging.
-            uint8_t *stg = lds + wave * 32768;
-            float *C = static_cast<float *>(Cv);
+            // fp32: four 32-row blocks through the wave's 16 KiB of staging.
+            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<4>(Cv, M, N, r0);
             u32x4 rows_out[16];
 #pragma unroll
             for (int i = 0; i < F; ++i) {
-                stage_wave_block_f32<HAS_BIAS>(acc, stg, bias_lds + 2 * wn * WT, lane, s, i);
-                read_staged_block_f32(stg, lane, rows_out);
+                stage_wave_block_f32<HAS_BIAS>(acc, stg, bl, el, s, i);
+                read_staged_block_f32(stg, el, rows_out);
                 if (i == F - 1) {
                     __syncthreads();            // staging and bias read by every wave
-                    if (more) issue_prologue(rn);
+                    if (more) issue_stage(nbase, KS, sbuf);
                 }
-                store_staged_block_f32(C, rows_out, M, N, r0 + 32 * i, cc0, lane);
+                store_block_f32(ors, rows_out, N, i, cc0, el);
             }
 #pragma unroll
             for (int i = 0; i < F; ++i)
@@ -1148,7 +1256,16 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
 #pragma unroll
                     for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         }
-        if (more) finish_prologue();
+        if (more) {
+            // The next tile's bias and stage 0 have landed (its stage 1, 16
+            // loads, and the NST stores may still be in flight; stage 0's
+            // middle waits for stage 1); its first fragments into registers.
+            wait_vmem_but<NST + 16>();
+            __syncthreads();
+            read_first(buf);
+        }
+        slot ^= 1;
+        pend = true;
     }
     if constexpr (is_q_out<OUT>())
         finish_q_out(wkey, qo, so, reinterpret_cast<uint32_t *>(lds), so_fold);
@@ -1187,7 +1304,7 @@ hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
                       const float *sb, const uint16_t *bias, void *C, const QOut &qo,
                       hipStream_t stream) {
     auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS>;
-    constexpr int lds_bytes = 2 * (256 + 256) * 128 + 1024;   // two 64 KiB stages, bias
+    constexpr int lds_bytes = 2 * (256 + 256) * 128 + 2048;   // two 64 KiB stages, 2 bias slots
     static bool attr_set[64];
     static int cu_count[64];
     int dev = 0;
@@ -1244,7 +1361,10 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
     // The large kernel addresses operands with 32-bit buffer offsets.
     // It also needs at least four 64-byte K stages.
     const bool fits32 = (M + 256) * K < ((int64_t)1 << 31) && (N + 256) * K < ((int64_t)1 << 31);
-    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256 && K % 128 == 0)
+    // The LDS-DMA kernel also addresses 128 output rows with 32-bit offsets.
+    constexpr int64_t out_bytes = OUT == FP8_DTYPE_BF16 ? 2 : (OUT == FP8_DTYPE_FP32 ? 4 : 1);
+    const bool out32 = 128 * N * out_bytes < ((int64_t)1 << 31);
+    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && out32 && K >= 256 && K % 128 == 0)
         return launch_dma<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
                                                  qo, stream);
     if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256)
