@@ -687,73 +687,57 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows_rsrc(void *C, int M, 
                                              (short)0, nrec, 0x00020000);
 }
 
-// bf16 epilogue of one wave's 128 x 128 tile through 16 KiB of LDS at
-// `stg`, in two passes of 64 rows.  stage_wave_half_bf16<P>: out(acc * s +
-// bias) of fragment row blocks 2P and 2P + 1 is written in the matrix-core
-// layout (8 bytes per lane, one output row per lane) into 64 staging rows of
-// 256 bytes whose 16-byte chunk c of row q sits at chunk c ^ (q & 15); the
-// bias of the wave's 128 columns is read from LDS (`bias_lds`, bf16, column
-// c0 first; zero past N).  Clears those accumulators.
-template <int P, bool HAS_BIAS>
-__device__ __forceinline__ void stage_wave_half_bf16(v16f (&acc)[4][4], uint8_t *stg,
-                                                     const uint8_t *bias_lds, int lane, float s) {
-    const int frow = lane & 31;
-    const int half = lane >> 5;
+// bf16 epilogue of one wave's 128 x 128 tile through LDS, one 32-row
+// fragment block i at a time: 32 staging rows of 272 bytes (256 + 16 of
+// padding, 8.5 KiB at `stg`).  With the padding every lane's LDS address is
+// one per-lane base plus a constant, and both the matrix-core-layout writes
+// and the row reads take the minimum number of LDS cycles (rows 16 apart
+// share banks only between the two halves of a write).
+// stage_block_bf16: out(acc * s + bias) of block i in the matrix-core layout
+// (8 bytes per lane: lane l holds row l % 32 and, per register group g of
+// fragment column block j, columns 32 j + 8 g + 4 (l / 32) .. +3).
+// `bias` holds those columns' bf16 bias values, packed in pairs (zero past
+// N, or none).
+template <bool HAS_BIAS>
+__device__ __forceinline__ void stage_block_bf16(const v16f (&acc)[4][4], uint8_t *stg,
+                                                 const u32x2 (&bias)[4][4], int lane,
+                                                 float s, int i) {
+    uint8_t *const w = stg + (lane & 31) * 272 + 8 * (lane >> 5);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (HAS_BIAS) {
-                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
-                    bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
-                bv[0] = __uint_as_float(b2.x << 16);
-                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-                bv[2] = __uint_as_float(b2.y << 16);
-                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
-            }
-            const int c = 4 * j + g;                     // 16-byte chunk of the staging row
+            const float bv[4] = {__uint_as_float(bias[j][g].x << 16),
+                                 __uint_as_float(bias[j][g].x & 0xFFFF0000u),
+                                 __uint_as_float(bias[j][g].y << 16),
+                                 __uint_as_float(bias[j][g].y & 0xFFFF0000u)};
+            float v[4];
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const int i = 2 * P + ii;
-                const int q = ii * 32 + frow;
-                const bf16x4 o = {(__bf16)(acc[i][j][4 * g + 0] * s + bv[0]),
-                                  (__bf16)(acc[i][j][4 * g + 1] * s + bv[1]),
-                                  (__bf16)(acc[i][j][4 * g + 2] * s + bv[2]),
-                                  (__bf16)(acc[i][j][4 * g + 3] * s + bv[3])};
-                *reinterpret_cast<bf16x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4) + 8 * half) = o;
-            }
+            for (int q = 0; q < 4; ++q)
+                v[q] = HAS_BIAS ? acc[i][j][4 * g + q] * s + bv[q] : acc[i][j][4 * g + q] * s;
+            const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            *reinterpret_cast<bf16x4 *>(w + 16 * (4 * j + g)) = o;
         }
     }
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[2 * P + ii][j][q] = 0.f;
 }
 
-// Read a staged half back, 16 lanes per 256-byte row: v[16 P + it] is tile
-// row 64 P + 4 it + lane / 16, columns 8 (lane % 16) .. +7.
-template <int P>
-__device__ __forceinline__ void read_staged_half(const uint8_t *stg, int lane, u32x4 (&v)[32]) {
-    const int c = lane & 15;
+// Read a staged bf16 block back, 16 lanes per 256-byte row: v[it] is row
+// 4 it + lane / 16 of the block, columns 8 (lane % 16) .. +7.
+__device__ __forceinline__ void read_block_bf16(const uint8_t *stg, int lane, u32x4 (&v)[8]) {
+    const uint8_t *const r = stg + (lane >> 4) * 272 + 16 * (lane & 15);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int q = 4 * it + (lane >> 4);
-        v[16 * P + it] = *reinterpret_cast<const u32x4 *>(stg + q * 256 + ((c ^ (q & 15)) << 4));
-    }
+    for (int it = 0; it < 8; ++it) v[it] = *reinterpret_cast<const u32x4 *>(r + it * 4 * 272);
 }
 
-// Store the rows of read_staged_half<0> and <1>: 32 instructions, each
-// writing four 256-byte row segments.
-__device__ __forceinline__ void store_rows_bf16(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[32],
-                                                int N, int c0, int lane) {
+// Store a block read by read_block_bf16 (tile rows 32 i .. 32 i + 31 of the
+// resource's 128): 8 instructions, each writing four 256-byte row segments.
+__device__ __forceinline__ void store_block_bf16(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[8],
+                                                 int N, int i, int c0, int lane) {
     const int gc = c0 + 8 * (lane & 15);
     const uint32_t cb = gc < N ? (uint32_t)gc * 2u : OUT_OOB;   // + row offset < 2^31
 #pragma unroll
-    for (int it = 0; it < 32; ++it) {
-        const int row = 4 * it + (lane >> 4);
+    for (int it = 0; it < 8; ++it) {
+        const int row = 32 * i + 4 * it + (lane >> 4);
         const uint32_t off = cb + (uint32_t)(row * N) * 2u;
         __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
     }
@@ -942,14 +926,19 @@ __device__ __forceinline__ void store_rows_q(__amdgpu_buffer_rsrc_t rs, const u3
 // stores alike on gfx9), so this waits for everything issued before them.
 template <int N>
 __device__ __forceinline__ void wait_vmem_but() {
-    static_assert(N == 16 || N == 32 || N == 48, "wait_vmem_but: unsupported count");
-    if constexpr (N == 16)
+    static_assert(N == 8 || N == 16 || N == 24 || N == 32, "wait_vmem_but: unsupported count");
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 16)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (N == 32)
-        asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    else if constexpr (N == 24)
+        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
     else
-        asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
 }
+
+// Wait until this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Lane index from an instruction the compiler cannot merge with others, so
 // that values derived from it are recomputed where they are used instead of
@@ -984,15 +973,19 @@ __device__ __forceinline__ int fresh_lane_id() {
 //     requests the next tile's stage 0 and bias (two 1 KiB bias slots past
 //     the stages); the epilogue stages each wave's output in its own 16 KiB
 //     quarter of the buffer freed by stage nk-1 and reads it back as whole
-//     row segments into the (now free) fragment registers: bf16 in two
-//     passes of 64 rows (256-byte segments), fp32 in four 32-row blocks
-//     (512-byte segments), FP8 codes in one pass (128-byte segments).  Then
-//     the next tile's stage 1 goes into that buffer, and only after it the
-//     output stores, as buffer stores that are always issued (the hardware
+//     row segments into the (now free) fragment registers: bf16 in four
+//     32-row blocks (256-byte segments, 16 bytes of row padding), fp32 in
+//     four 32-row blocks (512-byte segments), FP8 codes in one pass
+//     (128-byte segments).  Each block's stores go out as soon as it is
+//     read back, so they drain while the next block is converted.  That
+//     quarter is exactly what the wave's own stage loads fill, so once its
+//     staging reads have returned the wave requests the next tile's stage 1
+//     there, with no barrier, and issues its last block's stores after it.
+//     The stores are buffer stores that are always issued (the hardware
 //     drops the out-of-range ones).  Vector memory instructions of a wave
 //     complete in order, so the next tile waits with exact counts: for its
-//     stage 0 with stage 1 and the stores in flight, then at stage 0's
-//     middle for stage 1 with the stores in flight.
+//     stage 0 with stage 1 and the last stores in flight, then at stage 0's
+//     middle for stage 1 with those stores in flight.
 //   * The per-lane load offsets and epilogue addresses are recomputed where
 //     they are used, from a lane index the compiler cannot hoist: kept live
 //     across the loop they spill, and a spill reload waits for every load
@@ -1090,7 +1083,7 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Output stores a tile leaves in flight past its last load request.
-    constexpr int NST = OUT == FP8_DTYPE_BF16 ? 32 : 16;
+    constexpr int NST = OUT == FP8_DTYPE_BF16 ? 8 : 16;
     // One stage: MFMAs on both K halves around the barrier.  DMA: issue the
     // loads of stage k+2 (or of the next tile's stage 0, at `base` and
     // `ld_k0`) into this stage's buffer; RD: read the next stage's first
@@ -1217,22 +1210,47 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         const int el = fresh_lane_id();
         uint8_t *stg = lds + sbuf + wave * 16384;
         const uint8_t *bl = bias_lds + 1024 * slot + 2 * wn * WT;
+        // The staging quarter of the buffer is the one this wave's own
+        // stage loads fill, and no other wave reads it after stage nk-1's
+        // barrier: so the next tile's stage 1 is requested as soon as this
+        // wave's own staging reads have returned, with no barrier.
         if constexpr (OUT == FP8_DTYPE_BF16) {
-            u32x4 rows_out[32];
-            stage_wave_half_bf16<0, HAS_BIAS>(acc, stg, bl, el, s);
-            read_staged_half<0>(stg, el, rows_out);
-            stage_wave_half_bf16<1, HAS_BIAS>(acc, stg, bl, el, s);
-            read_staged_half<1>(stg, el, rows_out);
-            __syncthreads();                    // staging and bias read by every wave
-            if (more) issue_stage(nbase, KS, sbuf);
-            store_rows_bf16(out_rows_rsrc<2>(Cv, M, N, r0), rows_out, N, cc0, el);
+            // Four 32-row blocks; each block's stores drain while the next
+            // block is converted.
+            u32x2 bv[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    bv[j][g] = u32x2{0u, 0u};
+                    if constexpr (HAS_BIAS)
+                        bv[j][g] = *reinterpret_cast<const u32x2 *>(bl + 2 * (j * 32 + 8 * g + 4 * (el >> 5)));
+                }
+            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<2>(Cv, M, N, r0);
+            u32x4 rows_out[8];
+#pragma unroll
+            for (int i = 0; i < F; ++i) {
+                stage_block_bf16<HAS_BIAS>(acc, stg, bv, el, s, i);
+                read_block_bf16(stg, el, rows_out);
+                if (i == F - 1) {
+                    wait_lds_reads();
+                    if (more) issue_stage(nbase, KS, sbuf);
+                }
+                store_block_bf16(ors, rows_out, N, i, cc0, el);
+            }
+#pragma unroll
+            for (int i = 0; i < F; ++i)
+#pragma unroll
+                for (int j = 0; j < F; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         } else if constexpr (is_q_out<OUT>()) {
             const uint32_t tk = stage_wave_tile_q<OUT, HAS_BIAS>(acc, stg, bl, el, s, so,
                                                                  so_fold, M, r0);
             wkey = max(wkey, wave_max_key(tk));
             u32x4 rows_out[16];
             read_staged_rows_q(stg, el, rows_out);
-            __syncthreads();                    // staging and bias read by every wave
+            wait_lds_reads();
             if (more) issue_stage(nbase, KS, sbuf);
             store_rows_q(out_rows_rsrc<1>(Cv, M, N, r0), rows_out, N, cc0, el);
         } else {
@@ -1244,7 +1262,7 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
                 stage_wave_block_f32<HAS_BIAS>(acc, stg, bl, el, s, i);
                 read_staged_block_f32(stg, el, rows_out);
                 if (i == F - 1) {
-                    __syncthreads();            // staging and bias read by every wave
+                    wait_lds_reads();
                     if (more) issue_stage(nbase, KS, sbuf);
                 }
                 store_block_f32(ors, rows_out, N, i, cc0, el);
