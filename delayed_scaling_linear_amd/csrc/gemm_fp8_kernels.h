@@ -698,27 +698,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows_rsrc(void *C, int M, 
 // fragment column block j, columns 32 j + 8 g + 4 (l / 32) .. +3).
 // `bias` holds those columns' bf16 bias values, packed in pairs (zero past
 // N, or none).
+// stage_group_bf16 converts and writes register group g of fragment (i, j);
+// `w` is the lane's staging base, stg + (lane % 32) * 272 + 8 (lane / 32).
+template <bool HAS_BIAS>
+__device__ __forceinline__ void stage_group_bf16(const v16f (&acc)[4][4], uint8_t *w,
+                                                 const u32x2 (&bias)[4][4], float s, int i,
+                                                 int j, int g) {
+    const float bv[4] = {__uint_as_float(bias[j][g].x << 16),
+                         __uint_as_float(bias[j][g].x & 0xFFFF0000u),
+                         __uint_as_float(bias[j][g].y << 16),
+                         __uint_as_float(bias[j][g].y & 0xFFFF0000u)};
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        v[q] = HAS_BIAS ? acc[i][j][4 * g + q] * s + bv[q] : acc[i][j][4 * g + q] * s;
+    const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4 *>(w + 16 * (4 * j + g)) = o;
+}
+
 template <bool HAS_BIAS>
 __device__ __forceinline__ void stage_block_bf16(const v16f (&acc)[4][4], uint8_t *stg,
                                                  const u32x2 (&bias)[4][4], int lane,
                                                  float s, int i) {
     uint8_t *const w = stg + (lane & 31) * 272 + 8 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float bv[4] = {__uint_as_float(bias[j][g].x << 16),
-                                 __uint_as_float(bias[j][g].x & 0xFFFF0000u),
-                                 __uint_as_float(bias[j][g].y << 16),
-                                 __uint_as_float(bias[j][g].y & 0xFFFF0000u)};
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                v[q] = HAS_BIAS ? acc[i][j][4 * g + q] * s + bv[q] : acc[i][j][4 * g + q] * s;
-            const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            *reinterpret_cast<bf16x4 *>(w + 16 * (4 * j + g)) = o;
-        }
-    }
+        for (int g = 0; g < 4; ++g) stage_group_bf16<HAS_BIAS>(acc, w, bias, s, i, j, g);
 }
 
 // Read a staged bf16 block back, 16 lanes per 256-byte row: v[it] is row
@@ -1125,6 +1131,44 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
 
     const int nk = K / KS;                      // >= 2 (caller guarantees)
     const float s = (*sinv_a) * (*sinv_b);
+    // bf16 output: a tile's last stage, whose buffer the epilogue stages
+    // into.  Fragment block 0 is final after the second half's first four
+    // MFMAs, so its sixteen register groups are converted and written to
+    // the staging rows (`w`) between the remaining twelve, while the
+    // matrix cores still run.  The staging quarter is free once every wave
+    // has passed the stage's barrier.
+    auto last_stage_bf16 = [&](uint32_t buf, uint8_t *w, const u32x2 (&bv)[4][4]) {
+#pragma unroll
+        for (int slot = 0; slot < 16; ++slot) {
+            const int i = slot >> 2, j = slot & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[0][j], af[0][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            if (slot < 8) {
+                read_frag(1, slot, 0, buf);
+                read_frag(1, slot, 1, buf);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int slot = 0; slot < 16; ++slot) {
+            const int i = slot >> 2, j = slot & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[1][j], af[1][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            // Groups 0-7 two per slot in slots 4-7, groups 8-15 one per
+            // slot in slots 8-15; group n is (j, g) = (n / 4, n % 4), whose
+            // last MFMA went out in slot n / 4.
+            if (slot >= 4 && slot < 8) {
+                const int n = 2 * (slot - 4);
+                stage_group_bf16<HAS_BIAS>(acc, w, bv, s, 0, n >> 2, n & 3);
+                stage_group_bf16<HAS_BIAS>(acc, w, bv, s, 0, (n + 1) >> 2, (n + 1) & 3);
+            } else if (slot >= 8) {
+                const int n = slot;
+                stage_group_bf16<HAS_BIAS>(acc, w, bv, s, 0, n >> 2, n & 3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     float so = 0.f;
     bool so_fold = false;
     if constexpr (is_q_out<OUT>()) {
@@ -1199,25 +1243,15 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         stage(buf, more, true, nbase, 0, (nk == 2 && pend) ? 1 : 0);   // stage nk-2
         if (more) load_bias(rn, slot ^ 1);
         buf ^= STAGE;
-        stage(buf, false, false, 0, 0, 2);      // stage nk-1: its buffer is free after the barrier
         const uint32_t sbuf = buf;              // staging; then the next tile's stage 1
-        buf ^= STAGE;                           // the next tile's stage 0
-
-        const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
         // The epilogue's per-lane addresses derive from a lane index read
         // here, so the compiler cannot hoist them out of the tile loop (where
         // they would be spilled and reloaded with a wait for every load).
         const int el = fresh_lane_id();
         uint8_t *stg = lds + sbuf + wave * 16384;
         const uint8_t *bl = bias_lds + 1024 * slot + 2 * wn * WT;
-        // The staging quarter of the buffer is the one this wave's own
-        // stage loads fill, and no other wave reads it after stage nk-1's
-        // barrier: so the next tile's stage 1 is requested as soon as this
-        // wave's own staging reads have returned, with no barrier.
+        [[maybe_unused]] u32x2 bv[4][4];
         if constexpr (OUT == FP8_DTYPE_BF16) {
-            // Four 32-row blocks; each block's stores drain while the next
-            // block is converted.
-            u32x2 bv[4][4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -1226,11 +1260,25 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
                     if constexpr (HAS_BIAS)
                         bv[j][g] = *reinterpret_cast<const u32x2 *>(bl + 2 * (j * 32 + 8 * g + 4 * (el >> 5)));
                 }
+            last_stage_bf16(buf, stg + (el & 31) * 272 + 8 * (el >> 5), bv);   // stage nk-1
+        } else {
+            stage(buf, false, false, 0, 0, 2);  // stage nk-1: its buffer is free after the barrier
+        }
+        buf ^= STAGE;                           // the next tile's stage 0
+
+        const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
+        // The staging quarter of the buffer is the one this wave's own
+        // stage loads fill, and no other wave reads it after stage nk-1's
+        // barrier: so the next tile's stage 1 is requested as soon as this
+        // wave's own staging reads have returned, with no barrier.
+        if constexpr (OUT == FP8_DTYPE_BF16) {
+            // Four 32-row blocks (block 0 was staged inside the last stage);
+            // each block's stores drain while the next block is converted.
             const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<2>(Cv, M, N, r0);
             u32x4 rows_out[8];
 #pragma unroll
             for (int i = 0; i < F; ++i) {
-                stage_block_bf16<HAS_BIAS>(acc, stg, bv, el, s, i);
+                if (i > 0) stage_block_bf16<HAS_BIAS>(acc, stg, bv, el, s, i);
                 read_block_bf16(stg, el, rows_out);
                 if (i == F - 1) {
                     wait_lds_reads();
