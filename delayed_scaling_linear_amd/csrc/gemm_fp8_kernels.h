@@ -40,6 +40,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "fp8_codec.h"
 #include "fp8dsl_internal.h"
@@ -754,7 +755,7 @@ __device__ __forceinline__ void store_block_bf16(__amdgpu_buffer_rsrc_t rs, cons
 // of row q at chunk c ^ (q & 15).  Lane l holds row (l % 32) of the block
 // and, per register group g of fragment column block j, the four columns
 // 32 j + 8 g + 4 (l / 32) .. +3, i.e. chunk 8 j + 2 g + l / 32.  Bias as in
-// stage_wave_tile_bf16.
+// stage_block_bf16.
 template <bool HAS_BIAS>
 __device__ __forceinline__ void stage_wave_block_f32(const v16f (&acc)[4][4], uint8_t *stg,
                                                      const uint8_t *bias_lds, int lane, float s,
@@ -814,7 +815,8 @@ __device__ __forceinline__ void store_block_f32(__amdgpu_buffer_rsrc_t rs, const
 // Lane l holds row (l % 32) of fragment row block i and, per register group
 // g of fragment column block j, the four columns 32 j + 8 g + 4 (l / 32) ..
 // +3: one code word at byte 16 (2 j + g / 2) + 8 (g % 2) + 4 (l / 32) of its
-// row.  Bias as in stage_wave_tile_bf16.  Clears the accumulators.
+// row.  Bias as in stage_block_bf16.  The accumulators are left as they are
+// (the next tile's first MFMAs start from zero).
 //   fold: t = acc * (s * so) + bias * so, the scaled value itself, is clamped
 //     and converted, and the amax keys are of |t| (the caller divides by
 //     |so| once at the end).  Otherwise t = v = acc * s + bias and the encode
@@ -831,7 +833,7 @@ __device__ __forceinline__ void store_block_f32(__amdgpu_buffer_rsrc_t rs, const
 // path of the group of four that holds it (or, unfolded, always: the scale
 // itself may make NaN products).
 template <int OUT, bool HAS_BIAS>
-__device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t *stg,
+__device__ __forceinline__ uint32_t stage_wave_tile_q(const v16f (&acc)[4][4], uint8_t *stg,
                                                       const uint8_t *bias_lds, int lane, float s,
                                                       float so, bool fold, int M, int r0) {
     constexpr int FMT = q_fmt<OUT>();
@@ -884,12 +886,6 @@ __device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         if (r0 + i * 32 + frow < M) key = max(key, max((uint32_t)kpos[i], kneg[i] & 0x7FFFFFFFu));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
     return key;
 }
 
@@ -1098,19 +1094,35 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     // tile's NST output stores, the only memory instructions issued after
     // stage k+1's loads, stay in flight; 2 = no wait (a tile's last stage:
     // nothing of the tile is loading, only the next tile's first stage).
-    auto stage = [&](uint32_t buf, bool dma, bool rd, uint32_t base, uint32_t ld_k0, int wait) {
-        const uint32_t nbuf = buf ^ STAGE;
+    // FIRST: the tile's first stage (see first_half).
+    // First half of a stage: 16 MFMAs on the first K half's fragments, with
+    // the reads of the second half's.  ZERO (a tile's first stage): the
+    // MFMAs start from zero instead of the accumulators, so the epilogue
+    // never clears them.
+    auto first_half = [&](uint32_t buf, auto zero) {
 #pragma unroll
         for (int slot = 0; slot < 16; ++slot) {
             const int i = slot >> 2, j = slot & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[0][j], af[0][i], acc[i][j], FB, FA, 0, 0, 0, 0);
+            if constexpr (decltype(zero)::value)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf[0][j], af[0][i], v16f{}, FB, FA, 0, 0, 0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf[0][j], af[0][i], acc[i][j], FB, FA, 0, 0, 0, 0);
             if (slot < 8) {
                 read_frag(1, slot, 0, buf);
                 read_frag(1, slot, 1, buf);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    auto stage = [&](uint32_t buf, bool dma, bool rd, uint32_t base, uint32_t ld_k0, int wait,
+                     bool first) {
+        const uint32_t nbuf = buf ^ STAGE;
+        if (first)
+            first_half(buf, std::true_type{});
+        else
+            first_half(buf, std::false_type{});
         // Stage k+1 has landed (own loads) and is visible (barrier); nobody
         // reads this stage's buffer any more.
         if (wait == 0)
@@ -1138,17 +1150,7 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     // matrix cores still run.  The staging quarter is free once every wave
     // has passed the stage's barrier.
     auto last_stage_bf16 = [&](uint32_t buf, uint8_t *w, const u32x2 (&bv)[4][4]) {
-#pragma unroll
-        for (int slot = 0; slot < 16; ++slot) {
-            const int i = slot >> 2, j = slot & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[0][j], af[0][i], acc[i][j], FB, FA, 0, 0, 0, 0);
-            if (slot < 8) {
-                read_frag(1, slot, 0, buf);
-                read_frag(1, slot, 1, buf);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        first_half(buf, std::false_type{});   // stage nk-1 >= 1 is never a tile's first
         __syncthreads();
 #pragma unroll
         for (int slot = 0; slot < 16; ++slot) {
@@ -1237,10 +1239,10 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         const bool more = rn < T;
         const uint32_t nbase = more ? tile_base(rn) : 0u;
         for (int k = 0; k + 2 < nk; ++k) {
-            stage(buf, true, true, base, (uint32_t)((k + 2) * KS), (k == 0 && pend) ? 1 : 0);
+            stage(buf, true, true, base, (uint32_t)((k + 2) * KS), (k == 0 && pend) ? 1 : 0, k == 0);
             buf ^= STAGE;
         }
-        stage(buf, more, true, nbase, 0, (nk == 2 && pend) ? 1 : 0);   // stage nk-2
+        stage(buf, more, true, nbase, 0, (nk == 2 && pend) ? 1 : 0, nk == 2);   // stage nk-2
         if (more) load_bias(rn, slot ^ 1);
         buf ^= STAGE;
         const uint32_t sbuf = buf;              // staging; then the next tile's stage 1
@@ -1262,7 +1264,7 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
                 }
             last_stage_bf16(buf, stg + (el & 31) * 272 + 8 * (el >> 5), bv);   // stage nk-1
         } else {
-            stage(buf, false, false, 0, 0, 2);  // stage nk-1: its buffer is free after the barrier
+            stage(buf, false, false, 0, 0, 2, false);   // stage nk-1: its buffer is free after the barrier
         }
         buf ^= STAGE;                           // the next tile's stage 0
 
@@ -1286,12 +1288,6 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
                 }
                 store_block_bf16(ors, rows_out, N, i, cc0, el);
             }
-#pragma unroll
-            for (int i = 0; i < F; ++i)
-#pragma unroll
-                for (int j = 0; j < F; ++j)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         } else if constexpr (is_q_out<OUT>()) {
             const uint32_t tk = stage_wave_tile_q<OUT, HAS_BIAS>(acc, stg, bl, el, s, so,
                                                                  so_fold, M, r0);
@@ -1315,12 +1311,6 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
                 }
                 store_block_f32(ors, rows_out, N, i, cc0, el);
             }
-#pragma unroll
-            for (int i = 0; i < F; ++i)
-#pragma unroll
-                for (int j = 0; j < F; ++j)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         }
         if (more) {
             // The next tile's bias and stage 0 have landed (its stage 1, 16
