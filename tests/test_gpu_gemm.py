@@ -181,6 +181,8 @@ def test_large_path_tails_sampled(M, N, K):
     (4096, 4352, 640, 1, 1, "fp32"),     # fp32 output, five stages
     (8192, 4096, 256, 0, 0, "bf16"),     # two stages per tile, two tiles per workgroup
     (8192, 4096, 256, 1, 0, "fp32"),     # the same with fp32 output
+    (8200, 4104, 256, 1, 1, "bf16"),     # two stages, ragged M and N, 2-3 tiles per workgroup
+    (4104, 8200, 256, 0, 1, "fp32"),     # the same with fp32 output
 ])
 def test_dma_path_rows_and_columns(M, N, K, fa, fb, out):
     """K % 128 == 0 at large M x N: whole output rows and columns at fragment
