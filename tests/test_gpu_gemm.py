@@ -212,3 +212,40 @@ def test_dma_path_rows_and_columns(M, N, K, fa, fb, out):
         ref = oracle.gemm_nt_sampled(A.numpy(), fa, B.numpy(), fb, sa, sb, r, c,
                                      out_kind=oracle.OUT_FP32)
         assert_gemm_close(f32(y)[r, c].astype(np.float64), ref.astype(np.float64), f"dma {M}x{N}x{K}")
+
+
+def test_dma_path_repeats_bit_identically():
+    """The large-tile kernel streams each workgroup's stages across tile
+    boundaries and waits on exact counts of memory instructions in flight.
+    A wait that released too early would read stale stage data; that shows
+    as outputs that change from call to call.  Five calls of the
+    8192x8192x2048 forward (four tiles per workgroup) and of an fp32-output
+    product with two-stage tiles must give identical bits, and the first
+    must match the oracle on sampled outputs."""
+    M, N, K = 8192, 8192, 2048
+    A = workloads.random_fp8_codes((M, K), 31, 0)
+    B = workloads.random_fp8_codes((N, K), 32, 0)
+    bias = _bias(N, 33)
+    sa, sb = np.float32(1 / 448.0), np.float32(1 / 3.0)
+    fa_, fb_ = _f8(A, 0, float(sa)), _f8(B, 0, float(sb))
+    bd = bias.to(DEV)
+    ys = [torch.empty(M, N, dtype=torch.bfloat16, device=DEV) for _ in range(5)]
+    for y in ys:
+        dsl.fp8_linear_fwd(fa_, fb_, bd, y)
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16)), "fwd output changed between calls"
+    rng = np.random.default_rng(3)
+    r, c = rng.integers(0, M, 1500), rng.integers(0, N, 1500)
+    ref = oracle.gemm_nt_sampled(A.numpy(), 0, B.numpy(), 0, sa, sb, r, c, bias=bits16(bias))
+    assert_gemm_close(bf16_values(bits16(ys[0]))[r, c], bf16_values(ref), "fwd repeat sampled")
+
+    Mw, Nw, Kw = 4104, 8200, 256           # wgrad-style fp32 output, two stages per tile
+    A2 = workloads.random_fp8_codes((Mw, Kw), 34, 1)
+    B2 = workloads.random_fp8_codes((Nw, Kw), 35, 0)
+    outs = [torch.empty(Mw, Nw, dtype=torch.float32, device=DEV) for _ in range(5)]
+    for o in outs:
+        dsl.fp8_linear_wgrad(_f8(A2, 1, 0.5, transpose_only=True), _f8(B2, 0, 0.25, transpose_only=True), o)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), "fp32 output changed between calls"
