@@ -153,6 +153,7 @@ def _sampled_case(M, N, K, fa, fb, fo, seed, with_bias=True, pow2=False):
     (4096, 4096, 256, 0, 0, oracle.E4M3),      # DMA path, two K stages per tile
     (4104, 4112, 384, 1, 0, oracle.E5M2),      # DMA path, ragged M and N
     (8200, 2064, 2048, 0, 1, oracle.E4M3),     # DMA path, several tiles per workgroup
+    (8200, 4112, 256, 1, 1, oracle.E5M2),      # DMA path, two stages, ragged, 2-3 tiles per workgroup
     (4104, 4112, 272, 0, 0, oracle.E4M3),      # register-staged path (K tail)
     (8192, 8192, 2048, 0, 0, oracle.E4M3),     # the toy-block MLP shape
 ])
