@@ -19,10 +19,11 @@ of the pages it follows:
 * ``dbias`` -- the bias gradient (column sums of the output gradient) that the
   training loop of "CPU Overhead of te.Linear FP8 Layers" needs for its biased
   linears (fp32, exact fp64 sum rounded once).
-* ``produce_cast`` -- the toy block's elementwise producers (``shift * x /
-  scale`` with its nan_to_num, the residual add, and the residual add of two
-  terms, each sum rounded) rounded to bf16 and followed by the cast ("CPU
-  Overhead of te.Linear FP8 Layers").
+* ``produce_cast`` -- the toy block's elementwise producers (the modulation,
+  a product divided by a quotient of the modulation linear's outputs, with
+  nothing sanitised; the residual add; and the residual add of two terms, each
+  sum rounded) rounded to bf16 and followed by the cast ("CPU Overhead of
+  te.Linear FP8 Layers", TEBlock.forward).
 * ``dynamic_cast`` -- dynamic scaling, the comparator the float8 all-gather
   page contrasts delayed scaling with (amax of the tensor itself, then the
   cast with fp8_max / amax).

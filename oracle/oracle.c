@@ -229,19 +229,23 @@ int orc_dbias(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, fl
 /*
  * Producer-fused cast: the elementwise operation that produces a linear's
  * input in the toy block of "CPU Overhead of te.Linear FP8 Layers"
- * (reproduction script: x = shift * x / scale after the modulation linear,
- * and the residual adds x = x + ...), rounded to bf16, followed by the cast of
- * its result.  All arithmetic in fp32, as torch does for bf16 tensors:
+ * (reproduction script, TEBlock.forward: the modulation multiplies the block
+ * input by one column slice of the modulation linear's output and divides it
+ * by another; the residual adds put linear outputs back onto the stream),
+ * rounded to bf16, followed by the cast of its result.  All arithmetic in
+ * fp32, as torch does for bf16 tensors:
  *   op 1 (modulate): y = bf16(a * x / b), one multiply then one correctly
- *        rounded division, round to nearest even; then an infinite or NaN y
- *        becomes +0 (the torch.nan_to_num that follows in that script);
+ *        rounded division, round to nearest even.  Nothing is sanitised: a
+ *        zero divisor gives +-inf, 0/0 gives NaN, a quotient beyond the bf16
+ *        range rounds to +-inf; a NaN result is written as 0x7FC0;
  *   op 2 (residual add): y = bf16(x + a); a NaN result is 0x7FC0;
- *   op 3 (two residual terms, the block's x = x + attn_q + attn_k[:, :H]):
- *        y = bf16(bf16(x + a) + b), the two bf16 adds torch performs one
- *        after the other, each rounded; a NaN at either step is 0x7FC0.
+ *   op 3 (residual add of two terms, as the block adds the cross-attention
+ *        outputs): y = bf16(bf16(x + a) + b), the two bf16 adds torch performs
+ *        one after the other, each rounded; a NaN at either step is 0x7FC0.
  * x, a, b are bf16 [rows, cols] with leading dimensions ldx, lda, ldb (b is
  * read by ops 1 and 3); y is bf16 [rows, cols], row-major.  The cast is then
- * exactly orc_cast_transpose_amax of y.  Returns 0, or -1 for a bad argument.
+ * exactly orc_cast_transpose_amax of y (so +-inf saturates to +-max and NaN
+ * becomes 0x7F with its sign).  Returns 0, or -1 for a bad argument.
  */
 static uint16_t orc_f32_to_bf16_canon(float f) {
     if (isnan(f)) return 0x7FC0;
@@ -263,9 +267,7 @@ int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, 
             if (op == 1) {
                 float bv = orc_bf16_to_f32(b[r * ldb + c]);
                 float prod = av * xv;
-                float v = prod / bv;
-                out = orc_f32_to_bf16_canon(v);
-                if ((out & 0x7F80u) == 0x7F80u) out = 0x0000;   /* inf or NaN -> +0 */
+                out = orc_f32_to_bf16_canon(prod / bv);
             } else if (op == 2) {
                 out = orc_f32_to_bf16_canon(xv + av);
             } else {
