@@ -46,7 +46,6 @@ DTYPE_FP32 = 1
 PRODUCE_MODULATE = 1
 PRODUCE_ADD = 2
 PRODUCE_ADD2 = 3
-FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libfp8dsl.so")
@@ -136,6 +135,19 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, what: str = "tensor") -> Optiona
     return t.data_ptr()
 
 
+def _need_shape(t: Optional[torch.Tensor], shape, what: str) -> None:
+    """The C ABI trusts the sizes it is given: a tensor smaller than the call
+    assumes would be read or written out of bounds on the device, so every
+    extent is checked here before the call."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_scalar(t: Optional[torch.Tensor], what: str) -> None:
+    if t is not None and t.numel() < 1:
+        raise ValueError(f"{what} must have at least one element")
+
+
 def _row_stride(t: torch.Tensor) -> int:
     """Row stride (elements) of a 2-D source.  torch gives an empty tensor an
     arbitrary stride; no memory is read for it, so its column count is
@@ -171,6 +183,13 @@ class Float8Tensor:
         return Float8Tensor(d, dt, si, fmt, rows, cols)
 
     def desc(self) -> _Desc:
+        if self.rows < 0 or self.cols < 0:
+            raise ValueError("Float8Tensor: negative size")
+        _need_shape(self.data, (self.rows, self.cols), "Float8Tensor.data")
+        _need_shape(self.data_t, (self.cols, self.rows), "Float8Tensor.data_t")
+        if self.scale_inv is None:
+            raise ValueError("Float8Tensor.scale_inv is required")
+        _need_scalar(self.scale_inv, "Float8Tensor.scale_inv")
         return _Desc(_ptr(self.data, torch.uint8, "data"), _ptr(self.data_t, torch.uint8, "data_t"),
                      _ptr(self.scale_inv, torch.float32, "scale_inv"), self.fmt, 0, self.rows,
                      self.cols)
@@ -200,6 +219,8 @@ class DelayedScalingState:
 def fp8_scale_update(amax_history: torch.Tensor, amax_cur: torch.Tensor, scale: torch.Tensor,
                      scale_inv: torch.Tensor, fmt: torch.Tensor, margin: int = 0, algo: int = 0,
                      stream=None) -> None:
+    if amax_history.dim() != 2:
+        raise ValueError("amax_history must be [T, H]")
     T, H = amax_history.shape
     for t, n in ((amax_cur, "amax_cur"), (scale, "scale"), (scale_inv, "scale_inv"), (fmt, "fmt")):
         if t.numel() != T:
@@ -219,6 +240,9 @@ def fp8_cast_transpose_amax(x: torch.Tensor, scale: torch.Tensor, out: Float8Ten
 
     `scale` and `amax_cur` are 1-element fp32 device tensors (views into a
     DelayedScalingState are fine)."""
+    _need_scalar(scale, "scale")
+    _need_scalar(amax_cur, "amax_cur")
+    _need_scalar(noop_flag, "noop_flag")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride in the last dimension")
     if x.dtype == torch.bfloat16:
@@ -252,6 +276,9 @@ def fp8_cast_transpose_amax_dbias(x: torch.Tensor, scale: torch.Tensor, out: Flo
     """fp8_cast_transpose_amax plus dbias [cols] (fp32) = column sums of x.
     `workspace` is a device uint8 tensor of at least
     fp8_cast_dbias_workspace_bytes(rows, cols) bytes."""
+    _need_scalar(scale, "scale")
+    _need_scalar(amax_cur, "amax_cur")
+    _need_scalar(noop_flag, "noop_flag")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride in the last dimension")
     if x.dtype == torch.bfloat16:
@@ -278,11 +305,14 @@ def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
                                     scale: torch.Tensor, out: Float8Tensor,
                                     amax_cur: Optional[torch.Tensor] = None,
                                     noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
-    """y = op(x, a, b) in bf16 (PRODUCE_MODULATE: a * x / b with inf/NaN -> 0;
-    PRODUCE_ADD: x + a; PRODUCE_ADD2: (x + a) + b, each sum rounded), then y
-    cast into `out`.  x, a, b: bf16 2-D device
+    """y = op(x, a, b) in bf16 (PRODUCE_MODULATE: a * x / b, unsanitised, so a
+    zero divisor gives +-inf and 0/0 NaN; PRODUCE_ADD: x + a; PRODUCE_ADD2:
+    (x + a) + b, each sum rounded), then y cast into `out`.  x, a, b: bf16 2-D device
     tensors of one shape with unit column stride (column slices are fine);
     y: contiguous bf16 of that shape."""
+    _need_scalar(scale, "scale")
+    _need_scalar(amax_cur, "amax_cur")
+    _need_scalar(noop_flag, "noop_flag")
     ins = [x, a] + ([b] if b is not None else [])
     for t in ins + [y]:
         if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
@@ -306,6 +336,11 @@ def fp8_cast_transpose_dynamic(x: torch.Tensor, scale: torch.Tensor, out: Float8
     """Dynamic scaling: amax of x, scale = fp8_max / (amax * 2^margin) (scale
     keeps its value for a zero or non-finite amax), then the cast into `out`.
     `scale` (in/out) and `amax` (out) are 1-element fp32 device tensors."""
+    _need_scalar(scale, "scale")
+    if amax is None:
+        raise ValueError("amax is required")
+    _need_scalar(amax, "amax")
+    _need_scalar(noop_flag, "noop_flag")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride in the last dimension")
     if x.dtype == torch.bfloat16:
@@ -326,6 +361,8 @@ def fp8_cast_transpose_dynamic(x: torch.Tensor, scale: torch.Tensor, out: Float8
 def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],
                    y: torch.Tensor, stream=None) -> None:
     """y [M, N] bf16 = x.data [M, K] . w.data [N, K]^T * sinv + bias."""
+    _need_shape(y, (x.rows, w.rows), "y")
+    _need_shape(bias, (w.rows,), "bias")
     dx, dw = x.desc(), w.desc()
     _check(lib().fp8_linear_fwd(ctypes.byref(dx), ctypes.byref(dw),
                                 _ptr(bias, torch.bfloat16, "bias"), _ptr(y, torch.bfloat16, "y"),
@@ -338,6 +375,9 @@ def fp8_linear_fwd_fp8out(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch
     """y.data [M, N] FP8 codes = the cast (scale_y) of v = x.data . w.data^T *
     sinv + bias in fp32; amax_y folds in max|v|; y.scale_inv = 1 / scale_y.
     y must have no transpose buffer."""
+    _need_shape(bias, (w.rows,), "bias")
+    _need_scalar(scale_y, "scale_y")
+    _need_scalar(amax_y, "amax_y")
     dx, dw, dy = x.desc(), w.desc(), y.desc()
     _check(lib().fp8_linear_fwd_fp8out(ctypes.byref(dx), ctypes.byref(dw),
                                        _ptr(bias, torch.bfloat16, "bias"),
@@ -348,6 +388,7 @@ def fp8_linear_fwd_fp8out(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch
 
 def fp8_linear_dgrad(dy: Float8Tensor, w: Float8Tensor, dx: torch.Tensor, stream=None) -> None:
     """dx [M, K] bf16 = dy.data [M, N] . w.data_t [K, N]^T * sinv."""
+    _need_shape(dx, (dy.rows, w.cols), "dx")
     d1, d2 = dy.desc(), w.desc()
     _check(lib().fp8_linear_dgrad(ctypes.byref(d1), ctypes.byref(d2),
                                   _ptr(dx, torch.bfloat16, "dx"), _stream(stream)),
@@ -362,6 +403,7 @@ def fp8_linear_wgrad(dy: Float8Tensor, x: Float8Tensor, dw: torch.Tensor, stream
         od = DTYPE_BF16
     else:
         raise TypeError("dw must be fp32 or bf16")
+    _need_shape(dw, (dy.cols, x.cols), "dw")
     d1, d2 = dy.desc(), x.desc()
     _check(lib().fp8_linear_wgrad(ctypes.byref(d1), ctypes.byref(d2), _ptr(dw, None, "dw"), od,
                                   _stream(stream)), "fp8_linear_wgrad")

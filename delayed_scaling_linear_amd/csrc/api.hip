@@ -17,20 +17,15 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_fmt(int32_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 
-// The current device must be a gfx950 (checked once per device).
-int check_device() {
-    static int state[64];   // 0 unknown, 1 good, 2 bad
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8_ERR_DEVICE;
-    if (state[dev] == 0) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8_ERR_DEVICE;
-        state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    }
-    return state[dev] == 1 ? FP8_OK : FP8_ERR_DEVICE;
+// A launch on a device this library has no code object for (anything but a
+// gfx950) fails in the runtime; that is reported as FP8_ERR_DEVICE.
+int status_of(hipError_t e) {
+    if (e == hipSuccess) return FP8_OK;
+    if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction ||
+        e == hipErrorInvalidImage || e == hipErrorInvalidDevice || e == hipErrorNoDevice)
+        return FP8_ERR_DEVICE;
+    return FP8_ERR_LAUNCH;
 }
-
-int status_of(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 // Shared checks of one GEMM: A [M, K], B [N, K], C [M, N].
 int check_gemm(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
@@ -71,6 +66,40 @@ int check_cast(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t l
 
 }  // namespace
 
+namespace fp8dsl {
+
+hipError_t current_cu_count(int *cu_count) {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (n <= 0) return hipErrorInvalidDevice;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    *cu_count = n;
+    return hipSuccess;
+}
+
+hipError_t enable_dynamic_lds(const void *kernel, int lds_bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    const uint64_t bit = uint64_t(1) << dev;
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+
+}  // namespace fp8dsl
+
 extern "C" {
 
 int fp8_abi_version(void) { return FP8DSL_ABI_VERSION; }
@@ -84,7 +113,7 @@ const char *fp8_status_string(int status) {
         case FP8_ERR_FORMAT: return "FP8_ERR_FORMAT: FP8 format not accepted here";
         case FP8_ERR_ARG: return "FP8_ERR_ARG: argument out of range";
         case FP8_ERR_LAUNCH: return "FP8_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
-        case FP8_ERR_DEVICE: return "FP8_ERR_DEVICE: the current device is not a gfx950 GPU";
+        case FP8_ERR_DEVICE: return "FP8_ERR_DEVICE: no gfx950 code object for the current device";
         default: return "unknown fp8dsl status";
     }
 }
@@ -97,7 +126,6 @@ int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *
         return FP8_ERR_ARG;
     if (T == 0) return FP8_OK;
     if (!amax_history || !amax_cur || !scale || !scale_inv || !fmt) return FP8_ERR_NULL;
-    if (int d = check_device()) return d;
     return status_of(launch_scale_update(amax_history, amax_cur, scale, scale_inv, fmt, T, H,
                                          margin, static_cast<hipStream_t>(stream)));
 }
@@ -109,7 +137,6 @@ int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t co
     const bool empty = (rows == 0 || cols == 0);
     // Nothing to cast in an empty tensor; the scale-inverse snapshot is still taken.
     if (empty && out->scale_inv == nullptr) return FP8_OK;
-    if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (empty) return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
     return status_of(launch_cast_transpose_amax(x, src, rows, cols, ld, scale, out->fmt,
@@ -138,7 +165,6 @@ int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int6
         if (!aligned16(workspace)) return FP8_ERR_ALIGN;
     }
     if (cols == 0 && out->scale_inv == nullptr) return FP8_OK;
-    if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (empty) {
         // No rows: the bias gradient is zero; the scale-inverse snapshot is still taken.
@@ -176,7 +202,6 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
     if ((x && !aligned16(x)) || (a && !aligned16(a)) || (reads_b && b && !aligned16(b)))
         return FP8_ERR_ALIGN;
     if (empty && out->scale_inv == nullptr) return FP8_OK;
-    if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (empty) return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
     return status_of(launch_produce_cast(op, x, ldx, a, lda, reads_b ? b : nullptr, ldb, y, rows,
@@ -190,7 +215,6 @@ int fp8_cast_transpose_dynamic(const void *x, int32_t src, int64_t rows, int64_t
     if (int e = check_cast(x, src, rows, cols, ld, scale, out)) return e;
     if (margin < -126 || margin > 126) return FP8_ERR_ARG;
     if (amax == nullptr) return FP8_ERR_NULL;
-    if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // amax of x and the scale derived from it, then the ordinary cast with
     // that scale (no amax accumulation: the amax is already known).
@@ -215,7 +239,6 @@ int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t 
     if (int e = check_gemm(x->data, w->data, M, N, K, x->scale_inv, w->scale_inv, y, 8)) return e;
     if (M == 0 || N == 0) return FP8_OK;
     if (bias && !aligned16(bias)) return FP8_ERR_ALIGN;
-    if (int d = check_device()) return d;
     return status_of(launch_gemm_nt(x->data, x->fmt, w->data, w->fmt, M, N, K, x->scale_inv,
                                     w->scale_inv, bias, FP8_DTYPE_BF16, y,
                                     static_cast<hipStream_t>(stream)));
@@ -231,7 +254,6 @@ int fp8_linear_fwd_fp8out(const fp8_tensor_t *x, const fp8_tensor_t *w, const ui
     if (w->cols != K || y->rows != M || y->cols != N) return FP8_ERR_SHAPE;
     if (int e = check_gemm(x->data, w->data, M, N, K, x->scale_inv, w->scale_inv, y->data, 16))
         return e;
-    if (int d = check_device()) return d;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M == 0 || N == 0) {
         // No output: the amax is untouched; the snapshot is still taken.
@@ -254,7 +276,6 @@ int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx
     if (int e = check_gemm(dy->data, w->data_t, M, K, N, dy->scale_inv, w->scale_inv, dx, 8))
         return e;
     if (M == 0 || K == 0) return FP8_OK;
-    if (int d = check_device()) return d;
     return status_of(launch_gemm_nt(dy->data, dy->fmt, w->data_t, w->fmt, M, K, N, dy->scale_inv,
                                     w->scale_inv, nullptr, FP8_DTYPE_BF16, dx,
                                     static_cast<hipStream_t>(stream)));
@@ -272,7 +293,6 @@ int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, in
                            out_dtype == FP8_DTYPE_BF16 ? 8 : 4))
         return e;
     if (N == 0 || K == 0) return FP8_OK;
-    if (int d = check_device()) return d;
     return status_of(launch_gemm_nt(dy->data_t, dy->fmt, x->data_t, x->fmt, N, K, M,
                                     dy->scale_inv, x->scale_inv, nullptr, out_dtype, dw,
                                     static_cast<hipStream_t>(stream)));

@@ -379,22 +379,15 @@ hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
                           const float *scale, uint8_t *q, uint8_t *qt, float *amax_cur,
                           float *scale_inv_out, const int32_t *noop, float *dbias_ws,
                           int64_t ws_ld, hipStream_t stream) {
-    static int cu_count[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cu_count[dev] == 0) {
-        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-    }
+    int cus = 0;
+    if (hipError_t e = current_cu_count(&cus)) return e;
     const int64_t tiles_r = (rows + TILE - 1) / TILE;
     const int64_t tiles_c = (cols + TILE - 1) / TILE;
     const int64_t ntiles = tiles_r * tiles_c;
     // As many workgroups as fit on the chip at once, each looping over tiles;
     // large tensors: one workgroup per tile.
     const int64_t resident =
-        (int64_t)cu_count[dev] * (dbias_ws ? kWavesPerSimd<SRC, true> : kWavesPerSimd<SRC, false>);
+        (int64_t)cus * (dbias_ws ? kWavesPerSimd<SRC, true> : kWavesPerSimd<SRC, false>);
     const bool per_tile = ntiles > 2 * resident;
     const dim3 grid((unsigned)(per_tile ? ntiles : std::min<int64_t>(ntiles, resident)));
     auto launch = [&](auto wq, auto wqt, auto db) {
@@ -456,14 +449,16 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
 }
 
 // Producer-fused cast.  The toy block of "CPU Overhead of te.Linear FP8
-// Layers" computes each linear's input with an elementwise operation in
-// torch (x = shift * x / scale after the modulation linear, then
-// nan_to_num; residual adds) and only then casts it.  Here one pass reads the
-// operands, writes the bf16 result y and casts y exactly as
-// cast_transpose_amax_kernel would:
+// Layers" (TEBlock.forward) computes each linear's input with an elementwise
+// operation in torch (the modulation: the input times one slice of the
+// modulation linear's output, divided by another; the residual adds) and
+// only then casts it.  Here one pass reads the operands, writes the bf16
+// result y and casts y exactly as cast_transpose_amax_kernel would:
 //   OP 1 (modulate): y = bf16(a * x / b) (fp32 multiply, correctly rounded
-//        fp32 division, round to nearest even), inf or NaN -> +0;
-//   OP 2 (residual add): y = bf16(x + a); a NaN sum becomes 0x7FC0.
+//        fp32 division, round to nearest even); infinities stay infinities,
+//        a NaN quotient becomes 0x7FC0, and the cast codes both by its rules;
+//   OP 2 (residual add): y = bf16(x + a); a NaN sum becomes 0x7FC0;
+//   OP 3 (two residual terms): y = bf16(bf16(x + a) + b), each sum rounded.
 // One workgroup per 128 x 128 tile, the lane layout of the cast (4 rows x 16
 // columns, 16-byte loads and stores).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits_rne(float f) {
@@ -482,8 +477,7 @@ __device__ __forceinline__ uint32_t produce_pair(uint32_t xw, uint32_t aw, uint3
         if constexpr (OP == FP8_PRODUCE_MODULATE) {
             const float bv = __uint_as_float(h ? (bw & 0xFFFF0000u) : (bw << 16));
             const float v = (av * xv) / bv;
-            y = (v != v) ? 0u : f32_to_bf16_bits_rne(v);
-            if ((y & 0x7F80u) == 0x7F80u) y = 0u;
+            y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);
         } else if constexpr (OP == FP8_PRODUCE_ADD) {
             const float v = xv + av;
             y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);

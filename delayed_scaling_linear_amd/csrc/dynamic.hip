@@ -91,20 +91,13 @@ __global__ void dynamic_scale_kernel(const float *__restrict__ amax, float *__re
 hipError_t launch_dynamic_scale(const void *x, int src, int64_t rows, int64_t cols, int64_t ld,
                                 int fmt, int margin, float *amax, float *scale,
                                 const int32_t *noop, hipStream_t stream) {
-    static int cu_count[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cu_count[dev] == 0) {
-        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-    }
+    int cus = 0;
+    if (hipError_t e = current_cu_count(&cus)) return e;
     hipLaunchKernelGGL(set_scalar_kernel, dim3(1), dim3(1), 0, stream, amax, 0.0f, noop);
     if (rows > 0 && cols > 0) {
         // Two workgroups per CU, each striding over many row groups: few
         // atomics on the one amax word.
-        const dim3 grid((unsigned)std::min<int64_t>(rows / 4, (int64_t)cu_count[dev] * 2));
+        const dim3 grid((unsigned)std::min<int64_t>(rows / 4, (int64_t)cus * 2));
         if (src == FP8_DTYPE_BF16)
             hipLaunchKernelGGL(amax_kernel<FP8_DTYPE_BF16>, grid, dim3(256), 0, stream, x, rows,
                                cols, ld, amax, noop);

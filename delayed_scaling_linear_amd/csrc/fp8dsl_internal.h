@@ -5,9 +5,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp8dsl.h"
 
 namespace fp8dsl {
+
+// Number of compute units of the current device.  Cached per device after the
+// first query (an immutable fact of the device; concurrent first calls store
+// the same value), so launchers can size persistent grids without a runtime
+// query per call.
+hipError_t current_cu_count(int *cu_count);
+
+// Enables `lds_bytes` of dynamic LDS for `kernel` on the current device once
+// (the runtime call is idempotent, so a race repeats it harmlessly).  `done`
+// is one bit per device owned by the calling launcher.
+hipError_t enable_dynamic_lds(const void *kernel, int lds_bytes, std::atomic<uint64_t> &done);
 
 // Launchers: each validates nothing (the C-ABI layer has done that), enqueues
 // one kernel on `stream` and returns the launch status.

@@ -17,22 +17,31 @@
 // a group loses less than 2^-10 of its largest product), and accumulates the
 // group sums in fp32.
 //
-// Design (gfx950, wave64):
-//   * v_mfma_f32_16x16x128_f8f6f4 with per-operand format select (E4M3 /
-//     E5M2), 8192 FLOP per instruction;
-//   * block tile BM x BN, K step 128 bytes, waves arranged WM x WN, each wave
-//     owning a (BM/WM) x (BN/WN) accumulator tile in AGPRs/VGPRs;
-//   * A and B K-slabs staged through LDS, double-buffered: the global loads
-//     of step k+1 are in flight while the matrix cores work on step k;
-//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//     c ^ (r & 7), so both the row-wise stores and the fragment reads (8 lanes
-//     on 8 consecutive rows) touch 8 distinct chunks: no bank conflicts;
-//   * the B fragment is fed as the matrix core's first operand, so each lane
-//     ends up holding four consecutive output columns of one output row: the
-//     epilogue applies sinv_a * sinv_b and the bias in fp32 and writes 8-byte
-//     (bf16) or 16-byte (fp32) vectors;
-//   * M and N tails: out-of-range operand rows are clamped to the last valid
-//     row for loading and never stored; a K tail (K % 128 != 0) is zero-filled.
+// Design (gfx950, wave64).  Three kernels; launch_fmt picks one per call:
+//
+//   * gemm_nt_dma_kernel -- every large product with K % 128 == 0 (all the
+//     toy-block shapes).  Persistent: one 256-thread workgroup per CU walks
+//     256 x 256 output tiles in an XCD-aware order (workgroup b runs on XCD
+//     b % 8, and each XCD gets a contiguous, row-grouped range of tiles).
+//     Four waves own 128 x 128 each as 4 x 4 v_mfma_f32_32x32x64_f8f6f4
+//     blocks (256 fp32 accumulators per lane).  Operand stages of 128
+//     K-bytes are written straight into two 64 KiB LDS buffers by buffer
+//     loads with the LDS flag (no staging registers), and stages stream on
+//     across tile boundaries.  The epilogue applies sinv_a * sinv_b and the
+//     bias in fp32, stages the output through the drained stage buffer in
+//     32-row blocks and stores whole row segments while the next tile's
+//     first stages are in flight.
+//   * gemm_nt_big_kernel -- the same tiling for large products whose K is a
+//     multiple of 16 only: 64-byte stages in three LDS buffers, loaded
+//     through registers, K tails read as zero through the buffer range check.
+//   * gemm_nt_kernel -- small products: 128 x 128 tiles, one workgroup per
+//     tile, v_mfma_f32_16x16x128_f8f6f4, double-buffered LDS.
+//
+// Shared by all three: LDS rows are 128 bytes with the 16-byte chunk c of row
+// r stored at a row-dependent XOR of c (conflict-free fragment reads); the B
+// fragment is the matrix core's first operand, so each lane holds four
+// consecutive output columns of one output row; out-of-range operand rows
+// are clamped for loading and never stored.
 //
 // The kernels and their launch templates live in this header; the library's
 // sources instantiate them per output kind (bf16 / fp32, FP8 codes) so that
@@ -1333,23 +1342,15 @@ hipError_t launch_big(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
                       hipStream_t stream) {
     auto kern = gemm_nt_big_kernel<FA, FB, OUT, HAS_BIAS>;
     constexpr int lds_bytes = 3 * (256 + 256) * 64;   // three 32 KiB stages
-    static bool attr_set[64];
-    static int cu_count[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};
+    if (hipError_t e = enable_dynamic_lds(reinterpret_cast<const void *>(kern), lds_bytes,
+                                          lds_enabled))
+        return e;
+    int cus = 0;
+    if (hipError_t e = current_cu_count(&cus)) return e;
     const int tiles_m = (M + 255) / 256;
     const int tiles_n = (N + 255) / 256;
-    const int grid = std::min(tiles_m * tiles_n, cu_count[dev]);
+    const int grid = std::min(tiles_m * tiles_n, cus);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
                        C, tiles_m, tiles_n, qo);
     return hipGetLastError();
@@ -1361,23 +1362,15 @@ hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
                       hipStream_t stream) {
     auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS>;
     constexpr int lds_bytes = 2 * (256 + 256) * 128 + 2048;   // two 64 KiB stages, 2 bias slots
-    static bool attr_set[64];
-    static int cu_count[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};
+    if (hipError_t e = enable_dynamic_lds(reinterpret_cast<const void *>(kern), lds_bytes,
+                                          lds_enabled))
+        return e;
+    int cus = 0;
+    if (hipError_t e = current_cu_count(&cus)) return e;
     const int tiles_m = (M + 255) / 256;
     const int tiles_n = (N + 255) / 256;
-    const int grid = std::min(tiles_m * tiles_n, cu_count[dev]);
+    const int grid = std::min(tiles_m * tiles_n, cus);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
                        C, tiles_m, tiles_n, qo);
     return hipGetLastError();
@@ -1390,17 +1383,10 @@ hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
     auto kern = gemm_nt_kernel<BM, BN, WM, WN, FA, FB, OUT, HAS_BIAS>;
     constexpr int lds_bytes = 2 * (BM + BN) * BK;
     // Dynamic LDS above 64 KiB must be enabled once per device and kernel.
-    static bool attr_set[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};
+    if (hipError_t e = enable_dynamic_lds(reinterpret_cast<const void *>(kern), lds_bytes,
+                                          lds_enabled))
+        return e;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(WM * WN * 64), lds_bytes, stream, A, B,

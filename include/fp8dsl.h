@@ -25,10 +25,15 @@
  *    the default stream).  No entry point synchronises, allocates, frees, or
  *    reads device memory from the host, so every call can be captured in a
  *    HIP graph.
- *  - The caller owns every buffer.  The library keeps no state between calls.
- *  - Return value: FP8_OK (0) or a negative fp8_status_t.  On an error
- *    nothing has been enqueued.  Faults inside a kernel surface later, as HIP
- *    reports them, on the stream.
+ *  - The caller owns every buffer.  The library keeps no state between calls
+ *    beyond per-device caches of immutable device facts (compute-unit count,
+ *    kernel attributes set once), filled on first use and safe to fill from
+ *    several threads at once.
+ *  - Return value: FP8_OK (0) or a negative fp8_status_t.  On an argument
+ *    error nothing has been enqueued.  The kernels are built for gfx950 only:
+ *    on any other device the runtime rejects the launch and the call returns
+ *    FP8_ERR_DEVICE.  Faults inside a kernel surface later, as HIP reports
+ *    them, on the stream.
  *  - Layouts are row-major with unit stride in the last dimension.
  *  - FP8 codes are OCP float8_e4m3fn / float8_e5m2 bytes.
  */
@@ -55,7 +60,7 @@ typedef enum {
     FP8_ERR_FORMAT = -4,    /* an FP8 format this entry point does not accept   */
     FP8_ERR_ARG = -5,       /* another argument out of range (dtype, algo, ...) */
     FP8_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch         */
-    FP8_ERR_DEVICE = -7     /* the current device is not a gfx950 GPU           */
+    FP8_ERR_DEVICE = -7     /* no gfx950 code object for the current device     */
 } fp8_status_t;
 
 /* OCP 8-bit float formats ("Accelerating PyTorch Training Workloads with FP8
@@ -213,20 +218,24 @@ int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int6
  * a linear's input, fused with that input's cast.
  *
  * In the toy block of "CPU Overhead of te.Linear FP8 Layers" (reproduction
- * script) the input of a linear is made by torch elementwise code right
- * before the linear: x = shift * x / scale (shift and scale are column slices
- * of the modulation linear's output) followed by torch.nan_to_num, and the
- * residual adds x = x + ... .  This call computes it and casts it in one pass:
+ * script, TEBlock.forward) the input of a linear is made by torch elementwise
+ * code right before the linear: the modulation (the block input times one
+ * column slice of the modulation linear's output, divided by another slice)
+ * and the residual adds onto the stream.  This call computes it and casts it
+ * in one pass:
  *
  *   op FP8_PRODUCE_MODULATE: y = bf16(a * x / b)   (fp32 multiply, correctly
  *                            rounded fp32 division, round to nearest even);
- *                            an infinite or NaN y becomes +0
+ *                            nothing is sanitised: a zero divisor gives
+ *                            +-inf, 0/0 a NaN written as 0x7FC0, and the
+ *                            cast then saturates the infinities and codes the
+ *                            NaN as 0x7F (the amax records the NaN)
  *   op FP8_PRODUCE_ADD:      y = bf16(x + a)       (fp32 add, round to nearest
  *                            even); a NaN y is written as 0x7FC0
  *   op FP8_PRODUCE_ADD2:     y = bf16(bf16(x + a) + b)   (the block's residual
- *                            x = x + attn_q + attn_k[:, :H], added one term at
- *                            a time as torch does, each sum rounded; a NaN at
- *                            either step is written as 0x7FC0)
+ *                            add of the two cross-attention outputs, one term
+ *                            at a time as torch adds them, each sum rounded;
+ *                            a NaN at either step is written as 0x7FC0)
  *
  * then writes y (bf16, row-major [rows, cols], ld = cols) and exactly what
  * fp8_cast_transpose_amax writes for the bf16 source y with this scale.

@@ -182,3 +182,46 @@ def test_dynamic_cast_validation():
     d2 = _desc(32, 40)
     assert L.fp8_cast_transpose_dynamic(0x4000, 0, 32, 40, 40, 0, 0x5000, byref(d2), 0x6000,
                                         None, None) == -2           # cols not a multiple of 16
+
+
+def test_binding_checks_extents_before_any_call():
+    """Every descriptor and output is checked against the sizes the call
+    will touch (the C ABI trusts them), before any pointer reaches it."""
+    import torch
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    one = torch.ones(1)
+    # descriptor storage that disagrees with rows / cols
+    with pytest.raises(ValueError, match="data must have shape"):
+        dsl.Float8Tensor(u8(16, 32), None, one, 0, 32, 16).desc()
+    with pytest.raises(ValueError, match="data_t must have shape"):
+        dsl.Float8Tensor(None, u8(16, 32), one, 0, 16, 32).desc()
+    with pytest.raises(ValueError, match="at least one element"):
+        dsl.Float8Tensor(u8(16, 32), None, torch.ones(0), 0, 16, 32).desc()
+    x = dsl.Float8Tensor(u8(64, 32), None, one, 0, 64, 32)
+    w = dsl.Float8Tensor(u8(48, 32), u8(32, 48), one, 0, 48, 32)
+    dy = dsl.Float8Tensor(u8(64, 48), u8(48, 64), one, 1, 64, 48)
+    xt = dsl.Float8Tensor(None, u8(32, 64), one, 0, 64, 32)
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="y must have shape"):
+        dsl.fp8_linear_fwd(x, w, None, bf(64, 40))
+    with pytest.raises(ValueError, match="bias must have shape"):
+        dsl.fp8_linear_fwd(x, w, bf(40), bf(64, 48))
+    with pytest.raises(ValueError, match="dx must have shape"):
+        dsl.fp8_linear_dgrad(dy, w, bf(64, 48))
+    with pytest.raises(ValueError, match="dw must have shape"):
+        dsl.fp8_linear_wgrad(dy, xt, torch.zeros(32, 48))
+    with pytest.raises(ValueError, match="bias must have shape"):
+        dsl.fp8_linear_fwd_fp8out(x, w, bf(47), one, dsl.Float8Tensor(u8(64, 48), None, one, 0,
+                                                                      64, 48), one)
+    with pytest.raises(ValueError, match="scale_y"):
+        dsl.fp8_linear_fwd_fp8out(x, w, None, torch.ones(0),
+                                  dsl.Float8Tensor(u8(64, 48), None, one, 0, 64, 48), one)
+    src = bf(64, 32)
+    with pytest.raises(ValueError, match="scale must have"):
+        dsl.fp8_cast_transpose_amax(src, torch.ones(0), x)
+    with pytest.raises(ValueError, match="amax_cur must have"):
+        dsl.fp8_cast_transpose_amax(src, one, x, torch.ones(0))
+    with pytest.raises(ValueError, match="amax is required"):
+        dsl.fp8_cast_transpose_dynamic(src, one, x, None)
+    with pytest.raises(ValueError, match="amax_history must be"):
+        dsl.fp8_scale_update(torch.zeros(16), one, one, one, u8(1))

@@ -249,3 +249,62 @@ def test_dma_path_repeats_bit_identically():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), "fp32 output changed between calls"
+
+
+def _plant_specials(A, fa, B, fb, rng):
+    """NaN codes and (E5M2 only) +-inf codes planted in a few operand rows.
+    Returns the planted rows of A and of B.  The oracle's exact product then
+    has NaN where a NaN meets anything or +inf meets -inf or 0, and +-inf
+    where one infinity meets nonzero finite values."""
+    M, K = A.shape
+    N = B.shape[0]
+    ra = [3, M // 2, M - 1]
+    rb = [5, N - 2]
+    A[ra[0], rng.integers(0, K)] = 0x7F                     # NaN (both formats)
+    if fa == 1:
+        A[ra[1], rng.integers(0, K)] = 0x7C                 # +inf
+        k1, k2 = rng.choice(K, 2, replace=False)
+        A[ra[2], k1], A[ra[2], k2] = 0x7C, 0xFC             # +inf and -inf in one row
+    else:
+        A[ra[1], rng.integers(0, K)] = 0xFF                 # -NaN
+    B[rb[0], rng.integers(0, K)] = 0xFF
+    if fb == 1:
+        B[rb[1], rng.integers(0, K)] = 0xFC                 # -inf
+    return ra, rb
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 264, 272),        # small-tile kernel
+                                   (1024, 16384, 272),     # register-staged large-tile kernel
+                                   (1024, 16384, 256)])    # direct-to-LDS large-tile kernel
+@pytest.mark.parametrize("fa,fb,out", [(1, 0, "bf16"), (0, 1, "fp32"), (1, 1, "bf16")])
+def test_nan_and_inf_operands(M, N, K, fa, fb, out):
+    """NaN and infinite operand codes (the cast emits 0x7F/0xFF for NaN
+    sources; E5M2 has infinities) reach bf16 and fp32 outputs as the exact
+    product says: NaN and +-inf at exactly the oracle's places, every finite
+    output within tolerance."""
+    rng = np.random.default_rng(M + N + K + fa + 2 * fb)
+    A = workloads.random_fp8_codes((M, K), M + 3, fa)
+    B = workloads.random_fp8_codes((N, K), N + 4, fb)
+    ra, rb = _plant_specials(A, fa, B, fb, rng)
+    sa, sb = np.float32(1 / 64.0), np.float32(1 / 3.0)
+    bias = _bias(N, 40) if out == "bf16" else None
+    if out == "bf16":
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        dsl.fp8_linear_fwd(_f8(A, fa, float(sa)), _f8(B, fb, float(sb)), bias.to(DEV), y)
+    else:
+        y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+        dsl.fp8_linear_wgrad(_f8(A, fa, float(sa), transpose_only=True),
+                             _f8(B, fb, float(sb), transpose_only=True), y)
+    torch.cuda.synchronize()
+    kind = oracle.OUT_BF16 if out == "bf16" else oracle.OUT_FP32
+    got = bf16_values(bits16(y)) if out == "bf16" else f32(y).astype(np.float64)
+    # the planted rows and columns whole, plus random samples
+    r = np.concatenate([np.repeat(ra, N), np.tile(np.arange(M), len(rb)), rng.integers(0, M, 3000)])
+    c = np.concatenate([np.tile(np.arange(N), len(ra)), np.repeat(rb, M), rng.integers(0, N, 3000)])
+    ref = oracle.gemm_nt_sampled(A.numpy(), fa, B.numpy(), fb, sa, sb, r, c,
+                                 bias=None if bias is None else bits16(bias), out_kind=kind)
+    ref = bf16_values(ref) if out == "bf16" else ref.astype(np.float64)
+    stats = assert_gemm_close(got[r, c], ref, f"specials {M}x{N}x{K} {fa}{fb} {out}")
+    assert stats["n_nonfinite"] >= N + M          # a NaN row and a NaN column at least
+    if fa == 1:
+        assert np.isinf(ref).any()                # the infinities really were exercised

@@ -8,7 +8,7 @@ import torch
 
 import delayed_scaling_linear_amd as dsl
 import oracle
-from tests.gpu_util import DEV, bits8, bits16, f32_bits
+from tests.gpu_util import DEV, bf16_values, bits8, bits16, f32_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -104,15 +104,21 @@ def test_toy_block_shapes_with_column_slices():
     _run_and_check(oracle.PROD_ADD2, y.cpu(), q_out, k_out[:, :2048], 3.5, oracle.E4M3)
 
 
-def test_special_values():
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_special_values(fmt):
     x, a, b = _rand((64, 64), 9), _rand((64, 64), 10), _rand((64, 64), 11)
-    b[0, :] = 0.0                        # a*x/0 -> inf -> 0
+    b[0, :] = 0.0                        # a*x/0 -> +-inf -> the cast saturates
+    b[5, :] = -0.0                       # the zero's sign flips the infinity
     x[1, :] = 0.0
-    b[1, :] = 0.0                        # 0/0 -> NaN -> 0
+    b[1, :] = 0.0                        # 0/0 -> NaN (0x7FC0) -> code 0x7F
     x[2, :] = 3.0e38
-    a[2, :] = 3.0e38                     # overflow -> 0
-    y = _run_and_check(oracle.PROD_MODULATE, x, a, b, 1.0, oracle.E5M2)
-    assert (bits16(y)[:3] == 0).all()
+    a[2, :] = 3.0e38                     # fp32 product overflows -> inf
+    x[3, :], a[3, :], b[3, :] = 1.0e20, 1.0e20, 1.0e-5   # beyond bf16 only -> inf
+    x[4, :], b[4, :] = float("inf"), float("inf")        # inf/inf -> NaN
+    y = _run_and_check(oracle.PROD_MODULATE, x, a, b, 1.0, fmt)
+    v = bits16(y)
+    assert np.isin(v[[0, 2, 3, 5]], [0x7F80, 0xFF80]).all()
+    assert (v[1] == 0x7FC0).all() and (v[4] == 0x7FC0).all()
     x2, a2 = _rand((64, 64), 12), _rand((64, 64), 13)
     x2[0, 0], a2[1, 1] = float("nan"), float("inf")
     x2[2, 2], a2[2, 2] = float("-inf"), float("inf")
@@ -125,6 +131,22 @@ def test_special_values():
     y = _run_and_check(oracle.PROD_ADD2, x2, a2, b2, 1.0, oracle.E4M3)
     v = bits16(y)
     assert v[0, 0] == 0x7FC0 and v[3, 3] == 0x7FC0 and v[4, 4] == 0x7FC0
+
+
+def test_toy_block_modulation_with_zero_divisors():
+    """The modulation at the block's real shape with a few exact zeros in the
+    divisor slice (a bf16 linear output can round to zero): the infinities
+    and NaNs flow into the cast, and the amax becomes NaN, as in the oracle."""
+    mod = _rand((8192, 12288), 22, 0.5)
+    g = torch.Generator().manual_seed(23)
+    zr = torch.randint(0, 8192, (64,), generator=g)
+    zc = torch.randint(2048, 4096, (64,), generator=g)
+    mod[zr, zc] = 0.0
+    x = torch.rand(8192, 2048, generator=torch.Generator().manual_seed(24)).to(torch.bfloat16)
+    x[zr[:8], zc[:8] - 2048] = 0.0                      # 0/0 at eight of them
+    y = _run_and_check(oracle.PROD_MODULATE, x, mod[:, :2048], mod[:, 2048:4096], 3.5,
+                       oracle.E4M3)
+    assert np.isnan(bf16_values(bits16(y))).any()
 
 
 def test_noop_flag_writes_nothing():
