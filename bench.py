@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-toy-stack", action="store_true",
                    help="skip the 32-block toy-stack forward timing (eager vs HIP graph)")
+    p.add_argument("--no-train-step", action="store_true",
+                   help="skip the 32-block toy-stack training step (FP8 vs torch bf16 autocast)")
     p.add_argument("--probe-kernels", action="store_true",
                    help="launch the forward GEMM, the [4096,4096] cast and a 64 MiB device copy "
                         "once each (after a warm-up) and exit: the command profiled for HBM "
@@ -268,25 +270,25 @@ def fp8_output_forward(dsl, st, iters: int = 20):
 def producer_cast_cost(dsl, workloads, iters: int = 20):
     """The toy block's glue in front of a linear at its real shapes, as torch
     elementwise code followed by the cast, and fused into one pass
-    (fp8_produce_cast_transpose_amax): x = nan_to_num(shift * x / scale) with
-    shift/scale column slices of the [8192, 12288] modulation output, and the
-    residual add x + qkv[:, :2048]; E4M3 codes + transpose + amax of the
-    result each time."""
+    (fp8_produce_cast_transpose_amax): the modulation, the input times one
+    column slice of the [8192, 12288] modulation output divided by another,
+    and the residual add of the first 2048 columns of the [8192, 6144]
+    self-attention output; E4M3 codes + transpose + amax of the result each
+    time."""
     dev = "cuda"
     H, Mt = workloads.HIDDEN, workloads.TOKENS
     g = torch.Generator(device=dev).manual_seed(30)
     mod = (torch.randn(Mt, 6 * H, generator=g, device=dev) * 0.5).to(torch.bfloat16)
     qkv = (torch.randn(Mt, 3 * H, generator=g, device=dev) * 0.02).to(torch.bfloat16)
     x = torch.rand(Mt, H, generator=g, device=dev).to(torch.bfloat16)
-    shift, scale_m, r = mod[:, :H], mod[:, H:2 * H], qkv[:, :H]
+    shift, scale_m, r = mod[:, :H], mod[:, H:2 * H], qkv[:, :H]   # gain, divisor, residual
     y = torch.empty_like(x)
     out = dsl.Float8Tensor.empty(Mt, H, 0, device=dev)
     s = torch.tensor([3.5], device=dev)
     amax = torch.zeros(1, device=dev)
 
     def torch_mod():
-        t = torch.nan_to_num((shift.float() * x.float() / scale_m.float()).to(torch.bfloat16),
-                             nan=0.0, posinf=0.0, neginf=0.0)
+        t = (shift.float() * x.float() / scale_m.float()).to(torch.bfloat16)
         dsl.fp8_cast_transpose_amax(t, s, out, amax)
 
     def torch_add():
@@ -315,155 +317,379 @@ def producer_cast_cost(dsl, workloads, iters: int = 20):
     return {k: round(v, 2) for k, v in res.items()}
 
 
+# ------------------------------------------------------------- toy stack ----
+
+# The six linears of one toy block, by position in workloads.toy_block_linears().
+L_MOD, L_SELF, L_CROSS_Q, L_CROSS_KV, L_UP, L_DOWN = range(6)
+# Delayed-scaling records of one linear: its input, its weight and (when
+# training) its output gradient.
+R_X, R_W, R_DY = 0, 1, 2
+
+
+class ToyStack:
+    """The toy transformer stack of "CPU Overhead of te.Linear FP8 Layers"
+    (hidden 2048, batch 8 x seq 1024 = 8192 tokens, mlp_ratio 4) run through
+    the library: every linear casts its input and weight with delayed scaling
+    and multiplies in FP8; when training, its output gradient is cast to E5M2
+    (with the bias gradient fused in for the biased linears) and dgrad and
+    wgrad run from the cached transposes.  One scale update per step covers
+    every record.
+
+    A block acts on the residual stream h (width H) through its six linears
+    (in -> out features, bias):
+
+        0  2048 -> 12288 +b   modulation: h <- out[:, :H] * h / out[:, H:2H]
+        1  2048 ->  6144      h <- h + out[:, :H]
+        2  2048 ->  2048      \\  both read the same h;
+        3  2048 ->  4096      /   h <- (h + out2) + out3[:, :H]
+        4  2048 ->  8192 +b   u = out
+        5  8192 ->  2048 +b   of u;  h <- h + out
+
+    `fused` computes the modulation and residual adds inside the casts of the
+    linear inputs they produce (fp8_produce_cast_transpose_amax); otherwise
+    they run as torch elementwise ops followed by plain casts.  Nothing is
+    sanitised: a zero in the modulation's divisor gives infinities, which the
+    casts saturate.  `train` keeps what the backward needs (every FP8 input
+    with its transpose, the block inputs and modulation outputs) and holds
+    fp32 master weights (the FP8 run of the page keeps fp32 parameters) whose
+    FP8 casts read fp32 directly.
+    """
+
+    def __init__(self, dsl, workloads, blocks: int, *, train: bool = False, dev: str = "cuda",
+                 seed: int = 20, weights=None):
+        self.dsl, self.blocks, self.train, self.dev = dsl, blocks, train, dev
+        self.H, self.M = workloads.HIDDEN, workloads.TOKENS
+        self.lin = workloads.toy_block_linears()
+        nl = len(self.lin)
+        self.R = 3 if train else 2
+        fmts = ([dsl.E4M3, dsl.E4M3, dsl.E5M2][:self.R]) * (nl * blocks)
+        self.state = dsl.DelayedScalingState(fmts, device=dev)
+        self.flag = torch.zeros(1, dtype=torch.int32, device=dev)   # 1: keep cached FP8 weights
+        # Optional checks called after each linear's forward product,
+        # probe(b, l, y), and after its backward, probe_bwd(b, l, dy); the
+        # bf16 tensor each input cast read is kept in last_in[l].
+        self.probe = self.probe_bwd = None
+        self.last_in = [None] * len(workloads.toy_block_linears())
+        M, H = self.M, self.H
+        wdt = torch.float32 if train else torch.bfloat16
+        if weights is None:
+            gen = torch.Generator(device=dev).manual_seed(seed)
+            weights = []
+            for _ in range(blocks):
+                ws = []
+                for fin, fout, hb in self.lin:
+                    w = torch.randn(fout, fin, generator=gen, device=dev) * 0.02
+                    b = torch.randn(fout, generator=gen, device=dev) * 0.02 if hb else None
+                    ws.append((w, b))
+                weights.append(ws)
+        self.w = [[w.to(wdt) for w, _ in ws] for ws in weights]
+        self.b32 = [[None if b is None else b.float() for _, b in ws] for ws in weights]
+        self.b16 = [[None if b is None else b.to(torch.bfloat16) for _, b in ws] for ws in weights]
+        self.qw = [[dsl.Float8Tensor.empty(fout, fin, dsl.E4M3, transpose=train, device=dev)
+                    for fin, fout, _ in self.lin] for _ in range(blocks)]
+        per_block = lambda make: [make() for _ in range(blocks)] if train else [make()] * blocks
+        self.qx = [per_block(lambda fin=fin: dsl.Float8Tensor.empty(M, fin, dsl.E4M3,
+                                                                    transpose=train, device=dev))
+                   for fin, _, _ in self.lin]                         # qx[l][b]
+        bf = lambda n: torch.empty(M, n, dtype=torch.bfloat16, device=dev)
+        self.out = [bf(fout) for _, fout, _ in self.lin]
+        self.mod_out = per_block(lambda: bf(6 * H)) if train else [self.out[L_MOD]] * blocks
+        self.h_in = per_block(lambda: bf(H)) if train else None       # block inputs
+        self.hbuf = [bf(H) for _ in range(4)]
+        if train:
+            self.grad_w = [[torch.zeros_like(w) for w in ws] for ws in self.w]
+            self.grad_b = [[None if b is None else torch.zeros_like(b) for b in bs]
+                           for bs in self.b32]
+            # output gradients, zero beyond the columns the block reads
+            self.dy = [torch.zeros(M, fout, dtype=torch.bfloat16, device=dev)
+                       for _, fout, _ in self.lin]
+            self.qdy = [dsl.Float8Tensor.empty(M, fout, dsl.E5M2, device=dev)
+                        for _, fout, _ in self.lin]
+            self.dx = [bf(fin) for fin, _, _ in self.lin]
+            ws_bytes = max(dsl.fp8_cast_dbias_workspace_bytes(M, fout) for _, fout, _ in self.lin)
+            self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def rec(self, b: int, l: int, kind: int) -> int:
+        return (len(self.lin) * b + l) * self.R + kind
+
+    def _sl(self, t, r):
+        return t[r:r + 1]
+
+    def refresh_bias_copies(self):
+        """bf16 copies of the fp32 master biases for the forward GEMMs."""
+        dst = [b for bs in self.b16 for b in bs if b is not None]
+        src = [b for bs in self.b32 for b in bs if b is not None]
+        torch._foreach_copy_(dst, src)
+
+    # -- forward --
+    def _cast_in(self, b, l, x):
+        r, st = self.rec(b, l, R_X), self.state
+        self.last_in[l] = x
+        self.dsl.fp8_cast_transpose_amax(x, self._sl(st.scale, r), self.qx[l][b],
+                                         self._sl(st.amax_cur, r))
+
+    def _linear(self, b, l, out=None):
+        """Weight cast (skipped on the device when the cache flag is set) and
+        the FP8 product of linear l of block b, its input already cast."""
+        r, st = self.rec(b, l, R_W), self.state
+        qw = self.qw[b][l]
+        self.dsl.fp8_cast_transpose_amax(self.w[b][l], self._sl(st.scale, r), qw,
+                                         self._sl(st.amax_cur, r), noop_flag=self.flag)
+        y = self.out[l] if out is None else out
+        self.dsl.fp8_linear_fwd(self.qx[l][b], qw, self.b16[b][l], y)
+        if self.probe is not None:
+            self.probe(b, l, y)
+        return y
+
+    def _produce(self, b, l, op, x, a, c, out, fused):
+        """out = op(x, a, c) in bf16, cast as the input of linear l of block b."""
+        dsl = self.dsl
+        if fused:
+            r, st = self.rec(b, l, R_X), self.state
+            self.last_in[l] = out
+            dsl.fp8_produce_cast_transpose_amax(op, x, a, c, out, self._sl(st.scale, r),
+                                                self.qx[l][b], self._sl(st.amax_cur, r))
+            return out
+        if op == dsl.PRODUCE_MODULATE:
+            out.copy_(torch.div(a.float() * x.float(), c.float()))
+        elif op == dsl.PRODUCE_ADD:
+            torch.add(x, a, out=out)
+        else:
+            torch.add(torch.add(x, a), c, out=out)
+        self._cast_in(b, l, out)
+        return out
+
+    def forward(self, x, fused: bool = True, update: bool = True):
+        dsl, H = self.dsl, self.H
+        h1, h2, h3, hn = self.hbuf
+        if self.train:
+            self.h_in[0].copy_(x)
+            x = self.h_in[0]
+        self._cast_in(0, L_MOD, x)
+        h = x
+        for b in range(self.blocks):
+            m = self._linear(b, L_MOD, out=self.mod_out[b])
+            self._produce(b, L_SELF, dsl.PRODUCE_MODULATE, h, m[:, :H], m[:, H:2 * H], h1, fused)
+            s = self._linear(b, L_SELF)
+            self._produce(b, L_CROSS_Q, dsl.PRODUCE_ADD, h1, s[:, :H], None, h2, fused)
+            self._cast_in(b, L_CROSS_KV, h2)
+            q = self._linear(b, L_CROSS_Q)
+            k = self._linear(b, L_CROSS_KV)
+            self._produce(b, L_UP, dsl.PRODUCE_ADD2, h2, q, k[:, :H], h3, fused)
+            u = self._linear(b, L_UP)
+            self._cast_in(b, L_DOWN, u)
+            o = self._linear(b, L_DOWN)
+            if b + 1 < self.blocks:
+                nxt = self.h_in[b + 1] if self.train else hn
+                h = self._produce(b + 1, L_MOD, dsl.PRODUCE_ADD, h3, o, None, nxt, fused)
+            else:
+                h = h3 + o
+        if update:
+            self.state.update()
+        return h
+
+    # -- backward (train) --
+    def _linear_bwd(self, b, l, dy):
+        """Output gradient dy [M, out] of linear l of block b: its E5M2 cast
+        (bias gradient fused for the biased linears), dgrad from the cached
+        weight transpose into self.dx[l], wgrad (fp32) into grad_w."""
+        dsl, st = self.dsl, self.state
+        r = self.rec(b, l, R_DY)
+        if self.grad_b[b][l] is not None:
+            dsl.fp8_cast_transpose_amax_dbias(dy, self._sl(st.scale, r), self.qdy[l],
+                                              self._sl(st.amax_cur, r), self.grad_b[b][l],
+                                              self.ws)
+        else:
+            dsl.fp8_cast_transpose_amax(dy, self._sl(st.scale, r), self.qdy[l],
+                                        self._sl(st.amax_cur, r))
+        dsl.fp8_linear_dgrad(self.qdy[l], self.qw[b][l], self.dx[l])
+        dsl.fp8_linear_wgrad(self.qdy[l], self.qx[l][b], self.grad_w[b][l])
+        if self.probe_bwd is not None:
+            self.probe_bwd(b, l, dy)
+        return self.dx[l]
+
+    def backward(self, g):
+        """g: bf16 [M, H], the loss gradient at the stack's output.  Returns
+        the gradient at the stack's input."""
+        H = self.H
+        for b in reversed(range(self.blocks)):
+            du = self._linear_bwd(b, L_DOWN, g)
+            g = g + self._linear_bwd(b, L_UP, du)
+            self.dy[L_CROSS_KV][:, :H].copy_(g)
+            dk = self._linear_bwd(b, L_CROSS_KV, self.dy[L_CROSS_KV])
+            g = g + self._linear_bwd(b, L_CROSS_Q, g) + dk
+            self.dy[L_SELF][:, :H].copy_(g)
+            g = g + self._linear_bwd(b, L_SELF, self.dy[L_SELF])
+            # modulation h1 = gain * h0 / div: gradients of gain, div and h0
+            m, h0 = self.mod_out[b], self.h_in[b].float()
+            gain, div = m[:, :H].float(), m[:, H:2 * H].float()
+            t = g.float() / div
+            self.dy[L_MOD][:, :H].copy_(t * h0)
+            self.dy[L_MOD][:, H:2 * H].copy_(-(t * gain) * h0 / div)
+            g_direct = (t * gain).to(torch.bfloat16)
+            g = g_direct + self._linear_bwd(b, L_MOD, self.dy[L_MOD])
+        return g
+
+    def train_step(self, x, target, optimizer=None):
+        """Forward, MSE loss gradient, backward, one scale update over every
+        record (inputs, weights, output gradients), optimizer step."""
+        self.refresh_bias_copies()
+        out = self.forward(x, fused=True, update=False)
+        g = torch.sub(out, target).mul_(2.0 / out.numel())
+        self.backward(g)
+        self.state.update()
+        if optimizer is not None:
+            optimizer.step()
+        return out
+
+
+def torch_block_forward(h, ws, H):
+    """The same block in plain torch (bf16 activations; weights used as
+    given, or under torch.autocast): the comparator of the FP8 stack."""
+    f = torch.nn.functional.linear
+    m = f(h, ws[L_MOD][0], ws[L_MOD][1])
+    h = m[:, :H] * h / m[:, H:2 * H]
+    h = h + f(h, ws[L_SELF][0])[:, :H]
+    h = (h + f(h, ws[L_CROSS_Q][0])) + f(h, ws[L_CROSS_KV][0])[:, :H]
+    return h + f(f(h, ws[L_UP][0], ws[L_UP][1]), ws[L_DOWN][0], ws[L_DOWN][1])
+
+
+def _time_loop(fn, reps: int, warmup: int = 1):
+    """GPU ms per call (one event pair around `reps` calls after `warmup`) and
+    host wall ms per call."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps, (time.perf_counter() - t0) * 1e3 / reps
+
+
 def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
-    """The 32-block toy transformer forward (hidden 2048, batch 8, seq 1024;
-    per block the linears 2048->12288 +b, 2048->6144, 2048->2048,
-    2048->4096, 2048->8192 +b and 8192->2048 +b with the shift/scale and
-    residual glue in torch), one scale update over all 384 records per
-    forward.  Timed eagerly and as one captured HIP graph, each with the
-    weights re-cast and with cached FP8 weights (the weight casts see a
-    device no-op flag, so the same graph serves both); as a graph with the
-    modulation and residual adds fused into the following casts; and the
+    """The 32-block toy stack forward (4.398e13 GEMM FLOP, one scale update
+    over all 384 records per forward), eagerly and as one captured HIP graph,
+    each with the weights re-cast and with cached FP8 weights (the weight
+    casts see a device no-op flag, so one graph serves both); as a graph with
+    the modulation and residual adds fused into the following casts; and the
     same stack in plain torch bf16.  Two interleaved rounds, best of each."""
     dev = "cuda"
     H, Mt = workloads.HIDDEN, workloads.TOKENS
-    lin = workloads.toy_block_linears()
-    gen = torch.Generator(device=dev).manual_seed(20)
-    flag = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = dsl.DelayedScalingState([0] * (12 * blocks), device=dev)
-    layers = []
-    for bi in range(blocks):
-        ls = []
-        for fin, fout, hb in lin:
-            w = (torch.randn(fout, fin, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-            b = (torch.randn(fout, generator=gen, device=dev) * 0.02).to(torch.bfloat16) if hb else None
-            ls.append((w, b, dsl.Float8Tensor.empty(fout, fin, 0, device=dev)))
-        layers.append(ls)
-    # FP8 inputs and outputs of linear l are reused by every block (each
-    # block consumes them before the next one overwrites them).
-    qxs = [dsl.Float8Tensor.empty(Mt, fin, 0, device=dev) for fin, _, _ in lin]
-    ys = [torch.empty(Mt, fout, dtype=torch.bfloat16, device=dev) for _, fout, _ in lin]
+    stack = ToyStack(dsl, workloads, blocks)
     x0 = workloads.uniform_bf16((Mt, H), workloads.SEED_X).to(dev)
     xin = torch.empty_like(x0)
-
-    def linear(bi, l, inp):
-        w, b, qw = layers[bi][l]
-        qx, y = qxs[l], ys[l]
-        tx, tw = 12 * bi + 2 * l, 12 * bi + 2 * l + 1
-        dsl.fp8_cast_transpose_amax(inp, st.scale[tx:tx + 1], qx, st.amax_cur[tx:tx + 1])
-        dsl.fp8_cast_transpose_amax(w, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1],
-                                    noop_flag=flag)
-        dsl.fp8_linear_fwd(qx, qw, b, y)
-        return y
-
-    def forward(x):
-        for bi in range(blocks):
-            mod = linear(bi, 0, x)
-            x = torch.nan_to_num((mod[:, :H].float() * x.float() / mod[:, H:2 * H].float())
-                                 .to(torch.bfloat16), nan=0.0, posinf=0.0, neginf=0.0)
-            x = x + linear(bi, 1, x)[:, :H]
-            x = x + linear(bi, 2, x) + linear(bi, 3, x)[:, :H]
-            h = linear(bi, 4, x)
-            x = x + linear(bi, 5, h)
-        st.update()
-        return x
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps, (time.perf_counter() - t0) * 1e3 / reps
-
-    def cast_in(bi, l, inp):
-        tx = 12 * bi + 2 * l
-        dsl.fp8_cast_transpose_amax(inp, st.scale[tx:tx + 1], qxs[l], st.amax_cur[tx:tx + 1])
-
-    def produce_in(bi, l, op, x, a, b):
-        tx = 12 * bi + 2 * l
-        y = torch.empty_like(x)
-        dsl.fp8_produce_cast_transpose_amax(op, x, a, b, y, st.scale[tx:tx + 1], qxs[l],
-                                            st.amax_cur[tx:tx + 1])
-        return y
-
-    def w_gemm(bi, l):
-        w, b, qw = layers[bi][l]
-        tw = 12 * bi + 2 * l + 1
-        dsl.fp8_cast_transpose_amax(w, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1],
-                                    noop_flag=flag)
-        dsl.fp8_linear_fwd(qxs[l], qw, b, ys[l])
-        return ys[l]
-
-    def forward_fused(x):
-        """forward() with the modulation and the residual adds fused into the
-        casts of the inputs they produce (fp8_produce_cast_transpose_amax)."""
-        cast_in(0, 0, x)
-        for bi in range(blocks):
-            mod = w_gemm(bi, 0)
-            x = produce_in(bi, 1, dsl.PRODUCE_MODULATE, x, mod[:, :H], mod[:, H:2 * H])
-            sa = w_gemm(bi, 1)
-            x = produce_in(bi, 2, dsl.PRODUCE_ADD, x, sa[:, :H], None)
-            cast_in(bi, 3, x)
-            ca_q = w_gemm(bi, 2)
-            ca_k = w_gemm(bi, 3)
-            x = produce_in(bi, 4, dsl.PRODUCE_ADD2, x, ca_q, ca_k[:, :H])
-            h = w_gemm(bi, 4)
-            cast_in(bi, 5, h)
-            o = w_gemm(bi, 5)
-            x = produce_in(bi + 1, 0, dsl.PRODUCE_ADD, x, o, None) if bi + 1 < blocks else x + o
-        st.update()
-        return x
-
-    def forward_bf16(x):
-        """The same stack with plain torch bf16 linears (no FP8): context for
-        the FP8-vs-BF16 forward comparison of the toy model's page."""
-        for bi in range(blocks):
-            lw = layers[bi]
-            f = lambda l, inp: torch.nn.functional.linear(inp, lw[l][0], lw[l][1])
-            mod = f(0, x)
-            x = torch.nan_to_num((mod[:, :H].float() * x.float() / mod[:, H:2 * H].float())
-                                 .to(torch.bfloat16), nan=0.0, posinf=0.0, neginf=0.0)
-            x = x + f(1, x)[:, :H]
-            x = x + f(2, x) + f(3, x)[:, :H]
-            x = x + f(5, f(4, x))
-        return x
-
     xin.copy_(x0)
-    forward(xin)                              # first launches (kernel attributes) outside capture
-    torch.cuda.synchronize()
-    forward_fused(xin)
+    stack.forward(xin, fused=False)            # first launches outside capture
+    stack.forward(xin, fused=True)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        forward(xin)
+        stack.forward(xin, fused=False)
     graph_fused = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_fused):
-        forward_fused(xin)
-    modes = {"eager": (lambda: forward(xin), 0), "eager_cached_weights": (lambda: forward(xin), 1),
+        out_fused = stack.forward(xin, fused=True)
+    ws16 = [list(zip(stack.w[b], stack.b16[b])) for b in range(blocks)]
+
+    def forward_bf16():
+        h = xin
+        for b in range(blocks):
+            h = torch_block_forward(h, ws16[b], H)
+        return h
+
+    modes = {"eager": (lambda: stack.forward(xin, fused=False), 0),
+             "eager_cached_weights": (lambda: stack.forward(xin, fused=False), 1),
              "graph": (graph.replay, 0), "graph_cached_weights": (graph.replay, 1),
              "graph_fused_producers": (graph_fused.replay, 0),
-             "bf16_torch_eager": (lambda: forward_bf16(xin), 0)}
+             "bf16_torch_eager": (forward_bf16, 0)}
     res = {}
-    for _ in range(2):                        # interleaved rounds, best of each mode
+    for _ in range(2):
         for name, (fn, fl) in modes.items():
-            flag.fill_(fl)
-            ms, wall = timed(fn)
+            stack.flag.fill_(fl)
+            ms, wall = _time_loop(fn, reps)
             if name + "_ms" not in res or ms < res[name + "_ms"]:
                 res[name + "_ms"], res[name + "_wall_ms"] = ms, wall
-    flop = 2 * Mt * sum(fin * fout for fin, fout, _ in lin) * blocks
+    stack.flag.fill_(0)
+    graph_fused.replay()
+    torch.cuda.synchronize()
+    nonfinite = int((~torch.isfinite(out_fused.float())).sum())
+    flop = 2 * Mt * sum(fin * fout for fin, fout, _ in stack.lin) * blocks
     out = {k: round(v, 3) for k, v in res.items()}
-    out.update({"blocks": blocks, "gemm_flop": flop, "library_launches_per_forward": blocks * 18 + 1,
+    out.update({"blocks": blocks, "gemm_flop": flop,
+                "library_launches_per_forward": blocks * 18 + 1,
                 "graph_fused_producers_gemm_tflops":
-                    round(flop / (res["graph_fused_producers_ms"] * 1e-3) / 1e12, 1)})
-    del graph, graph_fused, layers, qxs, ys
+                    round(flop / (res["graph_fused_producers_ms"] * 1e-3) / 1e12, 1),
+                "nonfinite_outputs": nonfinite})
+    del graph, graph_fused, stack
     torch.cuda.empty_cache()
     return out
+
+
+def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, iters: int = 50):
+    """One training step of the 32-block toy stack, timed as the page times
+    its model (10 warm-up iterations, then `iters` between one event pair):
+    forward, MSE loss, backward, AdamW on fp32 master weights.
+
+    FP8: the library stack (fused producers; per linear an E5M2 gradient cast
+    with fused bias gradient, dgrad from the cached weight transpose, fp32
+    wgrad written as the parameter's gradient; one scale update over 576
+    records).  BF16: the same parameters through torch autograd under
+    torch.autocast(bfloat16), the page's BF16 run.  The modulation's
+    backward and the residual sums of the FP8 run are torch ops."""
+    dev = "cuda"
+    H, Mt = workloads.HIDDEN, workloads.TOKENS
+    stack = ToyStack(dsl, workloads, blocks, train=True)
+    params = []
+    for b in range(blocks):
+        for l in range(len(stack.lin)):
+            w = stack.w[b][l]
+            w.requires_grad_(True)
+            w.grad = stack.grad_w[b][l]
+            params.append(w)
+            if stack.b32[b][l] is not None:
+                bb = stack.b32[b][l]
+                bb.requires_grad_(True)
+                bb.grad = stack.grad_b[b][l]
+                params.append(bb)
+    try:
+        opt = torch.optim.AdamW(params, lr=1e-3, fused=True)
+    except (RuntimeError, ValueError):
+        opt = torch.optim.AdamW(params, lr=1e-3, foreach=True)
+    x = workloads.uniform_bf16((Mt, H), workloads.SEED_X).to(dev)
+    target = workloads.uniform_bf16((Mt, H), workloads.SEED_X + 1).to(dev)
+    res = {}
+    with torch.no_grad():
+        fp8_ms, fp8_wall = _time_loop(lambda: stack.train_step(x, target, opt), iters, warmup)
+        opt_ms, _ = _time_loop(opt.step, 10, 2)
+    res["fp8_step_ms"], res["fp8_step_wall_ms"] = round(fp8_ms, 2), round(fp8_wall, 2)
+    res["adamw_alone_ms"] = round(opt_ms, 2)
+
+    ws32 = [list(zip(stack.w[b], stack.b32[b])) for b in range(blocks)]
+    crit = torch.nn.MSELoss()
+
+    def bf16_step():
+        opt.zero_grad(set_to_none=True)
+        with torch.autocast(device_type="cuda", dtype=torch.bfloat16):
+            h = x
+            for b in range(blocks):
+                h = torch_block_forward(h, ws32[b], H)
+            loss = crit(h.float(), target.float())
+        loss.backward()
+        opt.step()
+
+    bf_ms, bf_wall = _time_loop(bf16_step, iters, warmup)
+    res["bf16_autocast_step_ms"], res["bf16_autocast_step_wall_ms"] = round(bf_ms, 2), round(bf_wall, 2)
+    flop = 3 * 2 * Mt * sum(fin * fout for fin, fout, _ in stack.lin) * blocks
+    res.update({"blocks": blocks, "gemm_flop_per_step": flop, "records": stack.state.T,
+                "fp8_over_bf16_speedup": round(bf_ms / fp8_ms, 3),
+                "protocol": f"{warmup} warm-up + {iters} timed iterations, one event pair"})
+    del stack, opt, params
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(workloads, rows: int = 512):
@@ -625,6 +851,7 @@ def main():
     dyn_cost = dynamic_vs_delayed(dsl, st)
     fp8out_cost = fp8_output_forward(dsl, st)
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
+    train = None if args.no_train_step else toy_stack_train_step(dsl, workloads)
     traffic = traffic_record(root)
     result = {
         "metric": "FP8 GEMM TFLOP/s (M8192 K2048 N8192) + cast-transpose-amax HBM GB/s",
@@ -666,6 +893,8 @@ def main():
     result["fp8_output_forward"] = fp8out_cost
     if toy is not None:
         result["toy_stack_forward"] = toy
+    if train is not None:
+        result["toy_stack_train_step"] = train
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(workloads)
     print(json.dumps(result), flush=True)

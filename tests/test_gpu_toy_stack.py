@@ -1,15 +1,16 @@
-"""GPU parity for the toy transformer stack of "CPU Overhead of te.Linear FP8
-Layers" (hidden 2048, batch 8, seq 1024, mlp_ratio 4) and HIP-graph capture.
+"""GPU parity of the toy transformer stack of "CPU Overhead of te.Linear FP8
+Layers" (hidden 2048, batch 8 x seq 1024, mlp_ratio 4) run through the
+library by bench.ToyStack, against the oracle.
 
-The block (reproduction script of that page): timestep modulation
-2048 -> 12288 (+bias) chunked into shift/scale, x = shift * x / scale,
-self-attention qkv 2048 -> 6144 (first third added back), cross-attention q
-2048 -> 2048 and kv 2048 -> 4096 (first half added back), and an MLP
-2048 -> 8192 (+bias) -> 2048 (+bias), all FP8 linears with delayed scaling.
-The elementwise glue runs in torch; every linear is checked against the
-oracle on the identical bf16 input it received (codes, amax and scale-inverse
-bit-exact, outputs sampled within tolerance), and one scale update covers
-all 2 x 6 x depth records.
+Every probed linear is checked on the identical bf16 (or fp32 weight) tensor
+its cast read: codes, transposes, amax and scale-inverse bit-exact, products
+sampled within tolerance.  The scale update over all records is checked bit
+for bit against the oracle's update of the same state.  Also: cached FP8
+weights on a second micro-batch (the device no-op flag of "[PyTorch]
+Refactor FP8 workspaces in linear modules"), one captured HIP graph serving
+both micro-batches, fused producers against torch glue, a training step
+(E5M2 gradient casts with the bias gradient, dgrad from the cached weight
+transpose, fp32 wgrad) and the full 32-block forward.
 """
 import numpy as np
 import pytest
@@ -18,103 +19,252 @@ import torch
 import delayed_scaling_linear_amd as dsl
 import oracle
 import workloads
-from tests.gpu_util import DEV, assert_gemm_close, bf16_values, bits16, bits8, f32_bits
+from bench import R_DY, R_W, R_X, ToyStack
+from tests.gpu_util import DEV, assert_gemm_close, bf16_values, bits8, bits16, f32, f32_bits
 
 pytestmark = pytest.mark.gpu
 
 M = workloads.TOKENS
+H = workloads.HIDDEN
 
 
-def _linear(x_dev, w_dev, b_dev, st, tx, tw, check, rng):
-    """One FP8 linear through the C ABI; if `check`, compare with the oracle."""
-    K = x_dev.shape[1]
-    N = w_dev.shape[0]
-    qx = dsl.Float8Tensor.empty(M, K, 0, transpose=False, device=DEV)
-    qw = dsl.Float8Tensor.empty(N, K, 0, device=DEV)
-    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
-    amax_before = st.amax_cur.clone()
-    dsl.fp8_cast_transpose_amax(x_dev, st.scale[tx:tx + 1], qx, st.amax_cur[tx:tx + 1])
-    dsl.fp8_cast_transpose_amax(w_dev, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1])
-    dsl.fp8_linear_fwd(qx, qw, b_dev, y)
-    if check:
-        torch.cuda.synchronize()
-        sx, sw = float(st.scale[tx]), float(st.scale[tw])
-        ox, _, ax, six = oracle.cast_transpose_amax(bits16(x_dev), sx, 0, want_qt=False,
-                                                    amax_in=float(amax_before[tx]))
-        ow, owt, aw, siw = oracle.cast_transpose_amax(bits16(w_dev), sw, 0,
-                                                      amax_in=float(amax_before[tw]))
-        np.testing.assert_array_equal(bits8(qx.data), ox)
-        np.testing.assert_array_equal(bits8(qw.data), ow)
-        np.testing.assert_array_equal(bits8(qw.data_t), owt)
-        assert f32_bits(st.amax_cur)[tx] == np.float32(ax).view(np.uint32)
-        assert f32_bits(st.amax_cur)[tw] == np.float32(aw).view(np.uint32)
-        assert f32_bits(qx.scale_inv)[0] == six.view(np.uint32)
-        r, c = rng.integers(0, M, 400), rng.integers(0, N, 400)
-        ref = oracle.gemm_nt_sampled(ox, 0, ow, 0, six, siw, r, c,
-                                     bias=None if b_dev is None else bits16(b_dev))
-        assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), f"linear {N}x{K}")
-    return y
+def _src(t: torch.Tensor) -> np.ndarray:
+    """A cast source as the oracle takes it: bf16 bits or fp32 values."""
+    return bits16(t) if t.dtype == torch.bfloat16 else f32(t)
 
 
-def _block_weights(bi):
-    ws = []
-    for li, (fin, fout, has_bias) in enumerate(workloads.toy_block_linears()):
-        seed = 1000 * (bi + 1) + li
-        w = workloads.normal_bf16((fout, fin), 0.02, seed).to(DEV)
-        b = workloads.normal_bf16((fout,), 0.02, seed + 500).to(DEV) if has_bias else None
-        ws.append((w, b))
-    return ws
+def _state(st):
+    return {n: f32(getattr(st, n)).copy() for n in ("amax_history", "amax_cur", "scale",
+                                                     "scale_inv")}
 
 
-def _block(x, ws, st, base, check, rng):
-    """Forward of one toy block; tensor records base + 2*l (input), +1 (weight)."""
-    H = workloads.HIDDEN
-    lin = lambda l, inp: _linear(inp, ws[l][0], ws[l][1], st, base + 2 * l, base + 2 * l + 1,
-                                 check, rng)
-    mod = lin(0, x)
-    shift, scale = mod[:, :H], mod[:, H:2 * H]
-    x = (shift.float() * x.float() / scale.float()).to(torch.bfloat16)
-    x = torch.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0)   # heavy tails of the ratio
-    sa_q = lin(1, x)[:, :H]
-    x = x + sa_q
-    ca_q = lin(2, x)
-    ca_k = lin(3, x)[:, :H]
-    x = x + ca_q + ca_k
-    h = lin(4, x)
-    x = x + lin(5, h.contiguous())
-    return x.contiguous()
-
-
-def test_toy_stack_two_blocks_and_one_update_over_all_records():
-    depth = 32
-    T = 2 * 6 * depth                                   # 384 records
-    st = dsl.DelayedScalingState([0] * T, device=DEV)
-    rng = np.random.default_rng(0)
-    x = workloads.uniform_bf16((M, workloads.HIDDEN), workloads.SEED_X).to(DEV)
-    for bi in range(2):                                 # two blocks at the full shape
-        x = _block(x, _block_weights(bi), st, 12 * bi, check=True, rng=rng)
+def _update_and_check(stack, want_cur=None):
+    """Run the stack's one scale update and compare it, bit for bit, with the
+    oracle's update of the same pre-update state; `want_cur` (record ->
+    oracle amax) pins the recorded amaxes first."""
     torch.cuda.synchronize()
-    hist = st.amax_history.cpu().numpy().copy()
-    cur = st.amax_cur.cpu().numpy().copy()
-    scale = st.scale.cpu().numpy().copy()
-    sinv = st.scale_inv.cpu().numpy().copy()
-    recorded = cur.copy()
-    st.update()
+    st = stack.state
+    pre = _state(st)
+    if want_cur is not None:
+        for r, a in want_cur.items():
+            assert pre["amax_cur"][r].view(np.uint32) == np.float32(a).view(np.uint32), f"record {r}"
+    stack.state.update()
     torch.cuda.synchronize()
-    oracle.scale_update(hist, cur, scale, sinv, np.zeros(T, np.uint8))
+    hist, cur, scale, sinv = (pre["amax_history"], pre["amax_cur"], pre["scale"],
+                              pre["scale_inv"])
+    oracle.scale_update(hist, cur, scale, sinv, f32(st.fmt).astype(np.uint8))
     np.testing.assert_array_equal(f32_bits(st.amax_history), hist.view(np.uint32))
     np.testing.assert_array_equal(f32_bits(st.scale), scale.view(np.uint32))
     np.testing.assert_array_equal(f32_bits(st.scale_inv), sinv.view(np.uint32))
-    assert (recorded[:24] > 0).all() and (recorded[24:] == 0).all()
-    assert (st.scale[:24].cpu() != 1.0).all() and (st.scale[24:].cpu() == 1.0).all()
+    assert (f32(st.amax_cur) == 0).all()
+    return pre
+
+
+class ForwardCheck:
+    """stack.probe: after the product of linear l of block b, compare its
+    input and weight casts with the oracle's casts of the same tensors and
+    sampled outputs with the oracle's product of the oracle's codes.
+
+    cached: the weight casts were skipped by the no-op flag, so the weights
+    must still hold the codes, transpose and scale-inverse recorded on an
+    earlier micro-batch (self.w_codes) and the weight amax must stay 0."""
+
+    def __init__(self, stack, blocks=None, samples=400, seed=0):
+        self.stack, self.blocks, self.samples = stack, blocks, samples
+        self.rng = np.random.default_rng(seed)
+        self.cached = False
+        self.w_codes, self.x_codes, self.amax = {}, {}, {}
+
+    def __call__(self, b, l, y):
+        if self.blocks is not None and b not in self.blocks:
+            return
+        torch.cuda.synchronize()
+        s = self.stack
+        st, train = s.state, s.train
+        rx, rw = s.rec(b, l, R_X), s.rec(b, l, R_W)
+        scale, cur = f32(st.scale), f32(st.amax_cur)
+        qx, qw = s.qx[l][b], s.qw[b][l]
+        ox, oxt, ax, six = oracle.cast_transpose_amax(_src(s.last_in[l]), scale[rx], oracle.E4M3,
+                                                      want_qt=train)
+        np.testing.assert_array_equal(bits8(qx.data), ox, err_msg=f"x codes b{b} l{l}")
+        if train:
+            np.testing.assert_array_equal(bits8(qx.data_t), oxt, err_msg=f"x^T b{b} l{l}")
+        assert cur[rx].view(np.uint32) == np.float32(ax).view(np.uint32), f"x amax b{b} l{l}"
+        assert f32_bits(qx.scale_inv)[0] == six.view(np.uint32)
+        if self.cached:
+            ow, owt, siw = self.w_codes[(b, l)]
+            assert cur[rw] == 0.0, f"weight amax recorded on a cached micro-batch b{b} l{l}"
+            aw = np.float32(0.0)
+        else:
+            ow, owt, aw, siw = oracle.cast_transpose_amax(_src(s.w[b][l]), scale[rw],
+                                                          oracle.E4M3, want_qt=train)
+            assert cur[rw].view(np.uint32) == np.float32(aw).view(np.uint32), f"w amax b{b} l{l}"
+            self.w_codes[(b, l)] = (ow, owt, siw)
+        np.testing.assert_array_equal(bits8(qw.data), ow, err_msg=f"w codes b{b} l{l}")
+        if train:
+            np.testing.assert_array_equal(bits8(qw.data_t), owt, err_msg=f"w^T b{b} l{l}")
+        assert f32_bits(qw.scale_inv)[0] == np.float32(siw).view(np.uint32)
+        self.amax[rx], self.amax[rw] = ax, aw
+        self.x_codes[(b, l)] = (ox, oxt, six)
+        n = self.samples
+        r = self.rng.integers(0, M, n)
+        c = self.rng.integers(0, y.shape[1], n)
+        bias = s.b16[b][l]
+        ref = oracle.gemm_nt_sampled(ox, 0, ow, 0, six, siw, r, c,
+                                     bias=None if bias is None else bits16(bias))
+        assert_gemm_close(bf16_values(bits16(y))[r, c], bf16_values(ref), f"linear b{b} l{l}")
+
+
+class BackwardCheck:
+    """stack.probe_bwd: after the backward of linear l of block b, compare
+    the E5M2 cast of its output gradient (codes, transpose, amax,
+    scale-inverse) with the oracle bit for bit and the fused bias gradient
+    with the oracle's exact column sums within the stated summation bound;
+    for the blocks in `full`, also sampled dgrad and wgrad outputs against
+    the oracle's products of the oracle's codes."""
+
+    def __init__(self, stack, fwd: ForwardCheck, full=(0,), samples=400, seed=1):
+        self.stack, self.fwd, self.full, self.samples = stack, fwd, set(full), samples
+        self.rng = np.random.default_rng(seed)
+        self.amax = {}
+        self.checked = []
+
+    def __call__(self, b, l, dy):
+        torch.cuda.synchronize()
+        s = self.stack
+        st = s.state
+        r = s.rec(b, l, R_DY)
+        sdy = f32(st.scale)[r]
+        dyb = bits16(dy)
+        oq, oqt, ady, sidy = oracle.cast_transpose_amax(dyb, sdy, oracle.E5M2)
+        np.testing.assert_array_equal(bits8(s.qdy[l].data), oq, err_msg=f"dY codes b{b} l{l}")
+        np.testing.assert_array_equal(bits8(s.qdy[l].data_t), oqt, err_msg=f"dY^T b{b} l{l}")
+        assert f32_bits(st.amax_cur)[r] == np.float32(ady).view(np.uint32), f"dY amax b{b} l{l}"
+        assert f32_bits(s.qdy[l].scale_inv)[0] == np.float32(sidy).view(np.uint32)
+        self.amax[r] = ady
+        if s.grad_b[b][l] is not None:
+            ref = oracle.dbias(dyb).astype(np.float64)
+            got = f32(s.grad_b[b][l]).astype(np.float64)
+            absum = np.abs(bf16_values(dyb)).sum(axis=0)
+            bound = (np.ceil(M / 128) + 13) * 2.0 ** -24 * absum
+            assert (np.abs(got - ref) <= bound).all(), f"dbias b{b} l{l}"
+        if b in self.full:
+            ox, oxt, six = self.fwd.x_codes[(b, l)]
+            ow, owt, siw = self.fwd.w_codes[(b, l)]
+            n = self.samples
+            fin = s.dx[l].shape[1]
+            fout = dy.shape[1]
+            rr, cc = self.rng.integers(0, M, n), self.rng.integers(0, fin, n)
+            ref = oracle.gemm_nt_sampled(oq, 1, owt, 0, sidy, siw, rr, cc)
+            assert_gemm_close(bf16_values(bits16(s.dx[l]))[rr, cc], bf16_values(ref),
+                              f"dgrad b{b} l{l}")
+            rn, ck = self.rng.integers(0, fout, n), self.rng.integers(0, fin, n)
+            ref = oracle.gemm_nt_sampled(oqt, 1, oxt, 0, sidy, six, rn, ck,
+                                         out_kind=oracle.OUT_FP32)
+            assert_gemm_close(f32(s.grad_w[b][l])[rn, ck].astype(np.float64),
+                              ref.astype(np.float64), f"wgrad b{b} l{l}")
+            self.checked.append((b, l))
+
+
+def _x(seed):
+    return workloads.uniform_bf16((M, H), seed).to(DEV)
+
+
+def test_two_block_forward_every_linear_and_the_update_against_the_oracle():
+    stack = ToyStack(dsl, workloads, 2)
+    chk = ForwardCheck(stack)
+    stack.probe = chk
+    stack.forward(_x(workloads.SEED_X), fused=True, update=False)
+    assert len(chk.w_codes) == 12
+    _update_and_check(stack, chk.amax)
+    assert (f32(stack.state.scale) != 1.0).all()          # every record saw a nonzero amax
+
+
+def test_cached_weights_second_micro_batch_against_the_oracle():
+    """Micro-batch 1 casts the weights (flag 0); after the scale update,
+    micro-batch 2 keeps them (flag 1).  On micro-batch 2 every product must
+    equal the oracle's product of fresh input codes with the CACHED weight
+    codes and the weights' scale-inverse snapshot of micro-batch 1 (not the
+    updated weight scale), no weight amax is recorded, and the update after
+    it matches the oracle for all 24 records (the weights' histories take a
+    zero)."""
+    stack = ToyStack(dsl, workloads, 2)
+    chk = ForwardCheck(stack)
+    stack.probe = chk
+    stack.flag.fill_(0)
+    stack.forward(_x(11), fused=True, update=False)
+    _update_and_check(stack, chk.amax)
+    w_scales_after_1 = f32(stack.state.scale)[[stack.rec(b, l, R_W) for b in range(2)
+                                               for l in range(6)]]
+    assert (w_scales_after_1 != 1.0).all()                # the recipe moved the weight scales ...
+    chk.cached = True
+    stack.flag.fill_(1)
+    stack.forward(_x(12), fused=True, update=False)       # ... but the GEMMs use the snapshots
+    for (b, l), (_, _, siw) in chk.w_codes.items():
+        assert siw == np.float32(1.0)                     # micro-batch 1 cast with the initial scale
+    pre = _update_and_check(stack, chk.amax)
+    for b in range(2):
+        for l in range(6):
+            assert pre["amax_cur"][stack.rec(b, l, R_W)] == 0.0
+
+
+def test_one_graph_serves_both_micro_batches():
+    """The 2-block forward captured once and replayed with the flag flipped
+    on the device gives the eager run's bits and state for both micro-batches."""
+    x1, x2 = _x(11), _x(12)
+    eager = ToyStack(dsl, workloads, 2)
+    outs = []
+    for xv, fl in ((x1, 0), (x2, 1)):
+        eager.flag.fill_(fl)
+        outs.append(eager.forward(xv, fused=True).clone())
+    torch.cuda.synchronize()
+    g = ToyStack(dsl, workloads, 2)
+    warm = ToyStack(dsl, workloads, 1)
+    xin = torch.empty_like(x1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                 # first launches on a side stream
+        warm.forward(x1, fused=True)
+        warm.forward(x1, fused=False)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gout = g.forward(xin, fused=True)
+    for rep, (xv, fl) in enumerate(((x1, 0), (x2, 1))):
+        xin.copy_(xv)
+        g.flag.fill_(fl)
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(gout.view(torch.int16), outs[rep].view(torch.int16)), f"micro-batch {rep + 1}"
+    for name in ("amax_history", "scale", "scale_inv"):
+        assert torch.equal(getattr(g.state, name), getattr(eager.state, name)), name
+
+
+def test_fused_producers_match_torch_glue():
+    """Modulation and residual adds fused into the casts give the bits of
+    torch glue followed by plain casts, over two steps (the second with
+    updated scales), outputs and state."""
+    x = _x(21)
+    a, b = ToyStack(dsl, workloads, 2), ToyStack(dsl, workloads, 2)
+    for _ in range(2):
+        ya = a.forward(x, fused=False)
+        yb = b.forward(x, fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
+    for name in ("amax_history", "scale", "scale_inv"):
+        assert torch.equal(getattr(a.state, name), getattr(b.state, name)), name
 
 
 def test_graph_capture_replays_match_eager():
-    """One delayed-scaling iteration (two casts, the forward GEMM, the scale
-    update) captured in a HIP graph and replayed three times, with eager work
-    and synchronisations between replays, matches the same iteration run
-    eagerly on a separate copy of the state: nothing in the library
-    allocates, synchronises or reads device memory on the host."""
+    """One delayed-scaling iteration of one linear (two casts, the forward
+    GEMM, the scale update) captured in a HIP graph and replayed three times,
+    with eager work and synchronisations between replays, matches the same
+    iteration run eagerly on a separate copy of the state: nothing in the
+    library allocates, synchronises or reads device memory on the host."""
     Mg, N, K = 1024, 4096, 2048
     x = workloads.uniform_bf16((Mg, K), 7).to(DEV)
     w = workloads.normal_bf16((N, K), 0.02, 8).to(DEV)
@@ -135,7 +285,6 @@ def test_graph_capture_replays_match_eager():
 
     g_st, g_qx, g_qw, g_y = make()
     e_st, e_qx, e_qw, e_y = make()
-    # Warm up on a side stream (first launches set kernel attributes).
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -147,13 +296,12 @@ def test_graph_capture_replays_match_eager():
     with torch.cuda.graph(graph):
         iteration(g_st, g_qx, g_qw, g_y)
     torch.cuda.synchronize()
-    # Capture does not execute: the graph's state is still the initial one.
     assert float(g_st.scale[0]) == 1.0 and float(g_st.amax_history.abs().sum()) == 0.0
     for rep in range(3):
         graph.replay()
         iteration(e_st, e_qx, e_qw, e_y)
         torch.cuda.synchronize()
-        junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)  # eager work
+        junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
         torch.cuda.synchronize()
         del junk
         for got, want in ((g_qx.data, e_qx.data), (g_qw.data, e_qw.data), (g_qw.data_t, e_qw.data_t)):
@@ -161,156 +309,51 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(g_y.view(torch.int16), e_y.view(torch.int16)), f"replay {rep}: Y differs"
         for name in ("amax_history", "amax_cur", "scale", "scale_inv"):
             assert torch.equal(getattr(g_st, name), getattr(e_st, name)), f"replay {rep}: {name}"
-    assert float(g_st.scale[0]) != 1.0                  # the state did evolve
+    assert float(g_st.scale[0]) != 1.0
 
 
-class _CachedWeightStack:
-    """Toy-block forward whose FP8 weights persist across micro-batches: the
-    weight casts take a device no-op flag (0 = cast, 1 = keep the cached
-    codes, transpose and scale-inverse), so one captured graph serves both."""
-
-    def __init__(self, blocks):
-        H = workloads.HIDDEN
-        self.flag = torch.zeros(1, dtype=torch.int32, device=DEV)
-        self.st = dsl.DelayedScalingState([0] * (12 * blocks), device=DEV)
-        self.blocks = []
-        for bi in range(blocks):
-            lins = []
-            for (w, b), (fin, fout, _) in zip(_block_weights(bi), workloads.toy_block_linears()):
-                qw = dsl.Float8Tensor.empty(fout, fin, 0, device=DEV)
-                qx = dsl.Float8Tensor.empty(M, fin, 0, device=DEV)
-                lins.append((w, b, qw, qx, torch.empty(M, fout, dtype=torch.bfloat16, device=DEV)))
-            self.blocks.append(lins)
-        self.H = H
-
-    def _lin(self, bi, l, inp):
-        w, b, qw, qx, y = self.blocks[bi][l]
-        tx, tw = 12 * bi + 2 * l, 12 * bi + 2 * l + 1
-        st = self.st
-        dsl.fp8_cast_transpose_amax(inp, st.scale[tx:tx + 1], qx, st.amax_cur[tx:tx + 1])
-        dsl.fp8_cast_transpose_amax(w, st.scale[tw:tw + 1], qw, st.amax_cur[tw:tw + 1],
-                                    noop_flag=self.flag)
-        dsl.fp8_linear_fwd(qx, qw, b, y)
-        return y
-
-    def _cast_w_gemm(self, bi, l):
-        """Weight cast (flag-gated) and GEMM of linear l, its input already cast in qx."""
-        w, b, qw, qx, y = self.blocks[bi][l]
-        tw = 12 * bi + 2 * l + 1
-        dsl.fp8_cast_transpose_amax(w, self.st.scale[tw:tw + 1], qw, self.st.amax_cur[tw:tw + 1],
-                                    noop_flag=self.flag)
-        dsl.fp8_linear_fwd(qx, qw, b, y)
-        return y
-
-    def _cast_in(self, bi, l, inp):
-        tx = 12 * bi + 2 * l
-        dsl.fp8_cast_transpose_amax(inp, self.st.scale[tx:tx + 1], self.blocks[bi][l][3],
-                                    self.st.amax_cur[tx:tx + 1])
-
-    def _produce_in(self, bi, l, op, x, a, b, y):
-        tx = 12 * bi + 2 * l
-        dsl.fp8_produce_cast_transpose_amax(op, x, a, b, y, self.st.scale[tx:tx + 1],
-                                            self.blocks[bi][l][3], self.st.amax_cur[tx:tx + 1])
-        return y
-
-    def forward_fused(self, x):
-        """forward() with each linear's input produced and cast in one pass
-        (modulation, residual adds of one or two terms): no torch glue left
-        but the last block's residual add."""
-        H = self.H
-        nb = len(self.blocks)
-        self._cast_in(0, 0, x)
-        for bi in range(nb):
-            mod = self._cast_w_gemm(bi, 0)
-            x = self._produce_in(bi, 1, dsl.PRODUCE_MODULATE, x, mod[:, :H], mod[:, H:2 * H],
-                                 torch.empty_like(x))
-            sa = self._cast_w_gemm(bi, 1)
-            x = self._produce_in(bi, 2, dsl.PRODUCE_ADD, x, sa[:, :H], None, torch.empty_like(x))
-            self._cast_in(bi, 3, x)
-            ca_q = self._cast_w_gemm(bi, 2)
-            ca_k = self._cast_w_gemm(bi, 3)
-            x = self._produce_in(bi, 4, dsl.PRODUCE_ADD2, x, ca_q, ca_k[:, :H],
-                                 torch.empty_like(x))
-            h = self._cast_w_gemm(bi, 4)
-            self._cast_in(bi, 5, h)
-            o = self._cast_w_gemm(bi, 5)
-            if bi + 1 < nb:
-                x = self._produce_in(bi + 1, 0, dsl.PRODUCE_ADD, x, o, None, torch.empty_like(x))
-            else:
-                x = x + o
-        self.st.update()
-        return x
-
-    def forward(self, x):
-        H = self.H
-        for bi in range(len(self.blocks)):
-            mod = self._lin(bi, 0, x)
-            x = torch.nan_to_num((mod[:, :H].float() * x.float() / mod[:, H:2 * H].float())
-                                 .to(torch.bfloat16), nan=0.0, posinf=0.0, neginf=0.0)
-            x = x + self._lin(bi, 1, x)[:, :H]
-            x = x + self._lin(bi, 2, x) + self._lin(bi, 3, x)[:, :H]
-            h = self._lin(bi, 4, x)
-            x = x + self._lin(bi, 5, h)
-        self.st.update()
-        return x
-
-
-def test_cached_weights_and_whole_forward_graph():
-    """Two micro-batches of a 2-block forward (weights cast on the first,
-    kept on the second by the device flag), eager and as one captured graph
-    replayed with the flag flipped on the device: identical bits, and the
-    cached FP8 weights are left untouched by the second micro-batch."""
-    x1 = workloads.uniform_bf16((M, workloads.HIDDEN), 11).to(DEV)
-    x2 = workloads.uniform_bf16((M, workloads.HIDDEN), 12).to(DEV)
-
-    eager = _CachedWeightStack(2)
-    eager.flag.fill_(0)
-    e1 = eager.forward(x1).clone()
+def test_training_step_block0_against_the_oracle():
+    """A training step of a 2-block stack at full shape (HYBRID: E4M3
+    inputs and fp32-sourced weights, E5M2 output gradients).  The first step
+    moves every scale off its initial 1; on the second, every linear's
+    forward casts and products (both blocks), every gradient cast with its
+    fused bias gradient (both blocks), and block 0's dgrad and wgrad
+    products are checked against the oracle, and then the one update over
+    all 36 records."""
+    stack = ToyStack(dsl, workloads, 2, train=True)
+    x = _x(workloads.SEED_X)
+    target = workloads.uniform_bf16((M, H), workloads.SEED_X + 1).to(DEV)
+    stack.train_step(x, target)                         # step 1 (scales start at 1)
     torch.cuda.synchronize()
-    cached = [(qw.data.clone(), qw.data_t.clone(), qw.scale_inv.clone())
-              for lins in eager.blocks for (_, _, qw, _, _) in lins]
-    eager.flag.fill_(1)
-    e2 = eager.forward(x2).clone()
+    assert (f32(stack.state.scale) != 1.0).all()
+    fwd = ForwardCheck(stack)
+    bwd = BackwardCheck(stack, fwd, full=(0,))
+    stack.probe, stack.probe_bwd = fwd, bwd
+    stack.refresh_bias_copies()
+    out = stack.forward(x, fused=True, update=False)
+    g = torch.sub(out, target).mul_(2.0 / out.numel())
+    stack.backward(g)
+    assert sorted(bwd.checked) == [(0, l) for l in range(6)]
+    want = dict(fwd.amax)
+    want.update(bwd.amax)
+    assert len(want) == 36
+    _update_and_check(stack, want)
+    for l in range(6):
+        assert float(stack.grad_w[0][l].abs().max()) > 0.0   # gradients reached block 0
+
+
+def test_full_32_block_forward_late_records_against_the_oracle():
+    """The whole 32-block forward with fused producers: the last block's six
+    linears are checked against the oracle (their inputs carry 31 blocks of
+    residual growth and the unsanitised modulation), then the update over
+    all 384 records against the oracle's update of the same state.  The
+    output's non-finite count is reported, not required to be zero."""
+    stack = ToyStack(dsl, workloads, 32)
+    chk = ForwardCheck(stack, blocks={31})
+    stack.probe = chk
+    out = stack.forward(_x(workloads.SEED_X), fused=True, update=False)
     torch.cuda.synchronize()
-    after = [(qw.data, qw.data_t, qw.scale_inv) for lins in eager.blocks for (_, _, qw, _, _) in lins]
-    for (d0, t0, s0), (d1, t1, s1) in zip(cached, after):
-        assert torch.equal(d0, d1) and torch.equal(t0, t1) and torch.equal(s0, s1)
-    # weights amax: recorded on the first micro-batch only
-    assert float(eager.st.amax_history[1, 0]) == 0.0 and float(eager.st.amax_history[1, 1]) > 0.0
-
-    g = _CachedWeightStack(2)
-    xin = torch.empty_like(x1)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):                 # warm-up launches on a side stream
-        w = _CachedWeightStack(1)
-        w.forward(x1)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        gout = g.forward(xin)
-    for rep, (xv, flag, want) in enumerate(((x1, 0, e1), (x2, 1, e2))):
-        xin.copy_(xv)
-        g.flag.fill_(flag)
-        graph.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(gout.view(torch.int16), want.view(torch.int16)), f"micro-batch {rep + 1}"
-    for name in ("amax_history", "scale", "scale_inv"):
-        assert torch.equal(getattr(g.st, name), getattr(eager.st, name)), name
-
-
-def test_fused_producers_forward_matches_torch_glue():
-    """The 2-block forward with the modulation and the residual adds fused into
-    the following casts gives the same bits as the forward with torch glue
-    followed by separate casts (same scales, same weights): outputs, and the
-    whole delayed-scaling state after the update."""
-    x = workloads.uniform_bf16((M, workloads.HIDDEN), 21).to(DEV)
-    a, b = _CachedWeightStack(2), _CachedWeightStack(2)
-    for _ in range(2):                         # two steps: the second uses updated scales
-        ya = a.forward(x)
-        yb = b.forward_fused(x)
-        torch.cuda.synchronize()
-        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
-    for name in ("amax_history", "scale", "scale_inv"):
-        assert torch.equal(getattr(a.st, name), getattr(b.st, name)), name
+    assert len(chk.w_codes) == 6
+    _update_and_check(stack, chk.amax)
+    nonfinite = int((~torch.isfinite(out.float())).sum())
+    print(f"32-block forward: {nonfinite} non-finite of {out.numel()} outputs")
