@@ -347,17 +347,30 @@ class ToyStack:
 
     `fused` computes the modulation and residual adds inside the casts of the
     linear inputs they produce (fp8_produce_cast_transpose_amax); otherwise
-    they run as torch elementwise ops followed by plain casts.  Nothing is
-    sanitised: a zero in the modulation's divisor gives infinities, which the
-    casts saturate.  `train` keeps what the backward needs (every FP8 input
-    with its transpose, the block inputs and modulation outputs) and holds
-    fp32 master weights (the FP8 run of the page keeps fp32 parameters) whose
-    FP8 casts read fp32 directly.
+    they run as torch elementwise ops followed by plain casts.
+
+    `modulate="page"` is the page's modulation, unsanitised: a divisor that
+    is exactly zero gives infinities (the casts saturate them, residual sums
+    can turn them into NaNs).  At the initial scale 1 the E4M3 products sum
+    exactly on a coarse grid, so linear output + bf16 bias cancels to zero a
+    few times in 10^6; a record whose amax is then infinite keeps scale 1
+    under delayed scaling, so the stack never leaves it.  `modulate="finite"`
+    (this library's addition, on no page) replaces non-finite quotients by
+    +0; the timed workloads use it.
+
+    `train` keeps what the backward needs (every FP8 input with its
+    transpose, the block inputs and modulation outputs) and holds fp32 master
+    weights (the FP8 run of the page keeps fp32 parameters) whose FP8 casts
+    read fp32 directly.
     """
 
     def __init__(self, dsl, workloads, blocks: int, *, train: bool = False, dev: str = "cuda",
-                 seed: int = 20, weights=None):
+                 seed: int = 20, weights=None, modulate: str = "finite"):
         self.dsl, self.blocks, self.train, self.dev = dsl, blocks, train, dev
+        if modulate not in ("page", "finite"):
+            raise ValueError("modulate must be 'page' or 'finite'")
+        self.finite = modulate == "finite"
+        self.mod_op = dsl.PRODUCE_MODULATE_FINITE if self.finite else dsl.PRODUCE_MODULATE
         self.H, self.M = workloads.HIDDEN, workloads.TOKENS
         self.lin = workloads.toy_block_linears()
         nl = len(self.lin)
@@ -450,8 +463,10 @@ class ToyStack:
             dsl.fp8_produce_cast_transpose_amax(op, x, a, c, out, self._sl(st.scale, r),
                                                 self.qx[l][b], self._sl(st.amax_cur, r))
             return out
-        if op == dsl.PRODUCE_MODULATE:
+        if op in (dsl.PRODUCE_MODULATE, dsl.PRODUCE_MODULATE_FINITE):
             out.copy_(torch.div(a.float() * x.float(), c.float()))
+            if op == dsl.PRODUCE_MODULATE_FINITE:
+                torch.nan_to_num_(out, nan=0.0, posinf=0.0, neginf=0.0)
         elif op == dsl.PRODUCE_ADD:
             torch.add(x, a, out=out)
         else:
@@ -469,7 +484,7 @@ class ToyStack:
         h = x
         for b in range(self.blocks):
             m = self._linear(b, L_MOD, out=self.mod_out[b])
-            self._produce(b, L_SELF, dsl.PRODUCE_MODULATE, h, m[:, :H], m[:, H:2 * H], h1, fused)
+            self._produce(b, L_SELF, self.mod_op, h, m[:, :H], m[:, H:2 * H], h1, fused)
             s = self._linear(b, L_SELF)
             self._produce(b, L_CROSS_Q, dsl.PRODUCE_ADD, h1, s[:, :H], None, h2, fused)
             self._cast_in(b, L_CROSS_KV, h2)
@@ -521,9 +536,13 @@ class ToyStack:
             self.dy[L_SELF][:, :H].copy_(g)
             g = g + self._linear_bwd(b, L_SELF, self.dy[L_SELF])
             # modulation h1 = gain * h0 / div: gradients of gain, div and h0
+            # (zero where the finite modulation replaced a non-finite quotient)
             m, h0 = self.mod_out[b], self.h_in[b].float()
             gain, div = m[:, :H].float(), m[:, H:2 * H].float()
             t = g.float() / div
+            if self.finite:
+                kept = torch.isfinite((gain * h0 / div).to(torch.bfloat16))
+                t = torch.where(kept, t, torch.zeros((), device=t.device))
             self.dy[L_MOD][:, :H].copy_(t * h0)
             self.dy[L_MOD][:, H:2 * H].copy_(-(t * gain) * h0 / div)
             g_direct = (t * gain).to(torch.bfloat16)
@@ -543,12 +562,15 @@ class ToyStack:
         return out
 
 
-def torch_block_forward(h, ws, H):
+def torch_block_forward(h, ws, H, finite: bool = True):
     """The same block in plain torch (bf16 activations; weights used as
-    given, or under torch.autocast): the comparator of the FP8 stack."""
+    given, or under torch.autocast): the comparator of the FP8 stack, with
+    the same choice of modulation."""
     f = torch.nn.functional.linear
     m = f(h, ws[L_MOD][0], ws[L_MOD][1])
     h = m[:, :H] * h / m[:, H:2 * H]
+    if finite:
+        h = torch.nan_to_num(h, nan=0.0, posinf=0.0, neginf=0.0)
     h = h + f(h, ws[L_SELF][0])[:, :H]
     h = (h + f(h, ws[L_CROSS_Q][0])) + f(h, ws[L_CROSS_KV][0])[:, :H]
     return h + f(f(h, ws[L_UP][0], ws[L_UP][1]), ws[L_DOWN][0], ws[L_DOWN][1])
@@ -629,6 +651,17 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     return out
 
 
+def _adamw(params):
+    """torch's fused AdamW where this build has it, else the foreach one."""
+    try:
+        probe = torch.zeros(4, device="cuda", requires_grad=True)
+        probe.grad = torch.ones(4, device="cuda")
+        torch.optim.AdamW([probe], lr=1e-3, fused=True).step()
+        return torch.optim.AdamW(params, lr=1e-3, fused=True)
+    except (RuntimeError, ValueError):
+        return torch.optim.AdamW(params, lr=1e-3, foreach=True)
+
+
 def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, iters: int = 50):
     """One training step of the 32-block toy stack, timed as the page times
     its model (10 warm-up iterations, then `iters` between one event pair):
@@ -655,10 +688,7 @@ def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, ite
                 bb.requires_grad_(True)
                 bb.grad = stack.grad_b[b][l]
                 params.append(bb)
-    try:
-        opt = torch.optim.AdamW(params, lr=1e-3, fused=True)
-    except (RuntimeError, ValueError):
-        opt = torch.optim.AdamW(params, lr=1e-3, foreach=True)
+    opt = _adamw(params)
     x = workloads.uniform_bf16((Mt, H), workloads.SEED_X).to(dev)
     target = workloads.uniform_bf16((Mt, H), workloads.SEED_X + 1).to(dev)
     res = {}
@@ -692,11 +722,13 @@ def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, ite
     return res
 
 
-def cpu_baseline(workloads, rows: int = 512):
-    """The oracle (plain single-threaded C) on a bounded sample of one step:
-    the full X and W casts, 512 of the 8192 rows of the dY cast, and `rows` of
-    the output rows of each of the three GEMMs (operands cast by the oracle
-    itself); extrapolated linearly to one full step."""
+def cpu_baseline(workloads, scales):
+    """The oracle (plain C; OpenMP over independent outputs, on every thread
+    it is given) running one whole step of the benchmark on the same inputs:
+    the X, W and dY casts (codes, transpose, amax), the forward (with bias),
+    dgrad and wgrad (fp32) products of the oracle's own codes, and the scale
+    update.  No sampling and no extrapolation; `scales` are the GPU state's
+    scales for x, w and dY."""
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -704,29 +736,37 @@ def cpu_baseline(workloads, rows: int = 512):
     def b16(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    x, w, _ = workloads.mlp_forward(0)
+    x, w, b = workloads.mlp_forward(0)
     dy = workloads.mlp_grad()
-    t0 = time.perf_counter()
-    qx, qxt, ax, _ = oracle.cast_transpose_amax(b16(x), 448.0, 0)
-    qw, qwt, aw, _ = oracle.cast_transpose_amax(b16(w), 4000.0, 0)
-    t_cast_xw = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    qdy, _, _, _ = oracle.cast_transpose_amax(b16(dy[:512]), 5.0e6, 1, want_qt=False)
-    t_cast_dy = (time.perf_counter() - t0) * (M / 512)
-    # rows of dY^T (= columns of dY), for the wgrad sample
-    _, qdyt, _, _ = oracle.cast_transpose_amax(b16(dy[:, :rows]), 5.0e6, 1, want_q=False)
-    t0 = time.perf_counter()
-    oracle.gemm_nt(qx[:rows], 0, qw, 0, 1.0, 1.0)                          # fwd rows
-    oracle.gemm_nt(qdy[:rows], 1, qwt, 0, 1.0, 1.0)                        # dgrad rows
-    oracle.gemm_nt(qdyt, 1, qxt, 0, 1.0, 1.0, out_kind=oracle.OUT_FP32)    # wgrad rows
-    t_gemm = (time.perf_counter() - t0) * (M / rows)
-    t_step = t_cast_xw + t_cast_dy + t_gemm
-    sample_s = t_cast_xw + t_cast_dy * 512 / M + t_gemm * rows / M
-    return {"value": round(3 * GEMM_FLOP / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-            "kind": "oracle",
-            "sample": (f"oracle C, 1 thread: full X and W casts, 512/8192 rows of the dY cast, "
-                       f"{rows}/8192 output rows of each GEMM ({sample_s:.1f} s of CPU work), "
-                       f"extrapolated to one step = {t_step:.0f} s")}
+    xb, wb, bb, dyb = b16(x), b16(w), b16(b), b16(dy)
+    sx, sw, sdy = (float(v) for v in scales)
+    t = {}
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        t[name] = time.perf_counter() - t0
+        return r
+
+    qx, qxt, ax, six = timed("cast_x", lambda: oracle.cast_transpose_amax(xb, sx, oracle.E4M3))
+    qw, qwt, aw, siw = timed("cast_w", lambda: oracle.cast_transpose_amax(wb, sw, oracle.E4M3))
+    timed("gemm_fwd", lambda: oracle.gemm_nt(qx, 0, qw, 0, six, siw, bias=bb))
+    qd, qdt, ad, sid = timed("cast_dy", lambda: oracle.cast_transpose_amax(dyb, sdy, oracle.E5M2))
+    timed("gemm_dgrad", lambda: oracle.gemm_nt(qd, 1, qwt, 0, sid, siw))
+    timed("gemm_wgrad", lambda: oracle.gemm_nt(qdt, 1, qxt, 0, sid, six,
+                                               out_kind=oracle.OUT_FP32))
+    hist = np.zeros((3, 16), np.float32)
+    cur = np.array([ax, aw, ad], np.float32)
+    sc = np.array([sx, sw, sdy], np.float32)
+    timed("scale_update", lambda: oracle.scale_update(hist, cur, sc, np.zeros(3, np.float32),
+                                                      np.array([0, 0, 1], np.uint8)))
+    total = sum(t.values())
+    return {"value": round(3 * GEMM_FLOP / total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"one whole step, no sampling: casts of X, W [8192,2048] and dY "
+                       f"[8192,8192], fwd/dgrad/wgrad 8192x8192x2048 products, scale update; "
+                       f"{total:.1f} s on {oracle.num_threads()} threads"),
+            "seconds": {k: round(v, 3) for k, v in t.items()}}
 
 
 def probe_kernels(dsl, workloads, st):
@@ -774,6 +814,11 @@ def traffic_record(root: str):
     # is unchanged.
     return {k: v for k, v in rec["kernels"].items()
             if v.get("sources") and all(rec["source_sha256"].get(n) == sha(n) for n in v["sources"])}
+
+
+def progress(msg: str) -> None:
+    """A line on stderr as each part of the benchmark finishes."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -841,17 +886,22 @@ def main():
             k["GB/s"] = round(4 * M * K / (ms * 1e-3) / 1e9, 1)
         kernels[name] = k
 
+    progress(f"step timing done ({ms_step * 1e3:.1f} us per step)")
     fwd_ms = gemm_fwd_back_to_back(dsl, st, max(args.steps, 10))
     fwd_tflops = GEMM_FLOP / (fwd_ms * 1e-3) / 1e12
     cast_ms, cast_gbs = cast_bandwidth(dsl, workloads, args.cast_iters)
     copy_gbs = copy_ceiling()
 
+    progress("roofline loops done")
     dbias_cost = dbias_cast_cost(dsl, st)
     producer_cost = producer_cast_cost(dsl, workloads)
     dyn_cost = dynamic_vs_delayed(dsl, st)
     fp8out_cost = fp8_output_forward(dsl, st)
+    progress("variant comparisons done")
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
+    progress("toy-stack forward done")
     train = None if args.no_train_step else toy_stack_train_step(dsl, workloads)
+    progress("toy-stack training step done")
     traffic = traffic_record(root)
     result = {
         "metric": "FP8 GEMM TFLOP/s (M8192 K2048 N8192) + cast-transpose-amax HBM GB/s",
@@ -896,7 +946,8 @@ def main():
     if train is not None:
         result["toy_stack_train_step"] = train
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(workloads)
+        result["cpu_baseline"] = cpu_baseline(workloads, st["state"].scale.cpu().tolist())
+        progress("cpu baseline done")
     print(json.dumps(result), flush=True)
 
 

@@ -306,8 +306,10 @@ def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
                                     amax_cur: Optional[torch.Tensor] = None,
                                     noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
     """y = op(x, a, b) in bf16 (PRODUCE_MODULATE: a * x / b, unsanitised, so a
-    zero divisor gives +-inf and 0/0 NaN; PRODUCE_ADD: x + a; PRODUCE_ADD2:
-    (x + a) + b, each sum rounded), then y cast into `out`.  x, a, b: bf16 2-D device
+    zero divisor gives +-inf and 0/0 NaN; PRODUCE_MODULATE_FINITE, the
+    library's addition: the same with non-finite results replaced by +0;
+    PRODUCE_ADD: x + a; PRODUCE_ADD2: (x + a) + b, each sum rounded), then y
+    cast into `out`.  x, a, b: bf16 2-D device
     tensors of one shape with unit column stride (column slices are fine);
     y: contiguous bf16 of that shape."""
     _need_scalar(scale, "scale")

@@ -188,7 +188,8 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
                                     int64_t ldb, uint16_t *y, int64_t rows, int64_t cols,
                                     const float *scale, const fp8_tensor_t *out, float *amax_cur,
                                     const int32_t *noop_flag, fp8_stream_t stream) {
-    if (op != FP8_PRODUCE_MODULATE && op != FP8_PRODUCE_ADD && op != FP8_PRODUCE_ADD2)
+    if (op != FP8_PRODUCE_MODULATE && op != FP8_PRODUCE_ADD && op != FP8_PRODUCE_ADD2 &&
+        op != FP8_PRODUCE_MODULATE_FINITE)
         return FP8_ERR_ARG;
     // The cast of y: same rules as a bf16 cast of a contiguous [rows, cols].
     if (int e = check_cast(y, FP8_DTYPE_BF16, rows, cols, cols, scale, out)) return e;

@@ -458,7 +458,10 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
 //        fp32 division, round to nearest even); infinities stay infinities,
 //        a NaN quotient becomes 0x7FC0, and the cast codes both by its rules;
 //   OP 2 (residual add): y = bf16(x + a); a NaN sum becomes 0x7FC0;
-//   OP 3 (two residual terms): y = bf16(bf16(x + a) + b), each sum rounded.
+//   OP 3 (two residual terms): y = bf16(bf16(x + a) + b), each sum rounded;
+//   OP 4 (modulate, finite: this library's addition, not on the pages): as
+//        OP 1, then a y that is not finite becomes +0, so a zero divisor
+//        cannot put infinities or NaNs into a model's activations.
 // One workgroup per 128 x 128 tile, the lane layout of the cast (4 rows x 16
 // columns, 16-byte loads and stores).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits_rne(float f) {
@@ -474,10 +477,12 @@ __device__ __forceinline__ uint32_t produce_pair(uint32_t xw, uint32_t aw, uint3
         const float xv = __uint_as_float(h ? (xw & 0xFFFF0000u) : (xw << 16));
         const float av = __uint_as_float(h ? (aw & 0xFFFF0000u) : (aw << 16));
         uint32_t y;
-        if constexpr (OP == FP8_PRODUCE_MODULATE) {
+        if constexpr (OP == FP8_PRODUCE_MODULATE || OP == FP8_PRODUCE_MODULATE_FINITE) {
             const float bv = __uint_as_float(h ? (bw & 0xFFFF0000u) : (bw << 16));
             const float v = (av * xv) / bv;
             y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);
+            if constexpr (OP == FP8_PRODUCE_MODULATE_FINITE)
+                y = ((y & 0x7F80u) == 0x7F80u) ? 0u : y;
         } else if constexpr (OP == FP8_PRODUCE_ADD) {
             const float v = xv + av;
             y = (v != v) ? 0x7FC0u : f32_to_bf16_bits_rne(v);
@@ -634,6 +639,15 @@ hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uin
                 x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
                 stream);
         return launch_produce_op_fmt<FP8_PRODUCE_MODULATE, FP8_E5M2>(
+            x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+            stream);
+    }
+    if (op == FP8_PRODUCE_MODULATE_FINITE) {
+        if (fmt == FP8_E4M3)
+            return launch_produce_op_fmt<FP8_PRODUCE_MODULATE_FINITE, FP8_E4M3>(
+                x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
+                stream);
+        return launch_produce_op_fmt<FP8_PRODUCE_MODULATE_FINITE, FP8_E5M2>(
             x, ldx, a, lda, b, ldb, y, rows, cols, scale, q, qt, amax_cur, scale_inv_out, noop,
             stream);
     }

@@ -80,7 +80,8 @@ typedef enum { FP8_AMAX_ALGO_MAX = 0 } fp8_amax_algo_t;
 typedef enum {
     FP8_PRODUCE_MODULATE = 1,
     FP8_PRODUCE_ADD = 2,
-    FP8_PRODUCE_ADD2 = 3
+    FP8_PRODUCE_ADD2 = 3,
+    FP8_PRODUCE_MODULATE_FINITE = 4
 } fp8_produce_op_t;
 
 /*
@@ -236,6 +237,14 @@ int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int6
  *                            add of the two cross-attention outputs, one term
  *                            at a time as torch adds them, each sum rounded;
  *                            a NaN at either step is written as 0x7FC0)
+ *
+ *   op FP8_PRODUCE_MODULATE_FINITE: this library's addition, on no page:
+ *                            FP8_PRODUCE_MODULATE, then a y that is not
+ *                            finite becomes +0.  For models whose divisor
+ *                            can be exactly zero: under delayed scaling a
+ *                            record whose amax is infinite keeps its scale,
+ *                            so without it one zero divisor keeps a model at
+ *                            its initial scales and spreads NaNs
  *
  * then writes y (bf16, row-major [rows, cols], ld = cols) and exactly what
  * fp8_cast_transpose_amax writes for the bf16 source y with this scale.

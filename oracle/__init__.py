@@ -4,8 +4,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` import this package.  The GPU library never imports, links or runs
 anything here, and nothing here imports the GPU library: the two share no code.
 
-The arithmetic lives in ``oracle.c`` (plain C, built with gcc, single-threaded).
-This module only marshals numpy arrays into it.  Each wrapper names the passage
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc; OpenMP only over
+independent outputs, so results do not depend on the thread count).  This
+module only marshals numpy arrays into it.  Each wrapper names the passage
 of the pages it follows:
 
 * ``fp8_decode`` / ``fp8_encode`` -- the OCP float8_e4m3fn / float8_e5m2 formats
@@ -56,7 +57,8 @@ OUT_FP32 = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
-_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math"]
 
 _lib = None
 
@@ -65,7 +67,7 @@ def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (no HIP, no GPU)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm", "-lgomp"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_LIB)
         c = ctypes
         vp, i64, f32p = c.c_void_p, c.c_int64, c.POINTER(c.c_float)
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = c.c_int
         L.orc_fp8_max.argtypes = [c.c_int]
         L.orc_fp8_max.restype = c.c_double
         L.orc_fp8_decode.argtypes = [c.c_uint8, c.c_int]
@@ -120,6 +124,11 @@ def _ptr(a: np.ndarray | None):
         return None
     assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return lib().orc_num_threads()
 
 
 # ---------------------------------------------------------------- codec ----
@@ -203,6 +212,7 @@ def cast_transpose_amax(x: np.ndarray, scale: float, fmt: int, *, want_q: bool =
 PROD_MODULATE = 1
 PROD_ADD = 2
 PROD_ADD2 = 3
+PROD_MODULATE_FINITE = 4
 
 
 def produce_cast(op: int, x: np.ndarray, a: np.ndarray, b: np.ndarray | None, scale: float,

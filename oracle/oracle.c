@@ -5,8 +5,12 @@
  * baseline leg of the benchmark load this code.  It shares no source, header,
  * table or helper with the GPU library, and the GPU library never calls it.
  *
- * Everything here is a plain, slow, single-threaded restatement of what the
- * pages define, written so that it can be checked against them by eye:
+ * Everything here is a plain, slow restatement of what the pages define,
+ * written so that it can be checked against them by eye.  The only
+ * concession to speed is OpenMP over independent outputs (rows of a cast or a
+ * product, columns of a column sum, listed samples): each output is computed
+ * exactly as in a single-threaded loop, every sum in the same order, so the
+ * results do not depend on the thread count.  It follows:
  *
  *   - the OCP FP8 formats float8_e4m3fn and float8_e5m2 (the finfo table and
  *     the worked cast table in "Accelerating PyTorch Training Workloads with
@@ -36,13 +40,17 @@
  *     in fp64), times both scale-inverses, plus bias, rounded once to the
  *     output type.
  *
- * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
+ * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off -fno-fast-math
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the parallel loops below use (OMP_NUM_THREADS, else all cores). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 #define ORC_E4M3 0
 #define ORC_E5M2 1
@@ -184,6 +192,7 @@ int orc_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
     if (orc_get_fmt(fmt, &f) || (src != 0 && src != 1) || rows < 0 || cols < 0 || ld < cols)
         return -1;
     uint32_t amax_key = amax_inout ? orc_abs_key(*amax_inout) : 0u;
+#pragma omp parallel for reduction(max : amax_key) schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t c = 0; c < cols; ++c) {
             float xv = orc_load_src(x, src, r * ld + c);
@@ -218,6 +227,7 @@ int orc_cast_transpose_amax(const void *x, int src, int64_t rows, int64_t cols,
  */
 int orc_dbias(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, float *dbias) {
     if ((src != 0 && src != 1) || rows < 0 || cols < 0 || ld < cols || !dbias) return -1;
+#pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < cols; ++c) {
         double acc = 0.0;
         for (int64_t r = 0; r < rows; ++r) acc += (double)orc_load_src(x, src, r * ld + c);
@@ -241,7 +251,9 @@ int orc_dbias(const void *x, int src, int64_t rows, int64_t cols, int64_t ld, fl
  *   op 2 (residual add): y = bf16(x + a); a NaN result is 0x7FC0;
  *   op 3 (residual add of two terms, as the block adds the cross-attention
  *        outputs): y = bf16(bf16(x + a) + b), the two bf16 adds torch performs
- *        one after the other, each rounded; a NaN at either step is 0x7FC0.
+ *        one after the other, each rounded; a NaN at either step is 0x7FC0;
+ *   op 4 (the library's finite modulation, on no page): op 1, then a y that
+ *        is infinite or NaN becomes +0.
  * x, a, b are bf16 [rows, cols] with leading dimensions ldx, lda, ldb (b is
  * read by ops 1 and 3); y is bf16 [rows, cols], row-major.  The cast is then
  * exactly orc_cast_transpose_amax of y (so +-inf saturates to +-max and NaN
@@ -256,18 +268,20 @@ int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, 
                      const uint16_t *b, int64_t ldb, int64_t rows, int64_t cols, float scale,
                      int fmt, uint16_t *y, uint8_t *q, uint8_t *qt, float *amax_inout,
                      float *scale_inv_out) {
-    if ((op != 1 && op != 2 && op != 3) || rows < 0 || cols < 0 || ldx < cols || lda < cols ||
+    if ((op < 1 || op > 4) || rows < 0 || cols < 0 || ldx < cols || lda < cols ||
         !y || (op != 2 && (!b || ldb < cols)))
         return -1;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t c = 0; c < cols; ++c) {
             float xv = orc_bf16_to_f32(x[r * ldx + c]);
             float av = orc_bf16_to_f32(a[r * lda + c]);
             uint16_t out;
-            if (op == 1) {
+            if (op == 1 || op == 4) {
                 float bv = orc_bf16_to_f32(b[r * ldb + c]);
                 float prod = av * xv;
                 out = orc_f32_to_bf16_canon(prod / bv);
+                if (op == 4 && !isfinite(orc_bf16_to_f32(out))) out = 0x0000;
             } else if (op == 2) {
                 out = orc_f32_to_bf16_canon(xv + av);
             } else {
@@ -303,6 +317,7 @@ int orc_dynamic_cast(const void *x, int src, int64_t rows, int64_t cols, int64_t
         !scale_inout || !amax_out)
         return -1;
     uint32_t best = 0;
+#pragma omp parallel for reduction(max : best) schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
             uint32_t k = orc_abs_key(orc_load_src(x, src, r * ld + c));
@@ -379,6 +394,7 @@ static void orc_store_out(void *out, int out_kind, int64_t idx, double y) {
 static double *orc_decode_rows(const uint8_t *X, int fmt, int64_t ld, int64_t n, int64_t K) {
     double *d = (double *)malloc((size_t)(n * K > 0 ? n * K : 1) * sizeof(double));
     if (!d) return NULL;
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
         for (int64_t k = 0; k < K; ++k) d[i * K + k] = orc_fp8_decode(X[i * ld + k], fmt);
     return d;
@@ -410,6 +426,7 @@ int orc_gemm_nt(const uint8_t *A, int fa, int64_t lda, const uint8_t *B, int fb,
     double *da = orc_decode_rows(A, fa, lda, M, K);
     double *db = orc_decode_rows(B, fb, ldb, N, K);
     if (!da || !db) { free(da); free(db); return -1; }
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j) {
             double acc = orc_dot(da + i * K, db + j * K, K);

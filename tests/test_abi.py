@@ -157,7 +157,8 @@ def test_produce_cast_validation():
     ok = dict(ldx=48, lda=48, ldb=48)
     call = lambda op, ldx=48, lda=48, ldb=48, b=B, x=X, y=Y, desc=d: L.fp8_produce_cast_transpose_amax(
         op, x, ldx, A, lda, b, ldb, y, desc.rows, desc.cols, 0x5000, byref(desc), None, None, None)
-    assert call(4) == -5                          # unknown op
+    assert call(5) == -5                          # unknown op
+    assert call(4, b=None) == -1                  # the finite modulation needs b too
     assert call(1, b=None) == -1                  # modulate needs b
     assert call(3, b=None) == -1                  # the two-term add needs b
     assert call(3, ldb=44) == -2

@@ -65,15 +65,20 @@ def _check_codes(got, v_ref, mag, K, scale, fo, what, prod=None):
     e = 2.0 ** -10 * prod + (K + 2) * 2.0 * U * mag + 4.0 * U * np.abs(v_ref.astype(np.float64))
     lo = (v_ref.astype(np.float64) - e).astype(np.float32)
     hi = (v_ref.astype(np.float64) + e).astype(np.float32)
-    q_ref = oracle.cast_transpose_amax(v_ref[None, :].astype(np.float32), scale, fo,
-                                       want_qt=False)[0][0]
-    q_lo = oracle.cast_transpose_amax(lo[None, :], scale, fo, want_qt=False)[0][0]
-    q_hi = oracle.cast_transpose_amax(hi[None, :], scale, fo, want_qt=False)[0][0]
-    d_got = oracle.fp8_decode(got, fo)
-    ok = (d_got >= oracle.fp8_decode(q_lo, fo)) & (d_got <= oracle.fp8_decode(q_hi, fo))
+
+    def cast(v):
+        # rows of 256 let the oracle's per-row parallel loop spread large inputs
+        v2 = v.reshape(-1, 256) if v.size % 256 == 0 and v.size else v[None, :]
+        return oracle.cast_transpose_amax(np.ascontiguousarray(v2, dtype=np.float32), scale, fo,
+                                          want_qt=False)[0].ravel()
+
+    q_ref, q_lo, q_hi = cast(v_ref), cast(lo), cast(hi)
+    table = oracle.decode_table(fo)
+    d_got = table[got]
+    ok = (d_got >= table[q_lo]) & (d_got <= table[q_hi])
     assert ok.all(), (f"{what}: {int((~ok).sum())} codes outside the rounding interval, first at "
                       f"{np.argwhere(~ok)[:5].ravel().tolist()}")
-    differs = (got != q_ref) & (d_got != oracle.fp8_decode(q_ref, fo))
+    differs = (got != q_ref) & (d_got != table[q_ref])
     assert differs.mean() <= 1e-2, f"{what}: {differs.mean():.2e} of the codes differ"
     return float(e.max(initial=0.0))
 
@@ -184,6 +189,28 @@ def test_full_size_amax_and_codes_match_fp32_product_and_cast(M, N, K):
     torch.cuda.synchronize()
     assert amax == float(v.abs().max()) == float(a2[0])
     assert torch.equal(q.data.cpu(), torch.from_numpy(got))
+
+
+def test_full_size_every_code_and_the_amax_against_the_oracle():
+    """8192 x 8192 x 2048 with bias: all 67,108,864 codes against the
+    oracle's exact v within the rounding interval, and the output amax
+    against the oracle's max |v| over the whole output within the bound."""
+    M, N, K, fo = 8192, 8192, 2048, oracle.E4M3
+    A = workloads.random_fp8_codes((M, K), 61, 0)
+    B = workloads.random_fp8_codes((N, K), 62, 0)
+    bias = workloads.normal_bf16((N,), 0.5, 63)
+    sa, sb = np.float32(1 / 61.0), np.float32(1 / 9.0)
+    bb = bits16(bias)
+    _, v_ref, amax_ref, _ = oracle.gemm_nt_fp8out(A.numpy(), 0, B.numpy(), 0, sa, sb, 1.0, fo,
+                                                  bias=bb)
+    mag = oracle.gemm_nt(_abs_codes(A.numpy()), 0, _abs_codes(B.numpy()), 0, sa, sb,
+                         out_kind=oracle.OUT_FP32).astype(np.float64)
+    mag += np.abs(oracle.bf16_bits_to_f32(bb).astype(np.float64))[None, :]
+    scale = _scale_for(v_ref, fo, 1.5)
+    got, amax, sinv = _run(A, 0, B, 0, float(sa), float(sb), bias, scale, fo)
+    emax = _check_codes(got.ravel(), v_ref.ravel(), mag.ravel(), K, scale, fo, "full 8192^2")
+    assert abs(amax - float(amax_ref)) <= emax
+    assert sinv == (np.float32(1.0) / np.float32(scale)).view(np.uint32)
 
 
 def test_specials_nan_rows_saturation_and_k_zero():

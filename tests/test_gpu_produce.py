@@ -133,6 +133,21 @@ def test_special_values(fmt):
     assert v[0, 0] == 0x7FC0 and v[3, 3] == 0x7FC0 and v[4, 4] == 0x7FC0
 
 
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_finite_modulation(fmt):
+    """The library's finite modulation: the page's quotient with non-finite
+    results replaced by +0, on special values and a ragged shape."""
+    x, a, b = _rand((400, 272), 25), _rand((400, 272), 26), _rand((400, 272), 27, 0.7)
+    b[0, :] = 0.0
+    x[1, :] = 0.0
+    b[1, :] = 0.0
+    x[2, :], a[2, :], b[2, :] = 1.0e20, 1.0e20, 1.0e-5
+    a[3, :] = float("nan")
+    y = _run_and_check(oracle.PROD_MODULATE_FINITE, x, a, b, 41.0, fmt)
+    v = bits16(y)
+    assert (v[:4] == 0).all() and np.isfinite(bf16_values(v)).all()
+
+
 def test_toy_block_modulation_with_zero_divisors():
     """The modulation at the block's real shape with a few exact zeros in the
     divisor slice (a bf16 linear output can round to zero): the infinities

@@ -65,6 +65,31 @@ def test_modulate_against_torch_with_zero_divisors_and_overflow():
     np.testing.assert_array_equal(y[1] == 0xFF80, ax[1] > 0)
 
 
+def test_finite_modulation_against_torch_nan_to_num():
+    """The library's finite modulation (not on the pages): the page's
+    quotient, then every non-finite bf16 result replaced by +0 -- torch's
+    nan_to_num(..., nan=0, posinf=0, neginf=0) of the same quotient.  Finite
+    results are the page's modulation bit for bit."""
+    a, x, b = _rand_bf16((64, 64), 41), _rand_bf16((64, 64), 42), _rand_bf16((64, 64), 43, 0.5)
+    b[0, :] = 0.0
+    b[1, :] = -0.0
+    x[2, :] = 0.0
+    b[2, :] = 0.0
+    x[3, :], a[3, :], b[3, :] = 1.0e20, 1.0e20, 1.0e-5
+    a[4, :] = float("nan")
+    y, q, qt, amax, _ = oracle.produce_cast(oracle.PROD_MODULATE_FINITE, _bits(x), _bits(a),
+                                            _bits(b), 1.0, oracle.E4M3)
+    q_page = _torch_modulate(a, x, b)
+    want = torch.nan_to_num(q_page, nan=0.0, posinf=0.0, neginf=0.0)
+    np.testing.assert_array_equal(y, _bits(want))
+    assert (y[:5] == 0).all()
+    yp, *_ = oracle.produce_cast(oracle.PROD_MODULATE, _bits(x), _bits(a), _bits(b), 1.0,
+                                 oracle.E4M3)
+    fin = torch.isfinite(q_page).numpy()
+    np.testing.assert_array_equal(y[fin], yp[fin])
+    assert np.isfinite(amax)
+
+
 def test_add_against_torch_including_nan():
     x, a = _rand_bf16((64, 48), 4), _rand_bf16((64, 48), 5, 100.0)
     x[0, 0] = float("nan")
@@ -184,4 +209,6 @@ def test_bad_arguments():
     with pytest.raises(ValueError):
         oracle.produce_cast(oracle.PROD_ADD2, x, x, None, 1.0, oracle.E4M3)       # b missing
     with pytest.raises(ValueError):
-        oracle.produce_cast(4, x, x, x, 1.0, oracle.E4M3)
+        oracle.produce_cast(oracle.PROD_MODULATE_FINITE, x, x, None, 1.0, oracle.E4M3)
+    with pytest.raises(ValueError):
+        oracle.produce_cast(5, x, x, x, 1.0, oracle.E4M3)
