@@ -540,12 +540,14 @@ class ToyStack:
             m, h0 = self.mod_out[b], self.h_in[b].float()
             gain, div = m[:, :H].float(), m[:, H:2 * H].float()
             t = g.float() / div
+            d_gain, d_div, d_h0 = t * h0, -(t * gain) * h0 / div, t * gain
             if self.finite:
                 kept = torch.isfinite((gain * h0 / div).to(torch.bfloat16))
-                t = torch.where(kept, t, torch.zeros((), device=t.device))
-            self.dy[L_MOD][:, :H].copy_(t * h0)
-            self.dy[L_MOD][:, H:2 * H].copy_(-(t * gain) * h0 / div)
-            g_direct = (t * gain).to(torch.bfloat16)
+                zero = torch.zeros((), device=t.device)
+                d_gain, d_div, d_h0 = (torch.where(kept, d, zero) for d in (d_gain, d_div, d_h0))
+            self.dy[L_MOD][:, :H].copy_(d_gain)
+            self.dy[L_MOD][:, H:2 * H].copy_(d_div)
+            g_direct = d_h0.to(torch.bfloat16)
             g = g_direct + self._linear_bwd(b, L_MOD, self.dy[L_MOD])
         return g
 

@@ -50,8 +50,8 @@ def _update_and_check(stack, want_cur=None):
             assert pre["amax_cur"][r].view(np.uint32) == np.float32(a).view(np.uint32), f"record {r}"
     stack.state.update()
     torch.cuda.synchronize()
-    hist, cur, scale, sinv = (pre["amax_history"], pre["amax_cur"], pre["scale"],
-                              pre["scale_inv"])
+    hist, cur, scale, sinv = (pre["amax_history"].copy(), pre["amax_cur"].copy(),
+                              pre["scale"].copy(), pre["scale_inv"].copy())
     oracle.scale_update(hist, cur, scale, sinv, f32(st.fmt).astype(np.uint8))
     np.testing.assert_array_equal(f32_bits(st.amax_history), hist.view(np.uint32))
     np.testing.assert_array_equal(f32_bits(st.scale), scale.view(np.uint32))
