@@ -35,7 +35,9 @@ __all__ = [
     "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
     "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
     "fp8_produce_cast_transpose_amax", "PRODUCE_MODULATE", "PRODUCE_ADD", "PRODUCE_ADD2",
+    "PRODUCE_MODULATE_FINITE",
     "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
+    "fp8_cast_transpose_amax_dbias_noalloc", "NOALLOC_SCRATCH_BYTES",
     "library_path", "lib",
 ]
 
@@ -46,6 +48,8 @@ DTYPE_FP32 = 1
 PRODUCE_MODULATE = 1
 PRODUCE_ADD = 2
 PRODUCE_ADD2 = 3
+PRODUCE_MODULATE_FINITE = 4      # the library's addition: non-finite quotients -> +0
+NOALLOC_SCRATCH_BYTES = 4 << 20     # FP8DSL_NOALLOC_SCRATCH_BYTES
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libfp8dsl.so")
@@ -88,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_cast_transpose_amax.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp]
         L.fp8_cast_transpose_amax_dbias.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp,
                                                     i64, vp, vp]
+        L.fp8_cast_transpose_amax_dbias_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp,
+                                                            vp, vp, vp]
         L.fp8_produce_cast_transpose_amax.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64,
                                                       i64, vp, dp, vp, vp, vp]
         L.fp8_cast_transpose_dynamic.argtypes = [vp, i32, i64, i64, i64, i32, vp, dp, vp, vp, vp]
@@ -98,6 +104,7 @@ def lib() -> ctypes.CDLL:
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
         for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
+                  L.fp8_cast_transpose_amax_dbias_noalloc,
                   L.fp8_produce_cast_transpose_amax, L.fp8_cast_transpose_dynamic,
                   L.fp8_linear_fwd, L.fp8_linear_fwd_fp8out, L.fp8_linear_dgrad,
                   L.fp8_linear_wgrad):
@@ -298,6 +305,38 @@ def fp8_cast_transpose_amax_dbias(x: torch.Tensor, scale: torch.Tensor, out: Flo
         _ptr(dbias, torch.float32, "dbias"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)),
         "fp8_cast_transpose_amax_dbias")
+
+
+def fp8_cast_transpose_amax_dbias_noalloc(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,
+                                          amax_cur: Optional[torch.Tensor], dbias: torch.Tensor,
+                                          noop_flag: Optional[torch.Tensor] = None,
+                                          stream=None) -> None:
+    """fp8_cast_transpose_amax_dbias with the library's own per-device
+    scratch array instead of a workspace: the call allocates nothing.  Calls
+    that overlap on one GPU race on that array; sources needing more than
+    NOALLOC_SCRATCH_BYTES of column-sum scratch raise (FP8_ERR_SCRATCH)."""
+    _need_scalar(scale, "scale")
+    _need_scalar(amax_cur, "amax_cur")
+    _need_scalar(noop_flag, "noop_flag")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride in the last dimension")
+    if x.dtype == torch.bfloat16:
+        src = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        src = DTYPE_FP32
+    else:
+        raise TypeError("x must be bf16 or fp32")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if dbias.numel() != x.shape[1]:
+        raise ValueError("dbias must have cols elements")
+    d = out.desc()
+    _check(lib().fp8_cast_transpose_amax_dbias_noalloc(
+        x.data_ptr(), src, x.shape[0], x.shape[1], _row_stride(x),
+        _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
+        _ptr(amax_cur, torch.float32, "amax_cur"), _ptr(dbias, torch.float32, "dbias"),
+        _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)),
+        "fp8_cast_transpose_amax_dbias_noalloc")
 
 
 def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,

@@ -64,6 +64,32 @@ int check_cast(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t l
     return FP8_OK;
 }
 
+// Scratch of fp8_cast_transpose_amax_dbias_noalloc: each GPU holds its own
+// copy of this array.  In host code its name is only a stand-in for the
+// device symbol, so host code never passes it to a kernel: the device
+// address is looked up once per device (with that device current) and kept
+// in noalloc_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[FP8DSL_NOALLOC_SCRATCH_BYTES];
+std::atomic<void *> noalloc_scratch_ptr[64];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device; concurrent first calls store the same address).
+hipError_t noalloc_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void *p = noalloc_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        noalloc_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 namespace fp8dsl {
@@ -114,6 +140,9 @@ const char *fp8_status_string(int status) {
         case FP8_ERR_ARG: return "FP8_ERR_ARG: argument out of range";
         case FP8_ERR_LAUNCH: return "FP8_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
         case FP8_ERR_DEVICE: return "FP8_ERR_DEVICE: no gfx950 code object for the current device";
+        case FP8_ERR_SCRATCH:
+            return "FP8_ERR_SCRATCH: the call needs more scratch than the no-allocation entry "
+                   "point holds (FP8DSL_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown fp8dsl status";
     }
 }
@@ -147,6 +176,23 @@ int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t co
 int64_t fp8_cast_dbias_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return FP8_ERR_SHAPE;
     return ((rows + 127) / 128) * ((cols + 127) / 128) * 128 * (int64_t)sizeof(float);
+}
+
+int fp8_cast_transpose_amax_dbias_noalloc(const void *x, int32_t src, int64_t rows, int64_t cols,
+                                          int64_t ld, const float *scale, const fp8_tensor_t *out,
+                                          float *amax_cur, float *dbias,
+                                          const int32_t *noop_flag, fp8_stream_t stream) {
+    // Size and argument checks first: nothing is enqueued on an error.
+    if (int e = check_cast(x, src, rows, cols, ld, scale, out)) return e;
+    if (cols > 0 && dbias == nullptr) return FP8_ERR_NULL;
+    if (dbias && (reinterpret_cast<uintptr_t>(dbias) & 3) != 0) return FP8_ERR_ALIGN;
+    const int64_t need = fp8_cast_dbias_workspace_bytes(rows, cols);
+    if (need < 0) return (int)need;
+    if (need > FP8DSL_NOALLOC_SCRATCH_BYTES) return FP8_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (hipError_t e = noalloc_scratch(&ws)) return status_of(e);
+    return fp8_cast_transpose_amax_dbias(x, src, rows, cols, ld, scale, out, amax_cur, dbias, ws,
+                                         FP8DSL_NOALLOC_SCRATCH_BYTES, noop_flag, stream);
 }
 
 int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int64_t cols,

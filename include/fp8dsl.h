@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 6
+#define FP8DSL_ABI_VERSION 7
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -60,7 +60,8 @@ typedef enum {
     FP8_ERR_FORMAT = -4,    /* an FP8 format this entry point does not accept   */
     FP8_ERR_ARG = -5,       /* another argument out of range (dtype, algo, ...) */
     FP8_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch         */
-    FP8_ERR_DEVICE = -7     /* no gfx950 code object for the current device     */
+    FP8_ERR_DEVICE = -7,    /* no gfx950 code object for the current device     */
+    FP8_ERR_SCRATCH = -8    /* more scratch than a no-allocation call holds     */
 } fp8_status_t;
 
 /* OCP 8-bit float formats ("Accelerating PyTorch Training Workloads with FP8
@@ -213,6 +214,36 @@ int fp8_cast_transpose_amax_dbias(const void *x, int32_t src, int64_t rows, int6
                                   float *amax_cur, float *dbias, void *workspace,
                                   int64_t workspace_bytes, const int32_t *noop_flag,
                                   fp8_stream_t stream);
+
+/* Bytes of the device scratch array behind fp8_cast_transpose_amax_dbias_noalloc
+ * (one per GPU the library runs on, held until the process ends). */
+#define FP8DSL_NOALLOC_SCRATCH_BYTES (4 << 20)
+
+/*
+ * fp8_cast_transpose_amax_dbias_noalloc -- fp8_cast_transpose_amax_dbias
+ * without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Same kernels, same results (codes, transpose, amax, scale-inverse and dbias
+ * bit for bit) as fp8_cast_transpose_amax_dbias; the per-tile column sums go
+ * into a file-scope device array of FP8DSL_NOALLOC_SCRATCH_BYTES bytes
+ * instead of a caller workspace.  The call allocates and frees nothing.  The
+ * first call on a device looks up that device's copy of the array once.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or several host threads) race and must be ordered
+ * by the caller.  Nothing in the array needs to start at zero (every sum the
+ * second pass reads is written by the first).
+ *
+ * Limit: fp8_cast_dbias_workspace_bytes(rows, cols) must not exceed
+ * FP8DSL_NOALLOC_SCRATCH_BYTES (4 MiB: e.g. [8192, 16384] or [16384, 8192]);
+ * larger sources return FP8_ERR_SCRATCH before anything is enqueued.
+ * Other arguments, constraints and errors as fp8_cast_transpose_amax_dbias.
+ */
+int fp8_cast_transpose_amax_dbias_noalloc(const void *x, int32_t src, int64_t rows, int64_t cols,
+                                          int64_t ld, const float *scale, const fp8_tensor_t *out,
+                                          float *amax_cur, float *dbias,
+                                          const int32_t *noop_flag, fp8_stream_t stream);
 
 /*
  * fp8_produce_cast_transpose_amax -- the elementwise operation that produces

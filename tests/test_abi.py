@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
                  "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
                  "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
                  "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic",
-                 "fp8_linear_fwd_fp8out"):
+                 "fp8_linear_fwd_fp8out", "fp8_cast_transpose_amax_dbias_noalloc"):
         assert want in names
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 6
+    assert dsl.fp8_abi_version() == 7
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -226,3 +226,23 @@ def test_binding_checks_extents_before_any_call():
         dsl.fp8_cast_transpose_dynamic(src, one, x, None)
     with pytest.raises(ValueError, match="amax_history must be"):
         dsl.fp8_scale_update(torch.zeros(16), one, one, one, u8(1))
+
+
+def test_noalloc_dbias_validation():
+    """The no-allocation entry point rejects sources whose column-sum scratch
+    exceeds the fixed array, before anything is enqueued, and keeps the
+    cast's own checks."""
+    L = dsl.lib()
+    byref = ctypes.byref
+    assert dsl.NOALLOC_SCRATCH_BYTES == 4 << 20
+    big = _desc(16384, 16384)                    # 128 x 128 tiles x 512 B = 8 MiB of sums
+    assert dsl.fp8_cast_dbias_workspace_bytes(16384, 16384) > dsl.NOALLOC_SCRATCH_BYTES
+    assert L.fp8_cast_transpose_amax_dbias_noalloc(0x4000, 0, 16384, 16384, 16384, 0x5000,
+                                                   byref(big), None, 0x6000, None, None) == -8
+    assert "SCRATCH" in dsl.fp8_status_string(-8)
+    d = _desc(30, 48)                            # rows not a multiple of 16
+    assert L.fp8_cast_transpose_amax_dbias_noalloc(0x4000, 0, 30, 48, 48, 0x5000, byref(d),
+                                                   None, 0x6000, None, None) == -2
+    d = _desc(32, 48)
+    assert L.fp8_cast_transpose_amax_dbias_noalloc(0x4000, 0, 32, 48, 48, 0x5000, byref(d),
+                                                   None, None, None, None) == -1   # dbias NULL
