@@ -27,10 +27,12 @@
 //     blocks (256 fp32 accumulators per lane).  Operand stages of 128
 //     K-bytes are written straight into two 64 KiB LDS buffers by buffer
 //     loads with the LDS flag (no staging registers), and stages stream on
-//     across tile boundaries.  The epilogue applies sinv_a * sinv_b and the
-//     bias in fp32, stages the output through the drained stage buffer in
-//     32-row blocks and stores whole row segments while the next tile's
-//     first stages are in flight.
+//     across tile boundaries.  The bf16 / fp32 epilogue writes the raw fp32
+//     accumulators straight from the accumulator registers into the drained
+//     stage buffer in half-blocks (32 rows x 64 columns), reads them back as
+//     row segments, applies sinv_a * sinv_b and the bias and stores whole
+//     row segments; it starts inside the last stage, between its MFMAs, and
+//     runs while the next tile's first stages are in flight.
 //   * gemm_nt_big_kernel -- the same tiling for large products whose K is a
 //     multiple of 16 only: 64-byte stages in three LDS buffers, loaded
 //     through registers, K tails read as zero through the buffer range check.
@@ -63,6 +65,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;
 
@@ -697,125 +700,135 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows_rsrc(void *C, int M, 
                                              (short)0, nrec, 0x00020000);
 }
 
-// bf16 epilogue of one wave's 128 x 128 tile through LDS, one 32-row
-// fragment block i at a time: 32 staging rows of 272 bytes (256 + 16 of
-// padding, 8.5 KiB at `stg`).  With the padding every lane's LDS address is
-// one per-lane base plus a constant, and both the matrix-core-layout writes
-// and the row reads take the minimum number of LDS cycles (rows 16 apart
-// share banks only between the two halves of a write).
-// stage_block_bf16: out(acc * s + bias) of block i in the matrix-core layout
-// (8 bytes per lane: lane l holds row l % 32 and, per register group g of
-// fragment column block j, columns 32 j + 8 g + 4 (l / 32) .. +3).
-// `bias` holds those columns' bf16 bias values, packed in pairs (zero past
-// N, or none).
-// stage_group_bf16 converts and writes register group g of fragment (i, j);
-// `w` is the lane's staging base, stg + (lane % 32) * 272 + 8 (lane / 32).
-template <bool HAS_BIAS>
-__device__ __forceinline__ void stage_group_bf16(const v16f (&acc)[4][4], uint8_t *w,
-                                                 const u32x2 (&bias)[4][4], float s, int i,
-                                                 int j, int g) {
-    const float bv[4] = {__uint_as_float(bias[j][g].x << 16),
-                         __uint_as_float(bias[j][g].x & 0xFFFF0000u),
-                         __uint_as_float(bias[j][g].y << 16),
-                         __uint_as_float(bias[j][g].y & 0xFFFF0000u)};
-    float v[4];
+// bf16 / fp32 epilogue of the LDS-DMA kernel, in half-blocks.  A wave's
+// 128 x 128 tile is eight half-blocks h = 2 i + p: fragment row block i
+// (tile rows 32 i .. 32 i + 31) and fragment columns 2 p, 2 p + 1 (tile
+// columns 64 p .. 64 p + 63).  A half-block is staged as the raw fp32
+// accumulators, 32 rows of 256 bytes (8 KiB), 16-byte chunk c of row q at
+// chunk c ^ (q & 15); the wave's 16 KiB staging quarter holds two (regions
+// h % 2).  The swizzle makes both the matrix-core-layout writes and the row
+// reads conflict-free (16 lanes per LDS cycle touch 16 distinct chunks).
+//
+// stage_hb writes half-block h straight from the accumulator registers (the
+// LDS store reads them; no register reads, no arithmetic): lane l holds row
+// l % 32 and, per register group g of fragment column j, the four columns
+// 32 j + 8 g + 4 (l / 32) .. +3, i.e. chunk 8 (j - 2 p) + 2 g + l / 32.
+__device__ __forceinline__ void stage_hb(const v16f (&acc)[4][4], uint8_t *reg, int lane, int h) {
+    const int i = h >> 1, p = h & 1;
+    const int q = lane & 31;
+    const int sw = (q & 15) ^ (lane >> 5);
+    uint8_t *const row = reg + q * 256;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        v[q] = HAS_BIAS ? acc[i][j][4 * g + q] * s + bv[q] : acc[i][j][4 * g + q] * s;
-    const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    *reinterpret_cast<bf16x4 *>(w + 16 * (4 * j + g)) = o;
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int j = 2 * p + jj;
+            const v4f o = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
+            *reinterpret_cast<v4f *>(row + (((8 * jj + 2 * g) ^ sw) << 4)) = o;
+        }
 }
 
-template <bool HAS_BIAS>
-__device__ __forceinline__ void stage_block_bf16(const v16f (&acc)[4][4], uint8_t *stg,
-                                                 const u32x2 (&bias)[4][4], int lane,
-                                                 float s, int i) {
-    uint8_t *const w = stg + (lane & 31) * 272 + 8 * (lane >> 5);
+// Read a staged half-block back as row segments.
+// bf16 output: v[2 it + k] is row 8 it + l / 8, logical chunk 2 (l % 8) + k,
+//   so lane l holds columns 8 (l % 8) .. +7 of its row (one 16-byte store).
+// fp32 output: v[it] is row 4 it + l / 16, chunk l % 16 (columns 4 (l % 16)
+//   .. +3, one 16-byte store).
+template <int OUT>
+__device__ __forceinline__ void read_hb(const uint8_t *reg, int lane, u32x4 (&v)[8]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) stage_group_bf16<HAS_BIAS>(acc, w, bias, s, i, j, g);
-}
-
-// Read a staged bf16 block back, 16 lanes per 256-byte row: v[it] is row
-// 4 it + lane / 16 of the block, columns 8 (lane % 16) .. +7.
-__device__ __forceinline__ void read_block_bf16(const uint8_t *stg, int lane, u32x4 (&v)[8]) {
-    const uint8_t *const r = stg + (lane >> 4) * 272 + 16 * (lane & 15);
-#pragma unroll
-    for (int it = 0; it < 8; ++it) v[it] = *reinterpret_cast<const u32x4 *>(r + it * 4 * 272);
-}
-
-// Store a block read by read_block_bf16 (tile rows 32 i .. 32 i + 31 of the
-// resource's 128): 8 instructions, each writing four 256-byte row segments.
-__device__ __forceinline__ void store_block_bf16(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[8],
-                                                 int N, int i, int c0, int lane) {
-    const int gc = c0 + 8 * (lane & 15);
-    const uint32_t cb = gc < N ? (uint32_t)gc * 2u : OUT_OOB;   // + row offset < 2^31
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int row = 32 * i + 4 * it + (lane >> 4);
-        const uint32_t off = cb + (uint32_t)(row * N) * 2u;
-        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
+    for (int n = 0; n < 8; ++n) {
+        int q, c;
+        if constexpr (OUT == FP8_DTYPE_BF16) {
+            q = 8 * (n >> 1) + (lane >> 3);
+            c = 2 * (lane & 7) + (n & 1);
+        } else {
+            q = 4 * n + (lane >> 4);
+            c = lane & 15;
+        }
+        v[n] = *reinterpret_cast<const u32x4 *>(reg + q * 256 + ((c ^ (q & 15)) << 4));
     }
 }
 
-// fp32 epilogue of one wave's tile through LDS, one 32-row fragment block i
-// at a time: 32 staging rows of 512 bytes (16 KiB at `stg`), 16-byte chunk c
-// of row q at chunk c ^ (q & 15).  Lane l holds row (l % 32) of the block
-// and, per register group g of fragment column block j, the four columns
-// 32 j + 8 g + 4 (l / 32) .. +3, i.e. chunk 8 j + 2 g + l / 32.  Bias as in
-// stage_block_bf16.
-template <bool HAS_BIAS>
-__device__ __forceinline__ void stage_wave_block_f32(const v16f (&acc)[4][4], uint8_t *stg,
-                                                     const uint8_t *bias_lds, int lane, float s,
-                                                     int i) {
-    const int q = lane & 31;
-    const int half = lane >> 5;
+// This lane's bias columns of the tile as fp32: bf16 output, columns
+// 64 p + 8 (l % 8) .. +7 at b[8 p + k]; fp32 output, columns 64 p + 4 (l % 16)
+// .. +3 at b[4 p + k].  `bl` is the tile's bf16 bias in LDS (the wave's 128
+// columns).
+template <int OUT, bool HAS_BIAS>
+__device__ __forceinline__ void load_hb_bias(const uint8_t *bl, int lane, float (&b)[16]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int k = 0; k < 16; ++k) b[k] = 0.f;
+    if constexpr (HAS_BIAS) {
+        if constexpr (OUT == FP8_DTYPE_BF16) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (HAS_BIAS) {
-                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
-                    bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
-                bv[0] = __uint_as_float(b2.x << 16);
-                bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-                bv[2] = __uint_as_float(b2.y << 16);
-                bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+            for (int p = 0; p < 2; ++p) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(bl + 2 * (64 * p + 8 * (lane & 7)));
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    b[8 * p + 2 * k] = __uint_as_float(ws[k] << 16);
+                    b[8 * p + 2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+                }
             }
-            const int c = 8 * j + 2 * g + half;
-            const v4f o = {acc[i][j][4 * g + 0] * s + bv[0], acc[i][j][4 * g + 1] * s + bv[1],
-                           acc[i][j][4 * g + 2] * s + bv[2], acc[i][j][4 * g + 3] * s + bv[3]};
-            *reinterpret_cast<v4f *>(stg + q * 512 + ((c ^ (q & 15)) << 4)) = o;
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(bl + 2 * (64 * p + 4 * (lane & 15)));
+                b[4 * p + 0] = __uint_as_float(w.x << 16);
+                b[4 * p + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+                b[4 * p + 2] = __uint_as_float(w.y << 16);
+                b[4 * p + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+            }
         }
     }
 }
 
-// Read a staged fp32 block back, 32 lanes per 512-byte row: v[it] is row
-// 2 it + lane / 32 of the block, columns 4 (lane % 32) .. +3.
-__device__ __forceinline__ void read_staged_block_f32(const uint8_t *stg, int lane,
-                                                      u32x4 (&v)[16]) {
-    const int c = lane & 31;
+// out(acc * s + bias) of half-block h from read_hb's registers, rows
+// n0 .. n1 - 1 of its loop (bf16: row groups of 8 rows, 0..3; fp32: of 4
+// rows, 0..7), stored as whole row segments (bf16: 128 bytes per row, eight
+// rows per instruction; fp32: 256 bytes, four rows) through the resource
+// over the wave's 128 output rows.  Columns past N take OUT_OOB (N is a
+// multiple of 8 for bf16 and of 4 for fp32, so a lane's columns are all in
+// or all out).
+template <int OUT, bool HAS_BIAS>
+__device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16],
+                                       __amdgpu_buffer_rsrc_t rs, int N, int c0, int lane, float s,
+                                       int h, int n0, int n1) {
+    const int i = h >> 1, p = h & 1;
+    if constexpr (OUT == FP8_DTYPE_BF16) {
+        const int gc = c0 + 64 * p + 8 * (lane & 7);
+        const uint32_t cb = gc < N ? (uint32_t)gc * 2u : OUT_OOB;   // + row offset < 2^31
+        const uint32_t voff = cb + (uint32_t)((32 * i + (lane >> 3)) * N) * 2u;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int q = 2 * it + (lane >> 5);
-        v[it] = *reinterpret_cast<const u32x4 *>(stg + q * 512 + ((c ^ (q & 15)) << 4));
-    }
-}
-
-// Store a block read by read_staged_block_f32 (tile rows 32 i .. 32 i + 31
-// of the resource's 128): 16 instructions, each writing two 512-byte row
-// segments.
-__device__ __forceinline__ void store_block_f32(__amdgpu_buffer_rsrc_t rs, const u32x4 (&v)[16],
-                                                int N, int i, int c0, int lane) {
-    const int gc = c0 + 4 * (lane & 31);
-    const uint32_t cb = gc < N ? (uint32_t)gc * 4u : OUT_OOB;   // + row offset < 2^31
+        for (int it = n0; it < n1; ++it) {
+            const u32x4 lo = v[2 * it], hi = v[2 * it + 1];
+            const float x[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(lo.z),
+                                __uint_as_float(lo.w), __uint_as_float(hi.x), __uint_as_float(hi.y),
+                                __uint_as_float(hi.z), __uint_as_float(hi.w)};
+            float y[8];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int row = 32 * i + 2 * it + (lane >> 5);
-        const uint32_t off = cb + (uint32_t)(row * N) * 4u;
-        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
+            for (int k = 0; k < 8; ++k) y[k] = HAS_BIAS ? x[k] * s + b[8 * p + k] : x[k] * s;
+            const bf16x2 o0 = {(__bf16)y[0], (__bf16)y[1]}, o1 = {(__bf16)y[2], (__bf16)y[3]},
+                         o2 = {(__bf16)y[4], (__bf16)y[5]}, o3 = {(__bf16)y[6], (__bf16)y[7]};
+            const u32x4 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
+                             __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3)};
+            // the whole offset in the vector operand: the range check that
+            // drops rows past M and columns past N does not see the scalar one
+            __builtin_amdgcn_raw_buffer_store_b128(o, rs, (int)(voff + (uint32_t)(8 * it * N) * 2u),
+                                                   0, 0);
+        }
+    } else {
+        const int gc = c0 + 64 * p + 4 * (lane & 15);
+        const uint32_t cb = gc < N ? (uint32_t)gc * 4u : OUT_OOB;   // + row offset < 2^31
+        const uint32_t voff = cb + (uint32_t)((32 * i + (lane >> 4)) * N) * 4u;
+#pragma unroll
+        for (int it = n0; it < n1; ++it) {
+            const u32x4 x = v[it];
+            const v4f y = {__uint_as_float(x.x) * s + b[4 * p + 0], __uint_as_float(x.y) * s + b[4 * p + 1],
+                           __uint_as_float(x.z) * s + b[4 * p + 2], __uint_as_float(x.w) * s + b[4 * p + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs,
+                                                   (int)(voff + (uint32_t)(4 * it * N) * 4u), 0, 0);
+        }
     }
 }
 
@@ -824,7 +837,7 @@ __device__ __forceinline__ void store_block_f32(__amdgpu_buffer_rsrc_t rs, const
 // Lane l holds row (l % 32) of fragment row block i and, per register group
 // g of fragment column block j, the four columns 32 j + 8 g + 4 (l / 32) ..
 // +3: one code word at byte 16 (2 j + g / 2) + 8 (g % 2) + 4 (l / 32) of its
-// row.  Bias as in stage_block_bf16.  The accumulators are left as they are
+// row.  The bias is read from the tile's LDS bias slot.  The accumulators are left as they are
 // (the next tile's first MFMAs start from zero).
 //   fold: t = acc * (s * so) + bias * so, the scaled value itself, is clamped
 //     and converted, and the amax keys are of |t| (the caller divides by
@@ -937,8 +950,13 @@ __device__ __forceinline__ void store_rows_q(__amdgpu_buffer_rsrc_t rs, const u3
 // stores alike on gfx9), so this waits for everything issued before them.
 template <int N>
 __device__ __forceinline__ void wait_vmem_but() {
-    static_assert(N == 8 || N == 16 || N == 24 || N == 32, "wait_vmem_but: unsupported count");
-    if constexpr (N == 8)
+    static_assert(N == 4 || N == 8 || N == 16 || N == 20 || N == 24 || N == 32,
+                  "wait_vmem_but: unsupported count");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 20)
+        asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    else if constexpr (N == 8)
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (N == 16)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -984,11 +1002,11 @@ __device__ __forceinline__ int fresh_lane_id() {
 //     requests the next tile's stage 0 and bias (two 1 KiB bias slots past
 //     the stages); the epilogue stages each wave's output in its own 16 KiB
 //     quarter of the buffer freed by stage nk-1 and reads it back as whole
-//     row segments into the (now free) fragment registers: bf16 in four
-//     32-row blocks (256-byte segments, 16 bytes of row padding), fp32 in
-//     four 32-row blocks (512-byte segments), FP8 codes in one pass
-//     (128-byte segments).  Each block's stores go out as soon as it is
-//     read back, so they drain while the next block is converted.  That
+//     row segments: bf16 and fp32 as raw accumulators in eight half-blocks
+//     through two 8 KiB regions (see stage_hb; the first ones between the
+//     last stage's MFMAs), FP8 codes in one pass (128-byte segments).  Each
+//     half-block's stores go out as soon as it is read back, so they drain
+//     while the next one is converted.  That
 //     quarter is exactly what the wave's own stage loads fill, so once its
 //     staging reads have returned the wave requests the next tile's stage 1
 //     there, with no barrier, and issues its last block's stores after it.
@@ -1094,7 +1112,7 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Output stores a tile leaves in flight past its last load request.
-    constexpr int NST = OUT == FP8_DTYPE_BF16 ? 8 : 16;
+    constexpr int NST = OUT == FP8_DTYPE_BF16 ? 4 : (OUT == FP8_DTYPE_FP32 ? 8 : 16);
     // One stage: MFMAs on both K halves around the barrier.  DMA: issue the
     // loads of stage k+2 (or of the next tile's stage 0, at `base` and
     // `ld_k0`) into this stage's buffer; RD: read the next stage's first
@@ -1152,31 +1170,43 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
 
     const int nk = K / KS;                      // >= 2 (caller guarantees)
     const float s = (*sinv_a) * (*sinv_b);
-    // bf16 output: a tile's last stage, whose buffer the epilogue stages
-    // into.  Fragment block 0 is final after the second half's first four
-    // MFMAs, so its sixteen register groups are converted and written to
-    // the staging rows (`w`) between the remaining twelve, while the
-    // matrix cores still run.  The staging quarter is free once every wave
-    // has passed the stage's barrier.
-    auto last_stage_bf16 = [&](uint32_t buf, uint8_t *w, const u32x2 (&bv)[4][4]) {
+    // bf16 / fp32 output: a tile's last stage, with the epilogue's first
+    // half-blocks (see stage_hb) staged, read back and stored between the
+    // MFMAs of its second half.  The wave's staging quarter `stg` (regions
+    // stg and stg + 8 KiB) is free once every wave has passed the stage's
+    // barrier.  Fragment (i, j) is final after the MFMA of slot 4 i + j, so
+    // half-block h = 2 i + p can be staged one slot after slot 4 i + 2 p + 1.
+    // A wave's LDS instructions execute in issue order, so a region is
+    // rewritten right after the read of its previous half-block is issued,
+    // and read right after it is written.  The arithmetic of a half-block is
+    // spread one quarter (U store loops, about a dozen vector instructions)
+    // per MFMA, which the matrix core's 64 cycles per instruction cover.
+    // Half-blocks 0, 1 and the first quarter of 2 are stored here; va holds
+    // half-block 2 on return.
+    constexpr int U = OUT == FP8_DTYPE_BF16 ? 1 : 2;   // store loops per quarter
+    auto last_stage_hb = [&](uint32_t buf, uint8_t *stg, u32x4 (&va)[8], u32x4 (&vb)[8],
+                             const float (&bb)[16], __amdgpu_buffer_rsrc_t ors, int cc0, int el) {
         first_half(buf, std::false_type{});   // stage nk-1 >= 1 is never a tile's first
         __syncthreads();
+        auto quarter = [&](const u32x4 (&v)[8], int h, int qn) {
+            out_hb<OUT, HAS_BIAS>(v, bb, ors, N, cc0, el, s, h, qn * U, qn * U + U);
+        };
 #pragma unroll
-        for (int slot = 0; slot < 16; ++slot) {
-            const int i = slot >> 2, j = slot & 3;
+        for (int sl = 0; sl < 16; ++sl) {
+            const int i = sl >> 2, j = sl & 3;
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 bf[1][j], af[1][i], acc[i][j], FB, FA, 0, 0, 0, 0);
-            // Groups 0-7 two per slot in slots 4-7, groups 8-15 one per
-            // slot in slots 8-15; group n is (j, g) = (n / 4, n % 4), whose
-            // last MFMA went out in slot n / 4.
-            if (slot >= 4 && slot < 8) {
-                const int n = 2 * (slot - 4);
-                stage_group_bf16<HAS_BIAS>(acc, w, bv, s, 0, n >> 2, n & 3);
-                stage_group_bf16<HAS_BIAS>(acc, w, bv, s, 0, (n + 1) >> 2, (n + 1) & 3);
-            } else if (slot >= 8) {
-                const int n = slot;
-                stage_group_bf16<HAS_BIAS>(acc, w, bv, s, 0, n >> 2, n & 3);
-            }
+            if (sl == 2) stage_hb(acc, stg, el, 0);
+            if (sl == 4) stage_hb(acc, stg + 8192, el, 1);
+            if (sl == 5) read_hb<OUT>(stg, el, va);
+            if (sl == 6) stage_hb(acc, stg, el, 2);
+            if (sl >= 7 && sl <= 10) quarter(va, 0, sl - 7);
+            if (sl == 9) read_hb<OUT>(stg + 8192, el, vb);
+            if (sl == 10) stage_hb(acc, stg + 8192, el, 3);
+            if (sl >= 11 && sl <= 14) quarter(vb, 1, sl - 11);
+            if (sl == 13) read_hb<OUT>(stg, el, va);
+            if (sl == 14) stage_hb(acc, stg, el, 4);
+            if (sl == 15) quarter(va, 2, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -1261,43 +1291,45 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         const int el = fresh_lane_id();
         uint8_t *stg = lds + sbuf + wave * 16384;
         const uint8_t *bl = bias_lds + 1024 * slot + 2 * wn * WT;
-        [[maybe_unused]] u32x2 bv[4][4];
-        if constexpr (OUT == FP8_DTYPE_BF16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bv[j][g] = u32x2{0u, 0u};
-                    if constexpr (HAS_BIAS)
-                        bv[j][g] = *reinterpret_cast<const u32x2 *>(bl + 2 * (j * 32 + 8 * g + 4 * (el >> 5)));
-                }
-            last_stage_bf16(buf, stg + (el & 31) * 272 + 8 * (el >> 5), bv);   // stage nk-1
+        const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
+        if constexpr (!is_q_out<OUT>()) {
+            constexpr int EB = OUT == FP8_DTYPE_BF16 ? 2 : 4;
+            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<EB>(Cv, M, N, r0);
+            float bb[16];
+            load_hb_bias<OUT, HAS_BIAS>(bl, el, bb);
+            u32x4 va[8], vb[8];
+            last_stage_hb(buf, stg, va, vb, bb, ors, cc0, el);   // stage nk-1, half-blocks 0-2
+            buf ^= STAGE;                                     // the next tile's stage 0
+            uint8_t *const reg1 = stg + 8192;
+            // The rest of the tile, each read issued before the previous
+            // half-block's arithmetic so that its latency is covered.
+            read_hb<OUT>(reg1, el, vb);                        // 3
+            stage_hb(acc, reg1, el, 5);
+            out_hb<OUT, HAS_BIAS>(va, bb, ors, N, cc0, el, s, 2, U, 4 * U);
+            read_hb<OUT>(stg, el, va);                         // 4
+            stage_hb(acc, stg, el, 6);
+            out_hb<OUT, HAS_BIAS>(vb, bb, ors, N, cc0, el, s, 3, 0, 4 * U);
+            read_hb<OUT>(reg1, el, vb);                        // 5
+            stage_hb(acc, reg1, el, 7);
+            out_hb<OUT, HAS_BIAS>(va, bb, ors, N, cc0, el, s, 4, 0, 4 * U);
+            read_hb<OUT>(stg, el, va);                         // 6
+            out_hb<OUT, HAS_BIAS>(vb, bb, ors, N, cc0, el, s, 5, 0, 4 * U);
+            read_hb<OUT>(reg1, el, vb);                        // 7
+            out_hb<OUT, HAS_BIAS>(va, bb, ors, N, cc0, el, s, 6, 0, 4 * U);
+            // The staging quarter is the one this wave's own stage loads
+            // fill and no other wave reads it: once this wave's staging
+            // reads have returned, the next tile's stage 1 is requested into
+            // it (no barrier), and the last half-block's NST stores follow.
+            wait_lds_reads();
+            if (more) issue_stage(nbase, KS, sbuf);
+            out_hb<OUT, HAS_BIAS>(vb, bb, ors, N, cc0, el, s, 7, 0, 4 * U);
         } else {
             stage(buf, false, false, 0, 0, 2, false);   // stage nk-1: its buffer is free after the barrier
-        }
-        buf ^= STAGE;                           // the next tile's stage 0
-
-        const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
-        // The staging quarter of the buffer is the one this wave's own
-        // stage loads fill, and no other wave reads it after stage nk-1's
-        // barrier: so the next tile's stage 1 is requested as soon as this
-        // wave's own staging reads have returned, with no barrier.
-        if constexpr (OUT == FP8_DTYPE_BF16) {
-            // Four 32-row blocks (block 0 was staged inside the last stage);
-            // each block's stores drain while the next block is converted.
-            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<2>(Cv, M, N, r0);
-            u32x4 rows_out[8];
-#pragma unroll
-            for (int i = 0; i < F; ++i) {
-                if (i > 0) stage_block_bf16<HAS_BIAS>(acc, stg, bv, el, s, i);
-                read_block_bf16(stg, el, rows_out);
-                if (i == F - 1) {
-                    wait_lds_reads();
-                    if (more) issue_stage(nbase, KS, sbuf);
-                }
-                store_block_bf16(ors, rows_out, N, i, cc0, el);
-            }
-        } else if constexpr (is_q_out<OUT>()) {
+            buf ^= STAGE;                           // the next tile's stage 0
+            // The staging quarter of the buffer is the one this wave's own
+            // stage loads fill, and no other wave reads it after stage nk-1's
+            // barrier: so the next tile's stage 1 is requested as soon as this
+            // wave's own staging reads have returned, with no barrier.
             const uint32_t tk = stage_wave_tile_q<OUT, HAS_BIAS>(acc, stg, bl, el, s, so,
                                                                  so_fold, M, r0);
             wkey = max(wkey, wave_max_key(tk));
@@ -1306,20 +1338,6 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
             wait_lds_reads();
             if (more) issue_stage(nbase, KS, sbuf);
             store_rows_q(out_rows_rsrc<1>(Cv, M, N, r0), rows_out, N, cc0, el);
-        } else {
-            // fp32: four 32-row blocks through the wave's 16 KiB of staging.
-            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<4>(Cv, M, N, r0);
-            u32x4 rows_out[16];
-#pragma unroll
-            for (int i = 0; i < F; ++i) {
-                stage_wave_block_f32<HAS_BIAS>(acc, stg, bl, el, s, i);
-                read_staged_block_f32(stg, el, rows_out);
-                if (i == F - 1) {
-                    wait_lds_reads();
-                    if (more) issue_stage(nbase, KS, sbuf);
-                }
-                store_block_f32(ors, rows_out, N, i, cc0, el);
-            }
         }
         if (more) {
             // The next tile's bias and stage 0 have landed (its stage 1, 16
