@@ -38,6 +38,7 @@ __all__ = [
     "PRODUCE_MODULATE_FINITE",
     "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
     "fp8_cast_transpose_amax_dbias_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "fp8_cast_transpose_amax_cached", "fp8_reference_copy",
     "library_path", "lib",
 ]
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_cast_transpose_amax.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp]
         L.fp8_cast_transpose_amax_dbias.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp,
                                                     i64, vp, vp]
+        L.fp8_cast_transpose_amax_cached.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp, vp, vp]
+        L.fp8_reference_copy.argtypes = [vp, vp, i64, i32, i32, vp]
         L.fp8_cast_transpose_amax_dbias_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, dp, vp,
                                                             vp, vp, vp]
         L.fp8_produce_cast_transpose_amax.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64,
@@ -104,7 +107,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
         for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
-                  L.fp8_cast_transpose_amax_dbias_noalloc,
+                  L.fp8_cast_transpose_amax_dbias_noalloc, L.fp8_cast_transpose_amax_cached,
+                  L.fp8_reference_copy,
                   L.fp8_produce_cast_transpose_amax, L.fp8_cast_transpose_dynamic,
                   L.fp8_linear_fwd, L.fp8_linear_fwd_fp8out, L.fp8_linear_dgrad,
                   L.fp8_linear_wgrad):
@@ -266,6 +270,44 @@ def fp8_cast_transpose_amax(x: torch.Tensor, scale: torch.Tensor, out: Float8Ten
                                          _ptr(amax_cur, torch.float32, "amax_cur"),
                                          _ptr(noop_flag, torch.int32, "noop_flag"),
                                          _stream(stream)), "fp8_cast_transpose_amax")
+
+
+def fp8_cast_transpose_amax_cached(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,
+                                   amax_cur: Optional[torch.Tensor] = None,
+                                   noop_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """fp8_cast_transpose_amax with the source read through the caches
+    (ordinary loads instead of non-temporal ones); identical results."""
+    _need_scalar(scale, "scale")
+    _need_scalar(amax_cur, "amax_cur")
+    _need_scalar(noop_flag, "noop_flag")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride in the last dimension")
+    if x.dtype == torch.bfloat16:
+        src = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        src = DTYPE_FP32
+    else:
+        raise TypeError("x must be bf16 or fp32")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    d = out.desc()
+    _check(lib().fp8_cast_transpose_amax_cached(
+        x.data_ptr(), src, x.shape[0], x.shape[1], _row_stride(x),
+        _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
+        _ptr(amax_cur, torch.float32, "amax_cur"), _ptr(noop_flag, torch.int32, "noop_flag"),
+        _stream(stream)), "fp8_cast_transpose_amax_cached")
+
+
+def fp8_reference_copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int,
+                       nontemporal: bool = False, stream=None) -> None:
+    """Measurement reference: copy src into dst (contiguous device tensors of
+    the same byte size, a multiple of 16)."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must have the same byte size")
+    _check(lib().fp8_reference_copy(_ptr(src, None, "src"), _ptr(dst, None, "dst"), nb,
+                                    workgroups, int(nontemporal), _stream(stream)),
+           "fp8_reference_copy")
 
 
 def fp8_cast_dbias_workspace_bytes(rows: int, cols: int) -> int:

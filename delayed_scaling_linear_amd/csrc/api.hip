@@ -173,6 +173,32 @@ int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t co
                                                 noop_flag, nullptr, 0, s));
 }
 
+int fp8_cast_transpose_amax_cached(const void *x, int32_t src, int64_t rows, int64_t cols,
+                                   int64_t ld, const float *scale, const fp8_tensor_t *out,
+                                   float *amax_cur, const int32_t *noop_flag,
+                                   fp8_stream_t stream) {
+    if (int e = check_cast(x, src, rows, cols, ld, scale, out)) return e;
+    const bool empty = (rows == 0 || cols == 0);
+    if (empty && out->scale_inv == nullptr) return FP8_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (empty) return status_of(launch_scale_inv_only(scale, out->scale_inv, noop_flag, s));
+    return status_of(launch_cast_transpose_amax(x, src, rows, cols, ld, scale, out->fmt,
+                                                out->data, out->data_t, amax_cur, out->scale_inv,
+                                                noop_flag, nullptr, 0, s, /*cached=*/true));
+}
+
+int fp8_reference_copy(const void *src, void *dst, int64_t bytes, int32_t workgroups,
+                       int32_t nontemporal, fp8_stream_t stream) {
+    if (bytes < 0 || (bytes % 16) != 0 || workgroups < 1 || workgroups > 65536 ||
+        (nontemporal != 0 && nontemporal != 1))
+        return FP8_ERR_ARG;
+    if (bytes == 0) return FP8_OK;
+    if (src == nullptr || dst == nullptr) return FP8_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return FP8_ERR_ALIGN;
+    return status_of(launch_reference_copy(src, dst, bytes, workgroups, nontemporal != 0,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int64_t fp8_cast_dbias_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return FP8_ERR_SHAPE;
     return ((rows + 127) / 128) * ((cols + 127) / 128) * 128 * (int64_t)sizeof(float);

@@ -231,9 +231,9 @@ __device__ __forceinline__ void flush_amax(uint32_t key, float *amax_cur, uint32
 // its next tile in flight while the current one is encoded and stored, and
 // a double-buffered LDS transpose tile (one barrier per tile).
 // SRC: FP8_DTYPE_BF16 or FP8_DTYPE_FP32.  The source is read with
-// non-temporal loads: it is read once, and allocating it in the last-level
-// cache would push out the codes just written, which the matrix products
-// read next.  Measured on MI355X over the whole forward + backward step of
+// non-temporal loads (unless `cached`): it is read once, and allocating it in
+// the last-level cache would push out the codes just written, which the
+// matrix products read next.  Measured on MI355X over the whole forward + backward step of
 // one linear this is 4-5% faster than normal loads, though the cast alone
 // is about 9% slower on cold buffers.  Large tensors (more than two tiles per
 // resident workgroup) are launched with one workgroup per tile, so that the
@@ -256,7 +256,7 @@ cast_transpose_amax_kernel(
     const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
     float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
     const int32_t *__restrict__ noop, int64_t tiles_c, int64_t ntiles,
-    float *__restrict__ dbias_ws, int64_t ws_ld) {
+    float *__restrict__ dbias_ws, int64_t ws_ld, int cached) {
     if (noop != nullptr && *noop != 0) return;
 
     __shared__ uint32_t lds_t[2][TILE * (TILE / 4)];   // transposed tiles, 2 x 16 KiB
@@ -294,10 +294,16 @@ cast_transpose_amax_kernel(
         off = valid ? (uint32_t)(((4 * rg) * ld + 16 * cc) * EB) : 0x80000000u;
     };
     const uint32_t row_step = (uint32_t)(ld * EB);
+    // `cached` (wave-uniform) reads the source through the caches instead.
     auto load_tile = [&](SrcRow<SRC> (&dst)[4], __amdgpu_buffer_rsrc_t rs, uint32_t off) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[i].template load<2>(rs, off == 0x80000000u ? off : off + i * row_step);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = off == 0x80000000u ? off : off + i * row_step;
+            if (cached)
+                dst[i].template load<0>(rs, o);
+            else
+                dst[i].template load<2>(rs, o);
+        }
     };
     auto store_t = [&](const uint32_t *lt, int64_t t) {
         const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
@@ -374,28 +380,109 @@ cast_transpose_amax_kernel(
     if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
 }
 
+// One tile per workgroup, no loop: every lane issues its tile's source loads
+// at once, then encodes and stores them.  With no second tile's source in
+// registers a workgroup needs half the registers of the persistent kernel,
+// so four or more fit on a CU and all tiles of a [4096, 4096] tensor have
+// their loads in flight together (a copy of the same bytes needs about that
+// many bytes in flight to reach its best rate); the hardware dispatcher
+// balances larger tensors.  Used for casts without the bias gradient of
+// tensors with more than two tiles per resident persistent workgroup (there
+// it beats the persistent kernel; below that the persistent kernel's
+// overlap of one tile's loads with the previous tile's stores wins).
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
+cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
+                 const float *__restrict__ scale_ptr, uint8_t *__restrict__ q,
+                 uint8_t *__restrict__ qt, float *__restrict__ amax_cur,
+                 float *__restrict__ scale_inv_out, const int32_t *__restrict__ noop,
+                 int64_t tiles_c, int cached) {
+    if (noop != nullptr && *noop != 0) return;
+    __shared__ uint32_t lds_t[TILE * (TILE / 4)];      // the transposed tile, 16 KiB
+    __shared__ uint32_t lds_amax[THREADS / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cc = lane & 7;
+    const int rg = wave * 8 + (lane >> 3);
+    constexpr int EB = SrcRow<SRC>::kBytes;
+
+    const float s = *scale_ptr;
+    const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
+    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
+
+    const int64_t t = blockIdx.x;
+    const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
+    const int64_t row0 = tr * TILE, col0 = tcn * TILE;
+    const int64_t r = row0 + 4 * rg, c = col0 + 16 * cc;
+    const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
+    // The tile's descriptor ends at the tensor's last byte: rows past the
+    // end read as zeros.
+    const int64_t base = (row0 * ld + col0) * EB;
+    const int64_t avail = ((rows - 1) * ld + cols) * EB - base;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(xv)) + base, (short)0,
+        (int32_t)min(avail, (int64_t)0x7FFFFFFF), 0x00020000);
+    const uint32_t off = valid ? (uint32_t)(((4 * rg) * ld + 16 * cc) * EB) : 0x80000000u;
+    const uint32_t row_step = (uint32_t)(ld * EB);
+    SrcRow<SRC> src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t o = off == 0x80000000u ? off : off + i * row_step;
+        if (cached)
+            src[i].template load<0>(rs, o);
+        else
+            src[i].template load<2>(rs, o);
+    }
+    uint32_t key = 0;
+    encode_block<SRC, FMT, WANT_Q, WANT_QT>(src, s, s_special, valid, q, r, c, cols, cc, rg,
+                                            lds_t, key);
+    __syncthreads();
+    if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
+    if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
+}
+
 template <int SRC, int FMT>
 hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
                           const float *scale, uint8_t *q, uint8_t *qt, float *amax_cur,
                           float *scale_inv_out, const int32_t *noop, float *dbias_ws,
-                          int64_t ws_ld, hipStream_t stream) {
+                          int64_t ws_ld, bool cached, hipStream_t stream) {
     int cus = 0;
     if (hipError_t e = current_cu_count(&cus)) return e;
     const int64_t tiles_r = (rows + TILE - 1) / TILE;
     const int64_t tiles_c = (cols + TILE - 1) / TILE;
     const int64_t ntiles = tiles_r * tiles_c;
-    // As many workgroups as fit on the chip at once, each looping over tiles;
-    // large tensors: one workgroup per tile.
+    // As many workgroups as fit on the chip at once, each looping over tiles
+    // with the next tile's loads in flight; tensors with more than two tiles
+    // per resident workgroup: one workgroup per tile (cast_tile_kernel, or
+    // the persistent kernel when it also sums the bias gradient).
     const int64_t resident =
         (int64_t)cus * (dbias_ws ? kWavesPerSimd<SRC, true> : kWavesPerSimd<SRC, false>);
     const bool per_tile = ntiles > 2 * resident;
+    if (per_tile && dbias_ws == nullptr) {
+        auto launch1 = [&](auto wq, auto wqt) {
+            hipLaunchKernelGGL((cast_tile_kernel<SRC, FMT, decltype(wq)::value,
+                                                 decltype(wqt)::value>),
+                               dim3((unsigned)ntiles), dim3(THREADS), 0, stream, x, rows, cols,
+                               ld, scale, q, qt, amax_cur, scale_inv_out, noop, tiles_c,
+                               (int)cached);
+        };
+        using T1 = std::true_type;
+        using F1 = std::false_type;
+        if (q && qt) launch1(T1{}, T1{});
+        else if (q) launch1(T1{}, F1{});
+        else launch1(F1{}, T1{});
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)(per_tile ? ntiles : std::min<int64_t>(ntiles, resident)));
     auto launch = [&](auto wq, auto wqt, auto db) {
         hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, decltype(wq)::value,
                                                        decltype(wqt)::value,
                                                        decltype(db)::value>),
                            grid, dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt,
-                           amax_cur, scale_inv_out, noop, tiles_c, ntiles, dbias_ws, ws_ld);
+                           amax_cur, scale_inv_out, noop, tiles_c, ntiles, dbias_ws, ws_ld,
+                           (int)cached);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -430,22 +517,23 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
                                       int64_t ld, const float *scale, int fmt, uint8_t *q,
                                       uint8_t *qt, float *amax_cur, float *scale_inv_out,
                                       const int32_t *noop, float *dbias_ws, int64_t ws_ld,
-                                      hipStream_t stream) {
+                                      hipStream_t stream, bool cached) {
     if (src == FP8_DTYPE_BF16) {
         if (fmt == FP8_E4M3)
             return launch_src_fmt<FP8_DTYPE_BF16, FP8_E4M3>(x, rows, cols, ld, scale, q, qt,
                                                             amax_cur, scale_inv_out, noop,
-                                                            dbias_ws, ws_ld, stream);
+                                                            dbias_ws, ws_ld, cached, stream);
         return launch_src_fmt<FP8_DTYPE_BF16, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
                                                         scale_inv_out, noop, dbias_ws, ws_ld,
-                                                        stream);
+                                                        cached, stream);
     }
     if (fmt == FP8_E4M3)
         return launch_src_fmt<FP8_DTYPE_FP32, FP8_E4M3>(x, rows, cols, ld, scale, q, qt, amax_cur,
                                                         scale_inv_out, noop, dbias_ws, ws_ld,
-                                                        stream);
+                                                        cached, stream);
     return launch_src_fmt<FP8_DTYPE_FP32, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
-                                                    scale_inv_out, noop, dbias_ws, ws_ld, stream);
+                                                    scale_inv_out, noop, dbias_ws, ws_ld, cached,
+                                                    stream);
 }
 
 // Producer-fused cast.  The toy block of "CPU Overhead of te.Linear FP8

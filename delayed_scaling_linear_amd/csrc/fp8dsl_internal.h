@@ -34,7 +34,13 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
                                       int64_t ld, const float *scale, int fmt, uint8_t *q,
                                       uint8_t *qt, float *amax_cur, float *scale_inv_out,
                                       const int32_t *noop, float *dbias_ws, int64_t ws_ld,
-                                      hipStream_t stream);
+                                      hipStream_t stream, bool cached = false);
+
+// Measurement reference: copy `bytes` (a multiple of 16) from src to dst with
+// 16-byte loads and stores, `blocks` workgroups of 256 threads, loads
+// non-temporal or not.
+hipError_t launch_reference_copy(const void *src, void *dst, int64_t bytes, int blocks,
+                                 bool nontemporal, hipStream_t stream);
 
 // y = op(x, a, b) in bf16 (row-major [rows, cols]), then the cast of y.
 hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 7
+#define FP8DSL_ABI_VERSION 8
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -173,6 +173,38 @@ int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *
 int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
                             const float *scale, const fp8_tensor_t *out, float *amax_cur,
                             const int32_t *noop_flag, fp8_stream_t stream);
+
+/*
+ * fp8_cast_transpose_amax_cached -- fp8_cast_transpose_amax reading its
+ * source through the caches.
+ *
+ * fp8_cast_transpose_amax reads the source with non-temporal loads: the
+ * source is read once, and keeping it out of the last-level cache leaves the
+ * codes it writes there for the products that read them next (a whole
+ * forward + backward step of a linear is faster that way).  This variant
+ * reads the source with ordinary loads, for a source that is read again soon
+ * or a cast whose codes are not read next; a cast on its own is faster with
+ * it.  Results are identical.  Arguments, constraints and errors as
+ * fp8_cast_transpose_amax.
+ */
+int fp8_cast_transpose_amax_cached(const void *x, int32_t src, int64_t rows, int64_t cols,
+                                   int64_t ld, const float *scale, const fp8_tensor_t *out,
+                                   float *amax_cur, const int32_t *noop_flag,
+                                   fp8_stream_t stream);
+
+/*
+ * fp8_reference_copy -- a measurement reference, not part of the method: a
+ * plain device copy of `bytes` (a multiple of 16) from src to dst with
+ * 16-byte accesses, `workgroups` workgroups of 256 threads (1 .. 65536)
+ * striding over 16 KiB slabs, loads non-temporal when `nontemporal` is 1.
+ * The cast moves exactly the bytes of a copy (its source read once, its
+ * codes and their transpose written once), so the best copy rate of the
+ * same volume on the same device is the ceiling the cast is measured
+ * against.  src and dst: device, 16-byte aligned, not overlapping.
+ * Errors: FP8_ERR_ARG, FP8_ERR_NULL, FP8_ERR_ALIGN, FP8_ERR_LAUNCH.
+ */
+int fp8_reference_copy(const void *src, void *dst, int64_t bytes, int32_t workgroups,
+                       int32_t nontemporal, fp8_stream_t stream);
 
 /*
  * fp8_cast_dbias_workspace_bytes -- device workspace (bytes) that

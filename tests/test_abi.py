@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
                  "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_status_string", "fp8_abi_version",
                  "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
                  "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic",
-                 "fp8_linear_fwd_fp8out", "fp8_cast_transpose_amax_dbias_noalloc"):
+                 "fp8_linear_fwd_fp8out", "fp8_cast_transpose_amax_dbias_noalloc",
+                 "fp8_cast_transpose_amax_cached", "fp8_reference_copy"):
         assert want in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 7
+    assert dsl.fp8_abi_version() == 8
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -246,3 +247,17 @@ def test_noalloc_dbias_validation():
     d = _desc(32, 48)
     assert L.fp8_cast_transpose_amax_dbias_noalloc(0x4000, 0, 32, 48, 48, 0x5000, byref(d),
                                                    None, None, None, None) == -1   # dbias NULL
+
+
+def test_reference_copy_and_cached_cast_validation():
+    L = dsl.lib()
+    byref = ctypes.byref
+    assert L.fp8_reference_copy(0x1000, 0x2000, 24, 4, 0, None) == -5      # not a multiple of 16
+    assert L.fp8_reference_copy(0x1000, 0x2000, 32, 0, 0, None) == -5      # no workgroups
+    assert L.fp8_reference_copy(0x1000, 0x2000, 32, 4, 2, None) == -5      # bad policy
+    assert L.fp8_reference_copy(None, 0x2000, 32, 4, 0, None) == -1
+    assert L.fp8_reference_copy(0x1008, 0x2000, 32, 4, 0, None) == -3
+    assert L.fp8_reference_copy(0x1000, 0x2000, 0, 4, 0, None) == 0       # nothing to copy
+    d = _desc(30, 48)
+    assert L.fp8_cast_transpose_amax_cached(0x4000, 0, 30, 48, 48, 0x5000, byref(d), None, None,
+                                            None) == -2

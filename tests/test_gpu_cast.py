@@ -171,3 +171,35 @@ def test_large_tensors_one_workgroup_per_tile(shape, src, fmt, q, qt):
     x = torch.randn(*shape, generator=g) * 2
     x = x.to(torch.bfloat16) if src == "bf16" else x
     _check(x, 97.0, fmt, q=q, qt=qt)
+
+
+@pytest.mark.parametrize("shape,fmt,src", [((272, 400), 0, "bf16"), ((4096, 4096), 0, "bf16"),
+                                           ((400, 272), 1, "fp32"), ((8192, 8192), 1, "bf16")])
+def test_cached_source_variant_is_identical(shape, fmt, src):
+    """fp8_cast_transpose_amax_cached reads the source with ordinary loads
+    instead of non-temporal ones; codes, transpose, amax and scale-inverse
+    must be the oracle's, bit for bit."""
+    g = torch.Generator().manual_seed(shape[0] + fmt)
+    x = torch.randn(*shape, generator=g) * 3.0
+    x = x.to(torch.bfloat16) if src == "bf16" else x
+    out = dsl.Float8Tensor.empty(shape[0], shape[1], fmt, device=DEV)
+    s = torch.tensor([37.0], device=DEV)
+    amax = torch.zeros(1, device=DEV)
+    dsl.fp8_cast_transpose_amax_cached(x.to(DEV), s, out, amax)
+    torch.cuda.synchronize()
+    xs = bits16(x) if src == "bf16" else x.numpy()
+    oq, oqt, oamax, osinv = oracle.cast_transpose_amax(xs, 37.0, fmt)
+    np.testing.assert_array_equal(bits8(out.data), oq)
+    np.testing.assert_array_equal(bits8(out.data_t), oqt)
+    assert f32_bits(amax)[0] == np.float32(oamax).view(np.uint32)
+    assert f32_bits(out.scale_inv)[0] == np.float32(osinv).view(np.uint32)
+
+
+@pytest.mark.parametrize("nbytes,workgroups,nt", [(16, 1, 0), (16 * 1000 + 16, 3, 1),
+                                                  (64 << 20, 1024, 0), (64 << 20, 2048, 1)])
+def test_reference_copy_copies(nbytes, workgroups, nt):
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros_like(src)
+    dsl.fp8_reference_copy(src, dst, workgroups, bool(nt))
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
