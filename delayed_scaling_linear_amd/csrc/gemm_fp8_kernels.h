@@ -689,6 +689,15 @@ __device__ __forceinline__ int dma_swz(int r) { return (r & 7) ^ ((r >> 3) & 1);
 // count them in its vmcnt waits.  Column groups past N take OUT_OOB.  The
 // host guarantees 128 * N * EB < 2^31.
 constexpr uint32_t OUT_OOB = 0x80000000u;
+// They are non-temporal (the nt cache-policy bit).  With normal
+// stores a product's output stays dirty in the last-level cache and is
+// written back while the next memory-bound kernel streams its own bytes
+// (measured on MI355X: the E5M2 cast of an [8192, 8192] gradient takes 62 us
+// after a forward product of [8192, 8192] bf16 outputs and 49 us with
+// non-temporal output stores).  The product, compute-bound, pays for its own
+// writes instead, but less: one linear's forward + backward step is 4%
+// faster and a 32-block forward 3%.
+constexpr int OUT_POLICY = 2;
 template <int EB>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows_rsrc(void *C, int M, int N, int r0) {
     // Every input is wave-uniform, but the clamp compiles to a vector
@@ -815,7 +824,7 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
             // the whole offset in the vector operand: the range check that
             // drops rows past M and columns past N does not see the scalar one
             __builtin_amdgcn_raw_buffer_store_b128(o, rs, (int)(voff + (uint32_t)(8 * it * N) * 2u),
-                                                   0, 0);
+                                                   0, OUT_POLICY);
         }
     } else {
         const int gc = c0 + 64 * p + 4 * (lane & 15);
@@ -827,7 +836,7 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
             const v4f y = {__uint_as_float(x.x) * s + b[4 * p + 0], __uint_as_float(x.y) * s + b[4 * p + 1],
                            __uint_as_float(x.z) * s + b[4 * p + 2], __uint_as_float(x.w) * s + b[4 * p + 3]};
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs,
-                                                   (int)(voff + (uint32_t)(4 * it * N) * 4u), 0, 0);
+                                                   (int)(voff + (uint32_t)(4 * it * N) * 4u), 0, OUT_POLICY);
         }
     }
 }
@@ -941,7 +950,7 @@ __device__ __forceinline__ void store_rows_q(__amdgpu_buffer_rsrc_t rs, const u3
     for (int it = 0; it < 16; ++it) {
         const int row = 8 * it + (lane >> 3);
         const uint32_t off = cb + (uint32_t)(row * N);
-        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v[it], rs, (int)off, 0, OUT_POLICY);
     }
 }
 
