@@ -15,9 +15,13 @@
 //   * 128 x 128 tiles, 256 threads per tile; persistent workgroups (up to
 //     three per CU for bf16, two for fp32) walk the tiles with the next
 //     tile's loads in flight while the current one is encoded and stored;
-//   * lane l of wave w owns rows 4*rg .. 4*rg+3 (rg = 8w + l/8) and columns
-//     16*cc .. 16*cc+15 (cc = l%8) of the tile: 16-byte global loads, 8
-//     lanes per 256-byte bf16 row segment;
+//   * lane l of wave w owns rows 4*rg .. 4*rg+3 (rg = 8w + l/8) of the tile.
+//     A bf16 lane (cc = l%8) loads the 8-column chunks cc and 8+cc of each
+//     row (16-byte loads: the eight lanes of a row cover one whole 128-byte
+//     line per instruction), encodes them, and swaps half of its codes with
+//     its neighbour lane (l^1) so that it then holds the 16 columns
+//     16*cq .. 16*cq+15, cq = 4*(cc%2) + cc/2.  An fp32 lane loads and
+//     holds columns 16*cc .. 16*cc+15 (cq = cc);
 //   * each lane scales, clamps to +-fp8_max and converts with the hardware
 //     OCP FP8 converter (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, round to
 //     nearest even), writes its four 16-byte row-major code rows directly,
@@ -59,16 +63,19 @@ struct SrcRow;
 template <>
 struct SrcRow<FP8_DTYPE_BF16> {
     static constexpr int kBytes = 2;
+    // Two 8-element chunks 128 bytes apart (see src_offsets).
+    static constexpr bool kSplit = true;
     u32x4 v[2];
-    // 16 elements at byte offset `off` of the descriptor (an offset outside
-    // it reads zeros and touches no memory); POL is the cache policy (0, or
-    // 2 = non-temporal).
+    // Chunks at byte offsets off0 and off1 of the descriptor (an offset
+    // outside it reads zeros and touches no memory); POL is the cache policy
+    // (0, or 2 = non-temporal).
     template <int POL>
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
-        v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, POL));
-        v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, POL));
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off0, uint32_t off1) {
+        v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off0, 0, POL));
+        v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off1, 0, POL));
     }
-    // Elements 4j .. 4j+3 as fp32 (exact widening).
+    // Elements 4j .. 4j+3 as fp32 (exact widening): j = 0, 1 from the first
+    // chunk, 2, 3 from the second.
     __device__ __forceinline__ void get4(int j, float o[4]) const {
         const u32x4 &q = v[j >> 1];
         const uint32_t d0 = (j & 1) ? q.z : q.x;
@@ -95,12 +102,14 @@ struct SrcRow<FP8_DTYPE_BF16> {
 template <>
 struct SrcRow<FP8_DTYPE_FP32> {
     static constexpr int kBytes = 4;
+    // One run of 16 consecutive elements (off1 is unused).
+    static constexpr bool kSplit = false;
     f32x4 v[4];
     template <int POL>
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off0, uint32_t) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-            v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16 * h, 0, POL));
+            v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off0 + 16 * h, 0, POL));
     }
     __device__ __forceinline__ void get4(int j, float o[4]) const {
         o[0] = v[j].x;
@@ -121,6 +130,44 @@ struct SrcRow<FP8_DTYPE_FP32> {
     }
 };
 
+constexpr uint32_t SRC_OOB = 0x80000000u;
+
+// Byte offsets (from the tile's first element) of lane chunk cc's source in
+// the first of its four rows, 4*rg; a chunk past the tensor's columns, or a
+// row past its rows, takes SRC_OOB and reads zeros.  bf16: 8-element chunks
+// cc and 8 + cc; fp32: the 16 elements from column 16*cc.
+template <int SRC>
+__device__ __forceinline__ void src_offsets(bool row_ok, int64_t col0, int64_t cols, int64_t ld,
+                                            int rg, int cc, uint32_t &off0, uint32_t &off1) {
+    constexpr int EB = SrcRow<SRC>::kBytes;
+    const int64_t rb = (int64_t)(4 * rg) * ld;
+    if constexpr (SrcRow<SRC>::kSplit) {
+        off0 = (row_ok && col0 + 8 * cc < cols) ? (uint32_t)((rb + 8 * cc) * EB) : SRC_OOB;
+        off1 = (row_ok && col0 + 64 + 8 * cc < cols) ? (uint32_t)((rb + 64 + 8 * cc) * EB) : SRC_OOB;
+    } else {
+        off0 = (row_ok && col0 + 16 * cc < cols) ? (uint32_t)((rb + 16 * cc) * EB) : SRC_OOB;
+        off1 = SRC_OOB;
+    }
+}
+
+// The 16-column chunk whose codes lane chunk cc stores (after the bf16
+// neighbour exchange in encode_block).
+template <int SRC>
+__device__ __forceinline__ int store_chunk(int cc) {
+    return SrcRow<SRC>::kSplit ? 4 * (cc & 1) + (cc >> 1) : cc;
+}
+
+// Column (0..127 in the tile) of element k (0..15) of lane chunk cc's source.
+template <int SRC>
+__device__ __forceinline__ int src_col(int cc, int k) {
+    return SrcRow<SRC>::kSplit ? (k < 8 ? 8 * cc + k : 56 + 8 * cc + k) : 16 * cc + k;
+}
+
+// Lane l's value of v on lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ uint32_t from_neighbour(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+
 // 4x4 byte transpose: in[r] holds bytes (r, c=0..3); out[c] holds (r=0..3, c).
 __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
     const uint32_t lo01 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
@@ -139,12 +186,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// Encode this lane's 4 x 16 block of the tile held in `src`, store its
-// row-major codes and its transposed 4-row words into the LDS tile `lt`.
+// Encode this lane's 4 x 16 block of the tile held in `src`, store the
+// row-major codes of chunk cq (columns c .. c+15, c = col0 + 16*cq) and its
+// transposed 4-row words into the LDS tile `lt`.  bf16: the lane encodes its
+// two 8-column source chunks, then keeps the codes of the first (even lane)
+// or second (odd lane) and takes the neighbour's codes of the same chunk
+// parity, which together are chunk cq = store_chunk(cc).  Every lane of the
+// wave must call it (the exchange reads the neighbour's registers).
 template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
 __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float s, bool s_special,
                                              bool valid, uint8_t *__restrict__ q, int64_t r,
-                                             int64_t c, int64_t cols, int cc, int rg,
+                                             int64_t c, int64_t cols, int cq, int rg, int lane,
                                              uint32_t *lt, uint32_t &key) {
     uint32_t codes[4][4];                    // [row][word of 4 columns]
 #pragma unroll
@@ -166,6 +218,23 @@ __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float 
             }
         }
     }
+    if constexpr (SrcRow<SRC>::kSplit) {
+        // Even lane: columns 8cc..+7 | neighbour's 8cc+8..+15.  Odd lane:
+        // neighbour's 64+8cc-8..+7 | its own 64+8cc..+7.
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t r0 = from_neighbour(odd ? codes[i][0] : codes[i][2]);
+            const uint32_t r1 = from_neighbour(odd ? codes[i][1] : codes[i][3]);
+            if (odd) {
+                codes[i][0] = r0;
+                codes[i][1] = r1;
+            } else {
+                codes[i][2] = r0;
+                codes[i][3] = r1;
+            }
+        }
+    }
     if constexpr (WANT_Q) {
         if (valid) {
 #pragma unroll
@@ -176,7 +245,7 @@ __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float 
         }
     }
     if constexpr (WANT_QT) {
-        const int swz = 4 * cc;
+        const int swz = 4 * cq;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t in[4] = {codes[0][j], codes[1][j], codes[2][j], codes[3][j]};
@@ -184,7 +253,7 @@ __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float 
             transpose4x4(in, out);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int tc = 16 * cc + 4 * j + b;          // tile column
+                const int tc = 16 * cq + 4 * j + b;          // tile column
                 lt[tc * 32 + (rg ^ swz)] = out[b];
             }
         }
@@ -233,11 +302,12 @@ __device__ __forceinline__ void flush_amax(uint32_t key, float *amax_cur, uint32
 // SRC: FP8_DTYPE_BF16 or FP8_DTYPE_FP32.  The source is read with
 // non-temporal loads (unless `cached`): it is read once, and allocating it in
 // the last-level cache would push out the codes just written, which the
-// matrix products read next.  Measured on MI355X over the whole forward + backward step of
-// one linear this is 4-5% faster than normal loads, though the cast alone
-// is about 9% slower on cold buffers.  Large tensors (more than two tiles per
-// resident workgroup) are launched with one workgroup per tile, so that the
-// hardware dispatcher balances the last round.
+// matrix products read next.  Measured on MI355X, one linear's forward +
+// backward step is 6-9% faster than with normal loads, and the cast alone on
+// cold buffers runs at the same speed (within 2%) either way.  Large
+// tensors (more than two tiles per resident workgroup) are launched with one
+// workgroup per tile, so that the hardware dispatcher balances the last
+// round.
 // Resident workgroups per CU: the double-buffered source needs 64 (bf16) or
 // 128 (fp32) registers per lane.
 // The bias-gradient variant needs its 16 column sums on top: two per CU.
@@ -266,7 +336,8 @@ cast_transpose_amax_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int cc = lane & 7;                 // 16-column chunk of the tile
+    const int cc = lane & 7;                 // source chunk (src_offsets)
+    const int cq = store_chunk<SRC>(cc);     // 16-column chunk of the codes
     const int rg = wave * 8 + (lane >> 3);   // 4-row group of the tile
     constexpr int EB = SrcRow<SRC>::kBytes;
     const int64_t total_bytes = ((rows - 1) * ld + cols) * EB;
@@ -277,13 +348,13 @@ cast_transpose_amax_kernel(
     if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
 
     // Source descriptor of tile t (empty when t is past the last tile) and
-    // this lane's byte offset in it.
-    auto tile_rsrc = [&](int64_t t, __amdgpu_buffer_rsrc_t &rs, uint32_t &off, int64_t &r,
+    // this lane's byte offsets in it.
+    auto tile_rsrc = [&](int64_t t, __amdgpu_buffer_rsrc_t &rs, uint32_t (&off)[2], int64_t &r,
                          int64_t &c, bool &valid) {
         const int64_t tr = t / tiles_c, tcn = t - (t / tiles_c) * tiles_c;
         const int64_t row0 = tr * TILE, col0 = tcn * TILE;
         r = row0 + 4 * rg;
-        c = col0 + 16 * cc;
+        c = col0 + 16 * cq;
         valid = (t < ntiles) && (r < rows) && (c < cols);
         const int64_t base = (t < ntiles) ? (row0 * ld + col0) * EB : 0;
         const int64_t avail = (t < ntiles) ? total_bytes - base : 0;
@@ -291,18 +362,19 @@ cast_transpose_amax_kernel(
         rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(static_cast<const uint8_t *>(xv)) + base, (short)0, nrec,
             0x00020000);
-        off = valid ? (uint32_t)(((4 * rg) * ld + 16 * cc) * EB) : 0x80000000u;
+        src_offsets<SRC>((t < ntiles) && (r < rows), col0, cols, ld, rg, cc, off[0], off[1]);
     };
     const uint32_t row_step = (uint32_t)(ld * EB);
     // `cached` (wave-uniform) reads the source through the caches instead.
-    auto load_tile = [&](SrcRow<SRC> (&dst)[4], __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    auto load_tile = [&](SrcRow<SRC> (&dst)[4], __amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[2]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t o = off == 0x80000000u ? off : off + i * row_step;
+            const uint32_t o0 = off[0] == SRC_OOB ? SRC_OOB : off[0] + i * row_step;
+            const uint32_t o1 = off[1] == SRC_OOB ? SRC_OOB : off[1] + i * row_step;
             if (cached)
-                dst[i].template load<0>(rs, o);
+                dst[i].template load<0>(rs, o0, o1);
             else
-                dst[i].template load<2>(rs, o);
+                dst[i].template load<2>(rs, o0, o1);
         }
     };
     auto store_t = [&](const uint32_t *lt, int64_t t) {
@@ -313,7 +385,7 @@ cast_transpose_amax_kernel(
     uint32_t key = 0;                        // sign-cleared max, fp32 bit order
     SrcRow<SRC> src[2][4];
     __amdgpu_buffer_rsrc_t rs_cur, rs_nxt;
-    uint32_t off_cur, off_nxt;
+    uint32_t off_cur[2], off_nxt[2];
     int64_t r_cur, c_cur, r_nxt, c_nxt;
     bool v_cur, v_nxt;
     int64_t t = blockIdx.x;
@@ -328,7 +400,7 @@ cast_transpose_amax_kernel(
                 tile_rsrc(tn, rs_nxt, off_nxt, r_nxt, c_nxt, v_nxt);
                 load_tile(src[u ^ 1], rs_nxt, off_nxt);           // empty past the end
                 encode_block<SRC, FMT, WANT_Q, WANT_QT>(src[u], s, s_special, v_cur, q, r_cur,
-                                                        c_cur, cols, cc, rg, lds_t[u], key);
+                                                        c_cur, cols, cq, rg, lane, lds_t[u], key);
                 if constexpr (DBIAS) {
                     // Rows past the tensor were loaded as zeros and add nothing.
                     float cs[16];
@@ -353,10 +425,11 @@ cast_transpose_amax_kernel(
 #pragma unroll
                         for (int k = 0; k < 16; ++k) cs[k] += __shfl_xor(cs[k], m);
                     if ((lane >> 3) == 0) {
-                        float *d = &lds_db[(u * (THREADS / 64) + wave) * TILE + 16 * cc];
+                        float *d = &lds_db[(u * (THREADS / 64) + wave) * TILE];
 #pragma unroll
                         for (int k = 0; k < 16; k += 4)
-                            *reinterpret_cast<f32x4 *>(d + k) = f32x4{cs[k], cs[k + 1], cs[k + 2], cs[k + 3]};
+                            *reinterpret_cast<f32x4 *>(d + src_col<SRC>(cc, k)) =
+                                f32x4{cs[k], cs[k + 1], cs[k + 2], cs[k + 3]};
                     }
                 }
                 __syncthreads();
@@ -405,6 +478,7 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cc = lane & 7;
+    const int cq = store_chunk<SRC>(cc);
     const int rg = wave * 8 + (lane >> 3);
     constexpr int EB = SrcRow<SRC>::kBytes;
 
@@ -415,7 +489,7 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
     const int64_t t = blockIdx.x;
     const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
     const int64_t row0 = tr * TILE, col0 = tcn * TILE;
-    const int64_t r = row0 + 4 * rg, c = col0 + 16 * cc;
+    const int64_t r = row0 + 4 * rg, c = col0 + 16 * cq;
     const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
     // The tile's descriptor ends at the tensor's last byte: rows past the
     // end read as zeros.
@@ -424,19 +498,21 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(static_cast<const uint8_t *>(xv)) + base, (short)0,
         (int32_t)min(avail, (int64_t)0x7FFFFFFF), 0x00020000);
-    const uint32_t off = valid ? (uint32_t)(((4 * rg) * ld + 16 * cc) * EB) : 0x80000000u;
+    uint32_t off[2];
+    src_offsets<SRC>(r < rows, col0, cols, ld, rg, cc, off[0], off[1]);
     const uint32_t row_step = (uint32_t)(ld * EB);
     SrcRow<SRC> src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t o = off == 0x80000000u ? off : off + i * row_step;
+        const uint32_t o0 = off[0] == SRC_OOB ? SRC_OOB : off[0] + i * row_step;
+        const uint32_t o1 = off[1] == SRC_OOB ? SRC_OOB : off[1] + i * row_step;
         if (cached)
-            src[i].template load<0>(rs, o);
+            src[i].template load<0>(rs, o0, o1);
         else
-            src[i].template load<2>(rs, o);
+            src[i].template load<2>(rs, o0, o1);
     }
     uint32_t key = 0;
-    encode_block<SRC, FMT, WANT_Q, WANT_QT>(src, s, s_special, valid, q, r, c, cols, cc, rg,
+    encode_block<SRC, FMT, WANT_Q, WANT_QT>(src, s, s_special, valid, q, r, c, cols, cq, rg, lane,
                                             lds_t, key);
     __syncthreads();
     if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
@@ -602,6 +678,7 @@ __global__ __launch_bounds__(THREADS) void produce_cast_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cc = lane & 7;
+    const int cq = store_chunk<FP8_DTYPE_BF16>(cc);
     const int rg = wave * 8 + (lane >> 3);
     const float s = *scale_ptr;
     const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
@@ -610,43 +687,44 @@ __global__ __launch_bounds__(THREADS) void produce_cast_kernel(
     const int64_t t = blockIdx.x;
     const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
     const int64_t row0 = tr * TILE, col0 = tcn * TILE;
-    const int64_t r = row0 + 4 * rg, c = col0 + 16 * cc;
+    const int64_t r = row0 + 4 * rg, c = col0 + 16 * cq;
     const bool valid = (r < rows) && (c < cols);   // rows, cols are multiples of 16
 
+    // The lane's two 8-column chunks (cc and 8 + cc, as in the cast), each
+    // loaded, combined and stored as y only when it lies inside the tensor.
     SrcRow<FP8_DTYPE_BF16> ys[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ys[i].v[0] = u32x4{0u, 0u, 0u, 0u};
         ys[i].v[1] = u32x4{0u, 0u, 0u, 0u};
     }
-    if (valid) {
-        u32x4 xv[4][2], av[4][2], bv[4][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+        const int64_t ch = col0 + 64 * h + 8 * cc;
+        if (r < rows && ch < cols) {
+            u32x4 xv[4], av[4], bv[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                xv[i][h] = *reinterpret_cast<const u32x4 *>(x + (r + i) * ldx + c + 8 * h);
-                av[i][h] = *reinterpret_cast<const u32x4 *>(a + (r + i) * lda + c + 8 * h);
+            for (int i = 0; i < 4; ++i) {
+                xv[i] = *reinterpret_cast<const u32x4 *>(x + (r + i) * ldx + ch);
+                av[i] = *reinterpret_cast<const u32x4 *>(a + (r + i) * lda + ch);
                 if constexpr (OP != FP8_PRODUCE_ADD)
-                    bv[i][h] = *reinterpret_cast<const u32x4 *>(b + (r + i) * ldb + c + 8 * h);
+                    bv[i] = *reinterpret_cast<const u32x4 *>(b + (r + i) * ldb + ch);
                 else
-                    bv[i][h] = u32x4{0u, 0u, 0u, 0u};
+                    bv[i] = u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4 X = xv[i][h], A = av[i][h], B = bv[i][h];
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 X = xv[i], A = av[i], B = bv[i];
                 const u32x4 Y = {produce_pair<OP>(X.x, A.x, B.x), produce_pair<OP>(X.y, A.y, B.y),
                                  produce_pair<OP>(X.z, A.z, B.z), produce_pair<OP>(X.w, A.w, B.w)};
                 ys[i].v[h] = Y;
-                *reinterpret_cast<u32x4 *>(y + (r + i) * cols + c + 8 * h) = Y;
+                *reinterpret_cast<u32x4 *>(y + (r + i) * cols + ch) = Y;
             }
         }
     }
     uint32_t key = 0;
-    encode_block<FP8_DTYPE_BF16, FMT, WANT_Q, WANT_QT>(ys, s, s_special, valid, q, r, c, cols, cc,
-                                                       rg, lds_t, key);
+    encode_block<FP8_DTYPE_BF16, FMT, WANT_Q, WANT_QT>(ys, s, s_special, valid, q, r, c, cols, cq,
+                                                       rg, lane, lds_t, key);
     __syncthreads();
     if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
     if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
