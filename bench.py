@@ -829,8 +829,11 @@ def probe_kernels(dsl, workloads, st):
 
 
 def scale_update_cost(dsl, iters: int = 50):
-    """One fused update over the 384 records of the 32-block forward and over
-    the 576 of its training step (history 16), back to back: us per launch."""
+    """One fused update over 3 records (the step), the 384 of the 32-block
+    forward and the 576 of its training step (history 16): us per launch,
+    from `iters` launches captured in one HIP graph and replayed (the
+    kernel's own time; the update issues no memset), and from an eager loop
+    of the same launches (bound by the binding's host overhead per call)."""
     res = {}
     for T in (3, 384, 576):
         st = dsl.DelayedScalingState([0, 0, 1] * (T // 3), device="cuda")
@@ -838,14 +841,21 @@ def scale_update_cost(dsl, iters: int = 50):
         for _ in range(5):
             st.update()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            st.update()
-        e1.record()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                st.update()
+        g.replay()
         torch.cuda.synchronize()
-        res[f"T{T}_us"] = round(e0.elapsed_time(e1) / iters * 1e3, 2)
+        for name, run in (("graph", g.replay), ("eager", lambda: [st.update() for _ in range(iters)])):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            res[f"T{T}_{name}_us"] = round(e0.elapsed_time(e1) / iters * 1e3, 2)
+        del g
     return res
 
 
