@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.orc_produce_cast.argtypes = [c.c_int, vp, i64, vp, i64, vp, i64, i64, i64, c.c_float,
                                        c.c_int, vp, vp, vp, f32p, f32p]
         L.orc_produce_cast.restype = c.c_int
+        L.orc_modulate_backward.argtypes = [c.c_int, vp, i64, vp, i64, vp, i64, vp, i64, i64,
+                                            i64, vp, i64, vp, i64, vp, i64]
+        L.orc_modulate_backward.restype = c.c_int
         L.orc_dynamic_cast.argtypes = [vp, c.c_int, i64, i64, i64, c.c_int, c.c_int, f32p, vp, vp,
                                        f32p, f32p]
         L.orc_dynamic_cast.restype = c.c_int
@@ -237,6 +240,26 @@ def produce_cast(op: int, x: np.ndarray, a: np.ndarray, b: np.ndarray | None, sc
     if rc != 0:
         raise ValueError("oracle produce_cast rejected its arguments")
     return y, q, qt, np.float32(amax.value), np.float32(sinv.value)
+
+
+def modulate_backward(op: int, dy: np.ndarray, x: np.ndarray, a: np.ndarray, b: np.ndarray):
+    """Gradient of the modulation y = bf16(a * x / b) (op PROD_MODULATE or
+    PROD_MODULATE_FINITE) for the output gradient dy, with respect to x, a
+    and b.  All inputs: 2-D uint16 (bf16 bits) arrays of one shape, any row
+    stride.  Returns (dx, da, db), uint16 [R, C]."""
+    for t in (dy, x, a, b):
+        if t.dtype != np.uint16 or t.ndim != 2 or t.strides[1] != 2 or t.shape != dy.shape:
+            raise TypeError("inputs must be 2-D bf16 bit arrays of one shape, unit column stride")
+    rows, cols = dy.shape
+    ld = lambda t: t.strides[0] // 2
+    outs = [np.empty((rows, cols), dtype=np.uint16) for _ in range(3)]
+    vp = lambda t: ctypes.c_void_p(t.ctypes.data)
+    rc = lib().orc_modulate_backward(op, vp(dy), ld(dy), vp(x), ld(x), vp(a), ld(a), vp(b), ld(b),
+                                     rows, cols, _ptr(outs[0]), cols, _ptr(outs[1]), cols,
+                                     _ptr(outs[2]), cols)
+    if rc != 0:
+        raise ValueError("oracle modulate_backward rejected its arguments")
+    return tuple(outs)
 
 
 def dynamic_cast(x: np.ndarray, fmt: int, *, margin: int = 0, fallback_scale: float = 1.0,

@@ -297,6 +297,52 @@ int orc_produce_cast(int op, const uint16_t *x, int64_t ldx, const uint16_t *a, 
 }
 
 /*
+ * Gradient of the modulation producer (ops 1 and 4 above) with respect to
+ * its three inputs.  The forward is y = a * x / b; with the gradient dy of y,
+ * its derivatives are dx = dy * a / b, da = dy * x / b and
+ * db = -dy * (a * x / b) / b.  Steps, each an fp32 operation rounded to
+ * nearest even on the exactly widened bf16 inputs:
+ *   u  = (a * x) / b     the forward's quotient before its bf16 rounding
+ *   t  = dy / b
+ *   dx = bf16(t * a),  da = bf16(t * x),  db = bf16(-(t * u))
+ * A NaN result is written as 0x7FC0.  Op 4 (the finite modulation): where the
+ * forward's y = bf16(u) is infinite or NaN, the forward wrote the constant +0,
+ * so dx, da and db are +0 there.  All tensors bf16 [rows, cols] with their
+ * own leading dimensions.  Returns 0, or -1 for a bad argument.
+ */
+int orc_modulate_backward(int op, const uint16_t *dy, int64_t lddy, const uint16_t *x,
+                          int64_t ldx, const uint16_t *a, int64_t lda, const uint16_t *b,
+                          int64_t ldb, int64_t rows, int64_t cols, uint16_t *dx, int64_t lddx,
+                          uint16_t *da, int64_t ldda, uint16_t *db, int64_t lddb) {
+    if ((op != 1 && op != 4) || rows < 0 || cols < 0 || !dy || !x || !a || !b || !dx || !da ||
+        !db || lddy < cols || ldx < cols || lda < cols || ldb < cols || lddx < cols ||
+        ldda < cols || lddb < cols)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            float gv = orc_bf16_to_f32(dy[r * lddy + c]);
+            float xv = orc_bf16_to_f32(x[r * ldx + c]);
+            float av = orc_bf16_to_f32(a[r * lda + c]);
+            float bv = orc_bf16_to_f32(b[r * ldb + c]);
+            float prod = av * xv;
+            float u = prod / bv;
+            float t = gv / bv;
+            float ta = t * av, tx = t * xv, tu = t * u;
+            uint16_t ox = orc_f32_to_bf16_canon(ta);
+            uint16_t oa = orc_f32_to_bf16_canon(tx);
+            uint16_t ob = orc_f32_to_bf16_canon(-tu);
+            if (op == 4 && !isfinite(orc_bf16_to_f32(orc_f32_to_bf16_canon(u))))
+                ox = oa = ob = 0x0000;
+            dx[r * lddx + c] = ox;
+            da[r * ldda + c] = oa;
+            db[r * lddb + c] = ob;
+        }
+    }
+    return 0;
+}
+
+/*
  * Dynamic scaling, the comparator of delayed scaling: "support delayed
  * scaling of weight in float8 all-gather" contrasts the two recipes
  * (dynamic scaling reads a tensor twice -- once for its amax, once for the

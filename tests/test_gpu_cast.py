@@ -101,6 +101,31 @@ def test_shapes_and_ragged_tiles(shape, src):
     _check(x, 41.5, oracle.E4M3, qt=False)
 
 
+@pytest.mark.parametrize("extra", [16, 32, 48, 64, 80, 96, 112])
+@pytest.mark.parametrize("src", ["bf16", "fp32"])
+def test_every_column_residue_of_a_tile(extra, src):
+    """A right-edge tile of every width the shape rules allow (16 .. 112
+    columns): a bf16 lane loads the 8-column chunks c and 8 + c of a tile
+    row, so at these widths some lanes have one chunk inside the tensor and
+    the other outside, and the neighbour exchange must still hand every
+    stored chunk its own columns."""
+    g = torch.Generator().manual_seed(1000 + extra)
+    x = torch.randn(48, 128 + extra, generator=g) * 5
+    x = x.to(torch.bfloat16) if src == "bf16" else x
+    _check(x, 23.0, oracle.E4M3)
+    _check(x, 23.0, oracle.E5M2, q=False)
+    _check(x, 23.0, oracle.E4M3, qt=False)
+
+
+@pytest.mark.parametrize("shape", [(4096, 6224), (4096, 6256)])
+def test_ragged_columns_one_workgroup_per_tile(shape):
+    """Residues 80 and 112 on tensors large enough for the
+    one-workgroup-per-tile launch (1568 tiles)."""
+    g = torch.Generator().manual_seed(shape[1])
+    x = (torch.randn(*shape, generator=g) * 2).to(torch.bfloat16)
+    _check(x, 61.0, oracle.E5M2)
+
+
 def test_leading_dimension_and_amax_accumulation():
     g = torch.Generator().manual_seed(5)
     big = (torch.randn(96, 200, generator=g) * 2).to(torch.bfloat16).to(DEV)

@@ -68,6 +68,15 @@ def _check(x_cpu, scale, fmt, q=True, qt=True):
     return dbias
 
 
+@pytest.mark.parametrize("extra", [16, 48, 64, 80, 112])
+def test_dbias_every_column_residue_of_a_tile(extra):
+    """Right-edge tiles whose lanes hold one source chunk inside the tensor
+    and one outside: the column sums land on their own columns."""
+    g = torch.Generator().manual_seed(2000 + extra)
+    x = (torch.randn(272, 128 + extra, generator=g) * 3).to(torch.bfloat16)
+    _check(x, 0.75, oracle.E5M2)
+
+
 @pytest.mark.parametrize("shape,src,fmt,q,qt", [
     ((16, 16), "bf16", oracle.E5M2, True, True),
     ((400, 272), "bf16", oracle.E5M2, True, True),        # ragged tiles

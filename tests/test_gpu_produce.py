@@ -61,6 +61,17 @@ def _rand(shape, seed, scale=1.0):
     return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
 
 
+@pytest.mark.parametrize("extra", [16, 48, 64, 80, 112])
+@pytest.mark.parametrize("op", [oracle.PROD_MODULATE, oracle.PROD_ADD2])
+def test_every_column_residue_of_a_tile(extra, op):
+    """Right-edge tiles of every residue width: each 8-column chunk is
+    produced and written as y only when it lies inside the tensor."""
+    shape = (48, 128 + extra)
+    x, a = _rand(shape, 3000 + extra), _rand(shape, 3100 + extra, 0.5)
+    b = _rand(shape, 3200 + extra, 2.0)
+    _run_and_check(op, x, a, b, 9.0, oracle.E4M3)
+
+
 @pytest.mark.parametrize("shape", [(16, 16), (400, 272), (272, 400), (1024, 2048)])
 @pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
 def test_modulate_shapes(shape, fmt):
