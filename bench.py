@@ -438,6 +438,7 @@ class ToyStack:
             self.qdy = [dsl.Float8Tensor.empty(M, fout, dsl.E5M2, device=dev)
                         for _, fout, _ in self.lin]
             self.dx = [bf(fin) for fin, _, _ in self.lin]
+            self.g_h0 = bf(H)                    # gradient at a block's input, direct part
             ws_bytes = max(dsl.fp8_cast_dbias_workspace_bytes(M, fout) for _, fout, _ in self.lin)
             self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
@@ -554,20 +555,16 @@ class ToyStack:
             g = g + self._linear_bwd(b, L_CROSS_Q, g) + dk
             self.dy[L_SELF][:, :H].copy_(g)
             g = g + self._linear_bwd(b, L_SELF, self.dy[L_SELF])
-            # modulation h1 = gain * h0 / div: gradients of gain, div and h0
-            # (zero where the finite modulation replaced a non-finite quotient)
-            m, h0 = self.mod_out[b], self.h_in[b].float()
-            gain, div = m[:, :H].float(), m[:, H:2 * H].float()
-            t = g.float() / div
-            d_gain, d_div, d_h0 = t * h0, -(t * gain) * h0 / div, t * gain
-            if self.finite:
-                kept = torch.isfinite((gain * h0 / div).to(torch.bfloat16))
-                zero = torch.zeros((), device=t.device)
-                d_gain, d_div, d_h0 = (torch.where(kept, d, zero) for d in (d_gain, d_div, d_h0))
-            self.dy[L_MOD][:, :H].copy_(d_gain)
-            self.dy[L_MOD][:, H:2 * H].copy_(d_div)
-            g_direct = d_h0.to(torch.bfloat16)
-            g = g_direct + self._linear_bwd(b, L_MOD, self.dy[L_MOD])
+            # modulation h1 = gain * h0 / div: one library pass writes the
+            # gradients of gain and div into the modulation linear's output
+            # gradient and that of h0 into g_h0 (zero where the finite
+            # modulation replaced a non-finite quotient)
+            m = self.mod_out[b]
+            dmod = self.dy[L_MOD]
+            self.dsl.fp8_produce_modulate_backward(self.mod_op, g.contiguous(), self.h_in[b],
+                                                   m[:, :H], m[:, H:2 * H], self.g_h0,
+                                                   dmod[:, :H], dmod[:, H:2 * H])
+            g = self.g_h0 + self._linear_bwd(b, L_MOD, dmod)
         return g
 
     def train_step(self, x, target, optimizer=None):
@@ -692,8 +689,9 @@ def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, ite
     with fused bias gradient, dgrad from the cached weight transpose, fp32
     wgrad written as the parameter's gradient; one scale update over 576
     records).  BF16: the same parameters through torch autograd under
-    torch.autocast(bfloat16), the page's BF16 run.  The modulation's
-    backward and the residual sums of the FP8 run are torch ops."""
+    torch.autocast(bfloat16), the page's BF16 run.  The modulation's backward
+    of the FP8 run is the library's fp8_produce_modulate_backward; its
+    residual sums are torch ops."""
     dev = "cuda"
     H, Mt = workloads.HIDDEN, workloads.TOKENS
     stack = ToyStack(dsl, workloads, blocks, train=True)

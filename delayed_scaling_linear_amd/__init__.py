@@ -38,7 +38,7 @@ __all__ = [
     "PRODUCE_MODULATE_FINITE",
     "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
     "fp8_cast_transpose_amax_dbias_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "fp8_cast_transpose_amax_cached", "fp8_reference_copy",
+    "fp8_cast_transpose_amax_cached", "fp8_reference_copy", "fp8_produce_modulate_backward",
     "library_path", "lib",
 ]
 
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
                                                             vp, vp, vp]
         L.fp8_produce_cast_transpose_amax.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64,
                                                       i64, vp, dp, vp, vp, vp]
+        L.fp8_produce_modulate_backward.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, i64, vp,
+                                                    i64, vp, i64, vp, i64, i64, i64, vp]
         L.fp8_cast_transpose_dynamic.argtypes = [vp, i32, i64, i64, i64, i32, vp, dp, vp, vp, vp]
         L.fp8_cast_dbias_workspace_bytes.argtypes = [i64, i64]
         L.fp8_cast_dbias_workspace_bytes.restype = i64
@@ -411,6 +413,27 @@ def fp8_produce_cast_transpose_amax(op: int, x: torch.Tensor, a: torch.Tensor,
         x.shape[0], x.shape[1], _ptr(scale, torch.float32, "scale"), ctypes.byref(d),
         _ptr(amax_cur, torch.float32, "amax_cur"), _ptr(noop_flag, torch.int32, "noop_flag"),
         _stream(stream)), "fp8_produce_cast_transpose_amax")
+
+
+def fp8_produce_modulate_backward(op: int, dy: torch.Tensor, x: torch.Tensor, a: torch.Tensor,
+                                  b: torch.Tensor, dx: torch.Tensor, da: torch.Tensor,
+                                  db: torch.Tensor, stream=None) -> None:
+    """Gradient of the modulation y = a * x / b (op PRODUCE_MODULATE or
+    PRODUCE_MODULATE_FINITE) for the output gradient dy: writes dx, da and db.
+    All seven: 2-D bf16 device tensors of one shape with unit column stride
+    (column slices of wider tensors are fine); the outputs must not overlap
+    each other or the inputs."""
+    for t in (dy, x, a, b, dx, da, db):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+            raise ValueError("dy, x, a, b, dx, da, db must be 2-D bf16 device tensors with unit "
+                             "column stride")
+        if t.shape != dy.shape:
+            raise ValueError("dy, x, a, b, dx, da, db must have one shape")
+    _check(lib().fp8_produce_modulate_backward(
+        op, dy.data_ptr(), _row_stride(dy), x.data_ptr(), _row_stride(x), a.data_ptr(),
+        _row_stride(a), b.data_ptr(), _row_stride(b), dx.data_ptr(), _row_stride(dx),
+        da.data_ptr(), _row_stride(da), db.data_ptr(), _row_stride(db), dy.shape[0],
+        dy.shape[1], _stream(stream)), "fp8_produce_modulate_backward")
 
 
 def fp8_cast_transpose_dynamic(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,

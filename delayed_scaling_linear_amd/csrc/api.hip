@@ -282,6 +282,28 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
                                          out->scale_inv, noop_flag, s));
 }
 
+int fp8_produce_modulate_backward(int32_t op, const uint16_t *dy, int64_t lddy,
+                                  const uint16_t *x, int64_t ldx, const uint16_t *a, int64_t lda,
+                                  const uint16_t *b, int64_t ldb, uint16_t *dx, int64_t lddx,
+                                  uint16_t *da, int64_t ldda, uint16_t *db, int64_t lddb,
+                                  int64_t rows, int64_t cols, fp8_stream_t stream) {
+    if (op != FP8_PRODUCE_MODULATE && op != FP8_PRODUCE_MODULATE_FINITE) return FP8_ERR_ARG;
+    if (rows < 0 || cols < 0 || (cols % 8) != 0) return FP8_ERR_SHAPE;
+    for (int64_t ld : {lddy, ldx, lda, ldb, lddx, ldda, lddb})
+        if (ld < cols || (ld % 8) != 0) return FP8_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8_OK;
+    if (rows > INT64_MAX / ldx) return FP8_ERR_SHAPE;
+    if ((rows * (cols / 8) + 255) / 256 > (int64_t)UINT32_MAX) return FP8_ERR_SHAPE;
+    for (const void *p : {(const void *)dy, (const void *)x, (const void *)a, (const void *)b,
+                          (const void *)dx, (const void *)da, (const void *)db}) {
+        if (p == nullptr) return FP8_ERR_NULL;
+        if (!aligned16(p)) return FP8_ERR_ALIGN;
+    }
+    return status_of(launch_modulate_backward(op == FP8_PRODUCE_MODULATE_FINITE, dy, lddy, x, ldx,
+                                              a, lda, b, ldb, dx, lddx, da, ldda, db, lddb, rows,
+                                              cols, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_cast_transpose_dynamic(const void *x, int32_t src, int64_t rows, int64_t cols,
                                int64_t ld, int32_t margin, float *scale, const fp8_tensor_t *out,
                                float *amax, const int32_t *noop_flag, fp8_stream_t stream) {

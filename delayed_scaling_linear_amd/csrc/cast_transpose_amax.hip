@@ -753,6 +753,62 @@ hipError_t launch_produce_op_fmt(const uint16_t *x, int64_t ldx, const uint16_t 
     return hipGetLastError();
 }
 
+// Gradient of the modulation producer y = a * x / b (FP8_PRODUCE_MODULATE,
+// or _FINITE) with respect to x, a and b, for the output gradient dy of y.
+// fp32 on the widened bf16 inputs, each step rounded to nearest even:
+// u = (a * x) / b (the forward's quotient), t = dy / b, then
+// dx = bf16(t * a), da = bf16(t * x), db = bf16(-(t * u)); a NaN is written
+// 0x7FC0.  FINITE: +0 in all three where the forward's bf16(u) is infinite
+// or NaN (the forward wrote the constant +0 there).
+template <bool FINITE>
+__device__ __forceinline__ void modulate_grad_pair(uint32_t gw, uint32_t xw, uint32_t aw,
+                                                   uint32_t bw, uint32_t &ox, uint32_t &oa,
+                                                   uint32_t &ob) {
+    auto rne = [](float f) -> uint32_t { return (f != f) ? 0x7FC0u : f32_to_bf16_bits_rne(f); };
+    ox = oa = ob = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        auto wide = [h](uint32_t w) { return __uint_as_float(h ? (w & 0xFFFF0000u) : (w << 16)); };
+        const float gv = wide(gw), xv = wide(xw), av = wide(aw), bv = wide(bw);
+        const float u = (av * xv) / bv;
+        const float t = gv / bv;
+        uint32_t rx = rne(t * av), ra = rne(t * xv), rb = rne(-(t * u));
+        if constexpr (FINITE) {
+            if ((rne(u) & 0x7F80u) == 0x7F80u) rx = ra = rb = 0u;
+        }
+        ox |= rx << (16 * h);
+        oa |= ra << (16 * h);
+        ob |= rb << (16 * h);
+    }
+}
+
+// One lane per 8 consecutive columns of one row: four 16-byte loads, three
+// 16-byte stores.  vec_per_row = cols / 8.
+template <bool FINITE>
+__global__ __launch_bounds__(THREADS) void modulate_backward_kernel(
+    const uint16_t *__restrict__ dy, int64_t lddy, const uint16_t *__restrict__ x, int64_t ldx,
+    const uint16_t *__restrict__ a, int64_t lda, const uint16_t *__restrict__ b, int64_t ldb,
+    uint16_t *__restrict__ dx, int64_t lddx, uint16_t *__restrict__ da, int64_t ldda,
+    uint16_t *__restrict__ db, int64_t lddb, int64_t rows, int64_t vec_per_row) {
+    const int64_t v = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+    if (v >= rows * vec_per_row) return;
+    const int64_t r = v / vec_per_row;
+    const int64_t c = (v - r * vec_per_row) * 8;
+    const u32x4 G = *reinterpret_cast<const u32x4 *>(dy + r * lddy + c);
+    const u32x4 X = *reinterpret_cast<const u32x4 *>(x + r * ldx + c);
+    const u32x4 A = *reinterpret_cast<const u32x4 *>(a + r * lda + c);
+    const u32x4 B = *reinterpret_cast<const u32x4 *>(b + r * ldb + c);
+    const uint32_t g[4] = {G.x, G.y, G.z, G.w}, xs[4] = {X.x, X.y, X.z, X.w},
+                   as[4] = {A.x, A.y, A.z, A.w}, bs[4] = {B.x, B.y, B.z, B.w};
+    uint32_t ox[4], oa[4], ob[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        modulate_grad_pair<FINITE>(g[k], xs[k], as[k], bs[k], ox[k], oa[k], ob[k]);
+    *reinterpret_cast<u32x4 *>(dx + r * lddx + c) = u32x4{ox[0], ox[1], ox[2], ox[3]};
+    *reinterpret_cast<u32x4 *>(da + r * ldda + c) = u32x4{oa[0], oa[1], oa[2], oa[3]};
+    *reinterpret_cast<u32x4 *>(db + r * lddb + c) = u32x4{ob[0], ob[1], ob[2], ob[3]};
+}
+
 // Bias gradient, second pass: dbias[c] = sum over tile rows tr of
 // ws[tr * ws_ld + c].  A workgroup takes 64 columns; its four 64-thread
 // parts add the tile rows of four contiguous ranges (loads issued sixteen at
@@ -833,6 +889,25 @@ hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uin
     return launch_produce_op_fmt<FP8_PRODUCE_ADD, FP8_E5M2>(x, ldx, a, lda, b, ldb, y, rows, cols,
                                                             scale, q, qt, amax_cur, scale_inv_out,
                                                             noop, stream);
+}
+
+hipError_t launch_modulate_backward(bool finite, const uint16_t *dy, int64_t lddy,
+                                    const uint16_t *x, int64_t ldx, const uint16_t *a,
+                                    int64_t lda, const uint16_t *b, int64_t ldb, uint16_t *dx,
+                                    int64_t lddx, uint16_t *da, int64_t ldda, uint16_t *db,
+                                    int64_t lddb, int64_t rows, int64_t cols,
+                                    hipStream_t stream) {
+    const int64_t vec_per_row = cols / 8;
+    const dim3 grid((unsigned)((rows * vec_per_row + THREADS - 1) / THREADS));
+    if (finite)
+        hipLaunchKernelGGL(modulate_backward_kernel<true>, grid, dim3(THREADS), 0, stream, dy,
+                           lddy, x, ldx, a, lda, b, ldb, dx, lddx, da, ldda, db, lddb, rows,
+                           vec_per_row);
+    else
+        hipLaunchKernelGGL(modulate_backward_kernel<false>, grid, dim3(THREADS), 0, stream, dy,
+                           lddy, x, ldx, a, lda, b, ldb, dx, lddx, da, ldda, db, lddb, rows,
+                           vec_per_row);
+    return hipGetLastError();
 }
 
 }  // namespace fp8dsl

@@ -49,6 +49,15 @@ hipError_t launch_produce_cast(int op, const uint16_t *x, int64_t ldx, const uin
                                uint8_t *q, uint8_t *qt, float *amax_cur, float *scale_inv_out,
                                const int32_t *noop, hipStream_t stream);
 
+// Gradient of y = a * x / b: dx, da, db (bf16 [rows, cols], cols % 8 == 0,
+// row strides multiples of 8 elements, 16-byte aligned).
+hipError_t launch_modulate_backward(bool finite, const uint16_t *dy, int64_t lddy,
+                                    const uint16_t *x, int64_t ldx, const uint16_t *a,
+                                    int64_t lda, const uint16_t *b, int64_t ldb, uint16_t *dx,
+                                    int64_t lddx, uint16_t *da, int64_t ldda, uint16_t *db,
+                                    int64_t lddb, int64_t rows, int64_t cols,
+                                    hipStream_t stream);
+
 // Dynamic scaling: *amax = max |x| (cleared first), then *scale = fp8_max /
 // (amax * 2^margin) unless zero / non-finite (the scale update's guard).
 hipError_t launch_dynamic_scale(const void *x, int src, int64_t rows, int64_t cols, int64_t ld,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 8
+#define FP8DSL_ABI_VERSION 9
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -326,6 +326,38 @@ int fp8_produce_cast_transpose_amax(int32_t op, const uint16_t *x, int64_t ldx,
                                     int64_t ldb, uint16_t *y, int64_t rows, int64_t cols,
                                     const float *scale, const fp8_tensor_t *out, float *amax_cur,
                                     const int32_t *noop_flag, fp8_stream_t stream);
+
+/*
+ * fp8_produce_modulate_backward -- the gradient of the modulation producer
+ * (op FP8_PRODUCE_MODULATE or FP8_PRODUCE_MODULATE_FINITE above) with respect
+ * to its three inputs, in one pass: the backward of the toy block's
+ * modulation that the training loop of "CPU Overhead of te.Linear FP8
+ * Layers" runs through autograd, whose da and db form the modulation
+ * linear's output gradient (cast next, to E5M2 with the bias gradient).
+ *
+ * For y = a * x / b and the gradient dy of y, with fp32 arithmetic on the
+ * exactly widened bf16 inputs and every step rounded to nearest even:
+ *   u  = (a * x) / b          (the forward's quotient before its rounding)
+ *   t  = dy / b
+ *   dx = bf16(t * a),  da = bf16(t * x),  db = bf16(-(t * u))
+ * a NaN result is written as 0x7FC0.  Op FP8_PRODUCE_MODULATE_FINITE: where
+ * the forward's bf16(u) is infinite or NaN (the forward wrote +0 there, a
+ * constant) dx, da and db are +0.
+ *
+ * dy, x, a, b   device bf16 [rows, cols], row strides lddy, ldx, lda, ldb
+ * dx, da, db    device bf16 [rows, cols], row strides lddx, ldda, lddb;
+ *               column slices of wider tensors are fine for all seven.  The
+ *               outputs must not overlap each other or the inputs.
+ * rows >= 0; cols a multiple of 8; every stride >= cols and a multiple of 8
+ * elements; every pointer 16-byte aligned.  Allocates nothing.
+ * Errors: FP8_ERR_ARG (another op), FP8_ERR_SHAPE, FP8_ERR_NULL,
+ * FP8_ERR_ALIGN, FP8_ERR_LAUNCH / FP8_ERR_DEVICE.  rows or cols 0: no work.
+ */
+int fp8_produce_modulate_backward(int32_t op, const uint16_t *dy, int64_t lddy,
+                                  const uint16_t *x, int64_t ldx, const uint16_t *a, int64_t lda,
+                                  const uint16_t *b, int64_t ldb, uint16_t *dx, int64_t lddx,
+                                  uint16_t *da, int64_t ldda, uint16_t *db, int64_t lddb,
+                                  int64_t rows, int64_t cols, fp8_stream_t stream);
 
 /*
  * fp8_cast_transpose_dynamic -- dynamic scaling, the comparator of delayed

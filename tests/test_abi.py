@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
                  "fp8_cast_transpose_amax_dbias", "fp8_cast_dbias_workspace_bytes",
                  "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic",
                  "fp8_linear_fwd_fp8out", "fp8_cast_transpose_amax_dbias_noalloc",
-                 "fp8_cast_transpose_amax_cached", "fp8_reference_copy"):
+                 "fp8_cast_transpose_amax_cached", "fp8_reference_copy",
+                 "fp8_produce_modulate_backward"):
         assert want in names
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 8
+    assert dsl.fp8_abi_version() == 9
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -261,3 +262,28 @@ def test_reference_copy_and_cached_cast_validation():
     d = _desc(30, 48)
     assert L.fp8_cast_transpose_amax_cached(0x4000, 0, 30, 48, 48, 0x5000, byref(d), None, None,
                                             None) == -2
+
+
+def test_modulate_backward_validation():
+    """Every rejection happens on the host before anything is enqueued."""
+    L = dsl.lib()
+    f = L.fp8_produce_modulate_backward
+    P = [0x1000 + 0x1000 * i for i in range(7)]        # 16-byte aligned stand-ins
+
+    def call(op=dsl.PRODUCE_MODULATE, ptrs=P, lds=(64,) * 7, rows=16, cols=64):
+        args = []
+        for p, ld in zip(ptrs, lds):
+            args += [p, ld]
+        return f(op, *args, rows, cols, None)
+
+    assert call(op=dsl.PRODUCE_ADD) == -5                       # not a modulation
+    assert call(op=dsl.PRODUCE_ADD2) == -5
+    assert call(cols=60) == -2                                  # cols not a multiple of 8
+    assert call(rows=-1) == -2
+    assert call(lds=(64, 64, 56, 64, 64, 64, 64), cols=64) == -2   # a stride below cols
+    assert call(lds=(64, 64, 64, 64, 68, 64, 64), cols=64) == -2   # a stride not a multiple of 8
+    assert call(ptrs=P[:3] + [None] + P[4:]) == -1              # b NULL
+    assert call(ptrs=P[:6] + [None]) == -1                      # db NULL
+    assert call(ptrs=P[:1] + [0x2008] + P[2:]) == -3            # x misaligned
+    assert call(rows=0) == 0 and call(cols=0) == 0              # no work
+    assert call(ptrs=[None] * 7, rows=0) == 0

@@ -186,3 +186,59 @@ def test_noop_flag_writes_nothing():
                                         torch.ones(1, device=DEV), out, amax, noop_flag=flag)
     torch.cuda.synchronize()
     assert (y.float() == -7.0).all() and (out.data == 0xAA).all() and float(amax[0]) == 0.0
+
+
+def _grad_check(op, dy, x, a, b, outs=None):
+    """fp8_produce_modulate_backward on device copies of the CPU bf16 tensors
+    (views of wider tensors keep their strides), bit-exact against the oracle."""
+    def to_dev(t):
+        if t._base is not None:
+            full = t._base.to(DEV)
+            r0, c0 = divmod(t.storage_offset(), t._base.stride(0))
+            return full[r0:r0 + t.shape[0], c0:c0 + t.shape[1]]
+        return t.to(DEV)
+    if outs is None:
+        outs = [torch.full(dy.shape, -3.0, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    dsl.fp8_produce_modulate_backward(op, to_dev(dy), to_dev(x), to_dev(a), to_dev(b), *outs)
+    torch.cuda.synchronize()
+    want = oracle.modulate_backward(op, _bits_view(dy), _bits_view(x), _bits_view(a), _bits_view(b))
+    for got, w, name in zip(outs, want, ("dx", "da", "db")):
+        np.testing.assert_array_equal(bits16(got), w, err_msg=name)
+    return outs
+
+
+@pytest.mark.parametrize("shape", [(16, 8), (272, 400), (1000, 2056)])
+@pytest.mark.parametrize("op", [oracle.PROD_MODULATE, oracle.PROD_MODULATE_FINITE])
+def test_modulate_backward_shapes(shape, op):
+    dy, x = _rand(shape, 11), _rand(shape, 12, 3.0)
+    a, b = _rand(shape, 13, 0.5), _rand(shape, 14, 0.8)
+    _grad_check(op, dy, x, a, b)
+
+
+@pytest.mark.parametrize("op", [oracle.PROD_MODULATE, oracle.PROD_MODULATE_FINITE])
+def test_modulate_backward_at_the_block_layout(op):
+    """The toy block's shapes: the gain and divisor are column slices of the
+    modulation linear's [8192, 12288] output, and da, db go straight into
+    the first two column slices of its [8192, 12288] output gradient."""
+    M, H = 8192, 2048
+    m = _rand((M, 6 * H), 21, 0.7)
+    dy, h0 = _rand((M, H), 22, 1e-3), _rand((M, H), 23)
+    gain, div = m[:, :H], m[:, H:2 * H]
+    dmod = torch.zeros(M, 6 * H, dtype=torch.bfloat16, device=DEV)
+    dh0 = torch.empty(M, H, dtype=torch.bfloat16, device=DEV)
+    _grad_check(op, dy, h0, gain, div, outs=[dh0, dmod[:, :H], dmod[:, H:2 * H]])
+    assert int(torch.count_nonzero(dmod[:, 2 * H:])) == 0       # untouched columns
+
+
+@pytest.mark.parametrize("op", [oracle.PROD_MODULATE, oracle.PROD_MODULATE_FINITE])
+def test_modulate_backward_specials(op):
+    """Zero divisors of both signs, 0/0, infinite and NaN operands, and a
+    quotient that overflows bf16: the finite op zeroes exactly where the
+    forward wrote its constant."""
+    inf, nan = float("inf"), float("nan")
+    vals_x = [1.0, 0.0, 3.0e38, 2.0, inf, nan, 1.0, -0.0, 1e-30, 5.0, 1.0, 2.0, 7.0, 0.5, -1.0, 3.0]
+    vals_a = [2.0, 0.0, 2.0, inf, 1.0, 1.0, nan, 1.0, 1e-30, 3.0, 1.0, 0.0, 1.0, 1.0, 1.0, 1.0]
+    vals_b = [0.0, 0.0, 1.0, 1.0, 2.0, 1.0, 1.0, -0.0, 1e-30, 4.0, inf, 1.0, 0.0, -0.0, 1.0, nan]
+    vals_g = [1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 2.0, 1.0, inf, -1.0, 1.0, nan, 1.0]
+    t = lambda v: torch.tensor([v], dtype=torch.bfloat16)
+    _grad_check(op, t(vals_g), t(vals_x), t(vals_a), t(vals_b))
