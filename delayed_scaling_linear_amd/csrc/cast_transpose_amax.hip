@@ -20,8 +20,10 @@
 //     row (16-byte loads: the eight lanes of a row cover one whole 128-byte
 //     line per instruction), encodes them, and swaps half of its codes with
 //     its neighbour lane (l^1) so that it then holds the 16 columns
-//     16*cq .. 16*cq+15, cq = 4*(cc%2) + cc/2.  An fp32 lane loads and
-//     holds columns 16*cc .. 16*cc+15 (cq = cc);
+//     16*cq .. 16*cq+15, cq = 4*(cc%2) + cc/2.  An fp32 lane loads the
+//     4-column chunks cc, 8+cc, 16+cc and 24+cc (again whole lines per
+//     instruction) and trades its codes through a per-wave row staging in
+//     LDS for the 16 columns 16*cc .. 16*cc+15 (cq = cc);
 //   * each lane scales, clamps to +-fp8_max and converts with the hardware
 //     OCP FP8 converter (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, round to
 //     nearest even), writes its four 16-byte row-major code rows directly,
@@ -56,23 +58,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
-// Sixteen consecutive source elements of one row, as loaded (16-byte loads).
+// A lane's sixteen source elements of one tile row, as loaded: kChunks
+// 16-byte chunks, chunk k at tile column (128 / kChunks) * k + (16 / kChunks)
+// * cc for lane chunk cc (src_offsets), so that the eight lanes of a row
+// cover whole 128-byte lines with every load instruction.
 template <int SRC>
 struct SrcRow;
 
 template <>
 struct SrcRow<FP8_DTYPE_BF16> {
     static constexpr int kBytes = 2;
-    // Two 8-element chunks 128 bytes apart (see src_offsets).
-    static constexpr bool kSplit = true;
+    static constexpr int kChunks = 2;        // 8 elements each, 128 bytes apart
     u32x4 v[2];
-    // Chunks at byte offsets off0 and off1 of the descriptor (an offset
-    // outside it reads zeros and touches no memory); POL is the cache policy
-    // (0, or 2 = non-temporal).
+    // Chunk k at byte offset off[k] of the descriptor (an offset outside it
+    // reads zeros and touches no memory); POL is the cache policy (0, or 2 =
+    // non-temporal).
     template <int POL>
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off0, uint32_t off1) {
-        v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off0, 0, POL));
-        v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off1, 0, POL));
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[2]) {
+        v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off[0], 0, POL));
+        v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off[1], 0, POL));
     }
     // Elements 4j .. 4j+3 as fp32 (exact widening): j = 0, 1 from the first
     // chunk, 2, 3 from the second.
@@ -102,15 +106,15 @@ struct SrcRow<FP8_DTYPE_BF16> {
 template <>
 struct SrcRow<FP8_DTYPE_FP32> {
     static constexpr int kBytes = 4;
-    // One run of 16 consecutive elements (off1 is unused).
-    static constexpr bool kSplit = false;
+    static constexpr int kChunks = 4;        // 4 elements each, 128 bytes apart
     f32x4 v[4];
     template <int POL>
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off0, uint32_t) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[4]) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-            v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off0 + 16 * h, 0, POL));
+            v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off[h], 0, POL));
     }
+    // Elements 4j .. 4j+3: chunk j.
     __device__ __forceinline__ void get4(int j, float o[4]) const {
         o[0] = v[j].x;
         o[1] = v[j].y;
@@ -132,36 +136,40 @@ struct SrcRow<FP8_DTYPE_FP32> {
 
 constexpr uint32_t SRC_OOB = 0x80000000u;
 
-// Byte offsets (from the tile's first element) of lane chunk cc's source in
-// the first of its four rows, 4*rg; a chunk past the tensor's columns, or a
-// row past its rows, takes SRC_OOB and reads zeros.  bf16: 8-element chunks
-// cc and 8 + cc; fp32: the 16 elements from column 16*cc.
+// Byte offsets (from the tile's first element) of lane chunk cc's source
+// chunks in the first of its four rows, 4*rg; a chunk past the tensor's
+// columns, or a row past its rows, takes SRC_OOB and reads zeros (columns
+// come in groups of 16, so a chunk is wholly inside or outside).
 template <int SRC>
 __device__ __forceinline__ void src_offsets(bool row_ok, int64_t col0, int64_t cols, int64_t ld,
-                                            int rg, int cc, uint32_t &off0, uint32_t &off1) {
-    constexpr int EB = SrcRow<SRC>::kBytes;
+                                            int rg, int cc,
+                                            uint32_t (&off)[SrcRow<SRC>::kChunks]) {
+    constexpr int EB = SrcRow<SRC>::kBytes, K = SrcRow<SRC>::kChunks;
     const int64_t rb = (int64_t)(4 * rg) * ld;
-    if constexpr (SrcRow<SRC>::kSplit) {
-        off0 = (row_ok && col0 + 8 * cc < cols) ? (uint32_t)((rb + 8 * cc) * EB) : SRC_OOB;
-        off1 = (row_ok && col0 + 64 + 8 * cc < cols) ? (uint32_t)((rb + 64 + 8 * cc) * EB) : SRC_OOB;
-    } else {
-        off0 = (row_ok && col0 + 16 * cc < cols) ? (uint32_t)((rb + 16 * cc) * EB) : SRC_OOB;
-        off1 = SRC_OOB;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int col = (128 / K) * k + (16 / K) * cc;
+        off[k] = (row_ok && col0 + col < cols) ? (uint32_t)((rb + col) * EB) : SRC_OOB;
     }
 }
 
-// The 16-column chunk whose codes lane chunk cc stores (after the bf16
-// neighbour exchange in encode_block).
+// The 16-column chunk whose codes lane chunk cc stores (after the exchange
+// in encode_block: bf16 with the neighbour lane, fp32 through LDS).
 template <int SRC>
 __device__ __forceinline__ int store_chunk(int cc) {
-    return SrcRow<SRC>::kSplit ? 4 * (cc & 1) + (cc >> 1) : cc;
+    return SrcRow<SRC>::kChunks == 2 ? 4 * (cc & 1) + (cc >> 1) : cc;
 }
 
 // Column (0..127 in the tile) of element k (0..15) of lane chunk cc's source.
 template <int SRC>
 __device__ __forceinline__ int src_col(int cc, int k) {
-    return SrcRow<SRC>::kSplit ? (k < 8 ? 8 * cc + k : 56 + 8 * cc + k) : 16 * cc + k;
+    constexpr int K = SrcRow<SRC>::kChunks, E = 16 / K;
+    return (128 / K) * (k / E) + E * cc + (k % E);
 }
+
+// Words of the per-wave row staging that the fp32 exchange uses: 32 rows of
+// 128 code bytes.
+constexpr int ROW_STAGE_WORDS = 32 * 32;
 
 // Lane l's value of v on lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).
 __device__ __forceinline__ uint32_t from_neighbour(uint32_t v) {
@@ -191,13 +199,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // transposed 4-row words into the LDS tile `lt`.  bf16: the lane encodes its
 // two 8-column source chunks, then keeps the codes of the first (even lane)
 // or second (odd lane) and takes the neighbour's codes of the same chunk
-// parity, which together are chunk cq = store_chunk(cc).  Every lane of the
-// wave must call it (the exchange reads the neighbour's registers).
+// parity, which together are chunk cq = store_chunk(cc).  fp32: the lane's
+// four 4-column chunks go through the wave's row staging `ls`
+// (ROW_STAGE_WORDS words) and come back as the 16 columns of chunk cq = cc.
+// Every lane of the wave must call it (the exchanges read other lanes' data).
 template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
 __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float s, bool s_special,
                                              bool valid, uint8_t *__restrict__ q, int64_t r,
                                              int64_t c, int64_t cols, int cq, int rg, int lane,
-                                             uint32_t *lt, uint32_t &key) {
+                                             uint32_t *ls, uint32_t *lt, uint32_t &key) {
     uint32_t codes[4][4];                    // [row][word of 4 columns]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -218,7 +228,35 @@ __device__ __forceinline__ void encode_block(const SrcRow<SRC> (&src)[4], float 
             }
         }
     }
-    if constexpr (SrcRow<SRC>::kSplit) {
+    if constexpr (SrcRow<SRC>::kChunks == 4) {
+        // Word group g (columns 4g .. 4g+3) of staging row qr at 16-byte
+        // chunk (g / 4) ^ (qr / 4), word g % 4 (at most two lanes per bank on
+        // the writes).  A wave's LDS operations complete in issue order, so
+        // the reads see every lane's writes; the fences keep the compiler
+        // from moving them across.
+        const int cc = lane & 7, rl = lane >> 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int qr = 4 * rl + i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int g = 8 * j + cc;
+                ls[qr * 32 + (((g >> 2) ^ rl) << 2) + (g & 3)] = codes[i][j];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 w =
+                *reinterpret_cast<const u32x4 *>(&ls[(4 * rl + i) * 32 + ((cq ^ rl) << 2)]);
+            codes[i][0] = w.x;
+            codes[i][1] = w.y;
+            codes[i][2] = w.z;
+            codes[i][3] = w.w;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    } else {
         // Even lane: columns 8cc..+7 | neighbour's 8cc+8..+15.  Odd lane:
         // neighbour's 64+8cc-8..+7 | its own 64+8cc..+7.
         const bool odd = lane & 1;
@@ -332,6 +370,8 @@ cast_transpose_amax_kernel(
     __shared__ uint32_t lds_t[2][TILE * (TILE / 4)];   // transposed tiles, 2 x 16 KiB
     __shared__ uint32_t lds_amax[THREADS / 64];
     __shared__ float lds_db[DBIAS ? 2 * (THREADS / 64) * TILE : 1];   // [buffer][wave][column]
+    constexpr int K = SrcRow<SRC>::kChunks;
+    __shared__ uint32_t lds_rows[K == 4 ? (THREADS / 64) * ROW_STAGE_WORDS : 1];   // fp32 exchange
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -349,7 +389,7 @@ cast_transpose_amax_kernel(
 
     // Source descriptor of tile t (empty when t is past the last tile) and
     // this lane's byte offsets in it.
-    auto tile_rsrc = [&](int64_t t, __amdgpu_buffer_rsrc_t &rs, uint32_t (&off)[2], int64_t &r,
+    auto tile_rsrc = [&](int64_t t, __amdgpu_buffer_rsrc_t &rs, uint32_t (&off)[K], int64_t &r,
                          int64_t &c, bool &valid) {
         const int64_t tr = t / tiles_c, tcn = t - (t / tiles_c) * tiles_c;
         const int64_t row0 = tr * TILE, col0 = tcn * TILE;
@@ -362,19 +402,20 @@ cast_transpose_amax_kernel(
         rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(static_cast<const uint8_t *>(xv)) + base, (short)0, nrec,
             0x00020000);
-        src_offsets<SRC>((t < ntiles) && (r < rows), col0, cols, ld, rg, cc, off[0], off[1]);
+        src_offsets<SRC>((t < ntiles) && (r < rows), col0, cols, ld, rg, cc, off);
     };
     const uint32_t row_step = (uint32_t)(ld * EB);
     // `cached` (wave-uniform) reads the source through the caches instead.
-    auto load_tile = [&](SrcRow<SRC> (&dst)[4], __amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[2]) {
+    auto load_tile = [&](SrcRow<SRC> (&dst)[4], __amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[K]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t o0 = off[0] == SRC_OOB ? SRC_OOB : off[0] + i * row_step;
-            const uint32_t o1 = off[1] == SRC_OOB ? SRC_OOB : off[1] + i * row_step;
+            uint32_t o[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) o[k] = off[k] == SRC_OOB ? SRC_OOB : off[k] + i * row_step;
             if (cached)
-                dst[i].template load<0>(rs, o0, o1);
+                dst[i].template load<0>(rs, o);
             else
-                dst[i].template load<2>(rs, o0, o1);
+                dst[i].template load<2>(rs, o);
         }
     };
     auto store_t = [&](const uint32_t *lt, int64_t t) {
@@ -385,7 +426,7 @@ cast_transpose_amax_kernel(
     uint32_t key = 0;                        // sign-cleared max, fp32 bit order
     SrcRow<SRC> src[2][4];
     __amdgpu_buffer_rsrc_t rs_cur, rs_nxt;
-    uint32_t off_cur[2], off_nxt[2];
+    uint32_t off_cur[K], off_nxt[K];
     int64_t r_cur, c_cur, r_nxt, c_nxt;
     bool v_cur, v_nxt;
     int64_t t = blockIdx.x;
@@ -400,7 +441,9 @@ cast_transpose_amax_kernel(
                 tile_rsrc(tn, rs_nxt, off_nxt, r_nxt, c_nxt, v_nxt);
                 load_tile(src[u ^ 1], rs_nxt, off_nxt);           // empty past the end
                 encode_block<SRC, FMT, WANT_Q, WANT_QT>(src[u], s, s_special, v_cur, q, r_cur,
-                                                        c_cur, cols, cq, rg, lane, lds_t[u], key);
+                                                        c_cur, cols, cq, rg, lane,
+                                                        lds_rows + (K == 4 ? wave * ROW_STAGE_WORDS : 0),
+                                                        lds_t[u], key);
                 if constexpr (DBIAS) {
                     // Rows past the tensor were loaded as zeros and add nothing.
                     float cs[16];
@@ -473,6 +516,8 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
     if (noop != nullptr && *noop != 0) return;
     __shared__ uint32_t lds_t[TILE * (TILE / 4)];      // the transposed tile, 16 KiB
     __shared__ uint32_t lds_amax[THREADS / 64];
+    constexpr int K = SrcRow<SRC>::kChunks;
+    __shared__ uint32_t lds_rows[K == 4 ? (THREADS / 64) * ROW_STAGE_WORDS : 1];   // fp32 exchange
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -498,21 +543,23 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(static_cast<const uint8_t *>(xv)) + base, (short)0,
         (int32_t)min(avail, (int64_t)0x7FFFFFFF), 0x00020000);
-    uint32_t off[2];
-    src_offsets<SRC>(r < rows, col0, cols, ld, rg, cc, off[0], off[1]);
+    uint32_t off[K];
+    src_offsets<SRC>(r < rows, col0, cols, ld, rg, cc, off);
     const uint32_t row_step = (uint32_t)(ld * EB);
     SrcRow<SRC> src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t o0 = off[0] == SRC_OOB ? SRC_OOB : off[0] + i * row_step;
-        const uint32_t o1 = off[1] == SRC_OOB ? SRC_OOB : off[1] + i * row_step;
+        uint32_t o[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) o[k] = off[k] == SRC_OOB ? SRC_OOB : off[k] + i * row_step;
         if (cached)
-            src[i].template load<0>(rs, o0, o1);
+            src[i].template load<0>(rs, o);
         else
-            src[i].template load<2>(rs, o0, o1);
+            src[i].template load<2>(rs, o);
     }
     uint32_t key = 0;
     encode_block<SRC, FMT, WANT_Q, WANT_QT>(src, s, s_special, valid, q, r, c, cols, cq, rg, lane,
+                                            lds_rows + (K == 4 ? wave * ROW_STAGE_WORDS : 0),
                                             lds_t, key);
     __syncthreads();
     if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
@@ -724,7 +771,7 @@ __global__ __launch_bounds__(THREADS) void produce_cast_kernel(
     }
     uint32_t key = 0;
     encode_block<FP8_DTYPE_BF16, FMT, WANT_Q, WANT_QT>(ys, s, s_special, valid, q, r, c, cols, cq,
-                                                       rg, lane, lds_t, key);
+                                                       rg, lane, nullptr, lds_t, key);
     __syncthreads();
     if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
     if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
