@@ -875,8 +875,12 @@ def traffic_record(root: str):
 
     # A kernel's bytes count only while every source file it was built from
     # is unchanged.
+    def unchanged(n):
+        now = sha(n)
+        return now is not None and rec["source_sha256"].get(n) == now
+
     return {k: v for k, v in rec["kernels"].items()
-            if v.get("sources") and all(rec["source_sha256"].get(n) == sha(n) for n in v["sources"])}
+            if v.get("sources") and all(unchanged(n) for n in v["sources"])}
 
 
 def progress(msg: str) -> None:

@@ -173,6 +173,40 @@ def test_full_size_forward_every_output_on_the_benchmark_inputs():
     assert_gemm_close(bf16_values(bits16(y)), bf16_values(ref), "fwd 8192x8192x2048, every output")
 
 
+def test_full_size_backward_every_output_on_the_benchmark_inputs():
+    """The benchmark's own backward: dY [8192, 8192] ~N(0,1e-3) cast to E5M2,
+    X and W [8192, 2048] cast to E4M3 (codes and transposes by the oracle,
+    amax-derived scales); every output of dgrad (dX [8192, 2048] bf16, from
+    W's transpose) and of wgrad (dW [8192, 2048] fp32, from both transposes)
+    against the oracle's full products (contraction 8192)."""
+    x, w, _ = workloads.mlp_forward(0)
+    dy = workloads.mlp_grad()
+    xb, wb, dyb = bits16(x), bits16(w), bits16(dy)
+    amax = lambda b: np.float32(np.abs(bf16_values(b)).max())
+    sx, sw, sdy = np.float32(448.0) / amax(xb), np.float32(448.0) / amax(wb), \
+        np.float32(57344.0) / amax(dyb)
+    _, oxT, _, six = oracle.cast_transpose_amax(xb, sx, oracle.E4M3, want_q=False)
+    _, owT, _, siw = oracle.cast_transpose_amax(wb, sw, oracle.E4M3, want_q=False)
+    ody, odyT, _, sidy = oracle.cast_transpose_amax(dyb, sdy, oracle.E5M2)
+    M, N, K = 8192, 8192, 2048
+    dyt = dsl.Float8Tensor(torch.from_numpy(ody).to(DEV), torch.from_numpy(odyT).to(DEV),
+                           torch.tensor([float(sidy)], device=DEV), 1, M, N)
+    wt = dsl.Float8Tensor(None, torch.from_numpy(owT).to(DEV),
+                          torch.tensor([float(siw)], device=DEV), 0, N, K)
+    xt = dsl.Float8Tensor(None, torch.from_numpy(oxT).to(DEV),
+                          torch.tensor([float(six)], device=DEV), 0, M, K)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    dw = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    dsl.fp8_linear_dgrad(dyt, wt, dx)
+    dsl.fp8_linear_wgrad(dyt, xt, dw)
+    torch.cuda.synchronize()
+    ref_dx = oracle.gemm_nt(ody, 1, owT, 0, sidy, siw)
+    assert_gemm_close(bf16_values(bits16(dx)), bf16_values(ref_dx), "dgrad 8192x2048x8192, every output")
+    ref_dw = oracle.gemm_nt(odyT, 1, oxT, 0, sidy, six, out_kind=oracle.OUT_FP32)
+    assert_gemm_close(f32(dw).astype(np.float64), ref_dw.astype(np.float64),
+                      "wgrad 8192x2048x8192 fp32, every output")
+
+
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 272),      # large-tile path with a K tail
                                    (4104, 4104, 320),      # ragged M and N on the large-tile path
                                    (8200, 2056, 2064)])    # ragged everything, several tiles per CU
