@@ -384,13 +384,13 @@ class ToyStack:
     """
 
     def __init__(self, dsl, workloads, blocks: int, *, train: bool = False, dev: str = "cuda",
-                 seed: int = 20, weights=None, modulate: str = "finite"):
+                 seed: int = 20, weights=None, modulate: str = "finite", tokens: int = 0):
         self.dsl, self.blocks, self.train, self.dev = dsl, blocks, train, dev
         if modulate not in ("page", "finite"):
             raise ValueError("modulate must be 'page' or 'finite'")
         self.finite = modulate == "finite"
         self.mod_op = dsl.PRODUCE_MODULATE_FINITE if self.finite else dsl.PRODUCE_MODULATE
-        self.H, self.M = workloads.HIDDEN, workloads.TOKENS
+        self.H, self.M = workloads.HIDDEN, tokens or workloads.TOKENS
         self.lin = workloads.toy_block_linears()
         nl = len(self.lin)
         self.R = 3 if train else 2
@@ -611,16 +611,18 @@ def _time_loop(fn, reps: int, warmup: int = 1):
     return e0.elapsed_time(e1) / reps, (time.perf_counter() - t0) * 1e3 / reps
 
 
-def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
-    """The 32-block toy stack forward (4.398e13 GEMM FLOP, one scale update
-    over all 384 records per forward), eagerly and as one captured HIP graph,
-    each with the weights re-cast and with cached FP8 weights (the weight
-    casts see a device no-op flag, so one graph serves both); as a graph with
-    the modulation and residual adds fused into the following casts; and the
-    same stack in plain torch bf16.  Two interleaved rounds, best of each."""
+def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3, tokens: int = 0):
+    """The 32-block toy stack forward (at the default 8192 tokens 4.398e13
+    GEMM FLOP, one scale update over all 384 records per forward), eagerly
+    and as one captured HIP graph, each with the weights re-cast and with
+    cached FP8 weights (the weight casts see a device no-op flag, so one
+    graph serves both); as a graph with the modulation and residual adds
+    fused into the following casts; and the same stack in plain torch bf16.
+    Two interleaved rounds, best of each.  With few tokens the eager forward
+    is bound by the host's launch rate, the case the graph is for."""
     dev = "cuda"
-    H, Mt = workloads.HIDDEN, workloads.TOKENS
-    stack = ToyStack(dsl, workloads, blocks)
+    H, Mt = workloads.HIDDEN, tokens or workloads.TOKENS
+    stack = ToyStack(dsl, workloads, blocks, tokens=Mt)
     x0 = workloads.uniform_bf16((Mt, H), workloads.SEED_X).to(dev)
     xin = torch.empty_like(x0)
     xin.copy_(x0)
@@ -659,7 +661,7 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3):
     nonfinite = int((~torch.isfinite(out_fused.float())).sum())
     flop = 2 * Mt * sum(fin * fout for fin, fout, _ in stack.lin) * blocks
     out = {k: round(v, 3) for k, v in res.items()}
-    out.update({"blocks": blocks, "gemm_flop": flop,
+    out.update({"blocks": blocks, "tokens": Mt, "gemm_flop": flop,
                 "library_launches_per_forward": blocks * 18 + 1,
                 "graph_fused_producers_gemm_tflops":
                     round(flop / (res["graph_fused_producers_ms"] * 1e-3) / 1e12, 1),
@@ -968,6 +970,8 @@ def main():
     fp8out_cost = fp8_output_forward(dsl, st)
     progress("variant comparisons done")
     toy = None if args.no_toy_stack else toy_stack_forward(dsl, workloads)
+    toy_small = None if args.no_toy_stack else toy_stack_forward(dsl, workloads, reps=10,
+                                                                 tokens=1024)
     progress("toy-stack forward done")
     train = None if args.no_train_step else toy_stack_train_step(dsl, workloads)
     progress("toy-stack training step done")
@@ -1021,6 +1025,7 @@ def main():
     result["fp8_output_forward"] = fp8out_cost
     if toy is not None:
         result["toy_stack_forward"] = toy
+        result["toy_stack_forward_1024_tokens"] = toy_small
     if train is not None:
         result["toy_stack_train_step"] = train
     if not args.no_cpu_baseline:

@@ -168,8 +168,18 @@ def _row_stride(t: torch.Tensor) -> int:
     return t.stride(0) if t.numel() > 0 else t.shape[1]
 
 
+# torch's raw getter of the current stream handle (the public
+# torch.cuda.current_stream() builds a Stream object on every call, which
+# costs more host time than the library call itself); the public call is the
+# fallback where the raw one does not exist.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_raw_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream) -> int:
     if stream is None:
+        if _raw_stream is not None and _raw_device is not None:
+            return _raw_stream(_raw_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
