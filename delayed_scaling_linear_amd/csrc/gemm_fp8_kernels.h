@@ -19,8 +19,9 @@
 //
 // Design (gfx950, wave64).  Three kernels; launch_fmt picks one per call:
 //
-//   * gemm_nt_dma_kernel -- every large product with K % 128 == 0 (all the
-//     toy-block shapes).  Persistent: one 256-thread workgroup per CU walks
+//   * gemm_nt_dma_kernel -- every large product (256^3 outputs or more, or
+//     at least three quarters of a 256 x 256 tile per CU) with K % 128 == 0
+//     (all the toy-block shapes at 8192 tokens).  Persistent: one 256-thread workgroup per CU walks
 //     256 x 256 output tiles in an XCD-aware order (workgroup b runs on XCD
 //     b % 8, and each XCD gets a contiguous, row-grouped range of tiles).
 //     Four waves own 128 x 128 each as 4 x 4 v_mfma_f32_32x32x64_f8f6f4
@@ -36,8 +37,9 @@
 //   * gemm_nt_big_kernel -- the same tiling for large products whose K is a
 //     multiple of 16 only: 64-byte stages in three LDS buffers, loaded
 //     through registers, K tails read as zero through the buffer range check.
-//   * gemm_nt_kernel -- small products: 128 x 128 tiles, one workgroup per
-//     tile, v_mfma_f32_16x16x128_f8f6f4, double-buffered LDS.
+//   * gemm_nt_kernel -- small products: 128 x 128 tiles (64 x 128 when
+//     there would be fewer tiles than CUs), one workgroup per tile,
+//     v_mfma_f32_16x16x128_f8f6f4, double-buffered LDS.
 //
 // Shared by all three: LDS rows are 128 bytes with the 16-byte chunk c of row
 // r stored at a row-dependent XOR of c (conflict-free fragment reads); the B
@@ -1426,19 +1428,33 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
                       const float *sa, const float *sb, const uint16_t *bias, void *C,
                       const QOut &qo, hipStream_t stream) {
     // Large problems: 256 x 256 tiles, four waves of 128 x 128 (32x32x64
-    // instructions); small ones: 128 x 128 tiles (16x16x128 instructions).
+    // instructions); small ones: 128 x 128 or 64 x 128 tiles (16x16x128
+    // instructions).
     // The large kernel addresses operands with 32-bit buffer offsets.
     // It also needs at least four 64-byte K stages.
     const bool fits32 = (M + 256) * K < ((int64_t)1 << 31) && (N + 256) * K < ((int64_t)1 << 31);
     // The LDS-DMA kernel also addresses 128 output rows with 32-bit offsets.
     constexpr int64_t out_bytes = OUT == FP8_DTYPE_BF16 ? 2 : (OUT == FP8_DTYPE_FP32 ? 4 : 1);
     const bool out32 = 128 * N * out_bytes < ((int64_t)1 << 31);
-    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && out32 && K >= 256 && K % 128 == 0)
+    int cus = 0;
+    if (hipError_t e = current_cu_count(&cus)) return e;
+    // The large kernels run at about twice the small kernel's rate per CU, so
+    // they take every product with at least three quarters of a 256 x 256
+    // tile per CU (e.g. 1024 x 12288: 192 tiles).
+    const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const bool large = M * N >= (int64_t)256 * 256 * 256 || 4 * tiles256 >= 3 * (int64_t)cus;
+    if (large && fits32 && out32 && K >= 256 && K % 128 == 0)
         return launch_dma<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
                                                  qo, stream);
-    if (M * N >= (int64_t)256 * 256 * 256 && fits32 && K >= 256)
+    if (large && fits32 && K >= 256)
         return launch_big<FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias, C,
                                                  qo, stream);
+    // Small problems with fewer 128 x 128 tiles than CUs (few tokens, narrow
+    // outputs: e.g. 1024 x 2048 with K = 8192 has 128) take 64 x 128 tiles,
+    // twice as many, so that more CUs share the K loop.
+    if (((M + 127) / 128) * ((N + 127) / 128) < cus)
+        return launch_cfg<64, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa,
+                                                                sb, bias, C, qo, stream);
     return launch_cfg<128, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
                                                              bias, C, qo, stream);
 }

@@ -55,6 +55,38 @@ def test_fwd_shapes_formats(M, N, K, fa, fb):
     assert_gemm_close(bf16_values(bits16(y)), ref, f"fwd {M}x{N}x{K} {fa}{fb}")
 
 
+@pytest.mark.parametrize("M,N,K,cfg", [
+    (1024, 2048, 8192, "64x128"),      # 128 tiles of 128x128 < 256 CUs: 64x128 tiles
+    (1000, 2056, 1040, "64x128"),      # the same with ragged M, N and a K tail
+    (2048, 2048, 256, "128x128"),      # 256 tiles of 128x128: 128x128 tiles
+    (2000, 2056, 272, "128x128"),      # ragged, 272 tiles
+])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_small_product_tile_shapes(M, N, K, cfg, out):
+    """Products below 256^3 outputs run the small kernel: with fewer 128x128
+    tiles than CUs it takes 64x128 tiles.  Every output of both tile shapes
+    against the oracle, with bias (bf16) or without (fp32)."""
+    A = workloads.random_fp8_codes((M, K), M + 3, 0)
+    B = workloads.random_fp8_codes((N, K), N + 5, 1)
+    sa, sb = 1.0 / 29.0, 5.0 / 448.0
+    if out == "bf16":
+        bias = _bias(N, N + 1)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        dsl.fp8_linear_fwd(_f8(A, 0, sa), _f8(B, 1, sb), bias.to(DEV), y)
+        torch.cuda.synchronize()
+        ref = _ref(A, 0, B, 1, np.float32(sa), np.float32(sb), bias)
+        assert_gemm_close(bf16_values(bits16(y)), ref, f"fwd {M}x{N}x{K} {cfg}")
+    else:
+        # wgrad form: dw [N', K'] = a [N', M'] . b [K', M']^T through the transposes
+        dyt = dsl.Float8Tensor(None, A.to(DEV), torch.tensor([sa], device=DEV), 0, K, M)
+        xt = dsl.Float8Tensor(None, B.to(DEV), torch.tensor([sb], device=DEV), 1, K, N)
+        dw = torch.empty(M, N, dtype=torch.float32, device=DEV)
+        dsl.fp8_linear_wgrad(dyt, xt, dw)
+        torch.cuda.synchronize()
+        ref = _ref(A, 0, B, 1, np.float32(sa), np.float32(sb), None, oracle.OUT_FP32)
+        assert_gemm_close(f32(dw).astype(np.float64), ref, f"wgrad-form {M}x{N}x{K} {cfg}")
+
+
 def test_fwd_without_bias_and_k_zero():
     A = workloads.random_fp8_codes((64, 128), 1, 0)
     B = workloads.random_fp8_codes((32, 128), 2, 0)
@@ -235,6 +267,8 @@ def test_large_path_tails_sampled(M, N, K):
     (8192, 4096, 256, 1, 0, "fp32"),     # the same with fp32 output
     (8200, 4104, 256, 1, 1, "bf16"),     # two stages, ragged M and N, 2-3 tiles per workgroup
     (4104, 8200, 256, 0, 1, "fp32"),     # the same with fp32 output
+    (1024, 12288, 2048, 0, 0, "bf16"),   # under 256^3 outputs, 192 tiles: three quarters per CU
+    (1000, 12304, 1024, 1, 0, "fp32"),   # the same, ragged M and N
 ])
 def test_dma_path_rows_and_columns(M, N, K, fa, fb, out):
     """K % 128 == 0 at large M x N: whole output rows and columns at fragment

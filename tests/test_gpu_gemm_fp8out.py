@@ -98,7 +98,9 @@ SHAPES = [(128, 512, 256),       # the tiny forward layer
           (16, 16, 16),          # the torch._scaled_mm example's shape
           (300, 784, 2064),
           (1, 1024, 48),
-          (520, 144, 1024)]
+          (520, 144, 1024),
+          (1000, 2048, 1024),    # 128 tiles of 128x128, fewer than the CUs: 64x128 tiles
+          (2000, 2064, 272)]     # 272 tiles of 128x128: 128x128 tiles, ragged
 
 
 @pytest.mark.parametrize("idx", range(len(SHAPES)))
