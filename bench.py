@@ -671,15 +671,36 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3, tokens: i
     return out
 
 
-def _adamw(params):
-    """torch's fused AdamW where this build has it, else the foreach one."""
+def _adamw(params, capturable: bool = False):
+    """torch's fused AdamW where this build has it, else the foreach one;
+    `capturable` keeps its step counts on the device so that a HIP graph can
+    replay its step."""
     try:
         probe = torch.zeros(4, device="cuda", requires_grad=True)
         probe.grad = torch.ones(4, device="cuda")
-        torch.optim.AdamW([probe], lr=1e-3, fused=True).step()
-        return torch.optim.AdamW(params, lr=1e-3, fused=True)
+        torch.optim.AdamW([probe], lr=1e-3, fused=True, capturable=capturable).step()
+        return torch.optim.AdamW(params, lr=1e-3, fused=True, capturable=capturable)
     except (RuntimeError, ValueError):
-        return torch.optim.AdamW(params, lr=1e-3, foreach=True)
+        return torch.optim.AdamW(params, lr=1e-3, foreach=True, capturable=capturable)
+
+
+def capture_train_step(stack, x, target, opt, warmup: int = 2):
+    """The whole training step of `stack` (forward, loss gradient, backward,
+    scale update, optimizer step) captured in one HIP graph.  `opt` must be
+    capturable; `warmup` eager steps on a side stream first create its state
+    (and run every launch once outside capture).  Returns the graph; each
+    replay is one more training step on the same x and target."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            stack.train_step(x, target, opt)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack.train_step(x, target, opt)
+    return graph
 
 
 def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, iters: int = 50):
@@ -718,6 +739,14 @@ def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, ite
         opt_ms, _ = _time_loop(opt.step, 10, 2)
     res["fp8_step_ms"], res["fp8_step_wall_ms"] = round(fp8_ms, 2), round(fp8_wall, 2)
     res["adamw_alone_ms"] = round(opt_ms, 2)
+    # The same step as one HIP graph (capturable AdamW), as the page's
+    # --cuda_graph run does.
+    opt_g = _adamw(params, capturable=True)
+    with torch.no_grad():
+        graph = capture_train_step(stack, x, target, opt_g)
+        g_ms, g_wall = _time_loop(graph.replay, iters, warmup)
+    res["fp8_step_graph_ms"], res["fp8_step_graph_wall_ms"] = round(g_ms, 2), round(g_wall, 2)
+    del graph, opt_g
 
     ws32 = [list(zip(stack.w[b], stack.b32[b])) for b in range(blocks)]
     crit = torch.nn.MSELoss()

@@ -381,3 +381,64 @@ def test_full_32_block_forward_late_records_against_the_oracle(modulate):
     print(f"32-block forward ({modulate} modulation): {nonfinite} non-finite of "
           f"{out.numel()} outputs")
 
+
+
+def test_training_step_graph_replays_match_eager_steps():
+    """Two identical 2-block training stacks at full shape, each with a
+    capturable AdamW: A takes eager steps; B takes its first two steps as the
+    capture's warm-up and then replays its captured step.  After the third
+    and fourth steps (eager work and a synchronisation between the replays)
+    B's fp32 weights, weight and bias gradients and whole scale state equal
+    A's bit for bit."""
+    from bench import _adamw, capture_train_step
+
+    def make():
+        stack = ToyStack(dsl, workloads, 2, train=True, modulate="finite")
+        params = []
+        for b in range(2):
+            for l in range(6):
+                w = stack.w[b][l]
+                w.requires_grad_(True)
+                w.grad = stack.grad_w[b][l]
+                params.append(w)
+                if stack.b32[b][l] is not None:
+                    bb = stack.b32[b][l]
+                    bb.requires_grad_(True)
+                    bb.grad = stack.grad_b[b][l]
+                    params.append(bb)
+        return stack, _adamw(params, capturable=True)
+
+    x = _x(workloads.SEED_X)
+    target = workloads.uniform_bf16((M, H), workloads.SEED_X + 1).to(DEV)
+    a, opt_a = make()
+    b, opt_b = make()
+
+    def same(step):
+        torch.cuda.synchronize()
+        for blk in range(2):
+            for l in range(6):
+                assert torch.equal(a.w[blk][l].view(torch.int32), b.w[blk][l].view(torch.int32)), \
+                    (step, blk, l)
+                assert torch.equal(a.grad_w[blk][l].view(torch.int32),
+                                   b.grad_w[blk][l].view(torch.int32)), (step, blk, l)
+                if a.grad_b[blk][l] is not None:
+                    assert torch.equal(a.grad_b[blk][l].view(torch.int32),
+                                       b.grad_b[blk][l].view(torch.int32)), (step, blk, l)
+        for name in ("amax_history", "amax_cur", "scale", "scale_inv"):
+            assert torch.equal(getattr(a.state, name).view(torch.int32),
+                               getattr(b.state, name).view(torch.int32)), (step, name)
+
+    with torch.no_grad():
+        for _ in range(2):
+            a.train_step(x, target, opt_a)
+        graph = capture_train_step(b, x, target, opt_b, warmup=2)
+        same(2)
+        a.train_step(x, target, opt_a)
+        graph.replay()
+        same(3)
+        junk = torch.randn(4096, 4096, device=DEV) @ torch.randn(4096, 4096, device=DEV)
+        torch.cuda.synchronize()
+        del junk
+        a.train_step(x, target, opt_a)
+        graph.replay()
+        same(4)
