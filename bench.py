@@ -647,6 +647,7 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3, tokens: i
              "eager_cached_weights": (lambda: stack.forward(xin, fused=False), 1),
              "graph": (graph.replay, 0), "graph_cached_weights": (graph.replay, 1),
              "graph_fused_producers": (graph_fused.replay, 0),
+             "graph_fused_producers_cached_weights": (graph_fused.replay, 1),
              "bf16_torch_eager": (forward_bf16, 0)}
     res = {}
     for _ in range(2):

@@ -15,6 +15,15 @@
  *   fp8_linear_dgrad         dX = dY W            E5M2 x E4M3 -> bf16
  *   fp8_linear_wgrad         dW = dY^T X          E5M2 x E4M3 -> fp32 / bf16
  *
+ * and around it: the gradient cast with the bias gradient fused
+ * (fp8_cast_transpose_amax_dbias, also as a no-allocation entry point), the
+ * toy block's elementwise producers fused into the cast and the modulation's
+ * gradient (fp8_produce_cast_transpose_amax, fp8_produce_modulate_backward),
+ * dynamic scaling as the comparator (fp8_cast_transpose_dynamic), the
+ * forward with FP8 output and output amax (fp8_linear_fwd_fp8out), the cast
+ * with cached source loads, and a device copy that serves as the bandwidth
+ * yardstick (fp8_reference_copy).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every pointer to tensor data is a DEVICE pointer (memory the caller got
@@ -28,7 +37,8 @@
  *  - The caller owns every buffer.  The library keeps no state between calls
  *    beyond per-device caches of immutable device facts (compute-unit count,
  *    kernel attributes set once), filled on first use and safe to fill from
- *    several threads at once.
+ *    several threads at once, and the per-device scratch array of
+ *    fp8_cast_transpose_amax_dbias_noalloc (described there).
  *  - Return value: FP8_OK (0) or a negative fp8_status_t.  On an argument
  *    error nothing has been enqueued.  The kernels are built for gfx950 only:
  *    on any other device the runtime rejects the launch and the call returns
