@@ -673,7 +673,7 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3, tokens: i
 
 
 def _adamw(params, capturable: bool = False):
-    """torch's fused AdamW where this build has it, else the foreach one;
+    """torch's fused AdamW where the installed torch has it, else the foreach one;
     `capturable` keeps its step counts on the device so that a HIP graph can
     replay its step."""
     try:
