@@ -549,12 +549,16 @@ class ToyStack:
         H = self.H
         for b in reversed(range(self.blocks)):
             du = self._linear_bwd(b, L_DOWN, g)
-            g = g + self._linear_bwd(b, L_UP, du)
-            self.dy[L_CROSS_KV][:, :H].copy_(g)
+            # The residual sums go straight into the first H columns of the
+            # zero-padded output gradients of the two projections that read
+            # only those columns (no copies); each bf16 add rounds as before.
+            g2 = self.dy[L_CROSS_KV][:, :H]
+            torch.add(g, self._linear_bwd(b, L_UP, du), out=g2)
             dk = self._linear_bwd(b, L_CROSS_KV, self.dy[L_CROSS_KV])
-            g = g + self._linear_bwd(b, L_CROSS_Q, g) + dk
-            self.dy[L_SELF][:, :H].copy_(g)
-            g = g + self._linear_bwd(b, L_SELF, self.dy[L_SELF])
+            g3 = self.dy[L_SELF][:, :H]
+            torch.add(g2, self._linear_bwd(b, L_CROSS_Q, g2), out=g3)
+            g3.add_(dk)
+            g = g3 + self._linear_bwd(b, L_SELF, self.dy[L_SELF])
             # modulation h1 = gain * h0 / div: one library pass writes the
             # gradients of gain and div into the modulation linear's output
             # gradient and that of h0 into g_h0 (zero where the finite
