@@ -217,6 +217,58 @@ def dbias_cast_cost(dsl, st, iters: int = 20):
     return {k: round(v, 2) for k, v in res.items()}
 
 
+def split_product_cost(dsl, workloads, iters: int = 20):
+    """Products whose output leaves CUs idle over a long contraction, plain
+    and through a workspace (split over K): the weight gradients of the toy
+    block's 2048 -> 2048 and 2048 -> 4096 linears over 8192 tokens (fp32),
+    the 1024-token forward of its 8192 -> 2048 linear (bf16, bias), and a
+    2048 x 2048 weight gradient over 16384 tokens.  Random E4M3 / E5M2
+    operand codes; interleaved rounds, best of each."""
+    one = torch.ones(1, device="cuda")
+    res = {}
+    for name, (M_, N_, K_, out) in {
+            "wgrad_2048x2048_k8192": (2048, 2048, 8192, "fp32"),
+            "wgrad_4096x2048_k8192": (4096, 2048, 8192, "fp32"),
+            "fwd_1024x2048_k8192": (1024, 2048, 8192, "bf16"),
+            "wgrad_2048x2048_k16384": (2048, 2048, 16384, "fp32")}.items():
+        a = workloads.random_fp8_codes((M_, K_), 31, 1).to("cuda")
+        b = workloads.random_fp8_codes((N_, K_), 32, 0).to("cuda")
+        need = dsl.fp8_gemm_workspace_bytes(M_, N_, K_)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        if out == "fp32":       # dW [M_, N_] = dY_t [M_, K_] . X_t [N_, K_]^T
+            dyt = dsl.Float8Tensor(None, a, one, 1, K_, M_)
+            xt = dsl.Float8Tensor(None, b, one, 0, K_, N_)
+            dw = torch.empty(M_, N_, dtype=torch.float32, device="cuda")
+            plain = lambda: dsl.fp8_linear_wgrad(dyt, xt, dw)
+            split = lambda: dsl.fp8_linear_wgrad(dyt, xt, dw, workspace=ws)
+        else:
+            x8 = dsl.Float8Tensor(a, None, one, 1, M_, K_)
+            w8 = dsl.Float8Tensor(b, None, one, 0, N_, K_)
+            bias = torch.zeros(N_, dtype=torch.bfloat16, device="cuda")
+            y = torch.empty(M_, N_, dtype=torch.bfloat16, device="cuda")
+            plain = lambda: dsl.fp8_linear_fwd(x8, w8, bias, y)
+            split = lambda: dsl.fp8_linear_fwd(x8, w8, bias, y, workspace=ws)
+        r = {"parts": need // (M_ * N_ * 4) if need else 1}
+        for _ in range(2):
+            for key, fn in (("plain_us", plain), ("split_us", split)):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(iters):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / iters * 1e3
+                r[key] = round(min(r.get(key, us), us), 2)
+        r["split_tflops"] = round(2 * M_ * N_ * K_ / (r["split_us"] * 1e-6) / 1e12, 1)
+        res[name] = r
+        del a, b, ws
+    return res
+
+
 def dynamic_vs_delayed(dsl, st, iters: int = 20):
     """Delayed scaling (one cast pass: codes + transpose + amax with the scale
     from earlier amaxes) against dynamic scaling (amax pass, scale, then the
@@ -428,6 +480,14 @@ class ToyStack:
         self.mod_out = per_block(lambda: bf(6 * H)) if train else [self.out[L_MOD]] * blocks
         self.h_in = per_block(lambda: bf(H)) if train else None       # block inputs
         self.hbuf = [bf(H) for _ in range(4)]
+        # One workspace for the products that alone would leave CUs idle
+        # (split over K); the stack's calls are ordered on one stream.
+        shapes = [(M, fout, fin) for fin, fout, _ in self.lin]
+        if train:
+            shapes += [(M, fin, fout) for fin, fout, _ in self.lin]     # dgrad
+            shapes += [(fout, fin, M) for fin, fout, _ in self.lin]     # wgrad
+        gbytes = max(dsl.fp8_gemm_workspace_bytes(*s) for s in shapes)
+        self.gemm_ws = torch.empty(gbytes, dtype=torch.uint8, device=dev) if gbytes else None
         if train:
             self.grad_w = [[torch.zeros_like(w) for w in ws] for ws in self.w]
             self.grad_b = [[None if b is None else torch.zeros_like(b) for b in bs]
@@ -469,7 +529,7 @@ class ToyStack:
         self.dsl.fp8_cast_transpose_amax(self.w[b][l], self._sl(st.scale, r), qw,
                                          self._sl(st.amax_cur, r), noop_flag=self.flag)
         y = self.out[l] if out is None else out
-        self.dsl.fp8_linear_fwd(self.qx[l][b], qw, self.b16[b][l], y)
+        self.dsl.fp8_linear_fwd(self.qx[l][b], qw, self.b16[b][l], y, workspace=self.gemm_ws)
         if self.probe is not None:
             self.probe(b, l, y)
         return y
@@ -537,8 +597,9 @@ class ToyStack:
         else:
             dsl.fp8_cast_transpose_amax(dy, self._sl(st.scale, r), self.qdy[l],
                                         self._sl(st.amax_cur, r))
-        dsl.fp8_linear_dgrad(self.qdy[l], self.qw[b][l], self.dx[l])
-        dsl.fp8_linear_wgrad(self.qdy[l], self.qx[l][b], self.grad_w[b][l])
+        dsl.fp8_linear_dgrad(self.qdy[l], self.qw[b][l], self.dx[l], workspace=self.gemm_ws)
+        dsl.fp8_linear_wgrad(self.qdy[l], self.qx[l][b], self.grad_w[b][l],
+                             workspace=self.gemm_ws)
         if self.probe_bwd is not None:
             self.probe_bwd(b, l, dy)
         return self.dx[l]
@@ -999,6 +1060,7 @@ def main():
     progress("roofline loops done")
     update_cost = scale_update_cost(dsl)
     dbias_cost = dbias_cast_cost(dsl, st)
+    split_cost = split_product_cost(dsl, workloads)
     producer_cost = producer_cast_cost(dsl, workloads)
     dyn_cost = dynamic_vs_delayed(dsl, st)
     fp8out_cost = fp8_output_forward(dsl, st)
@@ -1054,6 +1116,7 @@ def main():
     }
     result["scale_update_one_launch"] = update_cost
     result["dy_cast_dbias"] = dbias_cost
+    result["split_products"] = split_cost
     result["producer_fused_cast"] = producer_cost
     result["delayed_vs_dynamic_cast"] = dyn_cost
     result["fp8_output_forward"] = fp8out_cost

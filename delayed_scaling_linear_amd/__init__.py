@@ -39,7 +39,7 @@ __all__ = [
     "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
     "fp8_cast_transpose_amax_dbias_noalloc", "NOALLOC_SCRATCH_BYTES",
     "fp8_cast_transpose_amax_cached", "fp8_reference_copy", "fp8_produce_modulate_backward",
-    "library_path", "lib",
+    "fp8_gemm_workspace_bytes", "library_path", "lib",
 ]
 
 E4M3 = 0
@@ -108,12 +108,18 @@ def lib() -> ctypes.CDLL:
         L.fp8_linear_fwd_fp8out.argtypes = [dp, dp, vp, vp, dp, vp, vp]
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
+        L.fp8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp8_gemm_workspace_bytes.restype = i64
+        L.fp8_linear_fwd_ws.argtypes = [dp, dp, vp, vp, vp, i64, vp]
+        L.fp8_linear_dgrad_ws.argtypes = [dp, dp, vp, vp, i64, vp]
+        L.fp8_linear_wgrad_ws.argtypes = [dp, dp, vp, i32, vp, i64, vp]
         for f in (L.fp8_scale_update, L.fp8_cast_transpose_amax, L.fp8_cast_transpose_amax_dbias,
                   L.fp8_cast_transpose_amax_dbias_noalloc, L.fp8_cast_transpose_amax_cached,
                   L.fp8_reference_copy,
                   L.fp8_produce_cast_transpose_amax, L.fp8_cast_transpose_dynamic,
                   L.fp8_linear_fwd, L.fp8_linear_fwd_fp8out, L.fp8_linear_dgrad,
-                  L.fp8_linear_wgrad):
+                  L.fp8_linear_wgrad, L.fp8_linear_fwd_ws, L.fp8_linear_dgrad_ws,
+                  L.fp8_linear_wgrad_ws):
             f.restype = ctypes.c_int
         L.fp8_status_string.argtypes = [ctypes.c_int]
         L.fp8_status_string.restype = ctypes.c_char_p
@@ -474,15 +480,40 @@ def fp8_cast_transpose_dynamic(x: torch.Tensor, scale: torch.Tensor, out: Float8
         _ptr(noop_flag, torch.int32, "noop_flag"), _stream(stream)), "fp8_cast_transpose_dynamic")
 
 
+def fp8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes of the split form of a product with output [M, N] and
+    contraction K on the current device (0: it runs unsplit); the
+    `workspace` of fp8_linear_fwd / dgrad / wgrad."""
+    n = lib().fp8_gemm_workspace_bytes(M, N, K)
+    if n < 0:
+        raise Fp8Error(n, "fp8_gemm_workspace_bytes")
+    return n
+
+
+def _ws(workspace: Optional[torch.Tensor]):
+    """(pointer, bytes) of an optional uint8 device workspace."""
+    if workspace is None:
+        return None, 0
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    return _ptr(workspace, torch.uint8, "workspace"), workspace.numel()
+
+
 def fp8_linear_fwd(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],
-                   y: torch.Tensor, stream=None) -> None:
-    """y [M, N] bf16 = x.data [M, K] . w.data [N, K]^T * sinv + bias."""
+                   y: torch.Tensor, stream=None, workspace: Optional[torch.Tensor] = None) -> None:
+    """y [M, N] bf16 = x.data [M, K] . w.data [N, K]^T * sinv + bias.  With a
+    `workspace` (uint8 device tensor), fp8_linear_fwd_ws: the product split
+    over K where it alone would leave compute units idle."""
     _need_shape(y, (x.rows, w.rows), "y")
     _need_shape(bias, (w.rows,), "bias")
     dx, dw = x.desc(), w.desc()
-    _check(lib().fp8_linear_fwd(ctypes.byref(dx), ctypes.byref(dw),
-                                _ptr(bias, torch.bfloat16, "bias"), _ptr(y, torch.bfloat16, "y"),
-                                _stream(stream)), "fp8_linear_fwd")
+    args = (ctypes.byref(dx), ctypes.byref(dw), _ptr(bias, torch.bfloat16, "bias"),
+            _ptr(y, torch.bfloat16, "y"))
+    if workspace is None:
+        _check(lib().fp8_linear_fwd(*args, _stream(stream)), "fp8_linear_fwd")
+    else:
+        _check(lib().fp8_linear_fwd_ws(*args, *_ws(workspace), _stream(stream)),
+               "fp8_linear_fwd_ws")
 
 
 def fp8_linear_fwd_fp8out(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch.Tensor],
@@ -502,17 +533,24 @@ def fp8_linear_fwd_fp8out(x: Float8Tensor, w: Float8Tensor, bias: Optional[torch
            "fp8_linear_fwd_fp8out")
 
 
-def fp8_linear_dgrad(dy: Float8Tensor, w: Float8Tensor, dx: torch.Tensor, stream=None) -> None:
-    """dx [M, K] bf16 = dy.data [M, N] . w.data_t [K, N]^T * sinv."""
+def fp8_linear_dgrad(dy: Float8Tensor, w: Float8Tensor, dx: torch.Tensor, stream=None,
+                     workspace: Optional[torch.Tensor] = None) -> None:
+    """dx [M, K] bf16 = dy.data [M, N] . w.data_t [K, N]^T * sinv (with a
+    `workspace`: fp8_linear_dgrad_ws)."""
     _need_shape(dx, (dy.rows, w.cols), "dx")
     d1, d2 = dy.desc(), w.desc()
-    _check(lib().fp8_linear_dgrad(ctypes.byref(d1), ctypes.byref(d2),
-                                  _ptr(dx, torch.bfloat16, "dx"), _stream(stream)),
-           "fp8_linear_dgrad")
+    args = (ctypes.byref(d1), ctypes.byref(d2), _ptr(dx, torch.bfloat16, "dx"))
+    if workspace is None:
+        _check(lib().fp8_linear_dgrad(*args, _stream(stream)), "fp8_linear_dgrad")
+    else:
+        _check(lib().fp8_linear_dgrad_ws(*args, *_ws(workspace), _stream(stream)),
+               "fp8_linear_dgrad_ws")
 
 
-def fp8_linear_wgrad(dy: Float8Tensor, x: Float8Tensor, dw: torch.Tensor, stream=None) -> None:
-    """dw [N, K] (fp32 or bf16) = dy.data_t [N, M] . x.data_t [K, M]^T * sinv."""
+def fp8_linear_wgrad(dy: Float8Tensor, x: Float8Tensor, dw: torch.Tensor, stream=None,
+                     workspace: Optional[torch.Tensor] = None) -> None:
+    """dw [N, K] (fp32 or bf16) = dy.data_t [N, M] . x.data_t [K, M]^T * sinv
+    (with a `workspace`: fp8_linear_wgrad_ws)."""
     if dw.dtype == torch.float32:
         od = DTYPE_FP32
     elif dw.dtype == torch.bfloat16:
@@ -521,5 +559,9 @@ def fp8_linear_wgrad(dy: Float8Tensor, x: Float8Tensor, dw: torch.Tensor, stream
         raise TypeError("dw must be fp32 or bf16")
     _need_shape(dw, (dy.cols, x.cols), "dw")
     d1, d2 = dy.desc(), x.desc()
-    _check(lib().fp8_linear_wgrad(ctypes.byref(d1), ctypes.byref(d2), _ptr(dw, None, "dw"), od,
-                                  _stream(stream)), "fp8_linear_wgrad")
+    args = (ctypes.byref(d1), ctypes.byref(d2), _ptr(dw, None, "dw"), od)
+    if workspace is None:
+        _check(lib().fp8_linear_wgrad(*args, _stream(stream)), "fp8_linear_wgrad")
+    else:
+        _check(lib().fp8_linear_wgrad_ws(*args, *_ws(workspace), _stream(stream)),
+               "fp8_linear_wgrad_ws")

@@ -325,8 +325,25 @@ int fp8_cast_transpose_dynamic(const void *x, int32_t src, int64_t rows, int64_t
                                                 noop_flag, nullptr, 0, s));
 }
 
-int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
-                   uint16_t *y, fp8_stream_t stream) {
+// The split-product workspace of the *_ws entry points: a NULL workspace (any
+// size) is no workspace; a non-NULL one must be 16-byte aligned, with a
+// non-negative size.
+static int check_gemm_ws(const void *ws, int64_t ws_bytes) {
+    if (ws == nullptr) return FP8_OK;
+    if (ws_bytes < 0) return FP8_ERR_ARG;
+    return aligned16(ws) ? FP8_OK : FP8_ERR_ALIGN;
+}
+
+int64_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+    int cus = 0;
+    if (hipError_t e = current_cu_count(&cus)) return status_of(e);
+    const int parts = gemm_split_parts(M, N, K, cus, INT64_MAX);
+    return parts > 1 ? (int64_t)parts * M * N * (int64_t)sizeof(float) : 0;
+}
+
+static int linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                      uint16_t *y, void *ws, int64_t ws_bytes, fp8_stream_t stream) {
     if (!x || !w) return FP8_ERR_NULL;
     if (!valid_fmt(x->fmt) || !valid_fmt(w->fmt)) return FP8_ERR_FORMAT;
     const int64_t M = x->rows, K = x->cols, N = w->rows;
@@ -334,9 +351,21 @@ int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t 
     if (int e = check_gemm(x->data, w->data, M, N, K, x->scale_inv, w->scale_inv, y, 8)) return e;
     if (M == 0 || N == 0) return FP8_OK;
     if (bias && !aligned16(bias)) return FP8_ERR_ALIGN;
+    if (int e = check_gemm_ws(ws, ws_bytes)) return e;
     return status_of(launch_gemm_nt(x->data, x->fmt, w->data, w->fmt, M, N, K, x->scale_inv,
                                     w->scale_inv, bias, FP8_DTYPE_BF16, y,
-                                    static_cast<hipStream_t>(stream)));
+                                    static_cast<hipStream_t>(stream), ws, ws_bytes));
+}
+
+int fp8_linear_fwd(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                   uint16_t *y, fp8_stream_t stream) {
+    return linear_fwd(x, w, bias, y, nullptr, 0, stream);
+}
+
+int fp8_linear_fwd_ws(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                      uint16_t *y, void *workspace, int64_t workspace_bytes,
+                      fp8_stream_t stream) {
+    return linear_fwd(x, w, bias, y, workspace, workspace_bytes, stream);
 }
 
 int fp8_linear_fwd_fp8out(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
@@ -361,8 +390,8 @@ int fp8_linear_fwd_fp8out(const fp8_tensor_t *x, const fp8_tensor_t *w, const ui
                                            y->data, amax_y, y->scale_inv, s));
 }
 
-int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
-                     fp8_stream_t stream) {
+static int linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx, void *ws,
+                        int64_t ws_bytes, fp8_stream_t stream) {
     if (!dy || !w) return FP8_ERR_NULL;
     if (!valid_fmt(dy->fmt) || !valid_fmt(w->fmt)) return FP8_ERR_FORMAT;
     // dx [M, K] = dy [M, N] . (w_t [K, N])^T
@@ -371,13 +400,24 @@ int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx
     if (int e = check_gemm(dy->data, w->data_t, M, K, N, dy->scale_inv, w->scale_inv, dx, 8))
         return e;
     if (M == 0 || K == 0) return FP8_OK;
+    if (int e = check_gemm_ws(ws, ws_bytes)) return e;
     return status_of(launch_gemm_nt(dy->data, dy->fmt, w->data_t, w->fmt, M, K, N, dy->scale_inv,
                                     w->scale_inv, nullptr, FP8_DTYPE_BF16, dx,
-                                    static_cast<hipStream_t>(stream)));
+                                    static_cast<hipStream_t>(stream), ws, ws_bytes));
 }
 
-int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, int32_t out_dtype,
+int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
                      fp8_stream_t stream) {
+    return linear_dgrad(dy, w, dx, nullptr, 0, stream);
+}
+
+int fp8_linear_dgrad_ws(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
+                        void *workspace, int64_t workspace_bytes, fp8_stream_t stream) {
+    return linear_dgrad(dy, w, dx, workspace, workspace_bytes, stream);
+}
+
+static int linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw,
+                        int32_t out_dtype, void *ws, int64_t ws_bytes, fp8_stream_t stream) {
     if (!dy || !x) return FP8_ERR_NULL;
     if (!valid_fmt(dy->fmt) || !valid_fmt(x->fmt)) return FP8_ERR_FORMAT;
     if (out_dtype != FP8_DTYPE_BF16 && out_dtype != FP8_DTYPE_FP32) return FP8_ERR_ARG;
@@ -388,9 +428,21 @@ int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, in
                            out_dtype == FP8_DTYPE_BF16 ? 8 : 4))
         return e;
     if (N == 0 || K == 0) return FP8_OK;
+    if (int e = check_gemm_ws(ws, ws_bytes)) return e;
     return status_of(launch_gemm_nt(dy->data_t, dy->fmt, x->data_t, x->fmt, N, K, M,
                                     dy->scale_inv, x->scale_inv, nullptr, out_dtype, dw,
-                                    static_cast<hipStream_t>(stream)));
+                                    static_cast<hipStream_t>(stream), ws, ws_bytes));
+}
+
+int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, int32_t out_dtype,
+                     fp8_stream_t stream) {
+    return linear_wgrad(dy, x, dw, out_dtype, nullptr, 0, stream);
+}
+
+int fp8_linear_wgrad_ws(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw,
+                        int32_t out_dtype, void *workspace, int64_t workspace_bytes,
+                        fp8_stream_t stream) {
+    return linear_wgrad(dy, x, dw, out_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

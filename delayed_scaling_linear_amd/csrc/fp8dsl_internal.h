@@ -22,6 +22,32 @@ hipError_t current_cu_count(int *cu_count);
 // is one bit per device owned by the calling launcher.
 hipError_t enable_dynamic_lds(const void *kernel, int lds_bytes, std::atomic<uint64_t> &done);
 
+// K parts for the split form of the product C [M, N] (contraction K) on a
+// device with `cus` compute units and `ws_bytes` of workspace: 1 (no split)
+// for products with at least three quarters of a 256 x 256 tile per CU, or a
+// K that is not a multiple of 128; else the largest P with every unit on the
+// chip at once (tiles * P <= cus), K a multiple of 128 P, at least
+// SPLIT_MIN_K contraction bytes per part, and the parts' P * M * N fp32 sums
+// within ws_bytes.  The parts' sums go out to memory and are read back
+// (8 P M N bytes, at about the HBM rate), which a part repays only with a
+// long contraction: on MI355X 2048 bytes per part splits 2048 x 2048 x 8192
+// four ways (60.7 -> 51.8 us) and 4096 x 2048 x 8192 two ways (95.5 -> 74.3
+// us), while 1024-token products with K = 2048 ran 1.3-2.6x slower split
+// 2-8 ways than on the small kernel.
+constexpr int64_t SPLIT_MIN_K = 2048;
+inline int gemm_split_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_bytes) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (M <= 0 || N <= 0 || tiles == 0) return 1;
+    if (M * N >= (int64_t)256 * 256 * 256 || 4 * tiles >= 3 * (int64_t)cus) return 1;
+    if (K % 128 != 0) return 1;
+    int best = 1;
+    for (int p = 2; p <= 16; ++p) {
+        if (K / p < SPLIT_MIN_K || tiles * p > cus || (int64_t)p * M * N * 4 > ws_bytes) break;
+        if (K % (128 * p) == 0) best = p;
+    }
+    return best;
+}
+
 // Launchers: each validates nothing (the C-ABI layer has done that), enqueues
 // one kernel on `stream` and returns the launch status.
 hipError_t launch_scale_update(float *hist, float *amax_cur, float *scale, float *scale_inv,
@@ -74,9 +100,12 @@ hipError_t launch_scale_inv_only(const float *scale, float *scale_inv_out, const
 // C[i, j] = out( sum_k dec(A[i, k]) dec(B[j, k]) * (*sinv_a) * (*sinv_b) + bias[j] )
 // A [M, K], B [N, K] row-major FP8; C [M, N] row-major, bf16 (out_dtype 0) or
 // fp32 (1).  bias is bf16 [N] or nullptr.
+// ws (may be nullptr): the split form's workspace of ws_bytes bytes (16-byte
+// aligned), used when gemm_split_parts(M, N, K, CUs, ws_bytes) > 1.
 hipError_t launch_gemm_nt(const uint8_t *A, int fa, const uint8_t *B, int fb, int64_t M,
                           int64_t N, int64_t K, const float *sinv_a, const float *sinv_b,
-                          const uint16_t *bias, int out_dtype, void *C, hipStream_t stream);
+                          const uint16_t *bias, int out_dtype, void *C, hipStream_t stream,
+                          void *ws = nullptr, int64_t ws_bytes = 0);
 
 // The same product with an FP8 output (format fo): C [M, N] codes = the cast
 // of v = acc * (*sinv_a) * (*sinv_b) + bias[j] (fp32) with *scale_out;

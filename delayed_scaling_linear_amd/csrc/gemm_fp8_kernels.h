@@ -801,7 +801,7 @@ __device__ __forceinline__ void load_hb_bias(const uint8_t *bl, int lane, float 
 // over the wave's 128 output rows.  Columns past N take OUT_OOB (N is a
 // multiple of 8 for bf16 and of 4 for fp32, so a lane's columns are all in
 // or all out).
-template <int OUT, bool HAS_BIAS>
+template <int OUT, bool HAS_BIAS, int POL>
 __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16],
                                        __amdgpu_buffer_rsrc_t rs, int N, int c0, int lane, float s,
                                        int h, int n0, int n1) {
@@ -826,7 +826,7 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
             // the whole offset in the vector operand: the range check that
             // drops rows past M and columns past N does not see the scalar one
             __builtin_amdgcn_raw_buffer_store_b128(o, rs, (int)(voff + (uint32_t)(8 * it * N) * 2u),
-                                                   0, OUT_POLICY);
+                                                   0, POL);
         }
     } else {
         const int gc = c0 + 64 * p + 4 * (lane & 15);
@@ -838,7 +838,7 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
             const v4f y = {__uint_as_float(x.x) * s + b[4 * p + 0], __uint_as_float(x.y) * s + b[4 * p + 1],
                            __uint_as_float(x.z) * s + b[4 * p + 2], __uint_as_float(x.w) * s + b[4 * p + 3]};
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs,
-                                                   (int)(voff + (uint32_t)(4 * it * N) * 4u), 0, OUT_POLICY);
+                                                   (int)(voff + (uint32_t)(4 * it * N) * 4u), 0, POL);
         }
     }
 }
@@ -1030,11 +1030,13 @@ __device__ __forceinline__ int fresh_lane_id() {
 //     they are used, from a lane index the compiler cannot hoist: kept live
 //     across the loop they spill, and a spill reload waits for every load
 //     in flight.
-template <int FA, int FB, int OUT, bool HAS_BIAS>
+template <int FA, int FB, int OUT, bool HAS_BIAS, bool PART>
 __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
     const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
-    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n, QOut qo) {
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n, QOut qo,
+    int parts) {
+    static_assert(!PART || (OUT == FP8_DTYPE_FP32 && !HAS_BIAS), "parts are raw fp32 sums");
     constexpr int BM = 256, BN = 256;
     constexpr int KS = 128;                     // K bytes per stage
     constexpr int WT = 128;                     // wave tile (square)
@@ -1043,7 +1045,10 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int T = tiles_m * tiles_n;
-    if ((int)blockIdx.x >= T) return;
+    // Work units: unit r is tile r % T over K part r / T (PART), else tile r.
+    const int NU = PART ? T * parts : T;
+    if ((int)blockIdx.x >= NU) return;
+    const int KP = PART ? K / parts : K;        // K bytes of one unit
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1179,8 +1184,11 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         }
     };
 
-    const int nk = K / KS;                      // >= 2 (caller guarantees)
-    const float s = (*sinv_a) * (*sinv_b);
+    const int nk = KP / KS;                     // >= 2 (caller guarantees)
+    // A part is the raw sum: the reduction applies the scales and the bias.
+    const float s = PART ? 1.0f : (*sinv_a) * (*sinv_b);
+    // Parts are read back at once by the reduction: cached stores.
+    constexpr int OPOL = PART ? 0 : OUT_POLICY;
     // bf16 / fp32 output: a tile's last stage, with the epilogue's first
     // half-blocks (see stage_hb) staged, read back and stored between the
     // MFMAs of its second half.  The wave's staging quarter `stg` (regions
@@ -1200,7 +1208,7 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         first_half(buf, std::false_type{});   // stage nk-1 >= 1 is never a tile's first
         __syncthreads();
         auto quarter = [&](const u32x4 (&v)[8], int h, int qn) {
-            out_hb<OUT, HAS_BIAS>(v, bb, ors, N, cc0, el, s, h, qn * U, qn * U + U);
+            out_hb<OUT, HAS_BIAS, OPOL>(v, bb, ors, N, cc0, el, s, h, qn * U, qn * U + U);
         };
 #pragma unroll
         for (int sl = 0; sl < 16; ++sl) {
@@ -1228,11 +1236,16 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         so_fold = scale_is_foldable(so);
     }
     uint32_t wkey = 0;                          // FP8 output: the wave's amax key
-    // Operand byte offset of this wave's 128 rows of tile r.
+    // Operand byte offset of this wave's 128 rows of unit r's tile, at the
+    // start of its K part.  (T % 8 == 0 keeps tile r % T on unit r's XCD.)
+    auto unit_tile = [&](int r, int &tm, int &tn) {
+        tile_of_block(PART ? r % T : r, tiles_m, tiles_n, tm, tn);
+    };
     auto tile_base = [&](int r) {
         int tm, tn;
-        tile_of_block(r, tiles_m, tiles_n, tm, tn);
-        return (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+        unit_tile(r, tm, tn);
+        const uint32_t k0 = PART ? (uint32_t)((r / T) * KP) : 0u;
+        return (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K) + k0;
     };
     // Tile r's bias into bias slot `slot` (wave 0).
     auto load_bias = [&](int r, int slot) {
@@ -1279,14 +1292,15 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
     uint32_t buf = 0;
     int slot = 0;
     bool pend = false;                          // the previous tile's stores are in flight
-    for (int r = (int)blockIdx.x; r < T; r += (int)gridDim.x) {
+    for (int r = (int)blockIdx.x; r < NU; r += (int)gridDim.x) {
         int tm, tn;
         set_voff();
-        tile_of_block(r, tiles_m, tiles_n, tm, tn);
+        unit_tile(r, tm, tn);
         const uint32_t base =
-            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K);
+            (uint32_t)(((loads_b ? tn * BN : tm * BM) + (wave & 1) * 128) * K) +
+            (PART ? (uint32_t)((r / T) * KP) : 0u);
         const int rn = r + (int)gridDim.x;
-        const bool more = rn < T;
+        const bool more = rn < NU;
         const uint32_t nbase = more ? tile_base(rn) : 0u;
         for (int k = 0; k + 2 < nk; ++k) {
             stage(buf, true, true, base, (uint32_t)((k + 2) * KS), (k == 0 && pend) ? 1 : 0, k == 0);
@@ -1305,7 +1319,11 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
         const int r0 = tm * BM + wm * WT, cc0 = tn * BN + wn * WT;
         if constexpr (!is_q_out<OUT>()) {
             constexpr int EB = OUT == FP8_DTYPE_BF16 ? 2 : 4;
-            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<EB>(Cv, M, N, r0);
+            // A part goes to its own [M, N] fp32 slice of the workspace.
+            void *const Cu = PART ? static_cast<void *>(static_cast<float *>(Cv) +
+                                                        (int64_t)(r / T) * M * N)
+                                  : Cv;
+            const __amdgpu_buffer_rsrc_t ors = out_rows_rsrc<EB>(Cu, M, N, r0);
             float bb[16];
             load_hb_bias<OUT, HAS_BIAS>(bl, el, bb);
             u32x4 va[8], vb[8];
@@ -1316,24 +1334,24 @@ __global__ __launch_bounds__(256) void gemm_nt_dma_kernel(
             // half-block's arithmetic so that its latency is covered.
             read_hb<OUT>(reg1, el, vb);                        // 3
             stage_hb(acc, reg1, el, 5);
-            out_hb<OUT, HAS_BIAS>(va, bb, ors, N, cc0, el, s, 2, U, 4 * U);
+            out_hb<OUT, HAS_BIAS, OPOL>(va, bb, ors, N, cc0, el, s, 2, U, 4 * U);
             read_hb<OUT>(stg, el, va);                         // 4
             stage_hb(acc, stg, el, 6);
-            out_hb<OUT, HAS_BIAS>(vb, bb, ors, N, cc0, el, s, 3, 0, 4 * U);
+            out_hb<OUT, HAS_BIAS, OPOL>(vb, bb, ors, N, cc0, el, s, 3, 0, 4 * U);
             read_hb<OUT>(reg1, el, vb);                        // 5
             stage_hb(acc, reg1, el, 7);
-            out_hb<OUT, HAS_BIAS>(va, bb, ors, N, cc0, el, s, 4, 0, 4 * U);
+            out_hb<OUT, HAS_BIAS, OPOL>(va, bb, ors, N, cc0, el, s, 4, 0, 4 * U);
             read_hb<OUT>(stg, el, va);                         // 6
-            out_hb<OUT, HAS_BIAS>(vb, bb, ors, N, cc0, el, s, 5, 0, 4 * U);
+            out_hb<OUT, HAS_BIAS, OPOL>(vb, bb, ors, N, cc0, el, s, 5, 0, 4 * U);
             read_hb<OUT>(reg1, el, vb);                        // 7
-            out_hb<OUT, HAS_BIAS>(va, bb, ors, N, cc0, el, s, 6, 0, 4 * U);
+            out_hb<OUT, HAS_BIAS, OPOL>(va, bb, ors, N, cc0, el, s, 6, 0, 4 * U);
             // The staging quarter is the one this wave's own stage loads
             // fill and no other wave reads it: once this wave's staging
             // reads have returned, the next tile's stage 1 is requested into
             // it (no barrier), and the last half-block's NST stores follow.
             wait_lds_reads();
             if (more) issue_stage(nbase, KS, sbuf);
-            out_hb<OUT, HAS_BIAS>(vb, bb, ors, N, cc0, el, s, 7, 0, 4 * U);
+            out_hb<OUT, HAS_BIAS, OPOL>(vb, bb, ors, N, cc0, el, s, 7, 0, 4 * U);
         } else {
             stage(buf, false, false, 0, 0, 2, false);   // stage nk-1: its buffer is free after the barrier
             buf ^= STAGE;                           // the next tile's stage 0
@@ -1385,11 +1403,14 @@ hipError_t launch_big(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
     return hipGetLastError();
 }
 
-template <int FA, int FB, int OUT, bool HAS_BIAS>
+// PART: `parts` K parts per tile, raw fp32 sums into C = the [parts, M, N]
+// workspace (then splitk_reduce_kernel); one unit per workgroup when
+// tiles * parts <= CUs.
+template <int FA, int FB, int OUT, bool HAS_BIAS, bool PART = false>
 hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
                       const float *sb, const uint16_t *bias, void *C, const QOut &qo,
-                      hipStream_t stream) {
-    auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS>;
+                      hipStream_t stream, int parts = 1) {
+    auto kern = gemm_nt_dma_kernel<FA, FB, OUT, HAS_BIAS, PART>;
     constexpr int lds_bytes = 2 * (256 + 256) * 128 + 2048;   // two 64 KiB stages, 2 bias slots
     static std::atomic<uint64_t> lds_enabled{0};
     if (hipError_t e = enable_dynamic_lds(reinterpret_cast<const void *>(kern), lds_bytes,
@@ -1399,9 +1420,67 @@ hipError_t launch_dma(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
     if (hipError_t e = current_cu_count(&cus)) return e;
     const int tiles_m = (M + 255) / 256;
     const int tiles_n = (N + 255) / 256;
-    const int grid = std::min(tiles_m * tiles_n, cus);
+    const int grid = std::min(tiles_m * tiles_n * (PART ? parts : 1), cus);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds_bytes, stream, A, B, M, N, K, sa, sb, bias,
-                       C, tiles_m, tiles_n, qo);
+                       C, tiles_m, tiles_n, qo, PART ? parts : 1);
+    return hipGetLastError();
+}
+
+// The second pass of a split product: C[i, j] = out(sum over p of
+// part[p][i, j] (in part order, fp32) * (*sinv_a) * (*sinv_b) + bias[j]),
+// the unsplit kernels' epilogue arithmetic.  One lane per V consecutive
+// outputs of a row (V = 8 for bf16, 4 for fp32; N is a multiple of V).
+template <int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    const float *__restrict__ part, int parts, int64_t MN, int N, const float *__restrict__ sinv_a,
+    const float *__restrict__ sinv_b, const uint16_t *__restrict__ bias, void *__restrict__ Cv) {
+    constexpr int V = OUT == FP8_DTYPE_BF16 ? 8 : 4;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+    if (i >= MN) return;
+    const float s = (*sinv_a) * (*sinv_b);
+    float acc[V];
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(part + i) + h);
+        acc[4 * h + 0] = v[0]; acc[4 * h + 1] = v[1]; acc[4 * h + 2] = v[2]; acc[4 * h + 3] = v[3];
+    }
+    for (int p = 1; p < parts; ++p) {
+        const float *q = part + (int64_t)p * MN + i;
+#pragma unroll
+        for (int h = 0; h < V / 4; ++h) {
+            const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(q) + h);
+            acc[4 * h + 0] += v[0]; acc[4 * h + 1] += v[1];
+            acc[4 * h + 2] += v[2]; acc[4 * h + 3] += v[3];
+        }
+    }
+    const int c = (int)(i % N);
+    float b[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        b[k] = HAS_BIAS ? __uint_as_float((uint32_t)bias[c + k] << 16) : 0.f;
+    if constexpr (OUT == FP8_DTYPE_BF16) {
+        float y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = HAS_BIAS ? acc[k] * s + b[k] : acc[k] * s;
+        const bf16x2 o0 = {(__bf16)y[0], (__bf16)y[1]}, o1 = {(__bf16)y[2], (__bf16)y[3]},
+                     o2 = {(__bf16)y[4], (__bf16)y[5]}, o3 = {(__bf16)y[6], (__bf16)y[7]};
+        const u32x4 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
+                         __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3)};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(Cv) + i));
+    } else {
+        const v4f y = {acc[0] * s + b[0], acc[1] * s + b[1], acc[2] * s + b[2], acc[3] * s + b[3]};
+        __builtin_nontemporal_store(y, reinterpret_cast<v4f *>(static_cast<float *>(Cv) + i));
+    }
+}
+
+template <int OUT, bool HAS_BIAS>
+hipError_t launch_splitk_reduce(const float *part, int parts, int64_t M, int64_t N,
+                                const float *sa, const float *sb, const uint16_t *bias, void *C,
+                                hipStream_t stream) {
+    constexpr int V = OUT == FP8_DTYPE_BF16 ? 8 : 4;
+    const int64_t lanes = M * N / V;
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, HAS_BIAS>), dim3((unsigned)((lanes + 255) / 256)),
+                       dim3(256), 0, stream, part, parts, M * N, (int)N, sa, sb, bias, C);
     return hipGetLastError();
 }
 
@@ -1426,7 +1505,8 @@ hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
 template <int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
                       const float *sa, const float *sb, const uint16_t *bias, void *C,
-                      const QOut &qo, hipStream_t stream) {
+                      const QOut &qo, hipStream_t stream, void *ws = nullptr,
+                      int64_t ws_bytes = 0) {
     // Large problems: 256 x 256 tiles, four waves of 128 x 128 (32x32x64
     // instructions); small ones: 128 x 128 or 64 x 128 tiles (16x16x128
     // instructions).
@@ -1438,6 +1518,21 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
     const bool out32 = 128 * N * out_bytes < ((int64_t)1 << 31);
     int cus = 0;
     if (hipError_t e = current_cu_count(&cus)) return e;
+    // Products that leave CUs idle, given a workspace: K parts on the LDS-DMA
+    // kernel, then the part sum (gemm_split_parts picks the count).
+    if constexpr (!is_q_out<OUT>()) {
+        const bool part32 = 128 * N * 4 < ((int64_t)1 << 31);
+        const int parts = (ws != nullptr && fits32 && part32)
+                              ? gemm_split_parts(M, N, K, cus, ws_bytes)
+                              : 1;
+        if (parts > 1) {
+            if (hipError_t e = launch_dma<FA, FB, FP8_DTYPE_FP32, false, true>(
+                    A, B, (int)M, (int)N, (int)K, sa, sb, nullptr, ws, qo, stream, parts))
+                return e;
+            return launch_splitk_reduce<OUT, HAS_BIAS>(static_cast<const float *>(ws), parts, M,
+                                                       N, sa, sb, bias, C, stream);
+        }
+    }
     // The large kernels run at about twice the small kernel's rate per CU, so
     // they take every product with at least three quarters of a 256 x 256
     // tile per CU (e.g. 1024 x 12288: 192 tiles).

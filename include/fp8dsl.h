@@ -20,9 +20,11 @@
  * toy block's elementwise producers fused into the cast and the modulation's
  * gradient (fp8_produce_cast_transpose_amax, fp8_produce_modulate_backward),
  * dynamic scaling as the comparator (fp8_cast_transpose_dynamic), the
- * forward with FP8 output and output amax (fp8_linear_fwd_fp8out), the cast
- * with cached source loads, and a device copy that serves as the bandwidth
- * yardstick (fp8_reference_copy).
+ * forward with FP8 output and output amax (fp8_linear_fwd_fp8out), the three
+ * products split over K through a caller workspace for shapes that alone
+ * leave compute units idle (fp8_linear_{fwd,dgrad,wgrad}_ws,
+ * fp8_gemm_workspace_bytes), the cast with cached source loads, and a device
+ * copy that serves as the bandwidth yardstick (fp8_reference_copy).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 9
+#define FP8DSL_ABI_VERSION 10
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -473,6 +475,53 @@ int fp8_linear_dgrad(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx
  */
 int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, int32_t out_dtype,
                      fp8_stream_t stream);
+
+/*
+ * The same three products with a caller-owned workspace, for products whose
+ * output alone would leave compute units idle while their contraction is
+ * long: the weight gradient of a 2048 x 2048 or 4096 x 2048 linear over 8192
+ * tokens, the 1024-token forward of an 8192 -> 2048 linear.
+ *
+ * Each is the product of the entry point without "_ws" (same arguments,
+ * constraints, errors and rounding of the result), computed in K parts when
+ * the workspace allows: every part's fp32 sum of products goes to the
+ * workspace, then a second pass adds the parts in part order (fp32) and
+ * applies the scale-inverses, the bias and the output rounding.  The sum
+ * over K is thus grouped differently from the unsplit product (the result
+ * differs from it within fp32 accumulation error); repeated calls with the
+ * same workspace size give identical bits.  The part count P is the largest
+ * with every (tile, part) unit of 256 x 256 outputs resident at once, K a
+ * multiple of 128 P and at least 2048 contraction bytes per part (the parts'
+ * sums cost 8 P M N bytes of memory traffic, repaid only by long parts);
+ * products with at least three quarters of a 256 x 256 tile per compute unit
+ * are never split.
+ *
+ * fp8_gemm_workspace_bytes(M, N, K): the workspace bytes the split form of a
+ * product with output [M, N] and contraction K uses on the current device
+ * (M, N, K: fwd (tokens, out features, in features), dgrad (tokens, in, out),
+ * wgrad (out, in, tokens)); 0 when the product fills the device unsplit.  A
+ * negative value is a status code (FP8_ERR_SHAPE for negative sizes, or the
+ * device query's error).
+ *
+ * workspace        device, 16-byte aligned, owned by the caller; NULL (any
+ *                  size) computes unsplit.  A workspace smaller than
+ *                  fp8_gemm_workspace_bytes gives fewer parts or none, never
+ *                  an error.  Its contents on entry do not matter and on
+ *                  return are unspecified; calls that overlap on one
+ *                  workspace race.
+ * workspace_bytes  its size; negative with a non-NULL workspace is FP8_ERR_ARG.
+ * Errors: those of the unsplit entry point, FP8_ERR_ALIGN (workspace),
+ * FP8_ERR_ARG.
+ */
+int64_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int fp8_linear_fwd_ws(const fp8_tensor_t *x, const fp8_tensor_t *w, const uint16_t *bias,
+                      uint16_t *y, void *workspace, int64_t workspace_bytes,
+                      fp8_stream_t stream);
+int fp8_linear_dgrad_ws(const fp8_tensor_t *dy, const fp8_tensor_t *w, uint16_t *dx,
+                        void *workspace, int64_t workspace_bytes, fp8_stream_t stream);
+int fp8_linear_wgrad_ws(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw,
+                        int32_t out_dtype, void *workspace, int64_t workspace_bytes,
+                        fp8_stream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *fp8_status_string(int status);

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
                  "fp8_produce_cast_transpose_amax", "fp8_cast_transpose_dynamic",
                  "fp8_linear_fwd_fp8out", "fp8_cast_transpose_amax_dbias_noalloc",
                  "fp8_cast_transpose_amax_cached", "fp8_reference_copy",
-                 "fp8_produce_modulate_backward"):
+                 "fp8_produce_modulate_backward", "fp8_gemm_workspace_bytes",
+                 "fp8_linear_fwd_ws", "fp8_linear_dgrad_ws", "fp8_linear_wgrad_ws"):
         assert want in names
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 9
+    assert dsl.fp8_abi_version() == 10
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -113,6 +114,38 @@ def test_validation_rejects_before_device_use():
     assert L.fp8_linear_wgrad(byref(dy), byref(_desc(64, 48)), 0x5000, 2, None) == -5
     assert L.fp8_linear_wgrad(byref(dy), byref(_desc(48, 48)), 0x5000, 1, None) == -2
     assert L.fp8_linear_wgrad(byref(_desc(40, 32)), byref(_desc(40, 48)), 0x5000, 1, None) == -2
+
+
+def test_split_product_workspace_validation():
+    """The _ws products check what the unsplit ones check, then the
+    workspace: NULL is no workspace (any size); a non-NULL one must be 16-byte
+    aligned with a non-negative size.  Nothing reaches a device."""
+    L = dsl.lib()
+    byref = ctypes.byref
+    x, w = _desc(64, 48), _desc(32, 48)
+    # the unsplit checks come first
+    assert L.fp8_linear_fwd_ws(byref(_desc(64, 40)), byref(_desc(32, 40)), None, 0x5000, 0x9000,
+                               1 << 20, None) == -2
+    assert L.fp8_linear_fwd_ws(byref(x), byref(w), None, None, 0x9000, 1 << 20, None) == -1
+    # then the workspace
+    assert L.fp8_linear_fwd_ws(byref(x), byref(w), None, 0x5000, 0x9008, 1 << 20, None) == -3
+    assert L.fp8_linear_fwd_ws(byref(x), byref(w), None, 0x5000, 0x9000, -1, None) == -5
+    dy = _desc(64, 32)
+    assert L.fp8_linear_dgrad_ws(byref(dy), byref(_desc(32, 48)), 0x5000, 0x9004, 1 << 20,
+                                 None) == -3
+    assert L.fp8_linear_dgrad_ws(byref(dy), byref(_desc(32, 48)), 0x5000, 0x9000, -16,
+                                 None) == -5
+    assert L.fp8_linear_wgrad_ws(byref(dy), byref(_desc(64, 48)), 0x5000, 2, 0x9000, 1 << 20,
+                                 None) == -5
+    assert L.fp8_linear_wgrad_ws(byref(dy), byref(_desc(64, 48)), 0x5000, 1, 0x9002, 1 << 20,
+                                 None) == -3
+    # empty products return before the workspace matters
+    assert L.fp8_linear_fwd_ws(byref(_desc(0, 48)), byref(w), None, None, 0x9001, -1, None) == 0
+    # the size query: negative sizes are a shape error before any device query
+    assert L.fp8_gemm_workspace_bytes(-1, 16, 256) == -2
+    assert L.fp8_gemm_workspace_bytes(16, 16, -256) == -2
+    with pytest.raises(dsl.Fp8Error):
+        dsl.fp8_gemm_workspace_bytes(16, -16, 256)
 
 
 def test_binding_checks_tensor_arguments():
