@@ -219,35 +219,29 @@ def dbias_cast_cost(dsl, st, iters: int = 20):
 
 def split_product_cost(dsl, workloads, iters: int = 20):
     """Products whose output leaves CUs idle over a long contraction, plain
-    and through a workspace (split over K): the weight gradients of the toy
-    block's 2048 -> 2048 and 2048 -> 4096 linears over 8192 tokens (fp32),
-    the 1024-token forward of its 8192 -> 2048 linear (bf16, bias), and a
-    2048 x 2048 weight gradient over 16384 tokens.  Random E4M3 / E5M2
-    operand codes; interleaved rounds, best of each."""
+    and through a workspace (split over K where the library's rule splits):
+    weight gradients (fp32) of a 2048 -> 2048 linear over 16384 and 32768
+    tokens and of a 2048 -> 1024 linear over 32768 tokens, and that of the
+    toy block's 2048 -> 2048 linear over its 8192 tokens (which stays
+    unsplit: parts 1).  Random E5M2 / E4M3 operand codes; interleaved rounds,
+    best of each."""
     one = torch.ones(1, device="cuda")
     res = {}
-    for name, (M_, N_, K_, out) in {
-            "wgrad_2048x2048_k8192": (2048, 2048, 8192, "fp32"),
-            "wgrad_4096x2048_k8192": (4096, 2048, 8192, "fp32"),
-            "fwd_1024x2048_k8192": (1024, 2048, 8192, "bf16"),
-            "wgrad_2048x2048_k16384": (2048, 2048, 16384, "fp32")}.items():
+    for name, (M_, N_, K_) in {
+            "wgrad_2048x2048_k8192": (2048, 2048, 8192),
+            "wgrad_2048x2048_k16384": (2048, 2048, 16384),
+            "wgrad_2048x2048_k32768": (2048, 2048, 32768),
+            "wgrad_1024x2048_k32768": (1024, 2048, 32768)}.items():
         a = workloads.random_fp8_codes((M_, K_), 31, 1).to("cuda")
         b = workloads.random_fp8_codes((N_, K_), 32, 0).to("cuda")
         need = dsl.fp8_gemm_workspace_bytes(M_, N_, K_)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-        if out == "fp32":       # dW [M_, N_] = dY_t [M_, K_] . X_t [N_, K_]^T
-            dyt = dsl.Float8Tensor(None, a, one, 1, K_, M_)
-            xt = dsl.Float8Tensor(None, b, one, 0, K_, N_)
-            dw = torch.empty(M_, N_, dtype=torch.float32, device="cuda")
-            plain = lambda: dsl.fp8_linear_wgrad(dyt, xt, dw)
-            split = lambda: dsl.fp8_linear_wgrad(dyt, xt, dw, workspace=ws)
-        else:
-            x8 = dsl.Float8Tensor(a, None, one, 1, M_, K_)
-            w8 = dsl.Float8Tensor(b, None, one, 0, N_, K_)
-            bias = torch.zeros(N_, dtype=torch.bfloat16, device="cuda")
-            y = torch.empty(M_, N_, dtype=torch.bfloat16, device="cuda")
-            plain = lambda: dsl.fp8_linear_fwd(x8, w8, bias, y)
-            split = lambda: dsl.fp8_linear_fwd(x8, w8, bias, y, workspace=ws)
+        # dW [M_, N_] = dY_t [M_, K_] . X_t [N_, K_]^T
+        dyt = dsl.Float8Tensor(None, a, one, 1, K_, M_)
+        xt = dsl.Float8Tensor(None, b, one, 0, K_, N_)
+        dw = torch.empty(M_, N_, dtype=torch.float32, device="cuda")
+        plain = lambda: dsl.fp8_linear_wgrad(dyt, xt, dw)
+        split = lambda: dsl.fp8_linear_wgrad(dyt, xt, dw, workspace=ws)
         r = {"parts": need // (M_ * N_ * 4) if need else 1}
         for _ in range(2):
             for key, fn in (("plain_us", plain), ("split_us", split)):
@@ -265,7 +259,7 @@ def split_product_cost(dsl, workloads, iters: int = 20):
                 r[key] = round(min(r.get(key, us), us), 2)
         r["split_tflops"] = round(2 * M_ * N_ * K_ / (r["split_us"] * 1e-6) / 1e12, 1)
         res[name] = r
-        del a, b, ws
+        del a, b, ws, dw
     return res
 
 

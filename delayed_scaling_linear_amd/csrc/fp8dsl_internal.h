@@ -23,27 +23,28 @@ hipError_t current_cu_count(int *cu_count);
 hipError_t enable_dynamic_lds(const void *kernel, int lds_bytes, std::atomic<uint64_t> &done);
 
 // K parts for the split form of the product C [M, N] (contraction K) on a
-// device with `cus` compute units and `ws_bytes` of workspace: 1 (no split)
-// for products with at least three quarters of a 256 x 256 tile per CU, or a
-// K that is not a multiple of 128; else the largest P with every unit on the
-// chip at once (tiles * P <= cus), K a multiple of 128 P, at least
-// SPLIT_MIN_K contraction bytes per part, and the parts' P * M * N fp32 sums
-// within ws_bytes.  The parts' sums go out to memory and are read back
-// (8 P M N bytes, at about the HBM rate), which a part repays only with a
-// long contraction: on MI355X 2048 bytes per part splits 2048 x 2048 x 8192
-// four ways (60.7 -> 51.8 us) and 4096 x 2048 x 8192 two ways (95.5 -> 74.3
-// us), while 1024-token products with K = 2048 ran 1.3-2.6x slower split
-// 2-8 ways than on the small kernel.
-constexpr int64_t SPLIT_MIN_K = 2048;
+// device with `cus` compute units and `ws_bytes` of workspace.  The parts'
+// fp32 sums go out to memory and are read back (8 P M N bytes, at about the
+// HBM rate), so a split only pays where the unsplit kernels leave most CUs
+// idle for a long time: products with at most one 128 x 128 tile per CU and
+// fewer than three quarters of a 256 x 256 tile per CU, split into P parts
+// of at least SPLIT_MIN_K contraction bytes that occupy at least three
+// quarters of the CUs (tiles * P between 3/4 cus and cus, K a multiple of
+// 128 P, the P * M * N fp32 sums within ws_bytes); else 1 (no split).
+// Measured on MI355X against the direct-to-LDS small kernel: 2048 x 2048
+// and 4096 x 2048 over K = 8192 run faster unsplit (48-51 / 65-70 us
+// against 52 / 77 us in 4 / 2 parts), while K = 16384 and beyond split.
+constexpr int64_t SPLIT_MIN_K = 4096;
 inline int gemm_split_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_bytes) {
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
     if (M <= 0 || N <= 0 || tiles == 0) return 1;
     if (M * N >= (int64_t)256 * 256 * 256 || 4 * tiles >= 3 * (int64_t)cus) return 1;
+    if (((M + 127) / 128) * ((N + 127) / 128) > cus) return 1;
     if (K % 128 != 0) return 1;
     int best = 1;
     for (int p = 2; p <= 16; ++p) {
         if (K / p < SPLIT_MIN_K || tiles * p > cus || (int64_t)p * M * N * 4 > ws_bytes) break;
-        if (K % (128 * p) == 0) best = p;
+        if (K % (128 * p) == 0 && 4 * tiles * p >= 3 * (int64_t)cus) best = p;
     }
     return best;
 }

@@ -17,7 +17,7 @@
 // a group loses less than 2^-10 of its largest product), and accumulates the
 // group sums in fp32.
 //
-// Design (gfx950, wave64).  Three kernels; launch_fmt picks one per call:
+// Design (gfx950, wave64).  Four kernels; launch_fmt picks one per call:
 //
 //   * gemm_nt_dma_kernel -- every large product (256^3 outputs or more, or
 //     at least three quarters of a 256 x 256 tile per CU) with K % 128 == 0
@@ -37,15 +37,23 @@
 //   * gemm_nt_big_kernel -- the same tiling for large products whose K is a
 //     multiple of 16 only: 64-byte stages in three LDS buffers, loaded
 //     through registers, K tails read as zero through the buffer range check.
-//   * gemm_nt_kernel -- small products: 128 x 128 tiles (64 x 128 when
-//     there would be fewer tiles than CUs), one workgroup per tile,
-//     v_mfma_f32_16x16x128_f8f6f4, double-buffered LDS.
+//   * gemm_nt_sdma_kernel -- small products with K % 128 == 0 and 32-bit
+//     operand offsets: 128 x 128 tiles (64 x 128 when there would be fewer
+//     tiles than CUs), one workgroup per tile, v_mfma_f32_16x16x128_f8f6f4,
+//     operand stages written into LDS by buffer loads with the LDS flag, two
+//     or three stages in flight.
+//   * gemm_nt_kernel -- the other small products (K tails, FP8 outputs): the
+//     same tiles with loads staged through registers, double-buffered LDS.
+//   * The split form: gemm_nt_dma_kernel over (tile, K part) units writing
+//     raw fp32 sums to a caller workspace, then splitk_reduce_kernel, for
+//     products with few tiles and a long contraction (gemm_split_parts).
 //
-// Shared by all three: LDS rows are 128 bytes with the 16-byte chunk c of row
+// Shared by all four: LDS rows are 128 bytes with the 16-byte chunk c of row
 // r stored at a row-dependent XOR of c (conflict-free fragment reads); the B
 // fragment is the matrix core's first operand, so each lane holds four
 // consecutive output columns of one output row; out-of-range operand rows
-// are clamped for loading and never stored.
+// are clamped for loading (or read as zero through a buffer range) and
+// never stored.
 //
 // The kernels and their launch templates live in this header; the library's
 // sources instantiate them per output kind (bf16 / fp32, FP8 codes) so that
@@ -989,6 +997,176 @@ __device__ __forceinline__ int fresh_lane_id() {
     return l;
 }
 
+// vmcnt wait with any count (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A direct-to-LDS 16-byte-per-lane load whose K offset is the scalar offset.
+__device__ __forceinline__ void dma_b128_k(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                           uint32_t soff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// Small products with K % 128 == 0 and 32-bit operand offsets: the small
+// kernel's tiles (BM x 128, four waves of BM/2 x 64 outputs with
+// v_mfma_f32_16x16x128_f8f6f4, the same LDS layout and epilogue), with the
+// operand stages written into LDS by the load unit (buffer loads with the
+// LDS flag) instead of through registers: NS stages of 128 K-bytes, NS - 1
+// of them in flight while the matrix cores work on one, one barrier per
+// stage and no LDS write instructions.
+//   * A stage is BM + 128 rows of 128 bytes, fetched by (BM + 128) / 8
+//     instructions of 8 rows; wave w issues instructions w, w + 4, ...  Lane l
+//     loads row 8q + l / 8 of instruction q, logical chunk (l % 8) ^ (l / 8),
+//     which lands at chunk position l % 8: row r keeps chunk c at c ^ (r & 7).
+//     Operand rows past M (N) read as zero through the descriptor range.
+//   * In step k: wait for this wave's loads of stage k (a fixed count of
+//     later loads stays in flight), barrier (every wave's loads of stage k
+//     have landed and every wave has finished reading stage k - 1), request
+//     stage k + NS - 1 into the buffer stage k - 1 used, read and multiply.
+template <int BM, int NS, int FA, int FB, int OUT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void gemm_nt_sdma_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
+    const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n) {
+    static_assert(OUT == FP8_DTYPE_BF16 || OUT == FP8_DTYPE_FP32, "bf16 or fp32 output");
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    constexpr int BN = 128, WN = 2;
+    constexpr int WTM = BM / 2, WTN = BN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr uint32_t STAGE = (BM + BN) * BK;
+    constexpr int LPW = (BM + BN) / 32;     // load instructions per wave per stage
+    constexpr int LA = BM / 32;             // of them, on A rows
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+
+    int tile_m, tile_n;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(A), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(B), (short)0, N * K, 0x00020000);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    uint32_t voff[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int q = wave + 4 * i;         // instruction: rows 8q .. 8q + 7 of the stage
+        const int r = 8 * q + (lane >> 3);
+        const int kc = (lane & 7) ^ (lane >> 3);
+        const int grow = i < LA ? m0 + r : n0 + (r - BM);
+        voff[i] = (uint32_t)grow * (uint32_t)K + (uint32_t)(16 * kc);
+    }
+    auto issue = [&](int st, int buf) {
+        const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(st * BK);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            dma_b128_k(i < LA ? ra : rb, voff[i], k0,
+                       lds0 + (uint32_t)buf * STAGE + (uint32_t)(wave + 4 * i) * 1024u);
+    };
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int fc0 = (lane >> 4) * 2;
+    const int sw = frow & 7;
+    const int off0 = ((fc0 ^ sw) << 4);
+    const int off1 = (((fc0 + 1) ^ sw) << 4);
+
+    const int nk = K / BK;                  // >= 2 (the launcher guarantees)
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nk) issue(st, st);
+    for (int k = 0; k < nk; ++k) {
+        // stages issued after stage k: k + 1 .. min(k + NS - 2, nk - 1)
+        const int ahead = min(NS - 2, nk - 1 - k);
+        if (ahead <= 0)
+            wait_vmem_le<0>();
+        else if (NS >= 3 && ahead == 1)
+            wait_vmem_le<LPW>();
+        else
+            wait_vmem_le<(NS >= 4 ? 2 : 1) * LPW>();
+        __syncthreads();
+        if (k + NS - 1 < nk) issue(k + NS - 1, (k + NS - 1) % NS);
+
+        const uint8_t *stg = lds + (uint32_t)(k % NS) * STAGE;
+        const uint8_t *As = stg + (wm * WTM + frow) * BK;
+        const uint8_t *Bs = stg + BM * BK + (wn * WTN + frow) * BK;
+        v8i bf[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(Bs + j * 16 * BK + off0);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(Bs + j * 16 * BK + off1);
+            bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(As + i * 16 * BK + off0);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(As + i * 16 * BK + off1);
+            const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf[j], af, acc[i][j], FB, FA, 0, 0, 0, 0);
+        }
+    }
+
+    // Epilogue (the small kernel's): lane (l % 16, l / 16) holds output row
+    // l % 16 of each 16-row fragment, columns 4 (l / 16) .. +3.
+    const float s = (*sinv_a) * (*sinv_b);
+    const int orow = lane & 15;
+    const int ocol = (lane >> 4) * 4;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int gc = n0 + wn * WTN + j * 16 + ocol;
+        if (gc >= N) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_BIAS) {
+            const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + gc);
+            bv[0] = __uint_as_float(b2.x << 16);
+            bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+            bv[2] = __uint_as_float(b2.y << 16);
+            bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int gr = m0 + wm * WTM + i * 16 + orow;
+            if (gr >= M) continue;
+            const v4f a = acc[i][j];
+            const float y0 = a.x * s + bv[0];
+            const float y1 = a.y * s + bv[1];
+            const float y2 = a.z * s + bv[2];
+            const float y3 = a.w * s + bv[3];
+            if constexpr (OUT == FP8_DTYPE_BF16) {
+                uint16_t *C = static_cast<uint16_t *>(Cv);
+                const u32x2 o = u32x2{f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16),
+                                      f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16)};
+                *reinterpret_cast<u32x2 *>(C + (int64_t)gr * N + gc) = o;
+            } else {
+                float *C = static_cast<float *>(Cv);
+                *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
+            }
+        }
+    }
+}
+
 // Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
 // 256-thread workgroup per CU, four waves of 128 x 128 with
 // v_mfma_f32_32x32x64_f8f6f4) whose operand stages are written into LDS by
@@ -1502,6 +1680,27 @@ hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
     return hipGetLastError();
 }
 
+// LDS stages of the direct-to-LDS small kernel per tile height.
+constexpr int SDMA_STAGES_64 = 3;
+constexpr int SDMA_STAGES_128 = 2;
+
+template <int BM, int FA, int FB, int OUT, bool HAS_BIAS>
+hipError_t launch_sdma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
+                       const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
+    constexpr int NS = BM == 64 ? SDMA_STAGES_64 : SDMA_STAGES_128;
+    auto kern = gemm_nt_sdma_kernel<BM, NS, FA, FB, OUT, HAS_BIAS>;
+    constexpr int lds_bytes = NS * (BM + 128) * BK;
+    static std::atomic<uint64_t> lds_enabled{0};
+    if (hipError_t e = enable_dynamic_lds(reinterpret_cast<const void *>(kern), lds_bytes,
+                                          lds_enabled))
+        return e;
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + 127) / 128;
+    hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(256), lds_bytes, stream, A, B, M, N,
+                       K, sa, sb, bias, C, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 template <int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, int64_t K,
                       const float *sa, const float *sb, const uint16_t *bias, void *C,
@@ -1547,7 +1746,19 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
     // Small problems with fewer 128 x 128 tiles than CUs (few tokens, narrow
     // outputs: e.g. 1024 x 2048 with K = 8192 has 128) take 64 x 128 tiles,
     // twice as many, so that more CUs share the K loop.
-    if (((M + 127) / 128) * ((N + 127) / 128) < cus)
+    const bool half = ((M + 127) / 128) * ((N + 127) / 128) < cus;
+    // Whole 128-byte K stages and 32-bit operand offsets: the operand stages
+    // go straight into LDS (bf16 / fp32 outputs).
+    if constexpr (!is_q_out<OUT>()) {
+        if (fits32 && K >= 256 && K % 128 == 0) {
+            if (half)
+                return launch_sdma<64, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
+                                                              bias, C, stream);
+            return launch_sdma<128, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
+                                                           bias, C, stream);
+        }
+    }
+    if (half)
         return launch_cfg<64, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa,
                                                                 sb, bias, C, qo, stream);
     return launch_cfg<128, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,

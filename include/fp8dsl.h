@@ -478,9 +478,9 @@ int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, in
 
 /*
  * The same three products with a caller-owned workspace, for products whose
- * output alone would leave compute units idle while their contraction is
- * long: the weight gradient of a 2048 x 2048 or 4096 x 2048 linear over 8192
- * tokens, the 1024-token forward of an 8192 -> 2048 linear.
+ * few output tiles would leave compute units idle over a long contraction:
+ * the weight gradient of a 2048 x 2048 linear over 16384 or more tokens, of a
+ * 2048 x 1024 one over 32768.
  *
  * Each is the product of the entry point without "_ws" (same arguments,
  * constraints, errors and rounding of the result), computed in K parts when
@@ -490,11 +490,12 @@ int fp8_linear_wgrad(const fp8_tensor_t *dy, const fp8_tensor_t *x, void *dw, in
  * over K is thus grouped differently from the unsplit product (the result
  * differs from it within fp32 accumulation error); repeated calls with the
  * same workspace size give identical bits.  The part count P is the largest
- * with every (tile, part) unit of 256 x 256 outputs resident at once, K a
- * multiple of 128 P and at least 2048 contraction bytes per part (the parts'
- * sums cost 8 P M N bytes of memory traffic, repaid only by long parts);
- * products with at least three quarters of a 256 x 256 tile per compute unit
- * are never split.
+ * (at most 16) whose (tile, part) units of 256 x 256 outputs fill between
+ * three quarters of the compute units and all of them, with K a multiple of
+ * 128 P and at least 4096 contraction bytes per part (the parts' sums cost
+ * 8 P M N bytes of memory traffic, repaid only by long parts).  Products with
+ * more than one 128 x 128 tile or three quarters of a 256 x 256 tile per
+ * compute unit are never split: the unsplit kernels keep the chip busy.
  *
  * fp8_gemm_workspace_bytes(M, N, K): the workspace bytes the split form of a
  * product with output [M, N] and contraction K uses on the current device

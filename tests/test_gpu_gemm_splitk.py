@@ -1,14 +1,13 @@
 """GPU parity: the split form of the FP8 products (fp8_linear_{fwd,dgrad,
 wgrad}_ws), through the C ABI.
 
-Products that alone would leave compute units idle (few tokens, or a narrow
-output over a long contraction) are computed in K parts through the caller's
-workspace, then the parts are summed in part order.  Every output is checked
-against the oracle's exact product (same tolerance as the unsplit tests),
-for each role and output type, ragged shapes and a part count that is not a
-power of two; repeated calls give identical bits; a null workspace gives the
-unsplit entry point's bits; a short workspace gives fewer parts and still
-the right product."""
+Products whose few output tiles would leave compute units idle over a long
+contraction are computed in K parts through the caller's workspace, then
+the parts are summed in part order.  Every output is checked against the
+oracle's exact product (same tolerance as the unsplit tests), for each role
+and output type, ragged shapes and part counts that are not powers of two;
+repeated calls give identical bits; a null workspace, or one too short for
+any part count that fills the chip, gives the unsplit entry point's bits."""
 import numpy as np
 import pytest
 import torch
@@ -27,16 +26,19 @@ def _cus() -> int:
 
 def _parts(M, N, K, cus, ws_bytes=1 << 62):
     """The split rule of the library, restated: 1 for products with 3/4 of a
-    256 x 256 tile per CU (or 256^3 outputs), else the largest P with
-    tiles * P <= CUs, K / P >= 2048, K % (128 P) == 0 and P*M*N*4 bytes."""
+    256 x 256 tile per CU (or 256^3 outputs) or more than one 128 x 128 tile
+    per CU, else the largest P <= 16 with 3/4 CUs <= tiles * P <= CUs,
+    K / P >= 4096, K % (128 P) == 0 and P*M*N*4 workspace bytes."""
     tiles = -(-M // 256) * -(-N // 256)
     if M * N >= 256 ** 3 or 4 * tiles >= 3 * cus or K % 128:
         return 1
+    if -(-M // 128) * -(-N // 128) > cus:
+        return 1
     best = 1
     for p in range(2, 17):
-        if K // p < 2048 or tiles * p > cus or p * M * N * 4 > ws_bytes:
+        if K // p < 4096 or tiles * p > cus or p * M * N * 4 > ws_bytes:
             break
-        if K % (128 * p) == 0:
+        if K % (128 * p) == 0 and 4 * tiles * p >= 3 * cus:
             best = p
     return best
 
@@ -88,16 +90,12 @@ def _values(t):
 
 CASES = [
     # role, M, N, K, out, bias: long contractions over few output tiles (the
-    # 1024-token forward of the 8192 -> 2048 linear, the weight gradients of
-    # narrow linears over many tokens), ragged ones, and a part count of 3
-    ("fwd", 1024, 2048, 8192, "bf16", True),      # 32 tiles: 4 parts
-    ("fwd", 1024, 6144, 4096, "bf16", True),      # 96 tiles: 2 parts
-    ("fwd", 1000, 2056, 8192, "bf16", False),     # ragged M, N: 36 tiles, 4 parts
-    ("dgrad", 256, 4096, 8192, "bf16", False),    # 16 tiles: 4 parts
-    ("wgrad", 1024, 2048, 8192, "fp32", False),   # 4 parts, fp32 output
-    ("wgrad", 776, 1028, 4096, "fp32", False),    # ragged, N % 8 == 4: 20 tiles, 2 parts
-    ("wgrad", 520, 1032, 8192, "bf16", False),    # ragged, bf16 output: 15 tiles, 4 parts
-    ("fwd", 512, 520, 6528, "bf16", True),        # K = 51 * 128: 3 parts
+    # weight gradient of a 2048 x 2048 linear over 16384 tokens), ragged
+    # shapes, and part counts that are not powers of two
+    ("wgrad", 2048, 2048, 16384, "fp32", False),  # 64 tiles: 4 parts, fp32 output
+    ("fwd", 1000, 2056, 24576, "bf16", True),     # ragged M, N: 36 tiles, 6 parts
+    ("dgrad", 520, 1032, 65536, "bf16", False),   # ragged: 15 tiles, 16 parts
+    ("wgrad", 776, 1028, 49152, "fp32", False),   # ragged, N % 8 == 4: 20 tiles, 12 parts
 ]
 
 
@@ -128,8 +126,8 @@ def test_split_products_against_the_oracle(role, M, N, K, out, has_bias):
                        y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2.view(torch.int32))
 
 
-def test_null_workspace_is_the_unsplit_product_and_a_short_one_splits_less():
-    M, N, K = 1024, 2048, 8192
+def test_null_or_short_workspace_is_the_unsplit_product():
+    M, N, K = 1000, 2056, 24576
     cus = _cus()
     A = workloads.random_fp8_codes((M, K), 5, 0)
     B = workloads.random_fp8_codes((N, K), 6, 0)
@@ -140,7 +138,7 @@ def test_null_workspace_is_the_unsplit_product_and_a_short_one_splits_less():
     w8 = dsl.Float8Tensor(B.to(DEV), None, _si(sb), 0, N, K)
     dsl.fp8_linear_fwd(x8, w8, bias.to(DEV), y_plain)
     y_null = torch.empty_like(y_plain)
-    # the _ws entry point with a NULL workspace
+    # the _ws entry point with a NULL workspace (any size)
     d1, d2 = x8.desc(), w8.desc()
     import ctypes
     rc = dsl.lib().fp8_linear_fwd_ws(ctypes.byref(d1), ctypes.byref(d2), bias.to(DEV).data_ptr(),
@@ -148,17 +146,11 @@ def test_null_workspace_is_the_unsplit_product_and_a_short_one_splits_less():
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(y_plain.view(torch.int16), y_null.view(torch.int16))
-    ref = _ref(A, 0, B, 0, sa, sb, bias)
-    # workspaces for 3 and for 2.5 parts: 2 parts (8192 is not a multiple of 3 * 128)
-    for nbytes in (3 * M * N * 4, 5 * M * N * 2):
-        assert _parts(M, N, K, cus, nbytes) == 2
-        y = torch.empty_like(y_plain)
-        dsl.fp8_linear_fwd(x8, w8, bias.to(DEV), y, workspace=_ws(nbytes))
-        torch.cuda.synchronize()
-        assert_gemm_close(bf16_values(bits16(y)), ref, f"short workspace {nbytes}")
-    # a workspace for less than 2 parts: unsplit, the plain bits
+    # 36 tiles split 6 ways fill the chip; a workspace for 5.5 parts leaves
+    # no count that does (5 parts occupy 180 of 256 CUs): unsplit, the plain bits
+    assert _parts(M, N, K, cus) == 6 and _parts(M, N, K, cus, 11 * M * N * 2) == 1
     y = torch.empty_like(y_plain)
-    dsl.fp8_linear_fwd(x8, w8, bias.to(DEV), y, workspace=_ws(M * N * 4))
+    dsl.fp8_linear_fwd(x8, w8, bias.to(DEV), y, workspace=_ws(11 * M * N * 2))
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
 
@@ -168,6 +160,8 @@ def test_workspace_bytes_follow_the_rule():
     for M, N, K in [(1024, 12288, 2048), (1024, 6144, 2048), (1024, 2048, 2048),
                     (1024, 4096, 2048), (1024, 8192, 2048), (1024, 2048, 8192),
                     (2048, 2048, 16384), (1024, 6144, 4096), (512, 520, 6528),
+                    (1024, 2048, 32768), (2048, 2048, 32768), (4096, 2048, 16384),
+                    (520, 1032, 65536), (776, 1028, 49152), (1000, 2056, 24576),
                     (8192, 8192, 2048), (2048, 2048, 8192), (4096, 2048, 8192),
                     (12288, 2048, 8192), (1000, 2056, 2048), (512, 520, 1152),
                     (256, 256, 128), (64, 64, 4096), (1024, 2048, 1040), (0, 16, 256)]:
@@ -179,7 +173,7 @@ def test_workspace_bytes_follow_the_rule():
 def test_split_products_inside_a_graph_replay():
     """The split forward captured in a HIP graph (workspace from the graph's
     pool, as a framework allocator gives it) replays to the eager bits."""
-    M, N, K = 1024, 4096, 8192
+    M, N, K = 1024, 2048, 32768
     A = workloads.random_fp8_codes((M, K), 21, 0).to(DEV)
     B = workloads.random_fp8_codes((N, K), 22, 0).to(DEV)
     bias = workloads.normal_bf16((N,), 0.5, 23).to(DEV)
