@@ -56,6 +56,10 @@ def parse():
                    help="launch the forward GEMM, the [4096,4096] cast and a 64 MiB device copy "
                         "once each (after a warm-up) and exit: the command profiled for HBM "
                         "traffic counters")
+    p.add_argument("--probe-toy-stack", action="store_true",
+                   help="replay the 32-block 1024-token forward graph (fused producers, cached "
+                        "FP8 weights) 6 times, then run 4 training steps of the 8192-token "
+                        "stack, and exit: the command profiled for the toy stack's kernel traces")
     return p.parse_args()
 
 
@@ -731,6 +735,24 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3, tokens: i
     return out
 
 
+def _stack_params(stack):
+    """The training stack's fp32 master weights and biases as optimizer
+    parameters, each with the library-written gradient buffer as its .grad."""
+    params = []
+    for b in range(stack.blocks):
+        for l in range(len(stack.lin)):
+            w = stack.w[b][l]
+            w.requires_grad_(True)
+            w.grad = stack.grad_w[b][l]
+            params.append(w)
+            if stack.b32[b][l] is not None:
+                bb = stack.b32[b][l]
+                bb.requires_grad_(True)
+                bb.grad = stack.grad_b[b][l]
+                params.append(bb)
+    return params
+
+
 def _adamw(params, capturable: bool = False):
     """torch's fused AdamW where the installed torch has it, else the foreach one;
     `capturable` keeps its step counts on the device so that a HIP graph can
@@ -778,18 +800,7 @@ def toy_stack_train_step(dsl, workloads, blocks: int = 32, warmup: int = 10, ite
     dev = "cuda"
     H, Mt = workloads.HIDDEN, workloads.TOKENS
     stack = ToyStack(dsl, workloads, blocks, train=True)
-    params = []
-    for b in range(blocks):
-        for l in range(len(stack.lin)):
-            w = stack.w[b][l]
-            w.requires_grad_(True)
-            w.grad = stack.grad_w[b][l]
-            params.append(w)
-            if stack.b32[b][l] is not None:
-                bb = stack.b32[b][l]
-                bb.requires_grad_(True)
-                bb.grad = stack.grad_b[b][l]
-                params.append(bb)
+    params = _stack_params(stack)
     opt = _adamw(params)
     x = workloads.uniform_bf16((Mt, H), workloads.SEED_X).to(dev)
     target = workloads.uniform_bf16((Mt, H), workloads.SEED_X + 1).to(dev)
@@ -917,6 +928,39 @@ def probe_kernels(dsl, workloads, st):
     print("probe-kernels: " + ", ".join(n for n, _ in seq), flush=True)
 
 
+def probe_toy_stack(dsl, workloads):
+    """The toy stack's two measured workloads, synchronised between phases,
+    for a kernel trace: 6 replays of the 32-block forward at 1024 tokens as
+    one HIP graph with the producers fused and the FP8 weights cached (the
+    no-op flag set), then 4 training steps of the 32-block stack at 8192
+    tokens (fused AdamW on fp32 master weights)."""
+    stack = ToyStack(dsl, workloads, 32, tokens=1024)
+    xin = workloads.uniform_bf16((1024, workloads.HIDDEN), workloads.SEED_X).to("cuda")
+    stack.forward(xin, fused=True)               # first launches outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack.forward(xin, fused=True)
+    stack.flag.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(6):
+        graph.replay()
+    torch.cuda.synchronize()
+    progress("probe-toy-stack: 1024-token forward graph done")
+    del graph, stack
+    torch.cuda.empty_cache()
+    stack = ToyStack(dsl, workloads, 32, train=True)
+    opt = _adamw(_stack_params(stack))
+    x = workloads.uniform_bf16((workloads.TOKENS, workloads.HIDDEN), workloads.SEED_X).to("cuda")
+    target = workloads.uniform_bf16((workloads.TOKENS, workloads.HIDDEN),
+                                    workloads.SEED_X + 1).to("cuda")
+    with torch.no_grad():
+        for _ in range(4):
+            stack.train_step(x, target, opt)
+            torch.cuda.synchronize()
+    progress("probe-toy-stack: 4 training steps done")
+
+
 def scale_update_cost(dsl, iters: int = 50):
     """One fused update over 3 records (the step), the 384 of the 32-block
     forward and the 576 of its training step (history 16): us per launch,
@@ -993,6 +1037,9 @@ def main():
     import delayed_scaling_linear_amd as dsl
     import workloads
 
+    if args.probe_toy_stack:
+        probe_toy_stack(dsl, workloads)
+        return
     dev = "cuda"
     x, w, b = workloads.mlp_forward(0)
     dy = workloads.mlp_grad()
