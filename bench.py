@@ -399,7 +399,7 @@ class ToyStack:
     """The toy transformer stack of "CPU Overhead of te.Linear FP8 Layers"
     (hidden 2048, batch 8 x seq 1024 = 8192 tokens, mlp_ratio 4) run through
     the library: every linear casts its input and weight with delayed scaling
-    and multiplies in FP8; when training, its output gradient is cast to E5M2
+    and multiplies in FP8; when, its output gradient is cast to E5M2
     (with the bias gradient fused in for the biased linears) and dgrad and
     wgrad run from the cached transposes.  One scale update per step covers
     every record.
@@ -427,6 +427,14 @@ class ToyStack:
     (this library's addition, on no page) replaces non-finite quotients by
     +0; the timed workloads use it.
 
+    `group_weight_casts` casts a block's six weights in one launch at the
+    block's start (fp8_cast_transpose_amax_group) instead of each right before
+    its product; by default for 2048 tokens or fewer.  Measured on MI355X: at
+    1024 tokens the launches are the cost (fused graph with cached weights
+    6.59 -> 6.36 ms); at 8192 tokens a weight's codes cast right before its
+    product are still in the last-level cache when the product reads them,
+    and grouping loses that (fused graph 23.3 -> 26.2 ms).
+
     `train` keeps what the backward needs (every FP8 input with its
     transpose, the block inputs and modulation outputs) and holds fp32 master
     weights (the FP8 run of the page keeps fp32 parameters) whose FP8 casts
@@ -434,13 +442,15 @@ class ToyStack:
     """
 
     def __init__(self, dsl, workloads, blocks: int, *, train: bool = False, dev: str = "cuda",
-                 seed: int = 20, weights=None, modulate: str = "finite", tokens: int = 0):
+                 seed: int = 20, weights=None, modulate: str = "finite", tokens: int = 0,
+                 group_weight_casts=None):
         self.dsl, self.blocks, self.train, self.dev = dsl, blocks, train, dev
         if modulate not in ("page", "finite"):
             raise ValueError("modulate must be 'page' or 'finite'")
         self.finite = modulate == "finite"
         self.mod_op = dsl.PRODUCE_MODULATE_FINITE if self.finite else dsl.PRODUCE_MODULATE
         self.H, self.M = workloads.HIDDEN, tokens or workloads.TOKENS
+        self.group_w = self.M <= 2048 if group_weight_casts is None else bool(group_weight_casts)
         self.lin = workloads.toy_block_linears()
         nl = len(self.lin)
         self.R = 3 if train else 2
@@ -519,13 +529,26 @@ class ToyStack:
         self.dsl.fp8_cast_transpose_amax(x, self._sl(st.scale, r), self.qx[l][b],
                                          self._sl(st.amax_cur, r))
 
+    def _cast_weights(self, b):
+        """The six weight casts of block b in one launch (skipped on the
+        device when the cache flag is set), when they are grouped."""
+        if not self.group_w:
+            return
+        st = self.state
+        self.dsl.fp8_cast_transpose_amax_group(
+            [(self.w[b][l], self._sl(st.scale, self.rec(b, l, R_W)), self.qw[b][l],
+              self._sl(st.amax_cur, self.rec(b, l, R_W))) for l in range(len(self.lin))],
+            noop_flag=self.flag)
+
     def _linear(self, b, l, out=None):
-        """Weight cast (skipped on the device when the cache flag is set) and
-        the FP8 product of linear l of block b, its input already cast."""
-        r, st = self.rec(b, l, R_W), self.state
+        """The FP8 product of linear l of block b, its input already cast; its
+        weight cast first unless the block's weights were cast as a group
+        (either way skipped on the device when the cache flag is set)."""
         qw = self.qw[b][l]
-        self.dsl.fp8_cast_transpose_amax(self.w[b][l], self._sl(st.scale, r), qw,
-                                         self._sl(st.amax_cur, r), noop_flag=self.flag)
+        if not self.group_w:
+            r, st = self.rec(b, l, R_W), self.state
+            self.dsl.fp8_cast_transpose_amax(self.w[b][l], self._sl(st.scale, r), qw,
+                                             self._sl(st.amax_cur, r), noop_flag=self.flag)
         y = self.out[l] if out is None else out
         self.dsl.fp8_linear_fwd(self.qx[l][b], qw, self.b16[b][l], y, workspace=self.gemm_ws)
         if self.probe is not None:
@@ -561,6 +584,7 @@ class ToyStack:
         self._cast_in(0, L_MOD, x)
         h = x
         for b in range(self.blocks):
+            self._cast_weights(b)
             m = self._linear(b, L_MOD, out=self.mod_out[b])
             self._produce(b, L_SELF, self.mod_op, h, m[:, :H], m[:, H:2 * H], h1, fused)
             s = self._linear(b, L_SELF)
@@ -726,7 +750,8 @@ def toy_stack_forward(dsl, workloads, blocks: int = 32, reps: int = 3, tokens: i
     flop = 2 * Mt * sum(fin * fout for fin, fout, _ in stack.lin) * blocks
     out = {k: round(v, 3) for k, v in res.items()}
     out.update({"blocks": blocks, "tokens": Mt, "gemm_flop": flop,
-                "library_launches_per_forward": blocks * 18 + 1,
+                "library_launches_per_forward": blocks * (13 if stack.group_w else 18) + 1,
+                "grouped_weight_casts": stack.group_w,
                 "graph_fused_producers_gemm_tflops":
                     round(flop / (res["graph_fused_producers_ms"] * 1e-3) / 1e12, 1),
                 "nonfinite_outputs": nonfinite})

@@ -39,7 +39,8 @@ __all__ = [
     "fp8_cast_transpose_dynamic", "fp8_linear_fwd_fp8out",
     "fp8_cast_transpose_amax_dbias_noalloc", "NOALLOC_SCRATCH_BYTES",
     "fp8_cast_transpose_amax_cached", "fp8_reference_copy", "fp8_produce_modulate_backward",
-    "fp8_gemm_workspace_bytes", "library_path", "lib",
+    "fp8_gemm_workspace_bytes", "fp8_cast_transpose_amax_group", "CAST_GROUP_MAX",
+    "library_path", "lib",
 ]
 
 E4M3 = 0
@@ -51,6 +52,7 @@ PRODUCE_ADD = 2
 PRODUCE_ADD2 = 3
 PRODUCE_MODULATE_FINITE = 4      # the library's addition: non-finite quotients -> +0
 NOALLOC_SCRATCH_BYTES = 4 << 20     # FP8DSL_NOALLOC_SCRATCH_BYTES
+CAST_GROUP_MAX = 8                  # FP8DSL_CAST_GROUP_MAX
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libfp8dsl.so")
@@ -72,6 +74,19 @@ class _Desc(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+    ]
+
+
+class _GroupItem(ctypes.Structure):
+    """Mirror of fp8_cast_group_item_t."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("ld", ctypes.c_int64),
+        ("scale", ctypes.c_void_p),
+        ("out", ctypes.POINTER(_Desc)),
+        ("amax_cur", ctypes.c_void_p),
     ]
 
 
@@ -108,6 +123,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_linear_fwd_fp8out.argtypes = [dp, dp, vp, vp, dp, vp, vp]
         L.fp8_linear_dgrad.argtypes = [dp, dp, vp, vp]
         L.fp8_linear_wgrad.argtypes = [dp, dp, vp, i32, vp]
+        L.fp8_cast_transpose_amax_group.argtypes = [i32, ctypes.POINTER(_GroupItem), i32, vp, vp]
+        L.fp8_cast_transpose_amax_group.restype = ctypes.c_int
         L.fp8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8_gemm_workspace_bytes.restype = i64
         L.fp8_linear_fwd_ws.argtypes = [dp, dp, vp, vp, vp, i64, vp]
@@ -288,6 +305,41 @@ def fp8_cast_transpose_amax(x: torch.Tensor, scale: torch.Tensor, out: Float8Ten
                                          _ptr(amax_cur, torch.float32, "amax_cur"),
                                          _ptr(noop_flag, torch.int32, "noop_flag"),
                                          _stream(stream)), "fp8_cast_transpose_amax")
+
+
+def fp8_cast_transpose_amax_group(items, noop_flag: Optional[torch.Tensor] = None,
+                                  stream=None) -> None:
+    """Cast several tensors in one launch, each exactly as
+    fp8_cast_transpose_amax(x, scale, out, amax_cur) casts it.  `items` is a
+    sequence of (x, scale, out, amax_cur) tuples, 1 to CAST_GROUP_MAX of them,
+    with one source dtype (bf16 or fp32), one FP8 format and the same outputs
+    (codes, transpose or both) throughout."""
+    items = list(items)
+    if not 1 <= len(items) <= CAST_GROUP_MAX:
+        raise ValueError(f"a group holds 1 to {CAST_GROUP_MAX} tensors")
+    _need_scalar(noop_flag, "noop_flag")
+    dtypes = {x.dtype for x, _, _, _ in items}
+    if len(dtypes) != 1 or not dtypes <= {torch.bfloat16, torch.float32}:
+        raise TypeError("every source must be bf16, or every source fp32")
+    src = DTYPE_BF16 if dtypes == {torch.bfloat16} else DTYPE_FP32
+    arr = (_GroupItem * len(items))()
+    descs = []
+    for k, (x, scale, out, amax_cur) in enumerate(items):
+        _need_scalar(scale, "scale")
+        _need_scalar(amax_cur, "amax_cur")
+        if x.dim() != 2 or x.stride(1) != 1:
+            raise ValueError("x must be 2-D with unit stride in the last dimension")
+        if not x.is_cuda:
+            raise ValueError("x must be a device tensor")
+        d = out.desc()
+        descs.append(d)
+        arr[k] = _GroupItem(x.data_ptr(), x.shape[0], x.shape[1], _row_stride(x),
+                            _ptr(scale, torch.float32, "scale"), ctypes.pointer(d),
+                            _ptr(amax_cur, torch.float32, "amax_cur"))
+    _check(lib().fp8_cast_transpose_amax_group(src, arr, len(items),
+                                               _ptr(noop_flag, torch.int32, "noop_flag"),
+                                               _stream(stream)),
+           "fp8_cast_transpose_amax_group")
 
 
 def fp8_cast_transpose_amax_cached(x: torch.Tensor, scale: torch.Tensor, out: Float8Tensor,

@@ -173,6 +173,72 @@ int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t co
                                                 noop_flag, nullptr, 0, s));
 }
 
+int fp8_cast_transpose_amax_group(int32_t src, const fp8_cast_group_item_t *items, int32_t count,
+                                  const int32_t *noop_flag, fp8_stream_t stream) {
+    if (items == nullptr) return FP8_ERR_NULL;
+    if (count < 1 || count > FP8DSL_CAST_GROUP_MAX) return FP8_ERR_ARG;
+    // Every check first: nothing is enqueued on an error.
+    CastGroupArgs args{};
+    args.n = 0;
+    int64_t tiles = 0;
+    // One format for all; the same outputs asked of every non-empty item (an
+    // empty item writes no codes, whatever its pointers).
+    const fp8_tensor_t *first_out = nullptr;
+    for (int i = 0; i < count; ++i) {
+        const fp8_cast_group_item_t &it = items[i];
+        if (int e = check_cast(it.x, src, it.rows, it.cols, it.ld, it.scale, it.out)) return e;
+        if (it.out->fmt != items[0].out->fmt) return FP8_ERR_ARG;
+        if (it.rows == 0 || it.cols == 0) continue;
+        if (first_out == nullptr) {
+            first_out = it.out;
+        } else if ((it.out->data == nullptr) != (first_out->data == nullptr) ||
+                   (it.out->data_t == nullptr) != (first_out->data_t == nullptr)) {
+            return FP8_ERR_ARG;
+        }
+    }
+    int64_t all_tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        for (int j = 0; j < i; ++j) {
+            const fp8_tensor_t *a = items[i].out, *b = items[j].out;
+            if ((a->data && a->data == b->data) || (a->data_t && a->data_t == b->data_t))
+                return FP8_ERR_ARG;
+        }
+        all_tiles += ((items[i].rows + 127) / 128) * ((items[i].cols + 127) / 128);
+    }
+    if (all_tiles > INT32_MAX) return FP8_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < count; ++i) {
+        const fp8_cast_group_item_t &it = items[i];
+        if (it.rows == 0 || it.cols == 0) {
+            // Nothing to cast; the snapshot is still taken.
+            if (it.out->scale_inv) {
+                if (int e = status_of(launch_scale_inv_only(it.scale, it.out->scale_inv,
+                                                            noop_flag, s)))
+                    return e;
+            }
+            continue;
+        }
+        CastGroupItem &g = args.item[args.n];
+        g.x = it.x;
+        g.rows = it.rows;
+        g.cols = it.cols;
+        g.ld = it.ld;
+        g.tiles_c = (it.cols + 127) / 128;
+        g.scale = it.scale;
+        g.q = it.out->data;
+        g.qt = it.out->data_t;
+        g.amax_cur = it.amax_cur;
+        g.scale_inv = it.out->scale_inv;
+        args.first[args.n] = tiles;
+        tiles += ((it.rows + 127) / 128) * g.tiles_c;
+        ++args.n;
+    }
+    for (int i = args.n; i <= FP8DSL_CAST_GROUP_MAX; ++i) args.first[i] = tiles;
+    if (args.n == 0) return FP8_OK;   // only empty items: their snapshots are taken
+    return status_of(launch_cast_group(args, src, first_out->fmt, first_out->data != nullptr,
+                                       first_out->data_t != nullptr, noop_flag, false, s));
+}
+
 int fp8_cast_transpose_amax_cached(const void *x, int32_t src, int64_t rows, int64_t cols,
                                    int64_t ld, const float *scale, const fp8_tensor_t *out,
                                    float *amax_cur, const int32_t *noop_flag,

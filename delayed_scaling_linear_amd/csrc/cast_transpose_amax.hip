@@ -506,14 +506,16 @@ cast_transpose_amax_kernel(
 // tensors with more than two tiles per resident persistent workgroup (there
 // it beats the persistent kernel; below that the persistent kernel's
 // overlap of one tile's loads with the previous tile's stores wins).
+// Tile t (row-major over tiles_c tile columns) of one tensor; scale_inv_out,
+// if not null, receives 1 / scale (the caller passes it to one workgroup).
 template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
-cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
-                 const float *__restrict__ scale_ptr, uint8_t *__restrict__ q,
-                 uint8_t *__restrict__ qt, float *__restrict__ amax_cur,
-                 float *__restrict__ scale_inv_out, const int32_t *__restrict__ noop,
-                 int64_t tiles_c, int cached) {
-    if (noop != nullptr && *noop != 0) return;
+__device__ __forceinline__ void cast_one_tile(const void *__restrict__ xv, int64_t rows,
+                                              int64_t cols, int64_t ld,
+                                              const float *__restrict__ scale_ptr,
+                                              uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
+                                              float *__restrict__ amax_cur,
+                                              float *__restrict__ scale_inv_out, int64_t t,
+                                              int64_t tiles_c, int cached) {
     __shared__ uint32_t lds_t[TILE * (TILE / 4)];      // the transposed tile, 16 KiB
     __shared__ uint32_t lds_amax[THREADS / 64];
     constexpr int K = SrcRow<SRC>::kChunks;
@@ -529,9 +531,8 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
 
     const float s = *scale_ptr;
     const bool s_special = !(fabsf(s) > 0.0f && fabsf(s) <= 3.402823466e38f);
-    if (blockIdx.x == 0 && tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
+    if (tid == 0 && scale_inv_out != nullptr) *scale_inv_out = 1.0f / s;
 
-    const int64_t t = blockIdx.x;
     const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
     const int64_t row0 = tr * TILE, col0 = tcn * TILE;
     const int64_t r = row0 + 4 * rg, c = col0 + 16 * cq;
@@ -564,6 +565,42 @@ cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_
     __syncthreads();
     if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
     if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
+}
+
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
+cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
+                 const float *__restrict__ scale_ptr, uint8_t *__restrict__ q,
+                 uint8_t *__restrict__ qt, float *__restrict__ amax_cur,
+                 float *__restrict__ scale_inv_out, const int32_t *__restrict__ noop,
+                 int64_t tiles_c, int cached) {
+    if (noop != nullptr && *noop != 0) return;
+    cast_one_tile<SRC, FMT, WANT_Q, WANT_QT>(xv, rows, cols, ld, scale_ptr, q, qt, amax_cur,
+                                             blockIdx.x == 0 ? scale_inv_out : nullptr,
+                                             (int64_t)blockIdx.x, tiles_c, cached);
+}
+
+// Several tensors in one launch, one workgroup per 128 x 128 tile of their
+// concatenated tile lists: workgroup b casts tile b - first[i] of tensor i,
+// first[i] <= b < first[i + 1], exactly as cast_tile_kernel casts it (the
+// same codes, transpose, amax and scale-inverse as one launch per tensor).
+// The tensors' parameters are kernel arguments (by value), so the launch
+// reads no host memory at run time and can be captured in a HIP graph.
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
+cast_tile_group_kernel(const CastGroupArgs args, const int32_t *__restrict__ noop, int cached) {
+    if (noop != nullptr && *noop != 0) return;
+    const int64_t b = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int k = 1; k < kCastGroupMax; ++k)
+        if (k < args.n && b >= args.first[k]) i = k;
+    const CastGroupItem &it = args.item[i];
+    const int64_t t = b - args.first[i];
+    cast_one_tile<SRC, FMT, WANT_Q, WANT_QT>(it.x, it.rows, it.cols, it.ld, it.scale, it.q,
+                                             it.qt, it.amax_cur,
+                                             t == 0 ? it.scale_inv : nullptr, t, it.tiles_c,
+                                             cached);
 }
 
 template <int SRC, int FMT>
@@ -657,6 +694,43 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
     return launch_src_fmt<FP8_DTYPE_FP32, FP8_E5M2>(x, rows, cols, ld, scale, q, qt, amax_cur,
                                                     scale_inv_out, noop, dbias_ws, ws_ld, cached,
                                                     stream);
+}
+
+template <int SRC, int FMT>
+hipError_t launch_group_src_fmt(const CastGroupArgs &args, int64_t tiles, bool want_q,
+                                bool want_qt, const int32_t *noop, bool cached,
+                                hipStream_t stream) {
+    auto launch = [&](auto wq, auto wqt) {
+        hipLaunchKernelGGL((cast_tile_group_kernel<SRC, FMT, decltype(wq)::value,
+                                                   decltype(wqt)::value>),
+                           dim3((unsigned)tiles), dim3(THREADS), 0, stream, args, noop,
+                           (int)cached);
+    };
+    using T1 = std::true_type;
+    using F1 = std::false_type;
+    if (want_q && want_qt) launch(T1{}, T1{});
+    else if (want_q) launch(T1{}, F1{});
+    else launch(F1{}, T1{});
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_group(const CastGroupArgs &args, int src, int fmt, bool want_q,
+                             bool want_qt, const int32_t *noop, bool cached,
+                             hipStream_t stream) {
+    const int64_t tiles = args.first[args.n];
+    if (tiles == 0) return hipSuccess;
+    if (src == FP8_DTYPE_BF16) {
+        if (fmt == FP8_E4M3)
+            return launch_group_src_fmt<FP8_DTYPE_BF16, FP8_E4M3>(args, tiles, want_q, want_qt,
+                                                                  noop, cached, stream);
+        return launch_group_src_fmt<FP8_DTYPE_BF16, FP8_E5M2>(args, tiles, want_q, want_qt, noop,
+                                                              cached, stream);
+    }
+    if (fmt == FP8_E4M3)
+        return launch_group_src_fmt<FP8_DTYPE_FP32, FP8_E4M3>(args, tiles, want_q, want_qt, noop,
+                                                              cached, stream);
+    return launch_group_src_fmt<FP8_DTYPE_FP32, FP8_E5M2>(args, tiles, want_q, want_qt, noop,
+                                                          cached, stream);
 }
 
 // Producer-fused cast.  The toy block of "CPU Overhead of te.Linear FP8

@@ -63,6 +63,27 @@ hipError_t launch_cast_transpose_amax(const void *x, int src, int64_t rows, int6
                                       const int32_t *noop, float *dbias_ws, int64_t ws_ld,
                                       hipStream_t stream, bool cached = false);
 
+// A grouped cast: up to kCastGroupMax tensors (one source type, one format,
+// the same outputs wanted) in one launch of cast_tile_group_kernel.  first[i]
+// is the first tile of tensor i in the launch (first[n] = all tiles), each
+// tensor's tiles row-major over tiles_c tile columns.
+constexpr int kCastGroupMax = FP8DSL_CAST_GROUP_MAX;
+struct CastGroupItem {
+    const void *x;
+    int64_t rows, cols, ld, tiles_c;
+    const float *scale;
+    uint8_t *q, *qt;
+    float *amax_cur, *scale_inv;
+};
+struct CastGroupArgs {
+    int n;
+    int64_t first[kCastGroupMax + 1];
+    CastGroupItem item[kCastGroupMax];
+};
+hipError_t launch_cast_group(const CastGroupArgs &args, int src, int fmt, bool want_q,
+                             bool want_qt, const int32_t *noop, bool cached,
+                             hipStream_t stream);
+
 // Measurement reference: copy `bytes` (a multiple of 16) from src to dst with
 // 16-byte loads and stores, `blocks` workgroups of 256 threads, loads
 // non-temporal or not.

@@ -15,7 +15,8 @@
  *   fp8_linear_dgrad         dX = dY W            E5M2 x E4M3 -> bf16
  *   fp8_linear_wgrad         dW = dY^T X          E5M2 x E4M3 -> fp32 / bf16
  *
- * and around it: the gradient cast with the bias gradient fused
+ * and around it: several casts in one launch (fp8_cast_transpose_amax_group),
+ * the gradient cast with the bias gradient fused
  * (fp8_cast_transpose_amax_dbias, also as a no-allocation entry point), the
  * toy block's elementwise producers fused into the cast and the modulation's
  * gradient (fp8_produce_cast_transpose_amax, fp8_produce_modulate_backward),
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FP8DSL_ABI_VERSION 10
+#define FP8DSL_ABI_VERSION 11
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP include. */
@@ -185,6 +186,47 @@ int fp8_scale_update(float *amax_history, float *amax_cur, float *scale, float *
 int fp8_cast_transpose_amax(const void *x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
                             const float *scale, const fp8_tensor_t *out, float *amax_cur,
                             const int32_t *noop_flag, fp8_stream_t stream);
+
+/* Tensors per fp8_cast_transpose_amax_group call. */
+#define FP8DSL_CAST_GROUP_MAX 8
+
+/* One tensor of a grouped cast: the arguments of fp8_cast_transpose_amax. */
+typedef struct fp8_cast_group_item {
+    const void *x;              /* device source [rows, cols], row stride ld   */
+    int64_t rows;
+    int64_t cols;
+    int64_t ld;
+    const float *scale;         /* device, 1 float                             */
+    const fp8_tensor_t *out;    /* host descriptor of the codes                */
+    float *amax_cur;            /* device, 1 float, or NULL                    */
+} fp8_cast_group_item_t;
+
+/*
+ * fp8_cast_transpose_amax_group -- several casts in one launch.
+ *
+ * The launches a model spends on casts are what the pages' fused layers
+ * remove ("CPU Overhead of te.Linear FP8 Layers": fewer kernel launches when
+ * casts are fused); a block's weights are cast together here.  Each item is
+ * cast exactly as fp8_cast_transpose_amax(item.x, src, item.rows, item.cols,
+ * item.ld, item.scale, item.out, item.amax_cur, noop_flag) casts it (the same
+ * codes, transpose, amax and scale-inverse snapshot), all in one kernel
+ * launch with one workgroup per 128 x 128 tile.
+ *
+ * src        FP8_DTYPE_BF16 or FP8_DTYPE_FP32, for every item.
+ * items      host array of `count` items, 1 <= count <= FP8DSL_CAST_GROUP_MAX;
+ *            read during the call only.  Every item's out->fmt must be the
+ *            same, and so must the outputs it asks for (data, data_t or both:
+ *            NULL or not alike across the items); items may not share
+ *            outputs.  An item with no rows or columns only takes its
+ *            scale-inverse snapshot (one more small launch).
+ * noop_flag  as fp8_cast_transpose_amax: skips every item.
+ * Constraints per item as fp8_cast_transpose_amax.
+ * Errors: those of fp8_cast_transpose_amax for any item (nothing is enqueued
+ * then); FP8_ERR_ARG for a count out of range or items that differ in
+ * format or outputs; FP8_ERR_NULL for a NULL item array.
+ */
+int fp8_cast_transpose_amax_group(int32_t src, const fp8_cast_group_item_t *items, int32_t count,
+                                  const int32_t *noop_flag, fp8_stream_t stream);
 
 /*
  * fp8_cast_transpose_amax_cached -- fp8_cast_transpose_amax reading its

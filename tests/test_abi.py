@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
                  "fp8_linear_fwd_fp8out", "fp8_cast_transpose_amax_dbias_noalloc",
                  "fp8_cast_transpose_amax_cached", "fp8_reference_copy",
                  "fp8_produce_modulate_backward", "fp8_gemm_workspace_bytes",
-                 "fp8_linear_fwd_ws", "fp8_linear_dgrad_ws", "fp8_linear_wgrad_ws"):
+                 "fp8_linear_fwd_ws", "fp8_linear_dgrad_ws", "fp8_linear_wgrad_ws",
+                 "fp8_cast_transpose_amax_group"):
         assert want in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_only_calls():
-    assert dsl.fp8_abi_version() == 10
+    assert dsl.fp8_abi_version() == 11
     assert dsl.fp8_status_string(0) == "FP8_OK"
     assert "SHAPE" in dsl.fp8_status_string(-2)
     assert "unknown" in dsl.fp8_status_string(-99)
@@ -114,6 +115,51 @@ def test_validation_rejects_before_device_use():
     assert L.fp8_linear_wgrad(byref(dy), byref(_desc(64, 48)), 0x5000, 2, None) == -5
     assert L.fp8_linear_wgrad(byref(dy), byref(_desc(48, 48)), 0x5000, 1, None) == -2
     assert L.fp8_linear_wgrad(byref(_desc(40, 32)), byref(_desc(40, 48)), 0x5000, 1, None) == -2
+
+
+def test_cast_group_validation():
+    """The grouped cast checks every item as the single cast does, then the
+    group: 1..8 items, one format, the same outputs on every non-empty item,
+    no shared outputs.  Nothing reaches a device."""
+    L = dsl.lib()
+    G = dsl._GroupItem
+    P = ctypes.POINTER(dsl._Desc)
+
+    def items(*specs):
+        descs = [d for _, d in specs]
+        arr = (G * len(specs))()
+        for k, ((rows, cols), d) in enumerate(specs):
+            arr[k] = G(0x4000 + 0x10000 * k, rows, cols, cols, 0x10, ctypes.pointer(d), 0)
+        return arr, descs
+
+    call = lambda arr, n, src=0: L.fp8_cast_transpose_amax_group(src, arr, n, None, None)
+    ok = lambda r, c, **kw: ((r, c), _desc(r, c, data=0x100000 + 0x1000 * r + c,
+                                            data_t=0x200000 + 0x1000 * r + c, **kw))
+    arr, keep = items(ok(32, 48))
+    assert L.fp8_cast_transpose_amax_group(0, None, 1, None, None) == -1
+    assert call(arr, 0) == -5
+    arr9, keep9 = items(*[ok(32, 16 * (k + 1)) for k in range(9)])
+    assert call(arr9, 9) == -5
+    # an item's own errors: a shape not a multiple of 16, a bad source dtype
+    arr, keep = items(ok(32, 48), ((32, 40), _desc(32, 40)))
+    assert call(arr, 2) == -2
+    arr, keep = items(ok(32, 48))
+    assert call(arr, 1, src=2) == -5
+    # the group's: mixed formats, mixed outputs, shared outputs
+    arr, keep = items(ok(32, 48), ok(64, 48, fmt=1))
+    assert call(arr, 2) == -5
+    arr, keep = items(ok(32, 48), ((64, 48), _desc(64, 48, data=0x300000, data_t=0)))
+    assert call(arr, 2) == -5
+    arr, keep = items(((32, 48), _desc(32, 48, data=0x300000, data_t=0x310000)),
+                      ((64, 48), _desc(64, 48, data=0x300000, data_t=0x320000)))
+    assert call(arr, 2) == -5
+    # an empty item may carry any output pointers: only empty items, no
+    # scale-inverse to take -> nothing to enqueue
+    arr, keep = items(((0, 48), _desc(0, 48, data=0, data_t=0, sinv=0)),
+                      ((0, 16), _desc(0, 16, data=0x300000, data_t=0, sinv=0)))
+    assert call(arr, 2) == 0
+    with pytest.raises(ValueError):
+        dsl.fp8_cast_transpose_amax_group([])
 
 
 def test_split_product_workspace_validation():

@@ -277,6 +277,30 @@ def test_fused_producers_match_torch_glue(modulate):
         assert torch.equal(getattr(a.state, name), getattr(b.state, name)), name
 
 
+@pytest.mark.parametrize("tokens", [1024, 8192])
+def test_grouped_weight_casts_match_per_linear_casts(tokens):
+    """A block's six weight casts in one grouped launch give the bits of six
+    casts each right before its product: outputs, codes of every weight and
+    the whole scale state, over two steps (the second with updated scales)
+    and a third with the cached-weights flag set."""
+    x = _x(23) if tokens == 8192 else _x(23)[:tokens].contiguous()
+    a = ToyStack(dsl, workloads, 2, tokens=tokens, group_weight_casts=False)
+    b = ToyStack(dsl, workloads, 2, tokens=tokens, group_weight_casts=True)
+    for step in range(3):
+        if step == 2:
+            a.flag.fill_(1)
+            b.flag.fill_(1)
+        ya = a.forward(x)
+        yb = b.forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16)), f"step {step}: output"
+        for blk in range(2):
+            for l in range(len(a.lin)):
+                assert torch.equal(a.qw[blk][l].data, b.qw[blk][l].data), f"step {step}: codes"
+        for name in ("amax_history", "scale", "scale_inv"):
+            assert torch.equal(getattr(a.state, name), getattr(b.state, name)), name
+
+
 def test_graph_capture_replays_match_eager():
     """One delayed-scaling iteration of one linear (two casts, the forward
     GEMM, the scale update) captured in a HIP graph and replayed three times,
