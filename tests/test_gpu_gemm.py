@@ -398,3 +398,33 @@ def test_nan_and_inf_operands(M, N, K, fa, fb, out):
     assert stats["n_nonfinite"] >= N + M          # a NaN row and a NaN column at least
     if fa == 1:
         assert np.isinf(ref).any()                # the infinities really were exercised
+
+
+@pytest.mark.parametrize("M,N", [(1024, 2048), (1000, 2056), (2048, 2048), (2000, 2056)])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_direct_to_lds_small_kernel_equals_register_staged(M, N, out):
+    """The two small kernels run the same MFMA sequence, so they agree value
+    for value.  K = 2048 takes the direct-to-LDS kernel; the same operands
+    with 16 zero columns appended (K = 2064, a K tail) take the
+    register-staged one, whose last step adds exact zeros."""
+    K = 2048
+    A = workloads.random_fp8_codes((M, K), M + 31, 0)
+    B = workloads.random_fp8_codes((N, K), N + 37, 1)
+    pad = lambda t: torch.cat([t, torch.zeros(t.shape[0], 16, dtype=torch.uint8)], dim=1)
+    sa, sb = 1.0 / 13.0, 9.0 / 448.0
+    if out == "bf16":
+        bias = _bias(N, N + 2).to(DEV)
+        y1 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        y2 = torch.empty_like(y1)
+        dsl.fp8_linear_fwd(_f8(A, 0, sa), _f8(B, 1, sb), bias, y1)
+        dsl.fp8_linear_fwd(_f8(pad(A), 0, sa), _f8(pad(B), 1, sb), bias, y2)
+    else:
+        si = lambda v: torch.tensor([v], device=DEV)
+        y1 = torch.empty(M, N, dtype=torch.float32, device=DEV)
+        y2 = torch.empty_like(y1)
+        for a, b_, y in ((A, B, y1), (pad(A), pad(B), y2)):
+            k = a.shape[1]
+            dsl.fp8_linear_wgrad(dsl.Float8Tensor(None, a.to(DEV), si(sa), 0, k, M),
+                                 dsl.Float8Tensor(None, b_.to(DEV), si(sb), 1, k, N), y)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
