@@ -870,11 +870,14 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
 // largest positive t, NaN above inf) and unsigned (the most negative t); a
 // block's key is max(kpos, kneg & 0x7FFFFFFF).  Columns past N hold t = 0
 // (operand rows and bias read as zero there), so only rows past M (t =
-// bias) are masked, once per block.  A NaN t gets 0x7F | sign on the rare
-// path of the group of four that holds it (or, unfolded, always: the scale
-// itself may make NaN products).
+// bias) are masked, once per block.  The words are first encoded without
+// the NaN rule; when a key shows a NaN t in any lane of the wave (or the
+// scale is not folded: the scale itself may make NaN products), the wave
+// encodes the tile again with it, a NaN t getting 0x7F | sign.  One
+// wave-uniform branch per tile, taken only on NaN data, instead of the rule
+// evaluated and selected for every value.
 template <int OUT, bool HAS_BIAS>
-__device__ __forceinline__ uint32_t stage_wave_tile_q(const v16f (&acc)[4][4], uint8_t *stg,
+__device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t *stg,
                                                       const uint8_t *bias_lds, int lane, float s,
                                                       float so, bool fold, int M, int r0) {
     constexpr int FMT = q_fmt<OUT>();
@@ -883,15 +886,15 @@ __device__ __forceinline__ uint32_t stage_wave_tile_q(const v16f (&acc)[4][4], u
     const float sm = fold ? s * so : s;       // multiplier of the accumulator
     const float se = fold ? 1.0f : so;        // the encode's own scale
     const float sb = fold ? so : 1.0f;        // multiplier of the bias
-    auto bias4 = [&](int j, int g, float (&bv)[4]) {
+    auto bias4 = [&](int j, int g, float mul, float (&bv)[4]) {
         bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
         if constexpr (HAS_BIAS) {
             const u32x2 b2 = *reinterpret_cast<const u32x2 *>(
                 bias_lds + 2 * (j * 32 + 8 * g + 4 * half));
-            bv[0] = __uint_as_float(b2.x << 16) * sb;
-            bv[1] = __uint_as_float(b2.x & 0xFFFF0000u) * sb;
-            bv[2] = __uint_as_float(b2.y << 16) * sb;
-            bv[3] = __uint_as_float(b2.y & 0xFFFF0000u) * sb;
+            bv[0] = __uint_as_float(b2.x << 16) * mul;
+            bv[1] = __uint_as_float(b2.x & 0xFFFF0000u) * mul;
+            bv[2] = __uint_as_float(b2.y << 16) * mul;
+            bv[3] = __uint_as_float(b2.y & 0xFFFF0000u) * mul;
         }
     };
     auto word_addr = [&](int i, int j, int g) {
@@ -905,21 +908,48 @@ __device__ __forceinline__ uint32_t stage_wave_tile_q(const v16f (&acc)[4][4], u
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             float bv[4];
-            bias4(j, g, bv);
+            bias4(j, g, sb, bv);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float t[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) t[q] = acc[i][j][4 * g + q] * sm + bv[q];
-                uint32_t w = encode4<FMT>(t[0], t[1], t[2], t[3], se);
+                const uint32_t w = encode4<FMT>(t[0], t[1], t[2], t[3], se);
                 const int32_t p = max(max((int32_t)__float_as_uint(t[0]), (int32_t)__float_as_uint(t[1])),
                                       max((int32_t)__float_as_uint(t[2]), (int32_t)__float_as_uint(t[3])));
                 const uint32_t n = max(max(__float_as_uint(t[0]), __float_as_uint(t[1])),
                                        max(__float_as_uint(t[2]), __float_as_uint(t[3])));
-                if (!fold || p > 0x7F800000 || n > 0xFF800000u) w = patch_nan4(w, t, se);
                 *reinterpret_cast<uint32_t *>(word_addr(i, j, g)) = w;
                 kpos[i] = max(kpos[i], p);
                 kneg[i] = max(kneg[i], n);
+            }
+        }
+    }
+    bool nan_seen = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nan_seen |= kpos[i] > 0x7F800000 || kneg[i] > 0xFF800000u;
+    if (!fold || __builtin_amdgcn_ballot_w64(nan_seen) != 0) {
+        // The same values again, read afresh from the accumulator registers:
+        // the empty asm hides that they are unchanged, so the compiler does
+        // not keep the first loop's copies of all 256 alive across the branch.
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float bv[4];
+                bias4(j, g, sb, bv);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float t[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) t[q] = acc[i][j][4 * g + q] * sm + bv[q];
+                    const uint32_t w = encode4<FMT>(t[0], t[1], t[2], t[3], se);
+                    *reinterpret_cast<uint32_t *>(word_addr(i, j, g)) = patch_nan4(w, t, se);
+                }
             }
         }
     }

@@ -260,6 +260,55 @@ def test_specials_nan_rows_saturation_and_k_zero():
     assert float(a[0]) == float(am0)
 
 
+def test_large_path_nan_rows_and_a_scale_outside_the_folding_range():
+    """The large-tile kernel encodes a tile without the NaN rule and encodes
+    it again with the rule only where a wave met a NaN, or for every tile
+    when the output scale is outside the range it folds into the multiply.
+    4096 x 4096 x 256 (large-tile path): a NaN row and an inf row planted in
+    a few tiles, every code against the oracle; then operands scaled by
+    2^-33 each with output scale 2^61 (not folded), every code against the
+    oracle's."""
+    M, N, K = 4096, 4096, 256
+    A = workloads.random_fp8_codes((M, K), 71, oracle.E5M2)
+    B = workloads.random_fp8_codes((N, K), 72, oracle.E4M3)
+    A[7, 9] = 0x7F                         # NaN (E5M2): row 7 is NaN
+    A[3001, 5] = 0x7C                      # +inf: row 3001 NaN where the weight is 0
+    B[:, 5] = (B[:, 5] & 0x80) | 0x38      # +-1 at k = 5, but for two zeros
+    B[100, 5] = 0x00
+    B[2900, 5] = 0x80
+    bias = workloads.normal_bf16((N,), 0.5, 73)
+    sa, sb = np.float32(1 / 61.0), np.float32(1 / 9.0)
+    codes_ref, v_ref, amax_ref, _ = oracle.gemm_nt_fp8out(A.numpy(), 1, B.numpy(), 0, sa, sb,
+                                                          1.0, oracle.E4M3, bias=bits16(bias))
+    got, amax, _ = _run(A, 1, B, 0, float(sa), float(sb), bias, 1.0, oracle.E4M3)
+    assert np.isnan(amax) and np.isnan(amax_ref)
+    assert ((got[7] & 0x7F) == 0x7F).all()
+    nan3 = (codes_ref[3001] & 0x7F) == 0x7F
+    assert nan3.sum() == 2
+    assert ((got[3001][nan3] & 0x7F) == 0x7F).all()
+    np.testing.assert_array_equal(got[3001][~nan3], codes_ref[3001][~nan3])
+    keep = np.array([i for i in range(M) if i not in (7, 3001)])
+    mag = oracle.gemm_nt(_abs_codes(A.numpy()[keep]), 1, _abs_codes(B.numpy()), 0, sa, sb,
+                         out_kind=oracle.OUT_FP32).astype(np.float64)
+    mag += np.abs(oracle.bf16_bits_to_f32(bits16(bias)).astype(np.float64))[None, :]
+    _check_codes(got[keep].ravel(), v_ref[keep].ravel(), mag.ravel(), K, 1.0, oracle.E4M3,
+                 "large path, rows without NaN")
+    # A scale the kernel does not fold: v ~ 2^-60, v * 2^61 in range.
+    A2 = workloads.random_fp8_codes((M, K), 74, oracle.E4M3)
+    sa2 = sb2 = np.float32(2.0 ** -33)
+    scale = 2.0 ** 61
+    codes_ref, v_ref, amax_ref, _ = oracle.gemm_nt_fp8out(A2.numpy(), 0, B.numpy(), 0, sa2, sb2,
+                                                          scale, oracle.E5M2)
+    assert (codes_ref & 0x7F).max() > 0x40, "the codes must span the format"
+    got, amax, sinv = _run(A2, 0, B, 0, float(sa2), float(sb2), None, scale, oracle.E5M2)
+    mag = oracle.gemm_nt(_abs_codes(A2.numpy()), 0, _abs_codes(B.numpy()), 0, sa2, sb2,
+                         out_kind=oracle.OUT_FP32).astype(np.float64)
+    emax = _check_codes(got.ravel(), v_ref.ravel(), mag.ravel(), K, scale, oracle.E5M2,
+                        "large path, scale 2^61")
+    assert abs(amax - float(amax_ref)) <= emax
+    assert sinv == np.float32(2.0 ** -61).view(np.uint32)
+
+
 def test_empty_output_takes_snapshot_only_and_amax_accumulates():
     # Sign-free operands: no cancellation, so S = v and the bound is
     # (2^-10 + (K + 2) 2^-23) v.
