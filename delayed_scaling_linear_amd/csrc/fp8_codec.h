@@ -44,7 +44,10 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, 
     b = __builtin_amdgcn_fmed3f(b * s, -T::kMax, T::kMax);
     c = __builtin_amdgcn_fmed3f(c * s, -T::kMax, T::kMax);
     d = __builtin_amdgcn_fmed3f(d * s, -T::kMax, T::kMax);
-    int w = T::template cvt<false>(a, b, 0);
+    // The first convert fills the low half and keeps the high half of its
+    // third operand, which the second convert then overwrites: any register
+    // serves, and a's (dead after) saves a move of zero.
+    int w = T::template cvt<false>(a, b, (int)__float_as_uint(a));
     w = T::template cvt<true>(c, d, w);
     return (uint32_t)w;
 }

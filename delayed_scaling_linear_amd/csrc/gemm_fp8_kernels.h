@@ -127,6 +127,12 @@ __device__ __forceinline__ bool scale_is_special(float so) {
 // An output scale that can be folded into the epilogue's multiply-add
 // (v * so computed as acc * (s * so) + bias * so) without leaving fp32's
 // comfortable range; any other scale takes the cast's own order.
+// IEEE 754-2019 maximum: NaN if either input is NaN (v_maximum3_f32 on
+// gfx950, which takes |x| as a source modifier).
+__device__ __forceinline__ float nan_max(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ bool scale_is_foldable(float so) {
     return fabsf(so) >= 0x1p-60f && fabsf(so) <= 0x1p60f;
 }
@@ -865,10 +871,10 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
 //     0, inf or NaN scale gives the cast's results).  `fold` is wave-uniform;
 //     one copy of the code serves both (two inlined copies push the kernel
 //     past its register budget).
-// Returns this lane's amax key of the tile's in-range outputs.  Keys are
-// two maxima of t's raw bit patterns per fragment row block: signed (the
-// largest positive t, NaN above inf) and unsigned (the most negative t); a
-// block's key is max(kpos, kneg & 0x7FFFFFFF).  Columns past N hold t = 0
+// Returns this lane's amax key of the tile's in-range outputs: the bits of
+// max |t|, taken per fragment row block with the NaN-propagating maximum
+// (one three-input instruction per two values), so a NaN t gives a key
+// above inf's bits.  Columns past N hold t = 0
 // (operand rows and bias read as zero there), so only rows past M (t =
 // bias) are masked, once per block.  The words are first encoded without
 // the NaN rule; when a key shows a NaN t in any lane of the wave (or the
@@ -901,8 +907,9 @@ __device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t
         const int q = i * 32 + frow;
         return stg + q * 128 + (((2 * j + (g >> 1)) ^ (q & 7)) << 4) + 8 * (g & 1) + 4 * half;
     };
-    int32_t kpos[4] = {0, 0, 0, 0};
-    uint32_t kneg[4] = {0, 0, 0, 0};
+    // Per block i, max |t| by the NaN-propagating maximum (a NaN t makes the
+    // key NaN, whose bits exceed those of inf).
+    float kabs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -914,20 +921,18 @@ __device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t
                 float t[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) t[q] = acc[i][j][4 * g + q] * sm + bv[q];
-                const uint32_t w = encode4<FMT>(t[0], t[1], t[2], t[3], se);
-                const int32_t p = max(max((int32_t)__float_as_uint(t[0]), (int32_t)__float_as_uint(t[1])),
-                                      max((int32_t)__float_as_uint(t[2]), (int32_t)__float_as_uint(t[3])));
-                const uint32_t n = max(max(__float_as_uint(t[0]), __float_as_uint(t[1])),
-                                       max(__float_as_uint(t[2]), __float_as_uint(t[3])));
+                // Folded, the encode's own scale is 1; unfolded, the second
+                // pass below rewrites every word with it.
+                const uint32_t w = encode4<FMT>(t[0], t[1], t[2], t[3], 1.0f);
                 *reinterpret_cast<uint32_t *>(word_addr(i, j, g)) = w;
-                kpos[i] = max(kpos[i], p);
-                kneg[i] = max(kneg[i], n);
+                kabs[i] = nan_max(nan_max(kabs[i], fabsf(t[0])), fabsf(t[1]));
+                kabs[i] = nan_max(nan_max(kabs[i], fabsf(t[2])), fabsf(t[3]));
             }
         }
     }
     bool nan_seen = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nan_seen |= kpos[i] > 0x7F800000 || kneg[i] > 0xFF800000u;
+    for (int i = 0; i < 4; ++i) nan_seen |= __float_as_uint(kabs[i]) > 0x7F800000u;
     if (!fold || __builtin_amdgcn_ballot_w64(nan_seen) != 0) {
         // The same values again, read afresh from the accumulator registers:
         // the empty asm hides that they are unchanged, so the compiler does
@@ -956,7 +961,7 @@ __device__ __forceinline__ uint32_t stage_wave_tile_q(v16f (&acc)[4][4], uint8_t
     uint32_t key = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        if (r0 + i * 32 + frow < M) key = max(key, max((uint32_t)kpos[i], kneg[i] & 0x7FFFFFFFu));
+        if (r0 + i * 32 + frow < M) key = max(key, __float_as_uint(kabs[i]));
     return key;
 }
 
