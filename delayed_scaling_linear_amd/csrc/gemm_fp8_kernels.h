@@ -103,13 +103,19 @@ struct QOut {
     float *scale_inv;
 };
 
-// Codes of four consecutive outputs (byte i = y_i); their amax key
-// (sign-cleared fp32 pattern: a NaN dominates) is folded into `key`.
+// IEEE 754-2019 maximum: NaN if either input is NaN (v_maximum3_f32 on
+// gfx950, which takes |x| as a source modifier).
+__device__ __forceinline__ float nan_max(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
+// Codes of four consecutive outputs (byte i = y_i); their amax key (the
+// bits of max |y|, a NaN above inf's) is folded into `key`.
 template <int OUT>
 __device__ __forceinline__ uint32_t encode_out4(float y0, float y1, float y2, float y3, float so,
                                                 bool so_special, uint32_t &key) {
-    const uint32_t k = max(max(__float_as_uint(y0) & 0x7FFFFFFFu, __float_as_uint(y1) & 0x7FFFFFFFu),
-                           max(__float_as_uint(y2) & 0x7FFFFFFFu, __float_as_uint(y3) & 0x7FFFFFFFu));
+    const uint32_t k = __float_as_uint(
+        nan_max(nan_max(nan_max(fabsf(y0), fabsf(y1)), fabsf(y2)), fabsf(y3)));
     key = max(key, k);
     uint32_t w = encode4<q_fmt<OUT>()>(y0, y1, y2, y3, so);
     if (so_special || k > 0x7F800000u) {
@@ -127,12 +133,6 @@ __device__ __forceinline__ bool scale_is_special(float so) {
 // An output scale that can be folded into the epilogue's multiply-add
 // (v * so computed as acc * (s * so) + bias * so) without leaving fp32's
 // comfortable range; any other scale takes the cast's own order.
-// IEEE 754-2019 maximum: NaN if either input is NaN (v_maximum3_f32 on
-// gfx950, which takes |x| as a source modifier).
-__device__ __forceinline__ float nan_max(float a, float b) {
-    return __builtin_elementwise_maximum(a, b);
-}
-
 __device__ __forceinline__ bool scale_is_foldable(float so) {
     return fabsf(so) >= 0x1p-60f && fabsf(so) <= 0x1p60f;
 }
