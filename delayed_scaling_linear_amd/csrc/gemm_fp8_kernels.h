@@ -42,8 +42,9 @@
 //     tiles than CUs), one workgroup per tile, v_mfma_f32_16x16x128_f8f6f4,
 //     operand stages written into LDS by buffer loads with the LDS flag, two
 //     or three stages in flight.
-//   * gemm_nt_kernel -- the other small products (K tails, FP8 outputs): the
-//     same tiles with loads staged through registers, double-buffered LDS.
+//   * gemm_nt_kernel -- the other small products (K tails, K = 128, 64-bit
+//     offsets): the same tiles with loads staged through registers,
+//     double-buffered LDS.
 //   * The split form: gemm_nt_dma_kernel over (tile, K part) units writing
 //     raw fp32 sums to a caller workspace, then splitk_reduce_kernel, for
 //     products with few tiles and a long contraction (gemm_split_parts).
@@ -1067,8 +1068,8 @@ template <int BM, int NS, int FA, int FB, int OUT, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_nt_sdma_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
     const float *__restrict__ sinv_a, const float *__restrict__ sinv_b,
-    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n) {
-    static_assert(OUT == FP8_DTYPE_BF16 || OUT == FP8_DTYPE_FP32, "bf16 or fp32 output");
+    const uint16_t *__restrict__ bias, void *__restrict__ Cv, int tiles_m, int tiles_n,
+    const QOut qo) {
     static_assert(NS >= 2 && NS <= 4, "stages");
     constexpr int BN = 128, WN = 2;
     constexpr int WTM = BM / 2, WTN = BN / WN;
@@ -1166,6 +1167,13 @@ __global__ __launch_bounds__(256) void gemm_nt_sdma_kernel(
     // Epilogue (the small kernel's): lane (l % 16, l / 16) holds output row
     // l % 16 of each 16-row fragment, columns 4 (l / 16) .. +3.
     const float s = (*sinv_a) * (*sinv_b);
+    float so = 0.f;
+    bool so_special = false;
+    if constexpr (is_q_out<OUT>()) {
+        so = *qo.scale;
+        so_special = scale_is_special(so);
+    }
+    uint32_t key = 0;
     const int orow = lane & 15;
     const int ocol = (lane >> 4) * 4;
 #pragma unroll
@@ -1194,12 +1202,18 @@ __global__ __launch_bounds__(256) void gemm_nt_sdma_kernel(
                 const u32x2 o = u32x2{f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16),
                                       f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16)};
                 *reinterpret_cast<u32x2 *>(C + (int64_t)gr * N + gc) = o;
+            } else if constexpr (is_q_out<OUT>()) {
+                uint8_t *C = static_cast<uint8_t *>(Cv);
+                *reinterpret_cast<uint32_t *>(C + (int64_t)gr * N + gc) =
+                    encode_out4<OUT>(y0, y1, y2, y3, so, so_special, key);
             } else {
                 float *C = static_cast<float *>(Cv);
                 *reinterpret_cast<v4f *>(C + (int64_t)gr * N + gc) = v4f{y0, y1, y2, y3};
             }
         }
     }
+    // All waves are past their last stage reads at the reduction's barrier.
+    if constexpr (is_q_out<OUT>()) finish_q_out(key, qo, so, reinterpret_cast<uint32_t *>(lds));
 }
 
 // Large-problem kernel for K % 128 == 0: persistent 256 x 256 tiles (one
@@ -1724,7 +1738,8 @@ constexpr int SDMA_STAGES_128 = 2;
 
 template <int BM, int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_sdma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
-                       const float *sb, const uint16_t *bias, void *C, hipStream_t stream) {
+                       const float *sb, const uint16_t *bias, void *C, const QOut &qo,
+                       hipStream_t stream) {
     constexpr int NS = BM == 64 ? SDMA_STAGES_64 : SDMA_STAGES_128;
     auto kern = gemm_nt_sdma_kernel<BM, NS, FA, FB, OUT, HAS_BIAS>;
     constexpr int lds_bytes = NS * (BM + 128) * BK;
@@ -1735,7 +1750,7 @@ hipError_t launch_sdma(const uint8_t *A, const uint8_t *B, int M, int N, int K, 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + 127) / 128;
     hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(256), lds_bytes, stream, A, B, M, N,
-                       K, sa, sb, bias, C, tiles_m, tiles_n);
+                       K, sa, sb, bias, C, tiles_m, tiles_n, qo);
     return hipGetLastError();
 }
 
@@ -1786,15 +1801,13 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
     // twice as many, so that more CUs share the K loop.
     const bool half = ((M + 127) / 128) * ((N + 127) / 128) < cus;
     // Whole 128-byte K stages and 32-bit operand offsets: the operand stages
-    // go straight into LDS (bf16 / fp32 outputs).
-    if constexpr (!is_q_out<OUT>()) {
-        if (fits32 && K >= 256 && K % 128 == 0) {
-            if (half)
-                return launch_sdma<64, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
-                                                              bias, C, stream);
-            return launch_sdma<128, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
-                                                           bias, C, stream);
-        }
+    // go straight into LDS.
+    if (fits32 && K >= 256 && K % 128 == 0) {
+        if (half)
+            return launch_sdma<64, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
+                                                          bias, C, qo, stream);
+        return launch_sdma<128, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias,
+                                                       C, qo, stream);
     }
     if (half)
         return launch_cfg<64, 128, 2, 2, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa,

@@ -309,6 +309,40 @@ def test_large_path_nan_rows_and_a_scale_outside_the_folding_range():
     assert sinv == np.float32(2.0 ** -61).view(np.uint32)
 
 
+@pytest.mark.parametrize("M,N", [(1000, 2048), (1040, 4112)])
+def test_direct_to_lds_small_kernel_codes_equal_register_staged(M, N):
+    """Both small kernels run the same MFMA sequence and the same FP8
+    epilogue, so codes, amax and scale-inverse agree bit for bit: K = 2048
+    takes the direct-to-LDS kernel (64 x 128 tiles for 1000 x 2048, 128 x 128
+    for 1040 x 4112), the same operands with 16 zero columns appended
+    (K = 2064, a K tail) the register-staged one."""
+    K = 2048
+    A = workloads.random_fp8_codes((M, K), M + 41, 0)
+    B = workloads.random_fp8_codes((N, K), N + 43, 1)
+    pad = lambda t: torch.cat([t, torch.zeros(t.shape[0], 16, dtype=torch.uint8)], dim=1)
+    bias = workloads.normal_bf16((N,), 0.5, N + 5)
+    sa, sb = np.float32(1 / 13.0), np.float32(9 / 448.0)
+    _, v_ref, _, _ = oracle.gemm_nt_fp8out(A.numpy(), 0, B.numpy(), 1, sa, sb, 1.0, oracle.E4M3,
+                                           bias=bits16(bias))
+    scale = _scale_for(v_ref, oracle.E4M3, 2.0)
+    print(f"sdma fp8out {M}x{N}x{K} scale {scale}", flush=True)
+    got1, amax1, sinv1 = _run(A, 0, B, 1, float(sa), float(sb), bias, scale, oracle.E4M3)
+    got2, amax2, sinv2 = _run(pad(A), 0, pad(B), 1, float(sa), float(sb), bias, scale,
+                              oracle.E4M3)
+    np.testing.assert_array_equal(got1, got2)
+    assert np.float32(amax1).view(np.uint32) == np.float32(amax2).view(np.uint32)
+    assert sinv1 == sinv2
+    # and against the oracle, within the rounding interval
+    mag = oracle.gemm_nt(_abs_codes(A.numpy()), 0, _abs_codes(B.numpy()), 1, sa, sb,
+                         out_kind=oracle.OUT_FP32).astype(np.float64)
+    mag += np.abs(oracle.bf16_bits_to_f32(bits16(bias)).astype(np.float64))[None, :]
+    codes_ref, v_ref, amax_ref, _ = oracle.gemm_nt_fp8out(A.numpy(), 0, B.numpy(), 1, sa, sb,
+                                                          scale, oracle.E4M3, bias=bits16(bias))
+    emax = _check_codes(got1.ravel(), v_ref.ravel(), mag.ravel(), K, scale, oracle.E4M3,
+                        f"sdma {M}x{N}")
+    assert abs(amax1 - float(amax_ref)) <= emax
+
+
 def test_empty_output_takes_snapshot_only_and_amax_accumulates():
     # Sign-free operands: no cancellation, so S = v and the bound is
     # (2^-10 + (K + 2) 2^-23) v.
