@@ -80,12 +80,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;   // NaN
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Output kinds beyond FP8_DTYPE_BF16 / FP8_DTYPE_FP32: FP8 codes.
 constexpr int OUT_E4M3 = 2;
 constexpr int OUT_E5M2 = 3;
@@ -355,9 +349,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(
             const float y3 = a.w * s + bv[3];
             if constexpr (OUT == FP8_DTYPE_BF16) {
                 uint16_t *C = static_cast<uint16_t *>(Cv);
-                const u32x2 o = u32x2{f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16),
-                                      f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16)};
-                *reinterpret_cast<u32x2 *>(C + (int64_t)gr * N + gc) = o;
+                const bf16x4 o = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                *reinterpret_cast<bf16x4 *>(C + (int64_t)gr * N + gc) = o;
             } else if constexpr (is_q_out<OUT>()) {
                 uint8_t *C = static_cast<uint8_t *>(Cv);
                 *reinterpret_cast<uint32_t *>(C + (int64_t)gr * N + gc) =
@@ -1199,9 +1192,8 @@ __global__ __launch_bounds__(256) void gemm_nt_sdma_kernel(
             const float y3 = a.w * s + bv[3];
             if constexpr (OUT == FP8_DTYPE_BF16) {
                 uint16_t *C = static_cast<uint16_t *>(Cv);
-                const u32x2 o = u32x2{f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16),
-                                      f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16)};
-                *reinterpret_cast<u32x2 *>(C + (int64_t)gr * N + gc) = o;
+                const bf16x4 o = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                *reinterpret_cast<bf16x4 *>(C + (int64_t)gr * N + gc) = o;
             } else if constexpr (is_q_out<OUT>()) {
                 uint8_t *C = static_cast<uint8_t *>(Cv);
                 *reinterpret_cast<uint32_t *>(C + (int64_t)gr * N + gc) =
