@@ -349,27 +349,72 @@ __device__ __forceinline__ void flush_amax(uint32_t key, float *amax_cur, uint32
 // Resident workgroups per CU: the double-buffered source needs 64 (bf16) or
 // 128 (fp32) registers per lane.
 // The bias-gradient variant needs its 16 column sums on top: two per CU.
-template <int SRC, bool DBIAS>
-constexpr int kWavesPerSimd = (SRC == FP8_DTYPE_BF16 && !DBIAS) ? 3 : 2;
+template <int SRC>
+constexpr int kWavesPerSimd = SRC == FP8_DTYPE_BF16 ? 3 : 2;
 
-// DBIAS: also the bias gradient's per-tile column sums of the unscaled source
-// (fp32): each lane adds its four rows in order, the eight row groups of a
-// wave meet in a butterfly of lane exchanges, the four waves in LDS in wave
-// order; tile (tr, tc) writes its 128 sums to dbias_ws[tr * ws_ld + 128 tc ..].
-// Every step has a fixed order, so the result is the same on every run.
-template <int SRC, int FMT, bool WANT_Q, bool WANT_QT, bool DBIAS>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<SRC, DBIAS>))) void
+// The bias gradient's per-tile column sums of the unscaled source (fp32),
+// taken by the one-tile cast: each lane adds its four rows in order, the
+// eight row groups of a wave meet in a butterfly of lane exchanges, the four
+// waves in LDS in wave order; tile (tr, tc) writes its 128 sums to
+// dbias_ws[tr * ws_ld + 128 tc ..].  Every step has a fixed order, so the
+// result is the same on every run.
+//   tile_col_sums_to_lds: a wave's sums of its 32 rows into d[0 .. 127]
+//   (written by the lanes of row group 0); rows past the tensor were loaded
+//   as zeros and add nothing.
+template <int SRC>
+__device__ __forceinline__ void tile_col_sums_to_lds(const SrcRow<SRC> (&src)[4], float *d,
+                                                     int lane, int cc) {
+    float cs[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float o[4];
+        src[0].get4(j, o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cs[4 * j + k] = o[k];
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float o[4];
+            src[i].get4(j, o);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) cs[4 * j + k] += o[k];
+        }
+#pragma unroll
+    for (int m = 8; m < 64; m *= 2)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) cs[k] += __shfl_xor(cs[k], m);
+    if ((lane >> 3) == 0) {
+#pragma unroll
+        for (int k = 0; k < 16; k += 4)
+            *reinterpret_cast<f32x4 *>(d + src_col<SRC>(cc, k)) =
+                f32x4{cs[k], cs[k + 1], cs[k + 2], cs[k + 3]};
+    }
+}
+
+//   tile_col_sums_out: after a barrier, the four waves' sums (d = the
+//   first wave's 128, the others at strides of 128) added in wave order
+//   into the tile's workspace row.
+__device__ __forceinline__ void tile_col_sums_out(const float *d, int tid, float *dbias_ws,
+                                                  int64_t ws_ld, int64_t tr, int64_t tcn) {
+    if (tid < TILE) {
+        const float sum = ((d[tid] + d[TILE + tid]) + d[2 * TILE + tid]) + d[3 * TILE + tid];
+        dbias_ws[tr * ws_ld + tcn * TILE + tid] = sum;
+    }
+}
+
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<SRC>))) void
 cast_transpose_amax_kernel(
     const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     const float *__restrict__ scale_ptr, uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
     float *__restrict__ amax_cur, float *__restrict__ scale_inv_out,
-    const int32_t *__restrict__ noop, int64_t tiles_c, int64_t ntiles,
-    float *__restrict__ dbias_ws, int64_t ws_ld, int cached) {
+    const int32_t *__restrict__ noop, int64_t tiles_c, int64_t ntiles, int cached) {
     if (noop != nullptr && *noop != 0) return;
 
     __shared__ uint32_t lds_t[2][TILE * (TILE / 4)];   // transposed tiles, 2 x 16 KiB
     __shared__ uint32_t lds_amax[THREADS / 64];
-    __shared__ float lds_db[DBIAS ? 2 * (THREADS / 64) * TILE : 1];   // [buffer][wave][column]
     constexpr int K = SrcRow<SRC>::kChunks;
     __shared__ uint32_t lds_rows[K == 4 ? (THREADS / 64) * ROW_STAGE_WORDS : 1];   // fp32 exchange
 
@@ -444,47 +489,8 @@ cast_transpose_amax_kernel(
                                                         c_cur, cols, cq, rg, lane,
                                                         lds_rows + (K == 4 ? wave * ROW_STAGE_WORDS : 0),
                                                         lds_t[u], key);
-                if constexpr (DBIAS) {
-                    // Rows past the tensor were loaded as zeros and add nothing.
-                    float cs[16];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float o[4];
-                        src[u][0].get4(j, o);
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) cs[4 * j + k] = o[k];
-                    }
-#pragma unroll
-                    for (int i = 1; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            float o[4];
-                            src[u][i].get4(j, o);
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) cs[4 * j + k] += o[k];
-                        }
-#pragma unroll
-                    for (int m = 8; m < 64; m *= 2)
-#pragma unroll
-                        for (int k = 0; k < 16; ++k) cs[k] += __shfl_xor(cs[k], m);
-                    if ((lane >> 3) == 0) {
-                        float *d = &lds_db[(u * (THREADS / 64) + wave) * TILE];
-#pragma unroll
-                        for (int k = 0; k < 16; k += 4)
-                            *reinterpret_cast<f32x4 *>(d + src_col<SRC>(cc, k)) =
-                                f32x4{cs[k], cs[k + 1], cs[k + 2], cs[k + 3]};
-                    }
-                }
                 __syncthreads();
                 if constexpr (WANT_QT) store_t(lds_t[u], t);
-                if constexpr (DBIAS) {
-                    if (tid < TILE) {
-                        const float *d = &lds_db[u * (THREADS / 64) * TILE + tid];
-                        const float sum = ((d[0] + d[TILE]) + d[2 * TILE]) + d[3 * TILE];
-                        const int64_t tr = t / tiles_c, tcn = t - tr * tiles_c;
-                        dbias_ws[tr * ws_ld + tcn * TILE + tid] = sum;
-                    }
-                }
                 t = tn;
                 r_cur = r_nxt;
                 c_cur = c_nxt;
@@ -508,16 +514,19 @@ cast_transpose_amax_kernel(
 // overlap of one tile's loads with the previous tile's stores wins).
 // Tile t (row-major over tiles_c tile columns) of one tensor; scale_inv_out,
 // if not null, receives 1 / scale (the caller passes it to one workgroup).
-template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT, bool DBIAS = false>
 __device__ __forceinline__ void cast_one_tile(const void *__restrict__ xv, int64_t rows,
                                               int64_t cols, int64_t ld,
                                               const float *__restrict__ scale_ptr,
                                               uint8_t *__restrict__ q, uint8_t *__restrict__ qt,
                                               float *__restrict__ amax_cur,
                                               float *__restrict__ scale_inv_out, int64_t t,
-                                              int64_t tiles_c, int cached) {
+                                              int64_t tiles_c, int cached,
+                                              float *__restrict__ dbias_ws = nullptr,
+                                              int64_t ws_ld = 0) {
     __shared__ uint32_t lds_t[TILE * (TILE / 4)];      // the transposed tile, 16 KiB
     __shared__ uint32_t lds_amax[THREADS / 64];
+    __shared__ float lds_db[DBIAS ? (THREADS / 64) * TILE : 1];   // [wave][column]
     constexpr int K = SrcRow<SRC>::kChunks;
     __shared__ uint32_t lds_rows[K == 4 ? (THREADS / 64) * ROW_STAGE_WORDS : 1];   // fp32 exchange
 
@@ -562,22 +571,25 @@ __device__ __forceinline__ void cast_one_tile(const void *__restrict__ xv, int64
     encode_block<SRC, FMT, WANT_Q, WANT_QT>(src, s, s_special, valid, q, r, c, cols, cq, rg, lane,
                                             lds_rows + (K == 4 ? wave * ROW_STAGE_WORDS : 0),
                                             lds_t, key);
+    if constexpr (DBIAS) tile_col_sums_to_lds<SRC>(src, &lds_db[wave * TILE], lane, cc);
     __syncthreads();
     if constexpr (WANT_QT) store_transposed(lds_t, qt, rows, cols, row0, col0, lane, wave);
+    if constexpr (DBIAS) tile_col_sums_out(lds_db, tid, dbias_ws, ws_ld, tr, tcn);
     if (amax_cur != nullptr) flush_amax(key, amax_cur, lds_amax, lane, wave, tid);
 }
 
-template <int SRC, int FMT, bool WANT_Q, bool WANT_QT>
+template <int SRC, int FMT, bool WANT_Q, bool WANT_QT, bool DBIAS>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
 cast_tile_kernel(const void *__restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
                  const float *__restrict__ scale_ptr, uint8_t *__restrict__ q,
                  uint8_t *__restrict__ qt, float *__restrict__ amax_cur,
                  float *__restrict__ scale_inv_out, const int32_t *__restrict__ noop,
-                 int64_t tiles_c, int cached) {
+                 int64_t tiles_c, int cached, float *__restrict__ dbias_ws, int64_t ws_ld) {
     if (noop != nullptr && *noop != 0) return;
-    cast_one_tile<SRC, FMT, WANT_Q, WANT_QT>(xv, rows, cols, ld, scale_ptr, q, qt, amax_cur,
-                                             blockIdx.x == 0 ? scale_inv_out : nullptr,
-                                             (int64_t)blockIdx.x, tiles_c, cached);
+    cast_one_tile<SRC, FMT, WANT_Q, WANT_QT, DBIAS>(xv, rows, cols, ld, scale_ptr, q, qt, amax_cur,
+                                                    blockIdx.x == 0 ? scale_inv_out : nullptr,
+                                                    (int64_t)blockIdx.x, tiles_c, cached,
+                                                    dbias_ws, ws_ld);
 }
 
 // Several tensors in one launch, one workgroup per 128 x 128 tile of their
@@ -615,44 +627,41 @@ hipError_t launch_src_fmt(const void *x, int64_t rows, int64_t cols, int64_t ld,
     const int64_t ntiles = tiles_r * tiles_c;
     // As many workgroups as fit on the chip at once, each looping over tiles
     // with the next tile's loads in flight; tensors with more than two tiles
-    // per resident workgroup: one workgroup per tile (cast_tile_kernel, or
-    // the persistent kernel when it also sums the bias gradient).
-    const int64_t resident =
-        (int64_t)cus * (dbias_ws ? kWavesPerSimd<SRC, true> : kWavesPerSimd<SRC, false>);
-    const bool per_tile = ntiles > 2 * resident;
-    if (per_tile && dbias_ws == nullptr) {
-        auto launch1 = [&](auto wq, auto wqt) {
+    // per resident workgroup, and every cast that also sums the bias
+    // gradient: one workgroup per tile (cast_tile_kernel).
+    const int64_t resident = (int64_t)cus * kWavesPerSimd<SRC>;
+    const bool per_tile = ntiles > 2 * resident || dbias_ws != nullptr;
+    if (per_tile) {
+        auto launch1 = [&](auto wq, auto wqt, auto db) {
             hipLaunchKernelGGL((cast_tile_kernel<SRC, FMT, decltype(wq)::value,
-                                                 decltype(wqt)::value>),
+                                                 decltype(wqt)::value, decltype(db)::value>),
                                dim3((unsigned)ntiles), dim3(THREADS), 0, stream, x, rows, cols,
                                ld, scale, q, qt, amax_cur, scale_inv_out, noop, tiles_c,
-                               (int)cached);
+                               (int)cached, dbias_ws, ws_ld);
         };
         using T1 = std::true_type;
         using F1 = std::false_type;
-        if (q && qt) launch1(T1{}, T1{});
-        else if (q) launch1(T1{}, F1{});
-        else launch1(F1{}, T1{});
+        auto by_layout1 = [&](auto db) {
+            if (q && qt) launch1(T1{}, T1{}, db);
+            else if (q) launch1(T1{}, F1{}, db);
+            else launch1(F1{}, T1{}, db);
+        };
+        if (dbias_ws) by_layout1(T1{});
+        else by_layout1(F1{});
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)(per_tile ? ntiles : std::min<int64_t>(ntiles, resident)));
-    auto launch = [&](auto wq, auto wqt, auto db) {
+    const dim3 grid((unsigned)std::min<int64_t>(ntiles, resident));
+    auto launch = [&](auto wq, auto wqt) {
         hipLaunchKernelGGL((cast_transpose_amax_kernel<SRC, FMT, decltype(wq)::value,
-                                                       decltype(wqt)::value,
-                                                       decltype(db)::value>),
+                                                       decltype(wqt)::value>),
                            grid, dim3(THREADS), 0, stream, x, rows, cols, ld, scale, q, qt,
-                           amax_cur, scale_inv_out, noop, tiles_c, ntiles, dbias_ws, ws_ld,
-                           (int)cached);
+                           amax_cur, scale_inv_out, noop, tiles_c, ntiles, (int)cached);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    auto by_layout = [&](auto db) {
-        if (q && qt) launch(T_{}, T_{}, db);
-        else if (q) launch(T_{}, F_{}, db);
-        else launch(F_{}, T_{}, db);
-    };
-    if (dbias_ws) by_layout(T_{});
-    else by_layout(F_{});
+    if (q && qt) launch(T_{}, T_{});
+    else if (q) launch(T_{}, F_{});
+    else launch(F_{}, T_{});
     return hipGetLastError();
 }
 

@@ -132,3 +132,31 @@ def test_dbias_codes_equal_plain_cast():
     torch.cuda.synchronize()
     assert torch.equal(out_a.data, out_b.data) and torch.equal(out_a.data_t, out_b.data_t)
     assert torch.equal(amax_a, amax_b) and torch.equal(out_a.scale_inv, out_b.scale_inv)
+
+
+def test_dbias_column_slices_equal_the_whole_source():
+    """Column sums are taken per 128 x 128 tile and then over tile rows, so a
+    column slice (a strided view of the same memory) gives the whole
+    source's sums for its columns.  [4096, 8192] against its eight
+    [4096, 1024] slices: dbias, codes and transpose bit for bit, with a NaN,
+    an inf and an inf - inf column planted; then the whole source against
+    the oracle."""
+    g = torch.Generator().manual_seed(17)
+    x = (torch.randn(4096, 8192, generator=g) * 0.01).to(torch.bfloat16)
+    x[5, 3] = float("nan")
+    x[77, 1500] = float("inf")
+    x[9, 4000] = float("inf")
+    x[4000, 4000] = float("-inf")
+    x_dev = x.to(DEV)
+    print("dbias column slices, [4096, 8192]", flush=True)
+    full_out, full_amax, full_db = _run(x_dev, 300.0, oracle.E5M2)
+    for j in range(8):
+        sl = x_dev[:, 1024 * j:1024 * (j + 1)]
+        out, amax, db = _run(sl, 300.0, oracle.E5M2)
+        cs = slice(1024 * j, 1024 * (j + 1))
+        assert torch.equal(db.view(torch.int32), full_db[cs].view(torch.int32)), f"slice {j}: dbias"
+        assert torch.equal(out.data, full_out.data[:, cs]), f"slice {j}: codes"
+        assert torch.equal(out.data_t, full_out.data_t[cs, :]), f"slice {j}: transpose"
+    v = full_db.cpu().numpy()
+    assert np.isnan(v[3]) and v[1500] == np.inf and np.isnan(v[4000])
+    _check(x, 300.0, oracle.E5M2)
