@@ -368,3 +368,45 @@ def test_empty_output_takes_snapshot_only_and_amax_accumulates():
     torch.cuda.synchronize()
     m = max(float(m1), float(m2))
     assert abs(float(a[0]) - m) <= (2.0 ** -10 + (64 + 2) * 2.0 * U) * m
+
+
+def test_graph_replay_matches_eager():
+    """The FP8-output forward captured in a HIP graph (large-tile path,
+    8192 x 8192 x 2048 with bias): three replays, each after the outputs and
+    the amax were reset by eager work, give the eager codes, amax and
+    scale-inverse bit for bit."""
+    M, N, K = 8192, 8192, 2048
+    A = workloads.random_fp8_codes((M, K), 91, 0).to(DEV)
+    B = workloads.random_fp8_codes((N, K), 92, 0).to(DEV)
+    bias = workloads.normal_bf16((N,), 0.5, 93).to(DEV)
+    x8, w8 = _f8(A, 0, 1 / 61.0), _f8(B, 0, 1 / 9.0)
+    s = torch.tensor([0.75], device=DEV)
+    y_e = dsl.Float8Tensor.empty(M, N, oracle.E4M3, transpose=False, device=DEV)
+    a_e = torch.zeros(1, device=DEV)
+    dsl.fp8_linear_fwd_fp8out(x8, w8, bias, s, y_e, a_e)
+    torch.cuda.synchronize()
+    y = dsl.Float8Tensor.empty(M, N, oracle.E4M3, transpose=False, device=DEV)
+    a = torch.zeros(1, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dsl.fp8_linear_fwd_fp8out(x8, w8, bias, s, y, a)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dsl.fp8_linear_fwd_fp8out(x8, w8, bias, s, y, a)
+    for rep in range(3):
+        y.data.fill_(0xAA)
+        y.scale_inv.fill_(-1.0)
+        a.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(y.data, y_e.data), f"replay {rep}: codes"
+        assert torch.equal(a.view(torch.int32), a_e.view(torch.int32)), f"replay {rep}: amax"
+        assert torch.equal(y.scale_inv.view(torch.int32), y_e.scale_inv.view(torch.int32)), \
+            f"replay {rep}: scale_inv"
