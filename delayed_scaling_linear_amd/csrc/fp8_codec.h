@@ -52,8 +52,9 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, 
     return (uint32_t)w;
 }
 
-// Rare path: a NaN product gets 0x7F | (sign(x) ^ sign(s)).  Only lanes that
-// saw a NaN source (or every lane, when the scale is 0, inf or NaN) run it.
+// Rare path: a NaN product gets 0x7F | (sign(x) ^ sign(s)).  Callers run it
+// only where a NaN source was seen (or everywhere, when the scale is 0, inf
+// or NaN).
 __device__ __forceinline__ uint32_t patch_nan4(uint32_t w, const float x[4], float s) {
     const uint32_t sbits = __float_as_uint(s);
 #pragma unroll

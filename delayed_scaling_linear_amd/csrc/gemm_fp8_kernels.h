@@ -862,9 +862,9 @@ __device__ __forceinline__ void out_hb(const u32x4 (&v)[8], const float (&b)[16]
 //     and converted, and the amax keys are of |t| (the caller divides by
 //     |so| once at the end).  Otherwise t = v = acc * s + bias and the encode
 //     multiplies by so, exactly as the cast does (the only order in which a
-//     0, inf or NaN scale gives the cast's results).  `fold` is wave-uniform;
-//     one copy of the code serves both (two inlined copies push the kernel
-//     past its register budget).
+//     0, inf or NaN scale gives the cast's results); that encode happens
+//     only in the second pass below, which unfolded tiles always take.
+//     `fold` is wave-uniform.
 // Returns this lane's amax key of the tile's in-range outputs: the bits of
 // max |t|, taken per fragment row block with the NaN-propagating maximum
 // (one three-input instruction per two values), so a NaN t gives a key
