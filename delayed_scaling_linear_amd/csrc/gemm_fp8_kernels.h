@@ -1798,15 +1798,19 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
     // tiles put two workgroups (two waves per SIMD) on a CU, or spread the
     // product over more CUs (measured: 1024 x 1024 x 4096 17.3 -> 14.4 us,
     // 512 x 2048 x 2048 10.3 -> 8.6, 1024 x 2048 x 2048 12.2 -> 11.8).
-    const bool half = ((M + 127) / 128) * ((N + 127) / 128) < cus;
+    const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const bool half = tiles128 < cus;
     const bool quarter = ((M + 63) / 64) * ((N + 127) / 128) <= cus;
     // Whole 128-byte K stages and 32-bit operand offsets: the operand stages
-    // go straight into LDS.
+    // go straight into LDS.  Exactly one 128 x 128 tile per CU also takes
+    // 64-row tiles there, two per CU (1024 x 4096 x 2048: 15.9 -> 14.7 us,
+    // 2048 x 2048 x 2048: 16.0 -> 14.7); at 1.5 or 2 tiles per CU the
+    // 128-row tiles stay faster (1024 x 6144 x 2048: 20.5 against 23.7).
     if (fits32 && K >= 256 && K % 128 == 0) {
         if (quarter)
             return launch_sdma<32, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
                                                           bias, C, qo, stream);
-        if (half)
+        if (tiles128 <= cus)
             return launch_sdma<64, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
                                                           bias, C, qo, stream);
         return launch_sdma<128, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb, bias,

@@ -60,19 +60,20 @@ def test_fwd_shapes_formats(M, N, K, fa, fb):
     (520, 1032, 1024, "32x128"),       # ragged M, N: 81 tiles of 64x128, 162 of 32x128
     (1000, 2056, 1040, "64x128"),      # 136 tiles of 128x128, 272 of 64x128; K tail (register-staged)
     (1000, 2056, 1024, "64x128"),      # ragged M, N, whole K stages (direct to LDS)
-    (2048, 2048, 256, "128x128"),      # 256 tiles of 128x128: 128x128 tiles
+    (2048, 2048, 256, "64x128"),       # 256 tiles of 128x128, one per CU: 64x128 (direct to LDS)
+    (2048, 2048, 272, "128x128"),      # the same with a K tail: 128x128 (register-staged)
     (2000, 2056, 272, "128x128"),      # ragged, 272 tiles, a K tail (register-staged)
     (2000, 2056, 384, "128x128"),      # ragged, whole K stages (direct to LDS)
 ])
 @pytest.mark.parametrize("out", ["bf16", "fp32"])
 def test_small_product_tile_shapes(M, N, K, cfg, out):
     """Products below 256^3 outputs run the small kernels: with fewer 128x128
-    tiles than CUs they take 64x128 tiles, and with no more 64x128 tiles than
-    CUs 32x128 tiles (direct-to-LDS kernel only; the register-staged kernel
-    keeps 64x128); with whole 128-byte K stages the operand stages go
-    straight into LDS, otherwise through registers.  Every
-    output of each tile shape and kernel against the oracle, with bias (bf16)
-    or without (fp32)."""
+    tiles than CUs they take 64x128 tiles (the direct-to-LDS kernel also with
+    exactly one per CU), and with no more 64x128 tiles than CUs 32x128 tiles
+    (direct-to-LDS kernel only); with whole 128-byte K stages the operand
+    stages go straight into LDS, otherwise through registers.  Every output
+    of each tile shape and kernel against the oracle, with bias (bf16) or
+    without (fp32)."""
     A = workloads.random_fp8_codes((M, K), M + 3, 0)
     B = workloads.random_fp8_codes((N, K), N + 5, 1)
     sa, sb = 1.0 / 29.0, 5.0 / 448.0
