@@ -38,9 +38,8 @@
 //     multiple of 16 only: 64-byte stages in three LDS buffers, loaded
 //     through registers, K tails read as zero through the buffer range check.
 //   * gemm_nt_sdma_kernel -- small products with K % 128 == 0 and 32-bit
-//     operand offsets: 128 x 128 tiles (64 x 128 when there would be fewer
-//     tiles than CUs, 32 x 128 when 64 x 128 tiles would be no more than the
-//     CUs), one workgroup per tile, v_mfma_f32_16x16x128_f8f6f4,
+//     operand offsets: 128 x 128 tiles (64 x 128 when there would be no
+//     more tiles than CUs), one workgroup per tile, v_mfma_f32_16x16x128_f8f6f4,
 //     operand stages written into LDS by buffer loads with the LDS flag, two
 //     or three stages in flight.
 //   * gemm_nt_kernel -- the other small products (K tails, K = 128, 64-bit
@@ -1725,9 +1724,7 @@ hipError_t launch_cfg(const uint8_t *A, const uint8_t *B, int M, int N, int K, c
 // LDS stages of the direct-to-LDS small kernel per tile height: 72 KiB and
 // 64 KiB, so two workgroups share a CU (measured on MI355X: two 128-row
 // stages of 32 KiB beat three, which leave one workgroup per CU, by 10-40%;
-// two, three or four 64-row stages are within a few percent, and three or
-// four 32-row stages of 20 KiB).
-constexpr int SDMA_STAGES_32 = 3;
+// two, three or four 64-row stages are within a few percent).
 constexpr int SDMA_STAGES_64 = 3;
 constexpr int SDMA_STAGES_128 = 2;
 
@@ -1735,7 +1732,7 @@ template <int BM, int FA, int FB, int OUT, bool HAS_BIAS>
 hipError_t launch_sdma(const uint8_t *A, const uint8_t *B, int M, int N, int K, const float *sa,
                        const float *sb, const uint16_t *bias, void *C, const QOut &qo,
                        hipStream_t stream) {
-    constexpr int NS = BM == 32 ? SDMA_STAGES_32 : (BM == 64 ? SDMA_STAGES_64 : SDMA_STAGES_128);
+    constexpr int NS = BM == 64 ? SDMA_STAGES_64 : SDMA_STAGES_128;
     auto kern = gemm_nt_sdma_kernel<BM, NS, FA, FB, OUT, HAS_BIAS>;
     constexpr int lds_bytes = NS * (BM + 128) * BK;
     static std::atomic<uint64_t> lds_enabled{0};
@@ -1755,8 +1752,8 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
                       const QOut &qo, hipStream_t stream, void *ws = nullptr,
                       int64_t ws_bytes = 0) {
     // Large problems: 256 x 256 tiles, four waves of 128 x 128 (32x32x64
-    // instructions); small ones: 128 x 128, 64 x 128 or 32 x 128 tiles
-    // (16x16x128 instructions).
+    // instructions); small ones: 128 x 128 or 64 x 128 tiles (16x16x128
+    // instructions).
     // The large kernel addresses operands with 32-bit buffer offsets.
     // It also needs at least four 64-byte K stages.
     const bool fits32 = (M + 256) * K < ((int64_t)1 << 31) && (N + 256) * K < ((int64_t)1 << 31);
@@ -1793,23 +1790,15 @@ hipError_t launch_fmt(const uint8_t *A, const uint8_t *B, int64_t M, int64_t N, 
                                                  qo, stream);
     // Small problems with fewer 128 x 128 tiles than CUs (few tokens, narrow
     // outputs: e.g. 1024 x 2048 with K = 8192 has 128) take 64 x 128 tiles,
-    // twice as many, so that more CUs share the K loop; with no more 64 x 128
-    // tiles than CUs, the direct-to-LDS kernel halves them again: its 32-row
-    // tiles put two workgroups (two waves per SIMD) on a CU, or spread the
-    // product over more CUs (measured: 1024 x 1024 x 4096 17.3 -> 14.4 us,
-    // 512 x 2048 x 2048 10.3 -> 8.6, 1024 x 2048 x 2048 12.2 -> 11.8).
+    // twice as many, so that more CUs share the K loop.
     const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
     const bool half = tiles128 < cus;
-    const bool quarter = ((M + 63) / 64) * ((N + 127) / 128) <= cus;
     // Whole 128-byte K stages and 32-bit operand offsets: the operand stages
     // go straight into LDS.  Exactly one 128 x 128 tile per CU also takes
     // 64-row tiles there, two per CU (1024 x 4096 x 2048: 15.9 -> 14.7 us,
     // 2048 x 2048 x 2048: 16.0 -> 14.7); at 1.5 or 2 tiles per CU the
     // 128-row tiles stay faster (1024 x 6144 x 2048: 20.5 against 23.7).
     if (fits32 && K >= 256 && K % 128 == 0) {
-        if (quarter)
-            return launch_sdma<32, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
-                                                          bias, C, qo, stream);
         if (tiles128 <= cus)
             return launch_sdma<64, FA, FB, OUT, HAS_BIAS>(A, B, (int)M, (int)N, (int)K, sa, sb,
                                                           bias, C, qo, stream);

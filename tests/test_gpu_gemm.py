@@ -56,8 +56,8 @@ def test_fwd_shapes_formats(M, N, K, fa, fb):
 
 
 @pytest.mark.parametrize("M,N,K,cfg", [
-    (1024, 2048, 8192, "32x128"),      # 256 tiles of 64x128 <= 256 CUs: 32x128 tiles
-    (520, 1032, 1024, "32x128"),       # ragged M, N: 81 tiles of 64x128, 162 of 32x128
+    (1024, 2048, 8192, "64x128"),      # 128 tiles of 128x128 < 256 CUs: 64x128 tiles
+    (520, 1032, 1024, "64x128"),       # ragged M, N: 45 tiles of 128x128, 81 of 64x128
     (1000, 2056, 1040, "64x128"),      # 136 tiles of 128x128, 272 of 64x128; K tail (register-staged)
     (1000, 2056, 1024, "64x128"),      # ragged M, N, whole K stages (direct to LDS)
     (2048, 2048, 256, "64x128"),       # 256 tiles of 128x128, one per CU: 64x128 (direct to LDS)
@@ -69,9 +69,8 @@ def test_fwd_shapes_formats(M, N, K, fa, fb):
 def test_small_product_tile_shapes(M, N, K, cfg, out):
     """Products below 256^3 outputs run the small kernels: with fewer 128x128
     tiles than CUs they take 64x128 tiles (the direct-to-LDS kernel also with
-    exactly one per CU), and with no more 64x128 tiles than CUs 32x128 tiles
-    (direct-to-LDS kernel only); with whole 128-byte K stages the operand
-    stages go straight into LDS, otherwise through registers.  Every output
+    exactly one per CU); with whole 128-byte K stages the operand stages go
+    straight into LDS, otherwise through registers.  Every output
     of each tile shape and kernel against the oracle, with bias (bf16) or
     without (fp32)."""
     A = workloads.random_fp8_codes((M, K), M + 3, 0)

@@ -313,7 +313,7 @@ def test_large_path_nan_rows_and_a_scale_outside_the_folding_range():
 def test_direct_to_lds_small_kernel_codes_equal_register_staged(M, N):
     """Both small kernels run the same MFMA sequence and the same FP8
     epilogue, so codes, amax and scale-inverse agree bit for bit: K = 2048
-    takes the direct-to-LDS kernel (32 x 128 tiles for 1000 x 2048, 128 x 128
+    takes the direct-to-LDS kernel (64 x 128 tiles for 1000 x 2048, 128 x 128
     for 1040 x 4112), the same operands with 16 zero columns appended
     (K = 2064, a K tail) the register-staged one."""
     K = 2048
